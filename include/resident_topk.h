@@ -1,0 +1,158 @@
+/*
+ * resident_topk.h -- C ABI of libresident_topk: exact brute-force top-K over a
+ * device-resident fp32 corpus on an AMD Instinct MI355X (gfx950).
+ *
+ * The method ("GPU-Resident Top-K for Agentic RAG", A. Banerjee):
+ *   - the corpus is copied into device memory once and stays there (section 3,
+ *     "keep the corpus on the GPU"; section 4, Step 1);
+ *   - per query, every corpus row is scored by inner product (section 4, Step 2),
+ *     each block of rows keeps its own best-K list (Step 3), and the per-block
+ *     lists are merged into the global best-K (Step 4);
+ *   - only K indices and K scores come back (section 3; section 4, Step 6).
+ * The order is the pages' comparator (section 3, "Problem B"): a larger score
+ * wins; on an exact tie (float ==, so -0.0 ties +0.0) the lower index wins.
+ * The same two-stage selector is exported as a plain top-K over raw int32/fp32
+ * arrays ("CUDA Programming Model Series 9: Efficient TopK, two-stage
+ * reduction kernel design", sections 2 and 3: per-block partial top-K, then a
+ * second-stage merge).
+ *
+ * Conventions for every entry point
+ *   - Pointers named "device" must point to device memory of the engine's GPU
+ *     (hipMalloc, or a torch CUDA tensor).  They stay owned by the caller and
+ *     must remain valid until the work queued on `stream` has finished.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     search_resident and topk_select only enqueue work; the caller
+ *     synchronises the stream before reading outputs.
+ *   - All device memory the engine needs is allocated by rt_engine_create.  No
+ *     other entry point allocates (the pages' "Problem C": no allocation on the
+ *     hot path).
+ *   - Argument errors are detected on the host before anything is enqueued;
+ *     outputs are then left untouched.
+ *   - One engine runs one search or select at a time: calls on one engine that
+ *     overlap on different streams race on the engine's scratch memory.
+ *   - Results are best-first.  Indices are int32 (0-based row / element
+ *     positions), so n is limited to 2^31 - 1.
+ *   - Inputs must be NaN-free; the comparator does not order NaN.
+ */
+#ifndef RESIDENT_TOPK_H
+#define RESIDENT_TOPK_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct rt_engine rt_engine; /* opaque; owns every device buffer */
+
+typedef enum {
+    RT_OK = 0,
+    RT_EINVAL = 1, /* bad argument: null pointer, size out of range, k > n, ... */
+    RT_ESTATE = 2, /* wrong state: search before upload, dimension mismatch */
+    RT_ENOMEM = 3, /* device allocation failed in rt_engine_create */
+    RT_EHIP = 4    /* a HIP runtime call failed; see rt_last_hip_error */
+} rt_status;
+
+typedef enum { RT_DTYPE_INT32 = 0, RT_DTYPE_FLOAT32 = 1 } rt_dtype;
+
+/*
+ * Create an engine on HIP device `device` and allocate, once, everything later
+ * calls need, sized for the worst case: a corpus of max_n x max_d fp32, results
+ * up to max_k per query, batches up to max_q queries ("GPU-Resident Top-K for
+ * Agentic RAG", section 3 "Problem C" and section 4 Step 0: all device
+ * allocations happen at engine initialisation).
+ * Limits: 1 <= max_n <= 2^31-1; 1 <= max_d <= 65536; 1 <= max_k <= 1024;
+ * 1 <= max_q <= 32.  On success *out receives the engine (RT_OK); otherwise
+ * *out is set to NULL and RT_EINVAL / RT_ENOMEM / RT_EHIP is returned.
+ */
+rt_status rt_engine_create(int64_t max_n, int32_t max_d, int32_t max_k, int32_t max_q,
+                           int32_t device, rt_engine **out);
+
+/* Free every device buffer of the engine (waits for its pending work).  NULL is
+ * ignored. */
+void rt_engine_destroy(rt_engine *e);
+
+/*
+ * Copy an n x d row-major fp32 corpus into the engine's device memory and make
+ * it the resident corpus, replacing any previous one ("GPU-Resident Top-K for
+ * Agentic RAG", section 4, Step 1).  `corpus` may be host or device memory
+ * (hipMemcpyDefault); the caller keeps ownership.  Synchronous: when it returns
+ * RT_OK the copy is complete.  RT_EINVAL if e or corpus is NULL, n < 1,
+ * n > max_n, d < 1 or d > max_d (the pages return "invalid value" for
+ * N > max_n or D > max_d).  On failure the previous corpus stays resident
+ * unless the copy itself failed (RT_EHIP), in which case no corpus is resident.
+ */
+rt_status upload_corpus_rowmajor(rt_engine *e, const float *corpus, int64_t n, int32_t d);
+
+/*
+ * Exact top-k by inner product for q queries against the resident corpus
+ * ("GPU-Resident Top-K for Agentic RAG", section 4, Steps 2-5).
+ *   queries    device, q x d fp32 row-major, d = the resident dimension
+ *   out_idx    device, q x k int32: row indices, best-first per query
+ *   out_scores device, q x k fp32: the matching scores (fp32 dot products)
+ * Order: larger score first, exact ties to the lower row index.
+ * RT_EINVAL: null pointer, q < 1, q > max_q, k < 1, k > max_k, k > n.
+ * RT_ESTATE: no corpus resident.  RT_EHIP: a launch failed.
+ * Asynchronous on `stream`.
+ */
+rt_status search_resident(rt_engine *e, const float *queries, int32_t q, int32_t k,
+                          int32_t *out_idx, float *out_scores, void *stream);
+
+/*
+ * Plain top-k of a raw device array, no scoring ("CUDA Programming Model
+ * Series 9: Efficient TopK", sections 2-3: two-stage selection).
+ *   values     device, n elements of `dtype` (RT_DTYPE_INT32 or
+ *              RT_DTYPE_FLOAT32), 4-byte aligned
+ *   out_idx    device, k int32: element positions, best-first
+ *   out_values device, k elements of `dtype`: the selected values, bit-for-bit
+ *              copies of the input elements
+ * Order: larger value first (int32 compared as integers, fp32 as floats so -0.0
+ * ties +0.0), ties to the lower position.
+ * RT_EINVAL: null pointer, unknown dtype, misaligned values, n < 1,
+ * n > 2^31-1, k < 1, k > max_k, k > n.  Does not need a resident corpus.
+ * Asynchronous on `stream`.
+ */
+rt_status topk_select(rt_engine *e, const void *values, int32_t dtype, int64_t n, int32_t k,
+                      int32_t *out_idx, void *out_values, void *stream);
+
+/* Static, human-readable name of a status code. */
+const char *rt_status_string(rt_status s);
+
+/* The last hipError_t value recorded by the engine (0 if none). */
+int32_t rt_last_hip_error(const rt_engine *e);
+
+/*
+ * Kernel timing for measurement.  While enabled (on != 0), every search or
+ * select records HIP events on its stream around its two stages; after the
+ * stream has finished, rt_profile_read returns the last call's stage durations
+ * in milliseconds: [0] = partial stage (scoring / streaming selection, for a
+ * batch also the batched scoring kernel), [1] = merge stage, [2] = batched
+ * scoring kernel alone (0 when the call had none).  The events are created by
+ * rt_engine_create.  RT_EINVAL on NULL arguments.
+ */
+rt_status rt_profile_enable(rt_engine *e, int32_t on);
+rt_status rt_profile_read(rt_engine *e, float *ms3);
+
+/*
+ * Engine limits and state, for callers and tests: out7 receives
+ * [max_n, max_d, max_k, max_q, resident_n, resident_d, device].
+ */
+rt_status rt_engine_info(const rt_engine *e, int64_t *out7);
+
+/*
+ * Host-side argument checks, exported so they can be tested without a GPU.
+ * They apply exactly the rules the entry points above apply before enqueuing
+ * anything, given the engine limits and resident sizes as plain numbers
+ * (resident_n = 0 means no corpus).  Pointers are only tested for NULL.
+ */
+rt_status rt_check_create(int64_t max_n, int32_t max_d, int32_t max_k, int32_t max_q);
+rt_status rt_check_upload(int64_t max_n, int32_t max_d, const void *corpus, int64_t n, int32_t d);
+rt_status rt_check_search(int32_t max_k, int32_t max_q, int64_t resident_n, const void *queries,
+                          int32_t q, int32_t k, const void *out_idx, const void *out_scores);
+rt_status rt_check_select(int32_t max_k, const void *values, int32_t dtype, int64_t n, int32_t k,
+                          const void *out_idx, const void *out_values);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RESIDENT_TOPK_H */

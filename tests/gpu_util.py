@@ -1,0 +1,67 @@
+"""Helpers shared by the GPU parity tests: the acceptance rules for float
+retrieval and exact top-K, applied to HIP results against the CPU oracle."""
+import numpy as np
+
+REL_TOL = 1e-4  # float retrieval: scores within 1e-4 relative of the oracle
+
+
+def _rel_ok(g, o, tol=REL_TOL):
+    return np.abs(g - o) <= tol * np.maximum(np.abs(o), 1e-30)
+
+
+def check_retrieval(g_idx, g_sc, o_idx, o_sc, corpus, query, oracle_mod, tol=REL_TOL):
+    """Float retrieval acceptance for one query.
+
+    R1  the GPU list is sorted under the comparator on its own fp32 scores;
+    R2  each GPU score is within tol of the oracle's score of the same row and
+        of the oracle's score at the same rank;
+    R3  rows in the symmetric difference of the two index sets have oracle
+        scores within tol of the oracle's k-th score (boundary near-ties);
+    R4  indices are distinct and in range.
+    """
+    g_idx = np.asarray(g_idx).astype(np.int64)
+    g_sc = np.asarray(g_sc).astype(np.float32)
+    k = o_idx.shape[0]
+    n = corpus.shape[0]
+    assert g_idx.shape == (k,) and g_sc.shape == (k,)
+    # R4
+    assert np.all((g_idx >= 0) & (g_idx < n)), "index out of range"
+    assert np.unique(g_idx).size == k, "duplicate indices"
+    # R1
+    for j in range(k - 1):
+        a, b = g_sc[j], g_sc[j + 1]
+        assert a > b or (a == b and g_idx[j] < g_idx[j + 1]), f"not sorted at {j}"
+    # R2
+    o_of_g = oracle_mod.scores(corpus[g_idx], query)
+    assert np.all(_rel_ok(g_sc.astype(np.float64), o_of_g, tol)), "score differs from the oracle's score of that row"
+    assert np.all(_rel_ok(g_sc.astype(np.float64), o_sc, tol)), "score differs from the oracle's score at that rank"
+    # R3
+    diff = np.setxor1d(g_idx, o_idx.astype(np.int64))
+    if diff.size:
+        o_k = o_sc[-1]
+        o_diff = oracle_mod.scores(corpus[diff], query)
+        assert np.all(_rel_ok(o_diff, np.full_like(o_diff, o_k), tol)), \
+            f"index sets differ away from the k-th boundary: {diff[:8]}"
+
+
+def check_exact_topk_property(g_idx, g_val, values):
+    """Exactness of a raw top-k from properties that pin it uniquely: the list is
+    sorted under the comparator, indices are distinct and hold the returned
+    values, and exactly k-1 elements of the whole array beat the k-th entry."""
+    g_idx = np.asarray(g_idx).astype(np.int64)
+    g_val = np.asarray(g_val)
+    k = g_idx.shape[0]
+    v = values
+    assert np.unique(g_idx).size == k
+    assert np.array_equal(v[g_idx].view(np.uint32), g_val.view(np.uint32))
+    if v.dtype == np.float32:
+        key = v.astype(np.float64)
+        gk = g_val.astype(np.float64)
+    else:
+        key = v.astype(np.int64)
+        gk = g_val.astype(np.int64)
+    for j in range(k - 1):
+        assert gk[j] > gk[j + 1] or (gk[j] == gk[j + 1] and g_idx[j] < g_idx[j + 1]), j
+    last_v, last_i = gk[-1], g_idx[-1]
+    better = np.count_nonzero(key > last_v) + np.count_nonzero(key[:last_i] == last_v)
+    assert better == k - 1, f"{better} elements beat the k-th entry (expected {k - 1})"

@@ -1,0 +1,258 @@
+"""Parity of the HIP path with the CPU oracle at sizes the oracle finishes in
+seconds (several tiles, ragged tails, every kernel variant), plus edge cases.
+
+Float retrieval follows rules R1-R4 (gpu_util.check_retrieval); integer and
+exact-arithmetic cases are compared bit for bit, in order."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import check_exact_topk_property, check_retrieval
+from top_search_resident_amd import ResidentTopK, ResidentTopKError, workloads
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+MAX_N, MAX_D, MAX_K, MAX_Q = 200_000, 3072, 1024, 32
+
+
+@pytest.fixture(scope="module")
+def eng():
+    assert torch.cuda.is_available(), "a GPU is required for the parity tests"
+    e = ResidentTopK(MAX_N, MAX_D, MAX_K, MAX_Q, device=0)
+    yield e
+    e.close()
+
+
+def _search(eng, corpus, queries, k):
+    eng.upload_corpus_rowmajor(corpus)
+    q = torch.from_numpy(np.ascontiguousarray(queries)).cuda()
+    idx, sc = eng.search_resident(q, k)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), sc.cpu().numpy()
+
+
+def _check_against_oracle(eng, corpus, queries, k):
+    g_idx, g_sc = _search(eng, corpus, queries, k)
+    o_idx, o_sc = oracle.search(corpus, queries, k)
+    for qi in range(queries.shape[0]):
+        check_retrieval(g_idx[qi], g_sc[qi], o_idx[qi], o_sc[qi], corpus, queries[qi], oracle)
+    return g_idx, g_sc, o_idx, o_sc
+
+
+# Shapes that exercise every scoring variant: group widths 64/32/16/1 and
+# loads-per-lane 1/2/3/4/6/8 on the vector path, the scalar path for d % 4 != 0
+# and for d > 2048, ragged row counts, and list sizes 64..1024.
+@pytest.mark.parametrize("n,d,k", [
+    (10_000, 384, 8), (12_345, 1024, 8), (12_345, 1024, 100), (7_001, 768, 32), (3_333, 128, 64),
+    (5_000, 256, 65), (4_099, 1536, 128), (2_050, 2048, 129), (9_999, 4, 7), (1_000, 12, 3),
+    (6_000, 100, 16), (3_001, 3000, 10), (20_000, 64, 256), (30_000, 96, 512), (40_000, 384, 1024),
+    (1, 384, 1), (5, 8, 5), (63, 32, 63), (64, 1024, 64), (65, 768, 65), (1_000, 384, 1_000),
+])
+def test_single_query_gaussian(eng, n, d, k):
+    corpus = workloads.gaussian_rows(n, d, config_id=100 + d % 97, stream=0)
+    q = workloads.gaussian_rows(1, d, config_id=100 + d % 97, stream=1)
+    _check_against_oracle(eng, corpus, q, k)
+
+
+@pytest.mark.parametrize("n,d,k", [(20_000, 768, 32), (5_000, 100, 40), (3_000, 1024, 1024)])
+def test_exact_arithmetic_is_bit_exact(eng, n, d, k):
+    """Small-integer inputs make every fp32 dot product exact; the answer must then
+    equal the oracle's in indices and scores, including the order of exact ties."""
+    corpus = workloads.small_int_matrix(n, d, config_id=7, stream=d)
+    q = workloads.small_int_matrix(3, d, config_id=7, stream=d + 1)
+    for qi in range(3):
+        g_idx, g_sc = _search(eng, corpus, q[qi:qi + 1], k)
+        o_idx, o_sc = oracle.search(corpus, q[qi:qi + 1], k)
+        assert np.array_equal(g_idx, o_idx), (qi, g_idx[0, :10], o_idx[0, :10])
+        assert np.array_equal(g_sc.astype(np.float64), o_sc), qi
+
+
+def test_duplicate_rows_tie_by_index(eng):
+    """Identical rows anywhere in the corpus get bit-identical scores, so the lower
+    index wins the tie exactly as in the oracle."""
+    n, d, k = 50_000, 1024, 32
+    corpus = workloads.gaussian_rows(n, d, config_id=11)
+    q = workloads.gaussian_rows(1, d, config_id=11, stream=1)
+    best = int(np.argmax(corpus.astype(np.float64) @ q[0].astype(np.float64)))
+    rng = np.random.default_rng(3)
+    for pos in rng.choice(n, 20, replace=False):
+        corpus[pos] = corpus[best]
+    g_idx, g_sc = _search(eng, corpus, q, k)
+    dup = sorted(set(np.nonzero((corpus == corpus[best]).all(axis=1))[0].tolist()))
+    assert list(g_idx[0, :len(dup)]) == dup
+    assert np.unique(g_sc[0, :len(dup)]).size == 1
+    o_idx, o_sc = oracle.search(corpus, q, k)
+    check_retrieval(g_idx[0], g_sc[0], o_idx[0], o_sc[0], corpus, q[0], oracle)
+
+
+def test_planted_near_ties(eng):
+    """Mid-scale recipe at reduced size: 0.5% of rows planted around the query
+    anchor, so the k-th boundary sits inside a dense cluster."""
+    corpus, qs = workloads.retrieval_inputs("c2_50k_768", queries=6)
+    for k in (8, 32):
+        _check_against_oracle(eng, corpus, qs, k)
+
+
+@pytest.mark.parametrize("q,d,k", [(2, 768, 100), (7, 1024, 8), (32, 768, 1024), (32, 384, 100),
+                                   (5, 100, 20), (3, 2048, 16), (32, 1024, 1)])
+def test_batched_queries(eng, q, d, k):
+    """Batches go through the MFMA scorer when d % 4 == 0 and d <= 1024, else
+    through the vector path once per query."""
+    n = 20_011
+    corpus = workloads.gaussian_rows(n, d, config_id=55, stream=0)
+    qs = workloads.gaussian_rows(q, d, config_id=55, stream=1)
+    _check_against_oracle(eng, corpus, qs, k)
+
+
+def test_batched_exact_arithmetic(eng):
+    corpus = workloads.small_int_matrix(9_000, 256, config_id=8)
+    qs = workloads.small_int_matrix(32, 256, config_id=8, stream=1)
+    g_idx, g_sc = _search(eng, corpus, qs, 200)
+    o_idx, o_sc = oracle.search(corpus, qs, 200)
+    assert np.array_equal(g_idx, o_idx)
+    assert np.array_equal(g_sc.astype(np.float64), o_sc)
+
+
+def test_deterministic_repeat(eng):
+    corpus = workloads.gaussian_rows(60_000, 768, config_id=12)
+    qs = workloads.gaussian_rows(4, 768, config_id=12, stream=1)
+    a = _search(eng, corpus, qs, 100)
+    b = _search(eng, corpus, qs, 100)
+    eng.upload_corpus_rowmajor(corpus)
+    q1 = torch.from_numpy(qs[:1]).cuda()
+    c_idx, c_sc = eng.search_resident(q1, 100)
+    torch.cuda.synchronize()
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
+def test_stream_argument(eng):
+    corpus = workloads.gaussian_rows(8_000, 384, config_id=13)
+    q = workloads.gaussian_rows(1, 384, config_id=13, stream=1)
+    eng.upload_corpus_rowmajor(corpus)
+    s = torch.cuda.Stream()
+    qd = torch.from_numpy(q).cuda()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s):
+        idx, sc = eng.search_resident(qd, 8, stream=s)
+    s.synchronize()
+    o_idx, o_sc = oracle.search(corpus, q, 8)
+    check_retrieval(idx.cpu().numpy()[0], sc.cpu().numpy()[0], o_idx[0], o_sc[0], corpus, q[0], oracle)
+
+
+# ---------------------------------------------------------------- raw top-K
+
+def _select(eng, values, k, offset=0):
+    buf = torch.from_numpy(np.ascontiguousarray(values)).cuda()
+    view = buf[offset:]
+    idx, vals = eng.topk_select(view, k)
+    torch.cuda.synchronize()
+    return idx.cpu().numpy(), vals.cpu().numpy()
+
+
+@pytest.mark.parametrize("n,k", [(1, 1), (2, 2), (5, 3), (63, 20), (64, 64), (65, 50), (1_000, 1_000),
+                                 (100_003, 20), (1_000_000, 50), (3_000_000, 1024), (777_777, 129)])
+def test_topk_int32_matches_oracle(eng, n, k):
+    v = workloads.int32_values(n=n, config_id=40 + k % 7)
+    g_idx, g_val = _select(eng, v, k)
+    o_idx, o_val = oracle.topk(v, k)
+    assert np.array_equal(g_idx, o_idx)
+    assert np.array_equal(g_val, o_val)
+
+
+@pytest.mark.parametrize("offset", [1, 2, 3, 5])
+def test_topk_int32_misaligned_views(eng, offset):
+    v = workloads.int32_values(n=500_000 + offset, config_id=41)
+    g_idx, g_val = _select(eng, v, 50, offset=offset)
+    o_idx, o_val = oracle.topk(v[offset:], 50)
+    assert np.array_equal(g_idx, o_idx)
+    assert np.array_equal(g_val, o_val)
+
+
+def test_topk_int32_special_arrays(eng):
+    n = 300_000
+    cases = {
+        "all_equal": np.full(n, 7, dtype=np.int32),
+        "int_min": np.full(n, np.iinfo(np.int32).min, dtype=np.int32),
+        "int_max": np.full(n, np.iinfo(np.int32).max, dtype=np.int32),
+        "descending": np.arange(n, 0, -1).astype(np.int32),
+        "ascending": np.arange(n).astype(np.int32),
+        "periodic": (np.arange(n) % 1000).astype(np.int32),
+        "two_values": np.where(np.arange(n) % 3 == 0, -1, 1).astype(np.int32),
+    }
+    for name, v in cases.items():
+        for k in (1, 50, 1024):
+            g_idx, g_val = _select(eng, v, k)
+            o_idx, o_val = oracle.topk(v, k)
+            assert np.array_equal(g_idx, o_idx), (name, k)
+            assert np.array_equal(g_val, o_val), (name, k)
+
+
+def test_topk_int32_boundary_ties(eng):
+    """Copies of the top-(k+5) values scattered to random positions make the k-th
+    boundary an exact tie that only the index can break."""
+    rng = np.random.default_rng(5)
+    for k in (20, 50):
+        v = workloads.int32_values(n=2_000_000, config_id=42)
+        top = np.sort(v)[::-1][:k + 5]
+        v[rng.choice(v.size, 3 * (k + 5), replace=False)] = np.repeat(top, 3)
+        g_idx, g_val = _select(eng, v, k)
+        o_idx, o_val = oracle.topk(v, k)
+        assert np.array_equal(g_idx, o_idx)
+        assert np.array_equal(g_val, o_val)
+
+
+def test_topk_float32_special_values(eng):
+    rng = np.random.default_rng(6)
+    v = rng.standard_normal(400_000).astype(np.float32)
+    specials = np.array([0.0, -0.0, np.inf, -np.inf, 1e-45, -1e-45, 3.4e38, -3.4e38], dtype=np.float32)
+    v[rng.choice(v.size, 4000, replace=False)] = np.tile(specials, 500)
+    v[rng.choice(v.size, 2000, replace=False)] = v[rng.choice(v.size, 2000, replace=False)]
+    for k in (1, 17, 100, 1024):
+        g_idx, g_val = _select(eng, v, k)
+        o_idx, o_val = oracle.topk(v, k)
+        assert np.array_equal(g_idx, o_idx), k
+        assert np.array_equal(g_val.view(np.uint32), o_val.view(np.uint32)), k
+    zeros = np.where(np.arange(1000) % 2 == 0, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+    g_idx, g_val = _select(eng, zeros, 10)
+    assert list(g_idx) == list(range(10)), "-0.0 must tie +0.0 and fall to the index"
+    assert np.array_equal(g_val.view(np.uint32), zeros[:10].view(np.uint32)), "value bits must be preserved"
+
+
+def test_topk_float32_random(eng):
+    v = workloads.float32_values(2_000_003)
+    for k in (8, 100, 1000):
+        g_idx, g_val = _select(eng, v, k)
+        o_idx, o_val = oracle.topk(v, k)
+        assert np.array_equal(g_idx, o_idx)
+        assert np.array_equal(g_val.view(np.uint32), o_val.view(np.uint32))
+        check_exact_topk_property(g_idx, g_val, v)
+
+
+# ---------------------------------------------------------------- error paths
+
+def test_error_paths():
+    e = ResidentTopK(1000, 64, 32, 4, device=0)
+    try:
+        q = torch.zeros((1, 64), dtype=torch.float32, device="cuda")
+        with pytest.raises(ResidentTopKError) as ei:
+            e.search_resident(q, 8)  # nothing resident
+        assert ei.value.status == 2
+        with pytest.raises(ResidentTopKError) as ei:
+            e.upload_corpus_rowmajor(np.zeros((1001, 64), np.float32))  # n > max_n
+        assert ei.value.status == 1
+        e.upload_corpus_rowmajor(np.ones((10, 64), np.float32))
+        with pytest.raises(ResidentTopKError):
+            e.search_resident(q, 33)  # k > max_k
+        with pytest.raises(ResidentTopKError):
+            e.search_resident(q, 11)  # k > n
+        with pytest.raises(ResidentTopKError):
+            e.search_resident(torch.zeros((5, 64), dtype=torch.float32, device="cuda"), 2)  # q > max_q
+        idx, sc = e.search_resident(q, 10)  # k == n: a full sort of equal scores
+        torch.cuda.synchronize()
+        assert list(idx.cpu().numpy()[0]) == list(range(10))
+    finally:
+        e.close()
+    with pytest.raises(ResidentTopKError):
+        ResidentTopK(1 << 40, 64, 8, 1)  # beyond the int32 index range

@@ -1,0 +1,155 @@
+"""top_search_resident_amd -- exact resident top-K retrieval on AMD MI355X (gfx950).
+
+A thin binding over the C ABI of ``libresident_topk.so`` (include/resident_topk.h).
+It only marshals arguments: every step of the search runs in the library's HIP
+kernels.  PyTorch supplies device memory and streams.  Importing the package does
+not load the library; constructing an engine does, and fails loudly if the HIP
+library is not built.
+
+    eng = ResidentTopK(max_n=1_000_000, max_d=1024, max_k=128, max_q=32)
+    eng.upload_corpus_rowmajor(corpus)              # once; host or device fp32 [n, d]
+    idx, scores = eng.search_resident(queries, k)   # device fp32 [q, d] -> [q, k] each
+    idx, vals = eng.topk_select(values, k)          # device int32/fp32 [n] -> [k] each
+"""
+import ctypes
+
+from . import _lib
+from ._lib import ResidentTopKError, RT_DTYPE_FLOAT32, RT_DTYPE_INT32
+
+__all__ = ["ResidentTopK", "ResidentTopKError"]
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _check(status, what, eng=None):
+    if status != _lib.RT_OK:
+        hip = _lib.load().rt_last_hip_error(eng) if eng else 0
+        raise ResidentTopKError(status, what, hip)
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class ResidentTopK:
+    """One engine: owns all device memory for a resident corpus of up to
+    max_n x max_d fp32 rows, top-k up to max_k, batches up to max_q queries."""
+
+    def __init__(self, max_n, max_d, max_k=128, max_q=1, device=0):
+        self._lib = _lib.load()
+        self._h = ctypes.c_void_p()
+        st = self._lib.rt_engine_create(int(max_n), int(max_d), int(max_k), int(max_q), int(device),
+                                        ctypes.byref(self._h))
+        _check(st, "rt_engine_create")
+        self.device = int(device)
+        self.max_n, self.max_d, self.max_k, self.max_q = int(max_n), int(max_d), int(max_k), int(max_q)
+
+    # -- lifecycle ---------------------------------------------------------
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            self._lib.rt_engine_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def info(self):
+        out = (ctypes.c_int64 * 7)()
+        _check(self._lib.rt_engine_info(self._h, out), "rt_engine_info")
+        keys = ("max_n", "max_d", "max_k", "max_q", "resident_n", "resident_d", "device")
+        return dict(zip(keys, [int(v) for v in out]))
+
+    # -- the three calls ----------------------------------------------------
+    def upload_corpus_rowmajor(self, corpus):
+        """Copy an [n, d] fp32 row-major corpus (numpy array or torch tensor, host
+        or device) into the engine; synchronous."""
+        if hasattr(corpus, "data_ptr"):
+            torch = _torch()
+            if corpus.dtype != torch.float32 or not corpus.is_contiguous() or corpus.dim() != 2:
+                raise TypeError("corpus must be a contiguous 2-D float32 tensor")
+            ptr, (n, d) = corpus.data_ptr(), tuple(corpus.shape)
+        else:
+            import numpy as np
+            if corpus.dtype != np.float32 or corpus.ndim != 2 or not corpus.flags.c_contiguous:
+                raise TypeError("corpus must be a C-contiguous 2-D float32 array")
+            ptr, (n, d) = corpus.ctypes.data, corpus.shape
+        st = self._lib.upload_corpus_rowmajor(self._h, ctypes.c_void_p(ptr), int(n), int(d))
+        _check(st, "upload_corpus_rowmajor", self._h)
+        self._keep = corpus  # not needed after the synchronous copy; kept only until the next upload
+
+    def search_resident(self, queries, k, out_idx=None, out_scores=None, stream=None):
+        """Exact top-k by inner product.  queries: device fp32 [q, d] or [d].
+        Returns (idx int32 [q, k], scores fp32 [q, k]) on the device, best-first;
+        enqueued on `stream` (default: torch's current stream)."""
+        torch = _torch()
+        if queries.dim() == 1:
+            queries = queries.view(1, -1)
+        if queries.dtype != torch.float32 or not queries.is_cuda or not queries.is_contiguous():
+            raise TypeError("queries must be a contiguous float32 CUDA tensor")
+        q = queries.shape[0]
+        if out_idx is None:
+            out_idx = torch.empty((q, k), dtype=torch.int32, device=queries.device)
+        if out_scores is None:
+            out_scores = torch.empty((q, k), dtype=torch.float32, device=queries.device)
+        if out_idx.dtype != torch.int32 or out_scores.dtype != torch.float32:
+            raise TypeError("out_idx must be int32 and out_scores float32")
+        if out_idx.numel() < q * k or out_scores.numel() < q * k:
+            raise ValueError("output buffers are too small")
+        st = self._lib.search_resident(self._h, ctypes.c_void_p(queries.data_ptr()), int(q), int(k),
+                                       ctypes.c_void_p(out_idx.data_ptr()),
+                                       ctypes.c_void_p(out_scores.data_ptr()), _stream_handle(stream))
+        _check(st, "search_resident", self._h)
+        return out_idx, out_scores
+
+    def topk_select(self, values, k, out_idx=None, out_values=None, stream=None):
+        """Top-k of a raw device int32/fp32 1-D tensor, ties to the lower position.
+        Returns (idx int32 [k], values [k]) on the device, best-first."""
+        torch = _torch()
+        if values.dtype == torch.int32:
+            dt = RT_DTYPE_INT32
+        elif values.dtype == torch.float32:
+            dt = RT_DTYPE_FLOAT32
+        else:
+            raise TypeError("topk_select takes int32 or float32 tensors")
+        if not values.is_cuda or not values.is_contiguous():
+            raise TypeError("values must be a contiguous CUDA tensor")
+        values = values.view(-1)
+        if out_idx is None:
+            out_idx = torch.empty(k, dtype=torch.int32, device=values.device)
+        if out_values is None:
+            out_values = torch.empty(k, dtype=values.dtype, device=values.device)
+        if out_idx.dtype != torch.int32 or out_values.dtype != values.dtype:
+            raise TypeError("out_idx must be int32 and out_values must match the input dtype")
+        if out_idx.numel() < k or out_values.numel() < k:
+            raise ValueError("output buffers are too small")
+        st = self._lib.topk_select(self._h, ctypes.c_void_p(values.data_ptr()), dt, int(values.numel()),
+                                   int(k), ctypes.c_void_p(out_idx.data_ptr()),
+                                   ctypes.c_void_p(out_values.data_ptr()), _stream_handle(stream))
+        _check(st, "topk_select", self._h)
+        return out_idx, out_values
+
+    # -- measurement -----------------------------------------------------------
+    def profile(self, on=True):
+        _check(self._lib.rt_profile_enable(self._h, 1 if on else 0), "rt_profile_enable")
+
+    def profile_read(self):
+        """Stage durations (ms) of the last call: (partial stage, merge stage,
+        batched scoring kernel or 0).  The stream must have finished."""
+        out = (ctypes.c_float * 3)()
+        _check(self._lib.rt_profile_read(self._h, out), "rt_profile_read", self._h)
+        return float(out[0]), float(out[1]), float(out[2])

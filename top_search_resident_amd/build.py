@@ -1,0 +1,49 @@
+"""Build libresident_topk.so for gfx950 with hipcc, in-tree.
+
+Each HIP source is compiled to an object in parallel, then linked into
+``top_search_resident_amd/libresident_topk.so``.  Packed-fp32 instructions are
+disabled on every device compile.
+"""
+import os
+import subprocess
+from concurrent.futures import ThreadPoolExecutor
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+BUILD_DIR = os.path.join(ROOT, "_build")
+LIBRARY = os.path.join(HERE, "libresident_topk.so")
+SOURCES = ["engine.hip", "stream_topk.hip", "merge_topk.hip", "mfma_scores.hip"]
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
+         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+         "-I" + os.path.join(ROOT, "include")]
+
+
+def _run(cmd):
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("build step failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
+    return res
+
+
+def build(verbose=False):
+    os.makedirs(BUILD_DIR, exist_ok=True)
+
+    def compile_one(src):
+        obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
+        _run([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        return obj
+
+    with ThreadPoolExecutor(max(1, min(len(SOURCES), os.cpu_count() or 1))) as ex:
+        objs = list(ex.map(compile_one, SOURCES))
+    tmp = LIBRARY + ".tmp"
+    _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs])
+    os.replace(tmp, LIBRARY)
+    if verbose:
+        print("built", LIBRARY)
+    return LIBRARY
+
+
+if __name__ == "__main__":
+    build(verbose=True)

@@ -1,0 +1,225 @@
+// wave_topk.hpp -- wavefront-level (64-lane) exact top-K building blocks for gfx950.
+//
+// Ordering.  Every candidate is packed into one 64-bit "rank":
+//     rank = (order_key(value) << 32) | (0xFFFFFFFF - index)
+// order_key is a monotone map of the value to uint32 (larger value -> larger
+// key), and the low word is larger for a SMALLER index.  So unsigned 64-bit
+// comparison of ranks is exactly the pages' comparator: a larger score wins and
+// an exact tie goes to the lower index ("GPU-Resident Top-K for Agentic RAG",
+// section 3, "Problem B").  Ranks of distinct elements are distinct, and 0 is
+// below every real rank (real low words are >= 0x80000000 because indices are
+// < 2^31), so 0 serves as the empty-slot sentinel -- the pages' (-inf, INT_MAX)
+// starting point of the merge (section 4, Step 4).
+//
+// fp32 keys: -0.0 is mapped to +0.0's key, because float equality ties the two.
+// int32 keys: flip the sign bit (no negation, so INT32_MIN is safe).
+//
+// A sorted list of Kp = 64*R ranks lives in registers: entry j is lane (j % 64)
+// of register (j / 64), best first.  Candidates are batched 64 at a time,
+// bitonic-sorted across the wave and merged into the list with one bitonic merge
+// (the pages' per-block selector is an O(K^2) single-lane bubble sort, section 3
+// "Problem A"; the 64-lane networks replace it).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rt {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ uint32_t order_key_f32(float x) {
+    uint32_t b = __float_as_uint(x);
+    b = (b == 0x80000000u) ? 0u : b;
+    return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float f32_of_order_key(uint32_t k) {
+    return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+__device__ __forceinline__ uint32_t order_key_i32(int32_t x) { return (uint32_t)x ^ 0x80000000u; }
+
+__device__ __forceinline__ uint64_t make_rank(uint32_t key, uint32_t index) {
+    return ((uint64_t)key << 32) | (uint64_t)(0xffffffffu - index);
+}
+__device__ __forceinline__ uint32_t rank_index(uint64_t r) { return 0xffffffffu - (uint32_t)r; }
+__device__ __forceinline__ uint32_t rank_key(uint64_t r) { return (uint32_t)(r >> 32); }
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
+    const int lo = __shfl_xor((int)(uint32_t)v, m);
+    const int hi = __shfl_xor((int)(uint32_t)(v >> 32), m);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+__device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a > b ? b : a; }
+
+// Number of set bits of `mask` below this lane.
+__device__ __forceinline__ int lanes_below(uint64_t mask) {
+    return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                          __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Make this wave's earlier LDS writes visible to its later LDS reads from other lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Bitonic sort of 64 ranks (one per lane), best first.
+__device__ __forceinline__ uint64_t wave_sort64_desc(uint64_t x) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            const uint64_t y = shfl_xor_u64(x, j);
+            const bool desc_seg = (lane & k) == 0;
+            const bool lower = (lane & j) == 0;
+            x = (lower == desc_seg) ? umax64(x, y) : umin64(x, y);
+        }
+    }
+    return x;
+}
+
+// Sort a bitonic sequence of 64*R ranks (entry j = lane j%64 of register j/64)
+// into best-first order.
+template <int R>
+__device__ __forceinline__ void bitonic_merge_desc(uint64_t (&L)[R]) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int rs = R / 2; rs >= 1; rs >>= 1) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            if ((r & rs) == 0) {
+                const uint64_t a = L[r], c = L[r + rs];
+                L[r] = umax64(a, c);
+                L[r + rs] = umin64(a, c);
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 32; j >= 1; j >>= 1) {
+        const bool lower = (lane & j) == 0;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const uint64_t y = shfl_xor_u64(L[r], j);
+            L[r] = lower ? umax64(L[r], y) : umin64(L[r], y);
+        }
+    }
+}
+
+// L := best 64*R of (L u batch); L sorted best-first, batch sorted best-first
+// (64 entries, one per lane).  Elementwise max of a descending and an ascending
+// sequence keeps the best half and is bitonic.
+template <int R>
+__device__ __forceinline__ void list_absorb64(uint64_t (&L)[R], uint64_t batch_desc) {
+    const uint64_t asc = shfl_xor_u64(batch_desc, 63);  // lane l gets batch[63 - l]
+    L[R - 1] = umax64(L[R - 1], asc);
+    bitonic_merge_desc<R>(L);
+}
+
+// L := best 64*R of (L u M), both sorted best-first with 64*R entries.
+template <int R>
+__device__ __forceinline__ void list_absorb_list(uint64_t (&L)[R], const uint64_t (&M)[R]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) L[r] = umax64(L[r], shfl_xor_u64(M[R - 1 - r], 63));
+    bitonic_merge_desc<R>(L);
+}
+
+// Rank of list entry j (0 if the list has fewer than j+1 real entries).  Every
+// register is read out with readlane and the wanted one picked among the
+// uniform results, so the list is never indexed dynamically (which would push
+// it to scratch memory).
+template <int R>
+__device__ __forceinline__ uint64_t list_entry(const uint64_t (&L)[R], int j) {
+    const int reg = j >> 6;
+    const int src = j & 63;
+    uint64_t v = 0;
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+        const uint64_t t = readlane_u64(L[r], src);
+        v = (r == reg) ? t : v;
+    }
+    return v;
+}
+
+// Per-wave streaming selector.  Candidates are appended to a 128-entry LDS
+// staging buffer private to the wave; every 64 of them are sorted and absorbed
+// into the register list.  `thr` is a rank that some set of >= k already-seen
+// elements all reach or beat, so anything at or below it can never enter the
+// top-k: it starts at 0 and rises to the list's k-th entry and to the shared
+// per-segment value that other waves publish (a global atomic max of their own
+// k-th entries).  The staging buffer and the shared threshold are passed to
+// each call (not stored) so the compiler keeps LDS addressing and keeps the
+// list in registers.
+template <int R>
+struct WaveSelector {
+    uint64_t L[R];
+    uint64_t thr;        // wave-uniform
+    uint64_t published;  // wave-uniform: last value this wave pushed to the shared threshold
+    int pending;         // wave-uniform
+    int k;
+
+    __device__ __forceinline__ void init(int k_) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) L[r] = 0;
+        thr = 0;
+        published = 0;
+        pending = 0;
+        k = k_;
+    }
+
+    __device__ __forceinline__ void absorb_stage_front(uint64_t *__restrict__ stage, int count,
+                                                       uint64_t *__restrict__ shared) {
+        const int lane = lane_id();
+        wave_lds_sync();
+        uint64_t x = (lane < count) ? stage[lane] : 0ull;
+        x = wave_sort64_desc(x);
+        list_absorb64<R>(L, x);
+        const uint64_t kth = list_entry<R>(L, k - 1);
+        if (kth > thr) thr = kth;
+        if (kth > published) {
+            published = kth;
+            if (lane == 0) __hip_atomic_fetch_max(shared, kth, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+    }
+
+    // Offer one rank per lane; `take` must already include rank > thr.
+    __device__ __forceinline__ void offer(uint64_t *__restrict__ stage, uint64_t *__restrict__ shared,
+                                          uint64_t rank, bool take) {
+        const uint64_t m = __ballot(take);
+        if (m == 0) return;
+        const int lane = lane_id();
+        if (take) stage[pending + lanes_below(m)] = rank;
+        pending += __popcll(m);
+        if (pending >= 64) {
+            absorb_stage_front(stage, 64, shared);
+            const int rest = pending - 64;
+            uint64_t t = 0;
+            if (lane < rest) t = stage[64 + lane];
+            wave_lds_sync();
+            if (lane < rest) stage[lane] = t;
+            pending = rest;
+        }
+    }
+
+    __device__ __forceinline__ void refresh(const uint64_t *shared) {
+        const uint64_t g = __hip_atomic_load(shared, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (g > thr) thr = g;
+    }
+
+    __device__ __forceinline__ void finish(uint64_t *__restrict__ stage, uint64_t *__restrict__ shared) {
+        if (pending > 0) absorb_stage_front(stage, pending, shared);
+        pending = 0;
+    }
+};
+
+}  // namespace rt
