@@ -1,0 +1,406 @@
+#!/usr/bin/env python3
+"""Benchmark of exact resident top-K on one MI355X.
+
+Default workload: the 1,000,000 x 1024 fp32 resident corpus (rows iid N(0,1),
+L2-normalised), sequential single queries at K = 8, 32 and 100 -- the
+configuration whose queries/s and p50 latency are the headline metric.  One
+step = one query at each of the three K values (three search_resident calls,
+each synchronised before the next, as an agent issues them).  Queries are
+already resident in HBM when timing starts; the PCIe-inclusive interval
+(query H->D, search, 2K results D->H) is measured separately and reported as
+context, never as `value`.
+
+The dominant kernel (the fused streaming scorer + per-wave top-K) is timed with
+HIP events recorded by the library on the search stream inside the timed
+region; its algorithmic bytes (N*D*4 corpus + D*4 query) over its average
+duration give `roofline.achieved`.
+
+cpu_baseline: the CPU oracle (fp64 dots + full sort) timed on this host's cores
+on a bounded sample of the same queries; the same sample's GPU answers are
+checked against it (R1-R4) before the line is printed.
+
+Other workloads (--workload): c1_10k_384, c2_50k_768, c2_100k_768,
+c4_1e8_int32, c5_q32_500k_768 -- parity-test configurations, available for
+measurement; the default line is c3_1m_1024.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+METRIC = "queries/s + p50 latency at N=1M,D=1024,K∈{8,32,100}; % of HBM peak"
+
+
+def pct(a, p):
+    return float(np.percentile(np.asarray(a), p))
+
+
+def host_cores():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return os.cpu_count() or 1
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def time_search(eng, torch, qdev, ks, steps, warmup, profile=True):
+    """Sequential single queries; returns per-K lists of host latency (us),
+    partial-stage and merge-stage device times (ms)."""
+    n_q = qdev.shape[0]
+    outs = {k: (torch.empty((1, k), dtype=torch.int32, device="cuda"),
+                torch.empty((1, k), dtype=torch.float32, device="cuda")) for k in ks}
+    stream = torch.cuda.current_stream()
+    for i in range(warmup):
+        for k in ks:
+            eng.search_resident(qdev[i % n_q:i % n_q + 1], k, *outs[k], stream=stream)
+    torch.cuda.synchronize()
+    eng.profile(profile)
+    lat = {k: [] for k in ks}
+    part = {k: [] for k in ks}
+    merge = {k: [] for k in ks}
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        q = qdev[i % n_q:i % n_q + 1]
+        for k in ks:
+            s = time.perf_counter_ns()
+            eng.search_resident(q, k, *outs[k], stream=stream)
+            stream.synchronize()
+            lat[k].append((time.perf_counter_ns() - s) / 1e3)
+            if profile:
+                a, b, _ = eng.profile_read()
+                part[k].append(a)
+                merge[k].append(b)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    eng.profile(False)
+    return wall, lat, part, merge
+
+
+def time_end_to_end(eng, torch, qhost, ks, reps):
+    """Pages-style interval: pinned query H->D, search, K idx + K scores D->H."""
+    d = qhost.shape[1]
+    pin_q = torch.empty((1, d), dtype=torch.float32).pin_memory()
+    qdev = torch.empty((1, d), dtype=torch.float32, device="cuda")
+    res = {}
+    stream = torch.cuda.current_stream()
+    for k in ks:
+        oi = torch.empty((1, k), dtype=torch.int32, device="cuda")
+        os_ = torch.empty((1, k), dtype=torch.float32, device="cuda")
+        hi = torch.empty((1, k), dtype=torch.int32).pin_memory()
+        hs = torch.empty((1, k), dtype=torch.float32).pin_memory()
+        ts = []
+        for r in range(reps):
+            pin_q.copy_(torch.from_numpy(qhost[r % qhost.shape[0]:r % qhost.shape[0] + 1]))
+            s = time.perf_counter_ns()
+            qdev.copy_(pin_q, non_blocking=True)
+            eng.search_resident(qdev, k, oi, os_, stream=stream)
+            hi.copy_(oi, non_blocking=True)
+            hs.copy_(os_, non_blocking=True)
+            stream.synchronize()
+            ts.append((time.perf_counter_ns() - s) / 1e3)
+        res[k] = {"p50_us": pct(ts, 50), "p99_us": pct(ts, 99)}
+    return res
+
+
+def cpu_baseline_retrieval(corpus, qhost, kmax, gpu_results, budget_s, max_queries):
+    """Time the oracle on a bounded sample and check the GPU answers of the same
+    queries against it."""
+    import oracle
+    from tests.gpu_util import check_retrieval  # noqa: E402  (test helpers: acceptance rules)
+    times = []
+    t_start = time.perf_counter()
+    nq = 0
+    for qi in range(min(max_queries, qhost.shape[0])):
+        s = time.perf_counter()
+        o_idx, o_sc = oracle.search(corpus, qhost[qi:qi + 1], kmax)
+        times.append(time.perf_counter() - s)
+        for k, (g_idx, g_sc) in gpu_results.items():
+            check_retrieval(g_idx[qi], g_sc[qi], o_idx[0, :k], o_sc[0, :k], corpus, qhost[qi], oracle)
+        nq += 1
+        if time.perf_counter() - t_start > budget_s:
+            break
+    return {"value": nq / sum(times), "unit": "queries/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {nq} queries of the workload at K={kmax} (smaller K are prefixes), fp64 dots + full sort; "
+                      f"GPU answers of the same queries checked against it (R1-R4)",
+            "host_cores": host_cores(), "cpu_model": cpu_model(), "parity": "ok"}
+
+
+def run_retrieval(args, torch, ResidentTopK, workloads):
+    name = args.workload
+    w = workloads.WORKLOADS[name]
+    t = time.perf_counter()
+    corpus, qhost = workloads.retrieval_inputs(name, queries=min(w["queries"], args.num_queries))
+    gen_s = time.perf_counter() - t
+    n, d = corpus.shape
+    ks = tuple(w["ks"])
+    batch = w.get("batch", 1)
+    eng = ResidentTopK(max_n=n, max_d=d, max_k=max(ks), max_q=max(batch, 1))
+    eng.upload_corpus_rowmajor(corpus)
+    qdev = torch.from_numpy(qhost).cuda()
+    torch.cuda.synchronize()
+
+    if batch > 1:
+        return run_batched(args, torch, eng, corpus, qhost, qdev, ks, name, gen_s)
+
+    wall, lat, part, merge = time_search(eng, torch, qdev, ks, args.steps, args.warmup)
+    nq = args.steps * len(ks)
+    qps = nq / wall
+    corpus_bytes = n * d * 4 + d * 4
+    per_k = {}
+    all_part = []
+    for k in ks:
+        dev = np.asarray(part[k]) + np.asarray(merge[k])
+        per_k[str(k)] = {
+            "queries_per_s": len(lat[k]) / (np.sum(lat[k]) / 1e6),
+            "p50_us": pct(lat[k], 50), "p99_us": pct(lat[k], 99),
+            "device_p50_us": pct(dev * 1e3, 50), "device_p99_us": pct(dev * 1e3, 99),
+            "scan_kernel_avg_us": float(np.mean(part[k]) * 1e3),
+            "merge_avg_us": float(np.mean(merge[k]) * 1e3),
+            "scan_kernel_gbs": corpus_bytes / (np.mean(part[k]) * 1e-3) / 1e9,
+            "device_p50_hbm_frac": corpus_bytes / (pct(dev, 50) * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        }
+        all_part += part[k]
+    avg_ms = float(np.mean(all_part))
+    achieved = corpus_bytes / (avg_ms * 1e-3) / 1e9
+    line = {
+        "metric": METRIC if name == "c3_1m_1024" else f"queries/s + p50 latency ({name})",
+        "value": qps, "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+        "config": {"workload": f"{name}: resident {n} x {d} fp32 corpus (Gaussian, L2-normalised rows), "
+                               f"sequential single queries, K in {list(ks)}; one step = one query per K",
+                   "n": n, "d": d, "ks": list(ks), "queries_per_step": len(ks)},
+        "per_k": per_k,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "kernel": "gemv_topk_kernel (fused scoring + per-wave top-K)",
+                     "bytes_per_launch": corpus_bytes, "avg_launch_us": avg_ms * 1e3},
+        "input_gen_s": gen_s,
+    }
+    if args.e2e_reps:
+        line["end_to_end_pcie"] = time_end_to_end(eng, torch, qhost, ks, args.e2e_reps)
+    if not args.no_cpu_baseline:
+        sample = min(args.cpu_queries, qhost.shape[0])
+        gpu_res = {}
+        for k in ks:
+            gi = np.empty((sample, k), np.int32)
+            gs = np.empty((sample, k), np.float32)
+            for qi in range(sample):
+                a, b = eng.search_resident(qdev[qi:qi + 1], k)
+                torch.cuda.synchronize()
+                gi[qi], gs[qi] = a.cpu().numpy()[0], b.cpu().numpy()[0]
+            gpu_res[k] = (gi, gs)
+        line["cpu_baseline"] = cpu_baseline_retrieval(corpus, qhost, max(ks), gpu_res, args.cpu_budget, sample)
+    eng.close()
+    return line
+
+
+def run_batched(args, torch, eng, corpus, qhost, qdev, ks, name, gen_s):
+    n, d = corpus.shape
+    q = qdev.shape[0]
+    stream = torch.cuda.current_stream()
+    outs = {k: (torch.empty((q, k), dtype=torch.int32, device="cuda"),
+                torch.empty((q, k), dtype=torch.float32, device="cuda")) for k in ks}
+    for _ in range(args.warmup):
+        for k in ks:
+            eng.search_resident(qdev, k, *outs[k], stream=stream)
+    torch.cuda.synchronize()
+    eng.profile(True)
+    lat = {k: [] for k in ks}
+    mf = {k: [] for k in ks}
+    part = {k: [] for k in ks}
+    merge = {k: [] for k in ks}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for k in ks:
+            s = time.perf_counter_ns()
+            eng.search_resident(qdev, k, *outs[k], stream=stream)
+            stream.synchronize()
+            lat[k].append((time.perf_counter_ns() - s) / 1e3)
+            a, b, c = eng.profile_read()
+            part[k].append(a)
+            merge[k].append(b)
+            mf[k].append(c)
+    wall = time.perf_counter() - t0
+    eng.profile(False)
+    corpus_bytes = n * d * 4 + q * d * 4
+    flops = 2.0 * n * d * q
+    per_k = {}
+    for k in ks:
+        mfma_ms = float(np.mean(mf[k]))
+        per_k[str(k)] = {"batches_per_s": len(lat[k]) / (np.sum(lat[k]) / 1e6),
+                         "queries_per_s": q * len(lat[k]) / (np.sum(lat[k]) / 1e6),
+                         "p50_us": pct(lat[k], 50), "p99_us": pct(lat[k], 99),
+                         "mfma_kernel_avg_us": mfma_ms * 1e3,
+                         "select_avg_us": float(np.mean(part[k]) - mfma_ms) * 1e3,
+                         "merge_avg_us": float(np.mean(merge[k])) * 1e3,
+                         "mfma_kernel_gbs": corpus_bytes / (mfma_ms * 1e-3) / 1e9,
+                         "mfma_kernel_tflops": flops / (mfma_ms * 1e-3) / 1e12}
+    all_mf = np.concatenate([np.asarray(mf[k]) for k in ks])
+    achieved = corpus_bytes / (float(np.mean(all_mf)) * 1e-3) / 1e9
+    line = {"metric": f"queries/s ({name})", "value": q * args.steps * len(ks) / wall, "unit": "queries/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": f"{name}: batch of {q} queries vs resident {n} x {d} fp32, K in {list(ks)}",
+                       "n": n, "d": d, "q": q, "ks": list(ks)},
+            "per_k": per_k,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "mfma_scores_kernel", "bytes_per_launch": corpus_bytes,
+                         "avg_launch_us": float(np.mean(all_mf)) * 1e3},
+            "input_gen_s": gen_s}
+    if not args.no_cpu_baseline:
+        import oracle
+        from tests.gpu_util import check_retrieval
+        kmax = max(ks)
+        gi, gs = eng.search_resident(qdev, kmax)
+        torch.cuda.synchronize()
+        gi, gs = gi.cpu().numpy(), gs.cpu().numpy()
+        s = time.perf_counter()
+        o_idx, o_sc = oracle.search(corpus, qhost, kmax)
+        el = time.perf_counter() - s
+        for qi in range(q):
+            check_retrieval(gi[qi], gs[qi], o_idx[qi], o_sc[qi], corpus, qhost[qi], oracle)
+        line["cpu_baseline"] = {"value": q / el, "unit": "queries/s", "cores": oracle.num_threads(),
+                                "kind": "oracle", "sample": f"the full batch of {q} queries at K={kmax}",
+                                "host_cores": host_cores(), "cpu_model": cpu_model(), "parity": "ok"}
+    eng.close()
+    return line
+
+
+def run_int32(args, torch, ResidentTopK, workloads):
+    w = workloads.WORKLOADS["c4_1e8_int32"]
+    t = time.perf_counter()
+    v = workloads.int32_values()
+    gen_s = time.perf_counter() - t
+    n = v.shape[0]
+    ks = tuple(w["ks"])
+    vdev = torch.from_numpy(v).cuda()
+    eng = ResidentTopK(max_n=1, max_d=1, max_k=max(ks), max_q=1)
+    stream = torch.cuda.current_stream()
+    outs = {k: (torch.empty(k, dtype=torch.int32, device="cuda"), torch.empty(k, dtype=torch.int32, device="cuda"))
+            for k in ks}
+    for _ in range(args.warmup):
+        for k in ks:
+            eng.topk_select(vdev, k, *outs[k], stream=stream)
+    torch.cuda.synchronize()
+    eng.profile(True)
+    lat = {k: [] for k in ks}
+    part = {k: [] for k in ks}
+    merge = {k: [] for k in ks}
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        for k in ks:
+            s = time.perf_counter_ns()
+            eng.topk_select(vdev, k, *outs[k], stream=stream)
+            stream.synchronize()
+            lat[k].append((time.perf_counter_ns() - s) / 1e3)
+            a, b, _ = eng.profile_read()
+            part[k].append(a)
+            merge[k].append(b)
+    wall = time.perf_counter() - t0
+    eng.profile(False)
+    nbytes = n * 4
+    per_k = {str(k): {"calls_per_s": len(lat[k]) / (np.sum(lat[k]) / 1e6), "p50_us": pct(lat[k], 50),
+                      "p99_us": pct(lat[k], 99), "scan_kernel_avg_us": float(np.mean(part[k])) * 1e3,
+                      "merge_avg_us": float(np.mean(merge[k])) * 1e3,
+                      "scan_kernel_gbs": nbytes / (float(np.mean(part[k])) * 1e-3) / 1e9} for k in ks}
+    all_part = np.concatenate([np.asarray(part[k]) for k in ks])
+    achieved = nbytes / (float(np.mean(all_part)) * 1e-3) / 1e9
+    line = {"metric": "top-K calls/s (c4_1e8_int32)", "value": args.steps * len(ks) / wall, "unit": "calls/s",
+            "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int32",
+            "data": "synthetic",
+            "config": {"workload": f"c4_1e8_int32: raw top-K over {n} int32 (uniform, 1% duplicated), K in {list(ks)}",
+                       "n": n, "ks": list(ks)},
+            "per_k": per_k,
+            "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "select_topk_kernel",
+                         "bytes_per_launch": nbytes, "avg_launch_us": float(np.mean(all_part)) * 1e3},
+            "input_gen_s": gen_s}
+    if not args.no_cpu_baseline:
+        import oracle
+        from tests.gpu_util import check_exact_topk_property
+        m = min(n, 10_000_000)
+        s = time.perf_counter()
+        o_idx, o_val = oracle.topk(v[:m], max(ks))
+        el = time.perf_counter() - s
+        for k in ks:
+            gi, gv = eng.topk_select(vdev, k)
+            torch.cuda.synchronize()
+            check_exact_topk_property(gi.cpu().numpy(), gv.cpu().numpy(), v)
+        line["cpu_baseline"] = {"value": (m / n) / el, "unit": "calls/s", "cores": oracle.num_threads(),
+                                "kind": "oracle",
+                                "sample": f"the first {m} of {n} values at K={max(ks)}, scaled to a full call; "
+                                          "GPU answers checked exactly by rank counting over all values",
+                                "host_cores": host_cores(), "cpu_model": cpu_model(), "parity": "ok"}
+    eng.close()
+    return line
+
+
+def copy_calibration(torch, nbytes, reps):
+    """A plain device copy of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c3_1m_1024")
+    ap.add_argument("--num-queries", type=int, default=1000)
+    ap.add_argument("--cpu-queries", type=int, default=40)
+    ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time in cpu_baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--e2e-reps", type=int, default=200)
+    ap.add_argument("--copy-calibration", type=int, default=0, help="bytes; run only a plain copy kernel")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the row-sharded multi-GPU design is "
+                                   "documented but not built", "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration(torch, args.copy_calibration, max(1, args.steps))
+        return
+    from top_search_resident_amd import ResidentTopK, workloads
+    if args.workload == "c4_1e8_int32":
+        line = run_int32(args, torch, ResidentTopK, workloads)
+    else:
+        line = run_retrieval(args, torch, ResidentTopK, workloads)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

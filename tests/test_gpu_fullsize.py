@@ -1,0 +1,111 @@
+"""The five workloads at full size, in the launch configuration the benchmark
+times.  The oracle checks a sample of queries in full (R1-R4); the other queries
+are checked row by row (returned scores against the oracle's fp64 scores of the
+same rows), for sortedness and distinctness, and -- on a further sample -- for
+completeness against the oracle's scores of every row.  The raw int32 top-K is
+checked exactly: against the oracle once, and by rank counting for every K."""
+import numpy as np
+import pytest
+
+import oracle
+from gpu_util import REL_TOL, check_exact_topk_property, check_retrieval
+from top_search_resident_amd import ResidentTopK, workloads
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+
+def _sorted_distinct(idx, sc):
+    assert np.unique(idx).size == idx.size
+    for j in range(idx.size - 1):
+        assert sc[j] > sc[j + 1] or (sc[j] == sc[j + 1] and idx[j] < idx[j + 1])
+
+
+def _row_scores_match(idx, sc, corpus, q):
+    o = oracle.scores(corpus[idx.astype(np.int64)], q)
+    assert np.all(np.abs(sc.astype(np.float64) - o) <= REL_TOL * np.maximum(np.abs(o), 1e-30))
+
+
+def _complete(idx, sc, corpus, q):
+    """No row left out has an oracle score above the k-th returned row's oracle
+    score by more than the tolerance (R3 without a sort)."""
+    o_all = oracle.scores(corpus, q)
+    mask = np.ones(corpus.shape[0], dtype=bool)
+    mask[idx] = False
+    o_k = o_all[idx].min()
+    assert o_all[mask].max() <= o_k + REL_TOL * abs(o_k)
+
+
+def _run_sequential(eng, qdev, k):
+    out_i = np.empty((qdev.shape[0], k), np.int32)
+    out_s = np.empty((qdev.shape[0], k), np.float32)
+    for qi in range(qdev.shape[0]):
+        i, s = eng.search_resident(qdev[qi:qi + 1], k)
+        out_i[qi], out_s[qi] = i.cpu().numpy()[0], s.cpu().numpy()[0]
+    return out_i, out_s
+
+
+@pytest.mark.parametrize("name,n_full,n_complete", [
+    ("c1_10k_384", 1, 1), ("c2_50k_768", 40, 200), ("c2_100k_768", 40, 200), ("c3_1m_1024", 3, 12)])
+def test_single_query_workloads(name, n_full, n_complete):
+    w = workloads.WORKLOADS[name]
+    print(f"[fullsize] {name}: generating inputs", flush=True)
+    corpus, qs = workloads.retrieval_inputs(name)
+    n, d = corpus.shape
+    with ResidentTopK(n, d, max(w["ks"]), 1) as eng:
+        eng.upload_corpus_rowmajor(corpus)
+        qdev = torch.from_numpy(qs).cuda()
+        kmax = max(w["ks"])
+        o_idx, o_sc = oracle.search(corpus, qs[:n_full], kmax)
+        for k in w["ks"]:
+            print(f"[fullsize] {name}: {qs.shape[0]} sequential queries at k={k}", flush=True)
+            g_idx, g_sc = _run_sequential(eng, qdev, k)
+            for qi in range(qs.shape[0]):
+                _sorted_distinct(g_idx[qi], g_sc[qi])
+            for qi in range(0, qs.shape[0], max(1, qs.shape[0] // 100)):
+                _row_scores_match(g_idx[qi], g_sc[qi], corpus, qs[qi])
+            for qi in range(n_full):
+                check_retrieval(g_idx[qi], g_sc[qi], o_idx[qi, :k], o_sc[qi, :k], corpus, qs[qi], oracle)
+            step = max(1, qs.shape[0] // n_complete)
+            for qi in range(0, qs.shape[0], step)[:n_complete]:
+                _complete(g_idx[qi], g_sc[qi], corpus, qs[qi])
+
+
+def test_int32_1e8():
+    print("[fullsize] c4_1e8_int32: generating inputs", flush=True)
+    v = workloads.int32_values()
+    vdev = torch.from_numpy(v).cuda()
+    ks = workloads.WORKLOADS["c4_1e8_int32"]["ks"]
+    with ResidentTopK(1, 1, max(ks), 1) as eng:
+        res = {}
+        for k in ks:
+            i, x = eng.topk_select(vdev, k)
+            torch.cuda.synchronize()
+            res[k] = (i.cpu().numpy(), x.cpu().numpy())
+            check_exact_topk_property(res[k][0], res[k][1], v)
+        print("[fullsize] c4_1e8_int32: oracle full sort", flush=True)
+        o_idx, o_val = oracle.topk(v, max(ks))
+        for k in ks:
+            assert np.array_equal(res[k][0], o_idx[:k])
+            assert np.array_equal(res[k][1], o_val[:k])
+
+
+def test_batched_500k():
+    name = "c5_q32_500k_768"
+    w = workloads.WORKLOADS[name]
+    print(f"[fullsize] {name}: generating inputs", flush=True)
+    corpus, qs = workloads.retrieval_inputs(name)
+    n, d = corpus.shape
+    with ResidentTopK(n, d, max(w["ks"]), 32) as eng:
+        eng.upload_corpus_rowmajor(corpus)
+        qdev = torch.from_numpy(qs).cuda()
+        res = {}
+        for k in w["ks"]:
+            i, s = eng.search_resident(qdev, k)
+            torch.cuda.synchronize()
+            res[k] = (i.cpu().numpy(), s.cpu().numpy())
+        print(f"[fullsize] {name}: oracle for 32 queries", flush=True)
+        o_idx, o_sc = oracle.search(corpus, qs, max(w["ks"]))
+        for k in w["ks"]:
+            for qi in range(qs.shape[0]):
+                check_retrieval(res[k][0][qi], res[k][1][qi], o_idx[qi, :k], o_sc[qi, :k], corpus, qs[qi], oracle)
