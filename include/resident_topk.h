@@ -123,12 +123,12 @@ int32_t rt_last_hip_error(const rt_engine *e);
 
 /*
  * Kernel timing for measurement.  While enabled (on != 0), every search or
- * select records HIP events on its stream around its two stages; after the
- * stream has finished, rt_profile_read returns the last call's stage durations
- * in milliseconds: [0] = partial stage (scoring / streaming selection, for a
- * batch also the batched scoring kernel), [1] = merge stage, [2] = batched
- * scoring kernel alone (0 when the call had none).  The events are created by
- * rt_engine_create.  RT_EINVAL on NULL arguments.
+ * select records HIP events on its stream around its kernels; after the stream
+ * has finished, rt_profile_read returns the last call's device times in
+ * milliseconds: [0] = the whole call, [1] = the batched scoring kernel (0 when
+ * the call had none), [2] = the streaming top-K kernel (scoring or raw-array
+ * selection, per-block lists and the merge tree), i.e. [0] - [1].  The events
+ * are created by rt_engine_create.  RT_EINVAL on NULL arguments.
  */
 rt_status rt_profile_enable(rt_engine *e, int32_t on);
 rt_status rt_profile_read(rt_engine *e, float *ms3);

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 import oracle
-from gpu_util import REL_TOL, check_exact_topk_property, check_retrieval
+from gpu_util import REL_TOL, SCALE_FLOOR, check_exact_topk_property, check_retrieval, cs_bound
 from top_search_resident_amd import ResidentTopK, workloads
 
 pytestmark = pytest.mark.gpu
@@ -22,8 +22,10 @@ def _sorted_distinct(idx, sc):
 
 
 def _row_scores_match(idx, sc, corpus, q):
-    o = oracle.scores(corpus[idx.astype(np.int64)], q)
-    assert np.all(np.abs(sc.astype(np.float64) - o) <= REL_TOL * np.maximum(np.abs(o), 1e-30))
+    rows = corpus[idx.astype(np.int64)]
+    o = oracle.scores(rows, q)
+    den = np.maximum(np.abs(o), SCALE_FLOOR * cs_bound(rows, q))
+    assert np.all(np.abs(sc.astype(np.float64) - o) <= REL_TOL * den)
 
 
 def _complete(idx, sc, corpus, q):

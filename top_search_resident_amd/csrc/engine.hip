@@ -6,7 +6,7 @@
 // resident (Step 1), and each search is scoring + per-block top-K + merge on the
 // device (Steps 2-5).  This file owns the buffers, validates arguments on the
 // host before anything is enqueued, plans the launch shapes and enqueues the
-// kernels of stream_topk.hip, mfma_scores.hip and merge_topk.hip.
+// kernels of stream_topk.hip and mfma_scores.hip.
 #include <hip/hip_runtime.h>
 
 #include <new>
@@ -20,10 +20,13 @@ constexpr int64_t kMaxN = 2147483647LL;
 constexpr int32_t kMaxD = 65536;
 constexpr int32_t kMaxK = 1024;
 constexpr int32_t kMaxQ = 32;
-// Per-workgroup list storage (ranks) for each of the two ping-pong buffers.
-constexpr int64_t kListEntries = int64_t(1) << 22;
-// Most waves the streaming stage uses per segment.
-constexpr int64_t kMaxWavesPerSeg = 4096;
+// Merge-tree list storage (ranks) shared by all segments of a call: 64 MiB.
+constexpr int64_t kTreeRanks = int64_t(1) << 23;
+// Most streaming workgroups per segment (bounds the counter array).
+constexpr int64_t kMaxWgsPerSeg = 2048;
+// Streaming waves per CU the planner aims for: about 8 keeps HBM near its
+// measured ceiling at 1M x 1024 on MI355X.
+constexpr int64_t kWavesPerCu = 8;
 
 int kp_for(int k) {
     int kp = 64;
@@ -32,20 +35,23 @@ int kp_for(int k) {
 }
 
 struct Plan {
-    int wgs;            // workgroups per segment in the streaming stage
+    int wgs;            // workgroups per segment
     int64_t per_wave;   // rows (scoring) or 16-byte groups (raw arrays) per wave
 };
 
 // Split `units` (rows or 16-byte groups) of each of `segments` segments over
-// waves: at least `min_per_wave` units per wave, at most kMaxWavesPerSeg waves
-// per segment, and the per-workgroup lists must fit one ping-pong buffer.
-Plan plan_stream(int64_t units, int segments, int kp, int64_t min_per_wave) {
+// waves: at least `min_per_wave` units per wave, about kWavesPerCu waves per CU
+// in total, and the merge tree (<= 2 lists per workgroup) must fit its storage.
+Plan plan_stream(int64_t units, int segments, int kp, int64_t min_per_wave, int num_cus) {
+    int64_t target = (int64_t)num_cus * kWavesPerCu / segments;
+    if (target < rt::kStreamWaves) target = rt::kStreamWaves;
     int64_t waves = (units + min_per_wave - 1) / min_per_wave;
-    if (waves > kMaxWavesPerSeg) waves = kMaxWavesPerSeg;
+    if (waves > target) waves = target;
     if (waves < 1) waves = 1;
     int64_t wgs = (waves + rt::kStreamWaves - 1) / rt::kStreamWaves;
-    const int64_t cap = kListEntries / ((int64_t)segments * kp);
+    const int64_t cap = kTreeRanks / ((int64_t)segments * 2 * kp);
     if (wgs > cap) wgs = cap;
+    if (wgs > kMaxWgsPerSeg) wgs = kMaxWgsPerSeg;
     if (wgs < 1) wgs = 1;
     waves = wgs * rt::kStreamWaves;
     Plan p;
@@ -66,8 +72,8 @@ struct rt_engine {
     int32_t resident_d = 0;
     float *corpus = nullptr;
     float *scores = nullptr;  // batched scores, max_q x roundup(max_n, 64); only when max_q > 1
-    uint64_t *lists[2] = {nullptr, nullptr};
-    uint64_t *seg_thr = nullptr;
+    uint64_t *tree = nullptr;       // kTreeRanks merge-tree ranks
+    uint32_t *counters = nullptr;   // kMaxQ x kMaxWgsPerSeg arrival counters
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
     bool profiling = false;
     bool had_batch_kernel = false;
@@ -140,9 +146,8 @@ void rt_engine_destroy(rt_engine *e) {
     (void)hipDeviceSynchronize();
     (void)hipFree(e->corpus);
     (void)hipFree(e->scores);
-    (void)hipFree(e->lists[0]);
-    (void)hipFree(e->lists[1]);
-    (void)hipFree(e->seg_thr);
+    (void)hipFree(e->tree);
+    (void)hipFree(e->counters);
     for (auto &ev : e->ev)
         if (ev) (void)hipEventDestroy(ev);
     (void)hipSetDevice(prev);
@@ -186,16 +191,15 @@ rt_status rt_engine_create(int64_t max_n, int32_t max_d, int32_t max_k, int32_t 
     };
     const int64_t ld = (max_n + 63) / 64 * 64;
     bool ok = alloc(reinterpret_cast<void **>(&e->corpus), sizeof(float) * (size_t)max_n * (size_t)max_d) &&
-              alloc(reinterpret_cast<void **>(&e->lists[0]), sizeof(uint64_t) * (size_t)kListEntries) &&
-              alloc(reinterpret_cast<void **>(&e->lists[1]), sizeof(uint64_t) * (size_t)kListEntries) &&
-              alloc(reinterpret_cast<void **>(&e->seg_thr), sizeof(uint64_t) * (size_t)kMaxQ);
+              alloc(reinterpret_cast<void **>(&e->tree), sizeof(uint64_t) * (size_t)kTreeRanks) &&
+              alloc(reinterpret_cast<void **>(&e->counters), sizeof(uint32_t) * (size_t)(kMaxQ * kMaxWgsPerSeg));
     if (ok && max_q > 1) ok = alloc(reinterpret_cast<void **>(&e->scores), sizeof(float) * (size_t)max_q * (size_t)ld);
     if (!ok) {
         rt_engine_destroy(e);
         (void)hipSetDevice(prev);
         return RT_ENOMEM;
     }
-    err = hipMemset(e->seg_thr, 0, sizeof(uint64_t) * kMaxQ);
+    err = hipMemset(e->counters, 0, sizeof(uint32_t) * (size_t)(kMaxQ * kMaxWgsPerSeg));
     if (err == hipSuccess) err = rt::prepare_mfma_scores();
     for (int i = 0; i < 4 && err == hipSuccess; ++i) err = hipEventCreate(&e->ev[i]);
     if (err == hipSuccess) err = hipDeviceSynchronize();
@@ -229,31 +233,27 @@ rt_status upload_corpus_rowmajor(rt_engine *e, const float *corpus, int64_t n, i
     return RT_OK;
 }
 
-// Enqueue the merge levels for `segments` segments of `lists` per-workgroup lists
-// held in e->lists[0]; the last level writes the outputs.
-static hipError_t enqueue_merges(rt_engine *e, int lists, int segments, int kp, int mode, int k, int32_t *out_idx,
-                                 void *out_val, const void *src, int64_t src_stride, hipStream_t s) {
-    const int max_fan = rt::kMergeEntries / kp;
-    int cur = 0;
-    hipError_t err = hipSuccess;
-    while (true) {
-        int fan = 1;
-        while (fan < lists && fan < max_fan) fan <<= 1;
-        const int groups = (lists + fan - 1) / fan;
-        const bool last = groups == 1;
-        err = rt::launch_merge(e->lists[cur], lists, fan, segments, kp, e->lists[cur ^ 1], last ? mode : 0, k,
-                               out_idx, out_val, src, src_stride, e->seg_thr, s);
-        if (err != hipSuccess || last) break;
-        lists = groups;
-        cur ^= 1;
-    }
-    return err;
+static rt::TreeLaunch tree_for(rt_engine *e, const Plan &p, int kp, int k, int mode, int32_t *out_idx,
+                               void *out_val, const void *src, int64_t src_stride) {
+    rt::TreeLaunch t;
+    t.tree = e->tree;
+    t.counters = e->counters;
+    t.seg_tree_stride = 2 * (int64_t)p.wgs * kp;
+    t.seg_ctr_stride = p.wgs;
+    t.kp = kp;
+    t.k = k;
+    t.mode = mode;
+    t.out_idx = out_idx;
+    t.out_val = out_val;
+    t.src = src;
+    t.src_seg_stride = src_stride;
+    return t;
 }
 
 static hipError_t prologue(rt_engine *e, hipStream_t s) {
     hipError_t err = hipSuccess;
     if (e->dirty) {
-        err = rt::launch_reset(e->seg_thr, kMaxQ, s);
+        err = rt::launch_zero_counters(e->counters, (int64_t)kMaxQ * kMaxWgsPerSeg, s);
         if (err != hipSuccess) return err;
         e->dirty = false;
     }
@@ -276,24 +276,20 @@ rt_status search_resident(rt_engine *e, const float *queries, int32_t q, int32_t
     const bool batched = q > 1 && e->scores != nullptr && d % 4 == 0 && d <= rt::kMfmaMaxD;
     e->had_batch_kernel = batched;
     if (err == hipSuccess) err = prologue(e, s);
-    int wgs = 0;
     if (err == hipSuccess && batched) {
         const int64_t ld = (n + 63) / 64 * 64;
         err = rt::launch_mfma_scores(e->corpus, n, d, queries, q, e->scores, ld, e->num_cus, s);
         if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[3], s);
         // each wave streams at least 1024 scores (256 groups of 4)
-        const Plan p = plan_stream((n + 3) / 4, q, kp, 256);
-        wgs = p.wgs;
-        if (err == hipSuccess)
-            err = rt::launch_select_topk(e->scores, ld, n, 1, q, k, kp, p.per_wave, p.wgs, e->lists[0], e->seg_thr, s);
+        const Plan p = plan_stream((n + 3) / 4, q, kp, 256, e->num_cus);
+        const rt::TreeLaunch t = tree_for(e, p, kp, k, 1, out_idx, out_scores, nullptr, 0);
+        if (err == hipSuccess) err = rt::launch_select_topk(e->scores, ld, n, 1, q, p.per_wave, p.wgs, t, s);
     } else if (err == hipSuccess) {
-        const Plan p = plan_stream(n, q, kp, 32);
-        wgs = p.wgs;
-        err = rt::launch_gemv_topk(e->corpus, n, d, queries, q, k, kp, p.per_wave, p.wgs, e->lists[0], e->seg_thr, s);
+        const Plan p = plan_stream(n, q, kp, 32, e->num_cus);
+        const rt::TreeLaunch t = tree_for(e, p, kp, k, 1, out_idx, out_scores, nullptr, 0);
+        err = rt::launch_gemv_topk(e->corpus, n, d, queries, q, p.per_wave, p.wgs, t, s);
     }
     if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[1], s);
-    if (err == hipSuccess) err = enqueue_merges(e, wgs, q, kp, 1, k, out_idx, out_scores, nullptr, 0, s);
-    if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[2], s);
     (void)hipSetDevice(prev);
     if (err != hipSuccess) return hip_fail(e, err);
     return RT_OK;
@@ -312,12 +308,10 @@ rt_status topk_select(rt_engine *e, const void *values, int32_t dtype, int64_t n
     e->had_batch_kernel = false;
     if (err == hipSuccess) err = prologue(e, s);
     const int64_t head = (int64_t)((reinterpret_cast<uintptr_t>(values) & 15u) >> 2);
-    const Plan p = plan_stream((n + head + 3) / 4, 1, kp, 256);
-    if (err == hipSuccess)
-        err = rt::launch_select_topk(values, 0, n, dtype, 1, k, kp, p.per_wave, p.wgs, e->lists[0], e->seg_thr, s);
+    const Plan p = plan_stream((n + head + 3) / 4, 1, kp, 256, e->num_cus);
+    const rt::TreeLaunch t = tree_for(e, p, kp, k, 2, out_idx, out_values, values, 0);
+    if (err == hipSuccess) err = rt::launch_select_topk(values, 0, n, dtype, 1, p.per_wave, p.wgs, t, s);
     if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[1], s);
-    if (err == hipSuccess) err = enqueue_merges(e, p.wgs, 1, kp, 2, k, out_idx, out_values, values, 0, s);
-    if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[2], s);
     (void)hipSetDevice(prev);
     if (err != hipSuccess) return hip_fail(e, err);
     return RT_OK;
@@ -335,13 +329,13 @@ rt_status rt_profile_read(rt_engine *e, float *ms3) {
     if (!e || !ms3) return RT_EINVAL;
     ms3[0] = ms3[1] = ms3[2] = 0.f;
     hipError_t err = hipEventElapsedTime(&ms3[0], e->ev[0], e->ev[1]);
-    if (err == hipSuccess) err = hipEventElapsedTime(&ms3[1], e->ev[1], e->ev[2]);
-    if (err == hipSuccess && e->had_batch_kernel) err = hipEventElapsedTime(&ms3[2], e->ev[0], e->ev[3]);
+    if (err == hipSuccess && e->had_batch_kernel) err = hipEventElapsedTime(&ms3[1], e->ev[0], e->ev[3]);
     if (err != hipSuccess) {
         e->last_hip = (int32_t)err;
         (void)hipGetLastError();
         return RT_EHIP;
     }
+    ms3[2] = ms3[0] - ms3[1];
     return RT_OK;
 }
 

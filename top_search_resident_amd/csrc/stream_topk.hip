@@ -1,60 +1,172 @@
-// stream_topk.hip -- the streaming stage of exact top-K on gfx950.
+// stream_topk.hip -- exact top-K on gfx950 in one kernel launch per call.
 //
 // "GPU-Resident Top-K for Agentic RAG" (A. Banerjee), section 4: Step 2 scores
-// every corpus row by inner product, Step 3 lets each block of rows build its own
-// best-K list.  The pages run one thread per row for scoring (uncoalesced along
-// D) and a single-lane bubble sort per block for selection; here one kernel does
-// both: each wavefront streams a contiguous row range with 16-byte coalesced
-// loads, reduces each row's dot product across a group of lanes, and feeds the
-// scores straight into a register-resident best-K list (wave_topk.hpp), so the
-// N scores never go to HBM.  At the end the four waves of a workgroup merge their
-// lists into one list per workgroup.
+// every corpus row by inner product, Step 3 lets each block of rows build its
+// own best-K list, Step 4 merges the per-block lists into the global best-K, and
+// only K indices and K scores leave (Step 6).  The pages launch three kernels:
+// one thread per row for scoring (uncoalesced along D), one thread per block
+// for a bubble-sort selection, and one thread for the merge.  Here a single
+// kernel does all of it:
 //
-// The raw-array variant is the first stage of the two-stage top-K of "CUDA
-// Programming Model Series 9: Efficient TopK" (section 2: each block reduces its
-// share of the array to a local top-K), with vectorised loads and the same
-// register lists.
+//   1. streaming: each wavefront reads a contiguous row range with 16-byte
+//      non-temporal coalesced loads, reduces each row's dot product across a
+//      group of lanes, and feeds the scores into a register-resident best-K
+//      list (wave_topk.hpp) -- the N scores never reach HBM;
+//   2. the four waves of a workgroup merge their lists into one (LDS);
+//   3. merge tree: workgroups are grouped `fan` at a time; each workgroup stores
+//      its list, and the LAST workgroup of a group to finish (a global atomic
+//      counter per group, after a device-scope release fence) loads the group's
+//      lists, merges them and moves one level up; the last one at the root
+//      writes the K outputs.  Nothing waits on anything (a workgroup that is not
+//      last simply exits), and each counter is cleared by the workgroup that
+//      completes it, ready for the next call.
+//
+// Exactness of the two stages: the top-K of the union of per-block top-K lists
+// is the global top-K (anything that beats an element inside its block beats it
+// globally), so the grouping is free.
+//
+// The raw-array kernel is the two-stage top-K of "CUDA Programming Model Series
+// 9: Efficient TopK" (section 2: each block reduces its share to a local top-K;
+// section 3: a second stage merges the local results), with vector loads, the
+// same register lists and the same merge tree.
 #include "kernels.hpp"
 #include "wave_topk.hpp"
 
 namespace rt {
 
-// Rows per lane-group step unrolled so each lane keeps ~8 float4 loads in flight.
-template <int L>
-struct RowUnroll {
-    static constexpr int value = (L >= 6) ? 1 : (L >= 3 ? 2 : (L == 2 ? 4 : 8));
+struct TreeArgs {
+    uint64_t *tree;          // per segment: seg_tree_stride ranks of list storage
+    uint32_t *counters;      // per segment: seg_ctr_stride arrival counters (zero between calls)
+    int64_t seg_tree_stride;
+    int seg_ctr_stride;
+    int fan;                 // lists merged per tree node (power of two, fan * Kp <= kTreeEntries)
+    int k;
+    int mode;                // 1: write index + fp32 score from the rank; 2: index + source element
+    int32_t *out_idx;        // [segments][k]
+    uint32_t *out_val;       // [segments][k]
+    const uint32_t *src;     // mode 2: the array the ranks index into
+    int64_t src_seg_stride;
 };
 
-// Write the 4 waves' lists to LDS, merge them pairwise, store the workgroup's
-// list (best-first, Kp entries) to `out`.
+__device__ __forceinline__ void write_output(const TreeArgs &ta, int seg, int r, uint64_t v) {
+    const uint32_t idx = rank_index(v);
+    ta.out_idx[(int64_t)seg * ta.k + r] = (int32_t)idx;
+    ta.out_val[(int64_t)seg * ta.k + r] =
+        (ta.mode == 1) ? __float_as_uint(f32_of_order_key(rank_key(v))) : ta.src[(int64_t)seg * ta.src_seg_stride + idx];
+}
+
+// Merge `count` (1 <= count <= fan) best-first lists of 64*R ranks, stored
+// contiguously at `src`, into sm[0 .. 64*R).  Pairs of lists are merged by one
+// wave each, level by level.
 template <int R>
-__device__ __forceinline__ void workgroup_merge_store(WaveSelector<R> &sel, uint64_t *lds, uint64_t *out) {
+__device__ __forceinline__ void merge_lists_into_lds(const uint64_t *src, int count, uint64_t *sm) {
     constexpr int Kp = 64 * R;
     const int lane = lane_id();
-    const int wv = threadIdx.x >> 6;
+    const int wv = wave_in_group();
+    const int nwaves = blockDim.x >> 6;
+    for (int i = threadIdx.x; i < count * Kp; i += blockDim.x) sm[i] = src[i];
+    __syncthreads();
+    for (int s = 1; s < count; s <<= 1) {
+        for (int a = wv * 2 * s; a + s < count; a += nwaves * 2 * s) {
+            uint64_t A[R], B[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) lds[wv * Kp + r * 64 + lane] = sel.L[r];
+            for (int r = 0; r < R; ++r) {
+                A[r] = sm[a * Kp + r * 64 + lane];
+                B[r] = sm[(a + s) * Kp + r * 64 + lane];
+            }
+            list_absorb_list<R>(A, B);
+#pragma unroll
+            for (int r = 0; r < R; ++r) sm[a * Kp + r * 64 + lane] = A[r];
+        }
+        __syncthreads();
+    }
+}
+
+// Steps 2 and 3 above.  `sm` is kTreeEntries ranks of LDS; `s_flag` an int in LDS.
+template <int R>
+__device__ __forceinline__ void finish_workgroup(WaveSelector<R> &sel, uint64_t *sm, int *s_flag,
+                                                 const TreeArgs &ta, int seg) {
+    constexpr int Kp = 64 * R;
+    const int lane = lane_id();
+    const int wv = wave_in_group();
+
+    // 2. the workgroup's four wave lists -> one list in wave 0's registers.
+#pragma unroll
+    for (int r = 0; r < R; ++r) sm[wv * Kp + r * 64 + lane] = sel.L[r];
     __syncthreads();
     if ((wv & 1) == 0) {
         uint64_t M[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) M[r] = lds[(wv + 1) * Kp + r * 64 + lane];
+        for (int r = 0; r < R; ++r) M[r] = sm[(wv + 1) * Kp + r * 64 + lane];
         list_absorb_list<R>(sel.L, M);
 #pragma unroll
-        for (int r = 0; r < R; ++r) lds[wv * Kp + r * 64 + lane] = sel.L[r];
+        for (int r = 0; r < R; ++r) sm[wv * Kp + r * 64 + lane] = sel.L[r];
     }
     __syncthreads();
+    int count = gridDim.x;
     if (wv == 0) {
         uint64_t M[R];
 #pragma unroll
-        for (int r = 0; r < R; ++r) M[r] = lds[2 * Kp + r * 64 + lane];
+        for (int r = 0; r < R; ++r) M[r] = sm[2 * Kp + r * 64 + lane];
         list_absorb_list<R>(sel.L, M);
+        if (count == 1) {
 #pragma unroll
-        for (int r = 0; r < R; ++r) out[r * 64 + lane] = sel.L[r];
+            for (int r = 0; r < R; ++r)
+                if (r * 64 + lane < ta.k) write_output(ta, seg, r * 64 + lane, sel.L[r]);
+        }
+    }
+    if (count == 1) return;
+
+    // 3. merge tree over the workgroups of this segment.
+    uint64_t *base = ta.tree + (int64_t)seg * ta.seg_tree_stride;
+    uint32_t *ctr = ta.counters + (int64_t)seg * ta.seg_ctr_stride;
+    int node = blockIdx.x;
+    int64_t level_off = 0;
+    int ctr_off = 0;
+    if (wv == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r) base[(int64_t)node * Kp + r * 64 + lane] = sel.L[r];
+    }
+    while (true) {
+        const int parent = node / ta.fan;
+        const int first = parent * ta.fan;
+        const int children = (count - first < ta.fan) ? count - first : ta.fan;
+        __threadfence();  // release this workgroup's list to the other XCDs
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t arrived = atomicAdd(&ctr[ctr_off + parent], 1u);
+            const int last = (int)(arrived + 1 == (uint32_t)children);
+            if (last) ctr[ctr_off + parent] = 0u;  // all children have arrived: clear for the next call
+            *s_flag = last;
+        }
+        __syncthreads();
+        if (!*s_flag) return;
+        __threadfence();  // acquire the siblings' lists
+        merge_lists_into_lds<R>(base + level_off + (int64_t)first * Kp, children, sm);
+        const int up = (count + ta.fan - 1) / ta.fan;
+        if (up == 1) {
+            for (int r = threadIdx.x; r < ta.k; r += blockDim.x) write_output(ta, seg, r, sm[r]);
+            return;
+        }
+        const int64_t next_off = level_off + (int64_t)count * Kp;
+        for (int i = threadIdx.x; i < Kp; i += blockDim.x) base[next_off + (int64_t)parent * Kp + i] = sm[i];
+        level_off = next_off;
+        ctr_off += up;
+        node = parent;
+        count = up;
+        __syncthreads();
     }
 }
 
 // ---------------------------------------------------------------- scoring
+
+// Rows each lane group takes per step.  Measured on MI355X at 1M x 1024: one row
+// per step with ~8 waves per CU keeps HBM near 89% of peak; larger unrolls only
+// add register pressure.  Rows of a single float4 per lane take two.
+template <int L>
+struct RowUnroll {
+    static constexpr int value = (L == 1) ? 2 : 1;
+};
 
 // A group of G = 2^log2g lanes owns one row at a time; lane g of the group loads
 // float4 columns g, g+G, ..., g+(L-1)G of that row (masked past d/4), so a row is
@@ -65,33 +177,37 @@ __device__ __forceinline__ void workgroup_merge_store(WaveSelector<R> &sel, uint
 template <int L, int R>
 __global__ __launch_bounds__(kStreamThreads) void gemv_topk_kernel(
     const float *__restrict__ corpus, int64_t n, int d, int log2g, const float *__restrict__ queries,
-    int64_t rows_per_wave, int k, uint64_t *__restrict__ wg_lists, uint64_t *__restrict__ seg_thr) {
+    int64_t rows_per_wave, TreeArgs ta) {
     constexpr int U = RowUnroll<L>::value;
-    constexpr int Kp = 64 * R;
     __shared__ uint64_t stage[kStreamWaves][128];
-    __shared__ uint64_t lists[kStreamWaves * Kp];
+    __shared__ uint64_t sm[kTreeEntries];
+    __shared__ int s_flag;
 
     const int seg = blockIdx.y;
     const int lane = lane_id();
-    const int wv = threadIdx.x >> 6;
+    const int wv = wave_in_group();
     const int64_t wave = (int64_t)blockIdx.x * kStreamWaves + wv;
     const int G = 1 << log2g;
     const int g = lane & (G - 1);
     const int h = lane >> log2g;
     const int rps = 64 >> log2g;
     const int d4 = d >> 2;
+    const bool padded = G * L != d4;  // some lanes' columns fall past the row end
     const float4 *__restrict__ c4 = reinterpret_cast<const float4 *>(corpus);
     const float4 *__restrict__ q4 = reinterpret_cast<const float4 *>(queries + (int64_t)seg * d);
+    uint64_t *const my_stage = stage[wv];
 
     WaveSelector<R> sel;
-    sel.init(k);
-    uint64_t *const my_stage = stage[wv];
-    uint64_t *const my_thr = seg_thr + seg;
+    sel.init(ta.k);
 
+    // Columns past the row end are clamped to the last column for the load and
+    // their values replaced by 0, so every load is unconditional.
     float4 qv[L];
+    int colc[L];
 #pragma unroll
     for (int j = 0; j < L; ++j) {
         const int col = j * G + g;
+        colc[j] = (col < d4) ? col : d4 - 1;
         qv[j] = (col < d4) ? q4[col] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 
@@ -102,15 +218,19 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_topk_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t row = r0 + u * rps + h;
-            const bool ok = row < r_end;
-            const float4 *rp = c4 + row * d4;
+            const float4 *rp = c4 + ((row < r_end) ? row : r_end - 1) * d4;  // rows past the range: reload the last
+#pragma unroll
+            for (int j = 0; j < L; ++j) x[u][j] = load_nt(rp + colc[j]);
+        }
+        if (padded) {
 #pragma unroll
             for (int j = 0; j < L; ++j) {
-                const int col = j * G + g;
-                x[u][j] = (ok && col < d4) ? rp[col] : make_float4(0.f, 0.f, 0.f, 0.f);
+                if (j * G + g >= d4) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) x[u][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
             }
         }
-        sel.refresh(my_thr);
         float acc[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -122,42 +242,37 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_topk_kernel(
                 a = fmaf(x[u][j].z, qv[j].z, a);
                 a = fmaf(x[u][j].w, qv[j].w, a);
             }
-            acc[u] = a;
-        }
-        for (int m = G >> 1; m >= 1; m >>= 1) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) acc[u] += __shfl_xor(acc[u], m);
+            acc[u] = group_sum(a, log2g);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t row = r0 + u * rps + h;
             const bool valid = (g == 0) && (row < r_end);
             const uint64_t rank = make_rank(order_key_f32(acc[u]), (uint32_t)row);
-            sel.offer(my_stage, my_thr, rank, valid && rank > sel.thr);
+            sel.offer(my_stage, rank, valid && rank > sel.thr);
         }
     }
-    sel.finish(my_stage, my_thr);
-    workgroup_merge_store<R>(sel, lists, wg_lists + ((int64_t)seg * gridDim.x + blockIdx.x) * Kp);
+    sel.finish(my_stage);
+    finish_workgroup<R>(sel, sm, &s_flag, ta, seg);
 }
 
 // Any d: one row per wave at a time, scalar loads strided by 64 lanes.
 template <int R>
 __global__ __launch_bounds__(kStreamThreads) void gemv_topk_generic_kernel(
     const float *__restrict__ corpus, int64_t n, int d, const float *__restrict__ queries,
-    int64_t rows_per_wave, int k, uint64_t *__restrict__ wg_lists, uint64_t *__restrict__ seg_thr) {
-    constexpr int Kp = 64 * R;
+    int64_t rows_per_wave, TreeArgs ta) {
     constexpr int U = 4;
     __shared__ uint64_t stage[kStreamWaves][128];
-    __shared__ uint64_t lists[kStreamWaves * Kp];
+    __shared__ uint64_t sm[kTreeEntries];
+    __shared__ int s_flag;
     const int seg = blockIdx.y;
     const int lane = lane_id();
-    const int wv = threadIdx.x >> 6;
+    const int wv = wave_in_group();
     const int64_t wave = (int64_t)blockIdx.x * kStreamWaves + wv;
     const float *__restrict__ q = queries + (int64_t)seg * d;
-    WaveSelector<R> sel;
-    sel.init(k);
     uint64_t *const my_stage = stage[wv];
-    uint64_t *const my_thr = seg_thr + seg;
+    WaveSelector<R> sel;
+    sel.init(ta.k);
     const int64_t r_begin = wave * rows_per_wave;
     const int64_t r_end = (r_begin + rows_per_wave < n) ? r_begin + rows_per_wave : n;
     for (int64_t r0 = r_begin; r0 < r_end; r0 += U) {
@@ -173,7 +288,6 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_topk_generic_kernel(
                 acc[u] = fmaf(x, qc, acc[u]);
             }
         }
-        sel.refresh(my_thr);
         for (int m = 32; m >= 1; m >>= 1) {
 #pragma unroll
             for (int u = 0; u < U; ++u) acc[u] += __shfl_xor(acc[u], m);
@@ -183,11 +297,11 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_topk_generic_kernel(
             const int64_t row = r0 + u;
             const bool valid = (lane == 0) && (row < r_end);
             const uint64_t rank = make_rank(order_key_f32(acc[u]), (uint32_t)row);
-            sel.offer(my_stage, my_thr, rank, valid && rank > sel.thr);
+            sel.offer(my_stage, rank, valid && rank > sel.thr);
         }
     }
-    sel.finish(my_stage, my_thr);
-    workgroup_merge_store<R>(sel, lists, wg_lists + ((int64_t)seg * gridDim.x + blockIdx.x) * Kp);
+    sel.finish(my_stage);
+    finish_workgroup<R>(sel, sm, &s_flag, ta, seg);
 }
 
 // ---------------------------------------------------------------- raw arrays
@@ -199,25 +313,23 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_topk_generic_kernel(
 // page, so reading the part of a group outside the array cannot fault.
 template <int DT, int R>
 __global__ __launch_bounds__(kStreamThreads) void select_topk_kernel(
-    const uint32_t *__restrict__ base, int64_t seg_stride, int64_t n, int64_t groups_per_wave, int k,
-    uint64_t *__restrict__ wg_lists, uint64_t *__restrict__ seg_thr) {
-    constexpr int Kp = 64 * R;
+    const uint32_t *__restrict__ base, int64_t seg_stride, int64_t n, int64_t groups_per_wave, TreeArgs ta) {
     constexpr int U = 4;
     __shared__ uint64_t stage[kStreamWaves][128];
-    __shared__ uint64_t lists[kStreamWaves * Kp];
+    __shared__ uint64_t sm[kTreeEntries];
+    __shared__ int s_flag;
     const int seg = blockIdx.y;
     const int lane = lane_id();
-    const int wv = threadIdx.x >> 6;
+    const int wv = wave_in_group();
     const int64_t wave = (int64_t)blockIdx.x * kStreamWaves + wv;
     const uintptr_t addr = reinterpret_cast<uintptr_t>(base + seg * seg_stride);
     const int head = (int)((addr & 15u) >> 2);
     const uint4 *__restrict__ a4 = reinterpret_cast<const uint4 *>(addr - (uintptr_t)head * 4u);
     const int64_t total_groups = (n + head + 3) >> 2;
+    uint64_t *const my_stage = stage[wv];
 
     WaveSelector<R> sel;
-    sel.init(k);
-    uint64_t *const my_stage = stage[wv];
-    uint64_t *const my_thr = seg_thr + seg;
+    sel.init(ta.k);
     const int64_t g_begin = wave * groups_per_wave;
     const int64_t g_end = (g_begin + groups_per_wave < total_groups) ? g_begin + groups_per_wave : total_groups;
     for (int64_t g0 = g_begin; g0 < g_end; g0 += 64 * U) {
@@ -225,9 +337,8 @@ __global__ __launch_bounds__(kStreamThreads) void select_topk_kernel(
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int64_t grp = g0 + u * 64 + lane;
-            v[u] = (grp < g_end) ? a4[grp] : make_uint4(0u, 0u, 0u, 0u);
+            v[u] = load_nt(a4 + ((grp < g_end) ? grp : g_end - 1));  // past the range: reload the last group (masked below)
         }
-        sel.refresh(my_thr);
         uint32_t key[U][4];
         bool any = false;
         const uint32_t thr_key = rank_key(sel.thr);
@@ -252,17 +363,19 @@ __global__ __launch_bounds__(kStreamThreads) void select_topk_kernel(
                 const int64_t idx = grp * 4 + c - head;
                 const bool valid = (grp < g_end) && idx >= 0 && idx < n;
                 const uint64_t rank = make_rank(key[u][c], (uint32_t)idx);
-                sel.offer(my_stage, my_thr, rank, valid && rank > sel.thr);
+                sel.offer(my_stage, rank, valid && rank > sel.thr);
             }
         }
     }
-    sel.finish(my_stage, my_thr);
-    workgroup_merge_store<R>(sel, lists, wg_lists + ((int64_t)seg * gridDim.x + blockIdx.x) * Kp);
+    sel.finish(my_stage);
+    finish_workgroup<R>(sel, sm, &s_flag, ta, seg);
 }
 
 // ---------------------------------------------------------------- launchers
 
 bool gemv_fast_path_ok(int d) { return d % 4 == 0 && d / 4 <= 64 * 8; }
+
+int tree_fan(int kp) { return kTreeEntries / kp; }
 
 // Pick the lane-group width G (power of two <= 64) and loads per lane L (from
 // {1, 2, 3, 4, 6, 8}) that waste the fewest lane slots on a row, preferring wide
@@ -287,16 +400,34 @@ static void pick_group(int d4, int *log2g, int *L) {
     *L = best_L;
 }
 
+static TreeArgs make_tree(const TreeLaunch &t) {
+    TreeArgs ta;
+    ta.tree = t.tree;
+    ta.counters = t.counters;
+    ta.seg_tree_stride = t.seg_tree_stride;
+    ta.seg_ctr_stride = t.seg_ctr_stride;
+    ta.fan = tree_fan(t.kp);
+    ta.k = t.k;
+    ta.mode = t.mode;
+    ta.out_idx = t.out_idx;
+    ta.out_val = static_cast<uint32_t *>(t.out_val);
+    ta.src = static_cast<const uint32_t *>(t.src);
+    ta.src_seg_stride = t.src_seg_stride;
+    return ta;
+}
+
+#define RT_R_CASES(MACRO) MACRO(1) MACRO(2) MACRO(4) MACRO(8) MACRO(16)
+
 template <int L>
-static hipError_t gemv_by_r(int R, dim3 grid, hipStream_t s, const float *corpus, int64_t n, int d, int lg,
-                            const float *q, int64_t rpw, int k, uint64_t *lists, uint64_t *thr) {
-    switch (R) {
-#define RT_CASE(RR)                                                                                          \
-    case RR:                                                                                                 \
-        hipLaunchKernelGGL((gemv_topk_kernel<L, RR>), grid, dim3(kStreamThreads), 0, s, corpus, n, d, lg, q, \
-                           rpw, k, lists, thr);                                                              \
+static hipError_t gemv_by_r(dim3 grid, hipStream_t s, const float *corpus, int64_t n, int d, int lg, const float *q,
+                            int64_t rpw, const TreeLaunch &t) {
+    const TreeArgs ta = make_tree(t);
+    switch (t.kp / 64) {
+#define RT_CASE(RR)                                                                                                 \
+    case RR:                                                                                                        \
+        hipLaunchKernelGGL((gemv_topk_kernel<L, RR>), grid, dim3(kStreamThreads), 0, s, corpus, n, d, lg, q, rpw, ta); \
         break;
-        RT_CASE(1) RT_CASE(2) RT_CASE(4) RT_CASE(8) RT_CASE(16)
+        RT_R_CASES(RT_CASE)
 #undef RT_CASE
         default:
             return hipErrorInvalidValue;
@@ -304,19 +435,18 @@ static hipError_t gemv_by_r(int R, dim3 grid, hipStream_t s, const float *corpus
     return hipGetLastError();
 }
 
-hipError_t launch_gemv_topk(const float *corpus, int64_t n, int d, const float *queries, int segments, int k,
-                            int kp, int64_t rows_per_wave, int wgs_per_seg, uint64_t *wg_lists,
-                            uint64_t *seg_thr, hipStream_t stream) {
-    const int R = kp / 64;
+hipError_t launch_gemv_topk(const float *corpus, int64_t n, int d, const float *queries, int segments,
+                            int64_t rows_per_wave, int wgs_per_seg, const TreeLaunch &t, hipStream_t stream) {
     const dim3 grid(wgs_per_seg, segments);
     if (!gemv_fast_path_ok(d)) {
-        switch (R) {
+        const TreeArgs ta = make_tree(t);
+        switch (t.kp / 64) {
 #define RT_CASE(RR)                                                                                            \
     case RR:                                                                                                   \
         hipLaunchKernelGGL((gemv_topk_generic_kernel<RR>), grid, dim3(kStreamThreads), 0, stream, corpus, n, d, \
-                           queries, rows_per_wave, k, wg_lists, seg_thr);                                      \
+                           queries, rows_per_wave, ta);                                                        \
         break;
-            RT_CASE(1) RT_CASE(2) RT_CASE(4) RT_CASE(8) RT_CASE(16)
+            RT_R_CASES(RT_CASE)
 #undef RT_CASE
             default:
                 return hipErrorInvalidValue;
@@ -326,26 +456,26 @@ hipError_t launch_gemv_topk(const float *corpus, int64_t n, int d, const float *
     int lg = 6, L = 8;
     pick_group(d / 4, &lg, &L);
     switch (L) {
-        case 1: return gemv_by_r<1>(R, grid, stream, corpus, n, d, lg, queries, rows_per_wave, k, wg_lists, seg_thr);
-        case 2: return gemv_by_r<2>(R, grid, stream, corpus, n, d, lg, queries, rows_per_wave, k, wg_lists, seg_thr);
-        case 3: return gemv_by_r<3>(R, grid, stream, corpus, n, d, lg, queries, rows_per_wave, k, wg_lists, seg_thr);
-        case 4: return gemv_by_r<4>(R, grid, stream, corpus, n, d, lg, queries, rows_per_wave, k, wg_lists, seg_thr);
-        case 6: return gemv_by_r<6>(R, grid, stream, corpus, n, d, lg, queries, rows_per_wave, k, wg_lists, seg_thr);
-        case 8: return gemv_by_r<8>(R, grid, stream, corpus, n, d, lg, queries, rows_per_wave, k, wg_lists, seg_thr);
+        case 1: return gemv_by_r<1>(grid, stream, corpus, n, d, lg, queries, rows_per_wave, t);
+        case 2: return gemv_by_r<2>(grid, stream, corpus, n, d, lg, queries, rows_per_wave, t);
+        case 3: return gemv_by_r<3>(grid, stream, corpus, n, d, lg, queries, rows_per_wave, t);
+        case 4: return gemv_by_r<4>(grid, stream, corpus, n, d, lg, queries, rows_per_wave, t);
+        case 6: return gemv_by_r<6>(grid, stream, corpus, n, d, lg, queries, rows_per_wave, t);
+        case 8: return gemv_by_r<8>(grid, stream, corpus, n, d, lg, queries, rows_per_wave, t);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <int DT>
-static hipError_t select_by_r(int R, dim3 grid, hipStream_t s, const uint32_t *base, int64_t stride, int64_t n,
-                              int64_t gpw, int k, uint64_t *lists, uint64_t *thr) {
-    switch (R) {
-#define RT_CASE(RR)                                                                                           \
-    case RR:                                                                                                  \
-        hipLaunchKernelGGL((select_topk_kernel<DT, RR>), grid, dim3(kStreamThreads), 0, s, base, stride, n, gpw, \
-                           k, lists, thr);                                                                    \
+static hipError_t select_by_r(dim3 grid, hipStream_t s, const uint32_t *base, int64_t stride, int64_t n,
+                              int64_t gpw, const TreeLaunch &t) {
+    const TreeArgs ta = make_tree(t);
+    switch (t.kp / 64) {
+#define RT_CASE(RR)                                                                                                \
+    case RR:                                                                                                       \
+        hipLaunchKernelGGL((select_topk_kernel<DT, RR>), grid, dim3(kStreamThreads), 0, s, base, stride, n, gpw, ta); \
         break;
-        RT_CASE(1) RT_CASE(2) RT_CASE(4) RT_CASE(8) RT_CASE(16)
+        RT_R_CASES(RT_CASE)
 #undef RT_CASE
         default:
             return hipErrorInvalidValue;
@@ -353,14 +483,23 @@ static hipError_t select_by_r(int R, dim3 grid, hipStream_t s, const uint32_t *b
     return hipGetLastError();
 }
 
-hipError_t launch_select_topk(const void *base, int64_t seg_stride, int64_t n, int dtype, int segments, int k,
-                              int kp, int64_t groups_per_wave, int wgs_per_seg, uint64_t *wg_lists,
-                              uint64_t *seg_thr, hipStream_t stream) {
+hipError_t launch_select_topk(const void *base, int64_t seg_stride, int64_t n, int dtype, int segments,
+                              int64_t groups_per_wave, int wgs_per_seg, const TreeLaunch &t, hipStream_t stream) {
     const dim3 grid(wgs_per_seg, segments);
     const uint32_t *b = static_cast<const uint32_t *>(base);
-    if (dtype == 0) return select_by_r<0>(kp / 64, grid, stream, b, seg_stride, n, groups_per_wave, k, wg_lists, seg_thr);
-    if (dtype == 1) return select_by_r<1>(kp / 64, grid, stream, b, seg_stride, n, groups_per_wave, k, wg_lists, seg_thr);
+    if (dtype == 0) return select_by_r<0>(grid, stream, b, seg_stride, n, groups_per_wave, t);
+    if (dtype == 1) return select_by_r<1>(grid, stream, b, seg_stride, n, groups_per_wave, t);
     return hipErrorInvalidValue;
+}
+
+__global__ void zero_u32_kernel(uint32_t *p, int64_t count) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < count) p[i] = 0u;
+}
+
+hipError_t launch_zero_counters(uint32_t *counters, int64_t count, hipStream_t stream) {
+    hipLaunchKernelGGL(zero_u32_kernel, dim3((unsigned)((count + 255) / 256)), dim3(256), 0, stream, counters, count);
+    return hipGetLastError();
 }
 
 }  // namespace rt

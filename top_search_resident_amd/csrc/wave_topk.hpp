@@ -44,6 +44,8 @@ __device__ __forceinline__ uint32_t rank_index(uint64_t r) { return 0xffffffffu 
 __device__ __forceinline__ uint32_t rank_key(uint64_t r) { return (uint32_t)(r >> 32); }
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+// Index of this thread's wave in its workgroup, as a wave-uniform value.
+__device__ __forceinline__ int wave_in_group() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
     const int lo = __shfl_xor((int)(uint32_t)v, m);
@@ -57,8 +59,62 @@ __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
     return ((uint64_t)hi << 32) | lo;
 }
 
+// 16-byte streaming loads with the non-temporal hint: the corpus and raw arrays
+// are read exactly once per call, so they should not displace reused lines.
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 load_nt(const float4 *p) {
+    const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t *>(p));
+    return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ uint4 load_nt(const uint4 *p) {
+    const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a > b ? b : a; }
+
+// Cross-lane moves through DPP (no LDS round trip).  Controls: quad_perm
+// [1,0,3,2] and [2,3,0,1] swap neighbours at distance 1 and 2; row_half_mirror
+// reverses each 8-lane half-row and row_mirror each 16-lane row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppHalfMirror = 0x141;
+constexpr int kDppMirror = 0x140;
+
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+
+// Sum over each aligned group of G = 2^log2g lanes (log2g <= 6, wave-uniform).
+// Steps: neighbours at distance 1 and 2 (quad_perm), then the mirror partner in
+// the half-row and in the row -- after the earlier steps every lane of a quad
+// (resp. half-row) holds the same value, so the mirror partner stands in for the
+// xor partner -- then, for groups wider than a 16-lane row, the row sums are
+// read out and added as (r0 + r1) and ((r0 + r1) + (r2 + r3)).  Every group
+// is summed in the same fixed order, and every lane of a group ends with the
+// group's sum.
+__device__ __forceinline__ float group_sum(float v, int log2g) {
+    if (log2g >= 1) v += dpp_f32<kDppXor1>(v);
+    if (log2g >= 2) v += dpp_f32<kDppXor2>(v);
+    if (log2g >= 3) v += dpp_f32<kDppHalfMirror>(v);
+    if (log2g >= 4) v += dpp_f32<kDppMirror>(v);
+    if (log2g >= 5) {
+        const float s01 = readlane_f32(v, 0) + readlane_f32(v, 16);
+        const float s23 = readlane_f32(v, 32) + readlane_f32(v, 48);
+        if (log2g == 5) {
+            v = (lane_id() < 32) ? s01 : s23;
+        } else {
+            v = s01 + s23;
+        }
+    }
+    return v;
+}
 
 // Number of set bits of `mask` below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
@@ -153,32 +209,27 @@ __device__ __forceinline__ uint64_t list_entry(const uint64_t (&L)[R], int j) {
 
 // Per-wave streaming selector.  Candidates are appended to a 128-entry LDS
 // staging buffer private to the wave; every 64 of them are sorted and absorbed
-// into the register list.  `thr` is a rank that some set of >= k already-seen
-// elements all reach or beat, so anything at or below it can never enter the
-// top-k: it starts at 0 and rises to the list's k-th entry and to the shared
-// per-segment value that other waves publish (a global atomic max of their own
-// k-th entries).  The staging buffer and the shared threshold are passed to
-// each call (not stored) so the compiler keeps LDS addressing and keeps the
-// list in registers.
+// into the register list.  `thr` is the list's k-th entry (0 until the list holds
+// k real entries): k already-seen elements reach or beat it, so anything at or
+// below it can never enter the top-k and is not offered.  The staging buffer is
+// passed to each call (not stored) so the compiler keeps LDS addressing and
+// keeps the list in registers.
 template <int R>
 struct WaveSelector {
     uint64_t L[R];
-    uint64_t thr;        // wave-uniform
-    uint64_t published;  // wave-uniform: last value this wave pushed to the shared threshold
-    int pending;         // wave-uniform
+    uint64_t thr;  // wave-uniform
+    int pending;   // wave-uniform
     int k;
 
     __device__ __forceinline__ void init(int k_) {
 #pragma unroll
         for (int r = 0; r < R; ++r) L[r] = 0;
         thr = 0;
-        published = 0;
         pending = 0;
         k = k_;
     }
 
-    __device__ __forceinline__ void absorb_stage_front(uint64_t *__restrict__ stage, int count,
-                                                       uint64_t *__restrict__ shared) {
+    __device__ __forceinline__ void absorb_stage_front(uint64_t *__restrict__ stage, int count) {
         const int lane = lane_id();
         wave_lds_sync();
         uint64_t x = (lane < count) ? stage[lane] : 0ull;
@@ -186,22 +237,17 @@ struct WaveSelector {
         list_absorb64<R>(L, x);
         const uint64_t kth = list_entry<R>(L, k - 1);
         if (kth > thr) thr = kth;
-        if (kth > published) {
-            published = kth;
-            if (lane == 0) __hip_atomic_fetch_max(shared, kth, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
     }
 
     // Offer one rank per lane; `take` must already include rank > thr.
-    __device__ __forceinline__ void offer(uint64_t *__restrict__ stage, uint64_t *__restrict__ shared,
-                                          uint64_t rank, bool take) {
+    __device__ __forceinline__ void offer(uint64_t *__restrict__ stage, uint64_t rank, bool take) {
         const uint64_t m = __ballot(take);
         if (m == 0) return;
         const int lane = lane_id();
         if (take) stage[pending + lanes_below(m)] = rank;
         pending += __popcll(m);
         if (pending >= 64) {
-            absorb_stage_front(stage, 64, shared);
+            absorb_stage_front(stage, 64);
             const int rest = pending - 64;
             uint64_t t = 0;
             if (lane < rest) t = stage[64 + lane];
@@ -211,13 +257,8 @@ struct WaveSelector {
         }
     }
 
-    __device__ __forceinline__ void refresh(const uint64_t *shared) {
-        const uint64_t g = __hip_atomic_load(shared, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (g > thr) thr = g;
-    }
-
-    __device__ __forceinline__ void finish(uint64_t *__restrict__ stage, uint64_t *__restrict__ shared) {
-        if (pending > 0) absorb_stage_front(stage, pending, shared);
+    __device__ __forceinline__ void finish(uint64_t *__restrict__ stage) {
+        if (pending > 0) absorb_stage_front(stage, pending);
         pending = 0;
     }
 };
