@@ -1,0 +1,7 @@
+// stream_r1.hip -- streaming top-K kernels with 64-entry lists (see stream_topk.hpp).
+#include "stream_topk.hpp"
+
+namespace rt {
+template hipError_t launch_stream_r<1>(int, int, int, dim3, hipStream_t, const void *, int64_t, int, int64_t,
+                                         const float *, int64_t, const TreeLaunch &);
+}  // namespace rt

@@ -1,383 +1,19 @@
-// stream_topk.hip -- exact top-K on gfx950 in one kernel launch per call.
-//
-// "GPU-Resident Top-K for Agentic RAG" (A. Banerjee), section 4: Step 2 scores
-// every corpus row by inner product, Step 3 lets each block of rows build its
-// own best-K list, Step 4 merges the per-block lists into the global best-K, and
-// only K indices and K scores leave (Step 6).  The pages launch three kernels:
-// one thread per row for scoring (uncoalesced along D), one thread per block
-// for a bubble-sort selection, and one thread for the merge.  Here a single
-// kernel does all of it:
-//
-//   1. streaming: each wavefront reads a contiguous row range with 16-byte
-//      non-temporal coalesced loads, reduces each row's dot product across a
-//      group of lanes, and feeds the scores into a register-resident best-K
-//      list (wave_topk.hpp) -- the N scores never reach HBM;
-//   2. the four waves of a workgroup merge their lists into one (LDS);
-//   3. merge tree: workgroups are grouped `fan` at a time; each workgroup stores
-//      its list, and the LAST workgroup of a group to finish (a global atomic
-//      counter per group, after a device-scope release fence) loads the group's
-//      lists, merges them and moves one level up; the last one at the root
-//      writes the K outputs.  Nothing waits on anything (a workgroup that is not
-//      last simply exits), and each counter is cleared by the workgroup that
-//      completes it, ready for the next call.
-//
-// Exactness of the two stages: the top-K of the union of per-block top-K lists
-// is the global top-K (anything that beats an element inside its block beats it
-// globally), so the grouping is free.
-//
-// The raw-array kernel is the two-stage top-K of "CUDA Programming Model Series
-// 9: Efficient TopK" (section 2: each block reduces its share to a local top-K;
-// section 3: a second stage merges the local results), with vector loads, the
-// same register lists and the same merge tree.
-#include "kernels.hpp"
-#include "wave_topk.hpp"
+// stream_topk.hip -- host-side dispatch of the streaming top-K kernels
+// (stream_topk.hpp); the kernels for each list size are instantiated in their
+// own translation unit (stream_r*.hip) so they compile in parallel.
+#include "stream_topk.hpp"
 
 namespace rt {
 
-struct TreeArgs {
-    uint64_t *tree;          // per segment: seg_tree_stride ranks of list storage
-    uint32_t *counters;      // per segment: seg_ctr_stride arrival counters (zero between calls)
-    int64_t seg_tree_stride;
-    int seg_ctr_stride;
-    int fan;                 // lists merged per tree node (power of two, fan * Kp <= kTreeEntries)
-    int k;
-    int mode;                // 1: write index + fp32 score from the rank; 2: index + source element
-    int32_t *out_idx;        // [segments][k]
-    uint32_t *out_val;       // [segments][k]
-    const uint32_t *src;     // mode 2: the array the ranks index into
-    int64_t src_seg_stride;
-};
-
-__device__ __forceinline__ void write_output(const TreeArgs &ta, int seg, int r, uint64_t v) {
-    const uint32_t idx = rank_index(v);
-    ta.out_idx[(int64_t)seg * ta.k + r] = (int32_t)idx;
-    ta.out_val[(int64_t)seg * ta.k + r] =
-        (ta.mode == 1) ? __float_as_uint(f32_of_order_key(rank_key(v))) : ta.src[(int64_t)seg * ta.src_seg_stride + idx];
-}
-
-// Merge `count` (1 <= count <= fan) best-first lists of 64*R ranks, stored
-// contiguously at `src`, into sm[0 .. 64*R).  Pairs of lists are merged by one
-// wave each, level by level.
 template <int R>
-__device__ __forceinline__ void merge_lists_into_lds(const uint64_t *src, int count, uint64_t *sm) {
-    constexpr int Kp = 64 * R;
-    const int lane = lane_id();
-    const int wv = wave_in_group();
-    const int nwaves = blockDim.x >> 6;
-    for (int i = threadIdx.x; i < count * Kp; i += blockDim.x) sm[i] = src[i];
-    __syncthreads();
-    for (int s = 1; s < count; s <<= 1) {
-        for (int a = wv * 2 * s; a + s < count; a += nwaves * 2 * s) {
-            uint64_t A[R], B[R];
-#pragma unroll
-            for (int r = 0; r < R; ++r) {
-                A[r] = sm[a * Kp + r * 64 + lane];
-                B[r] = sm[(a + s) * Kp + r * 64 + lane];
-            }
-            list_absorb_list<R>(A, B);
-#pragma unroll
-            for (int r = 0; r < R; ++r) sm[a * Kp + r * 64 + lane] = A[r];
-        }
-        __syncthreads();
-    }
-}
-
-// Steps 2 and 3 above.  `sm` is kTreeEntries ranks of LDS; `s_flag` an int in LDS.
-template <int R>
-__device__ __forceinline__ void finish_workgroup(WaveSelector<R> &sel, uint64_t *sm, int *s_flag,
-                                                 const TreeArgs &ta, int seg) {
-    constexpr int Kp = 64 * R;
-    const int lane = lane_id();
-    const int wv = wave_in_group();
-
-    // 2. the workgroup's four wave lists -> one list in wave 0's registers.
-#pragma unroll
-    for (int r = 0; r < R; ++r) sm[wv * Kp + r * 64 + lane] = sel.L[r];
-    __syncthreads();
-    if ((wv & 1) == 0) {
-        uint64_t M[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) M[r] = sm[(wv + 1) * Kp + r * 64 + lane];
-        list_absorb_list<R>(sel.L, M);
-#pragma unroll
-        for (int r = 0; r < R; ++r) sm[wv * Kp + r * 64 + lane] = sel.L[r];
-    }
-    __syncthreads();
-    int count = gridDim.x;
-    if (wv == 0) {
-        uint64_t M[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) M[r] = sm[2 * Kp + r * 64 + lane];
-        list_absorb_list<R>(sel.L, M);
-        if (count == 1) {
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-                if (r * 64 + lane < ta.k) write_output(ta, seg, r * 64 + lane, sel.L[r]);
-        }
-    }
-    if (count == 1) return;
-
-    // 3. merge tree over the workgroups of this segment.
-    uint64_t *base = ta.tree + (int64_t)seg * ta.seg_tree_stride;
-    uint32_t *ctr = ta.counters + (int64_t)seg * ta.seg_ctr_stride;
-    int node = blockIdx.x;
-    int64_t level_off = 0;
-    int ctr_off = 0;
-    if (wv == 0) {
-#pragma unroll
-        for (int r = 0; r < R; ++r) base[(int64_t)node * Kp + r * 64 + lane] = sel.L[r];
-    }
-    while (true) {
-        const int parent = node / ta.fan;
-        const int first = parent * ta.fan;
-        const int children = (count - first < ta.fan) ? count - first : ta.fan;
-        __threadfence();  // release this workgroup's list to the other XCDs
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const uint32_t arrived = atomicAdd(&ctr[ctr_off + parent], 1u);
-            const int last = (int)(arrived + 1 == (uint32_t)children);
-            if (last) ctr[ctr_off + parent] = 0u;  // all children have arrived: clear for the next call
-            *s_flag = last;
-        }
-        __syncthreads();
-        if (!*s_flag) return;
-        __threadfence();  // acquire the siblings' lists
-        merge_lists_into_lds<R>(base + level_off + (int64_t)first * Kp, children, sm);
-        const int up = (count + ta.fan - 1) / ta.fan;
-        if (up == 1) {
-            for (int r = threadIdx.x; r < ta.k; r += blockDim.x) write_output(ta, seg, r, sm[r]);
-            return;
-        }
-        const int64_t next_off = level_off + (int64_t)count * Kp;
-        for (int i = threadIdx.x; i < Kp; i += blockDim.x) base[next_off + (int64_t)parent * Kp + i] = sm[i];
-        level_off = next_off;
-        ctr_off += up;
-        node = parent;
-        count = up;
-        __syncthreads();
-    }
-}
-
-// ---------------------------------------------------------------- scoring
-
-// Rows each lane group takes per step.  Measured on MI355X at 1M x 1024: one row
-// per step with ~8 waves per CU keeps HBM near 89% of peak; larger unrolls only
-// add register pressure.  Rows of a single float4 per lane take two.
-template <int L>
-struct RowUnroll {
-    static constexpr int value = (L == 1) ? 2 : 1;
-};
-
-// A group of G = 2^log2g lanes owns one row at a time; lane g of the group loads
-// float4 columns g, g+G, ..., g+(L-1)G of that row (masked past d/4), so a row is
-// covered by one instruction per j and consecutive lanes read consecutive 16 B.
-// Every row is reduced in exactly the same order (per-lane FMA chain over j and
-// the four components, then an xor butterfly over the group), so identical rows
-// get bit-identical scores wherever they sit, and exact ties resolve by index.
-template <int L, int R>
-__global__ __launch_bounds__(kStreamThreads) void gemv_topk_kernel(
-    const float *__restrict__ corpus, int64_t n, int d, int log2g, const float *__restrict__ queries,
-    int64_t rows_per_wave, TreeArgs ta) {
-    constexpr int U = RowUnroll<L>::value;
-    __shared__ uint64_t stage[kStreamWaves][128];
-    __shared__ uint64_t sm[kTreeEntries];
-    __shared__ int s_flag;
-
-    const int seg = blockIdx.y;
-    const int lane = lane_id();
-    const int wv = wave_in_group();
-    const int64_t wave = (int64_t)blockIdx.x * kStreamWaves + wv;
-    const int G = 1 << log2g;
-    const int g = lane & (G - 1);
-    const int h = lane >> log2g;
-    const int rps = 64 >> log2g;
-    const int d4 = d >> 2;
-    const bool padded = G * L != d4;  // some lanes' columns fall past the row end
-    const float4 *__restrict__ c4 = reinterpret_cast<const float4 *>(corpus);
-    const float4 *__restrict__ q4 = reinterpret_cast<const float4 *>(queries + (int64_t)seg * d);
-    uint64_t *const my_stage = stage[wv];
-
-    WaveSelector<R> sel;
-    sel.init(ta.k);
-
-    // Columns past the row end are clamped to the last column for the load and
-    // their values replaced by 0, so every load is unconditional.
-    float4 qv[L];
-    int colc[L];
-#pragma unroll
-    for (int j = 0; j < L; ++j) {
-        const int col = j * G + g;
-        colc[j] = (col < d4) ? col : d4 - 1;
-        qv[j] = (col < d4) ? q4[col] : make_float4(0.f, 0.f, 0.f, 0.f);
-    }
-
-    const int64_t r_begin = wave * rows_per_wave;
-    const int64_t r_end = (r_begin + rows_per_wave < n) ? r_begin + rows_per_wave : n;
-    for (int64_t r0 = r_begin; r0 < r_end; r0 += (int64_t)rps * U) {
-        float4 x[U][L];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t row = r0 + u * rps + h;
-            const float4 *rp = c4 + ((row < r_end) ? row : r_end - 1) * d4;  // rows past the range: reload the last
-#pragma unroll
-            for (int j = 0; j < L; ++j) x[u][j] = load_nt(rp + colc[j]);
-        }
-        if (padded) {
-#pragma unroll
-            for (int j = 0; j < L; ++j) {
-                if (j * G + g >= d4) {
-#pragma unroll
-                    for (int u = 0; u < U; ++u) x[u][j] = make_float4(0.f, 0.f, 0.f, 0.f);
-                }
-            }
-        }
-        float acc[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float a = 0.f;
-#pragma unroll
-            for (int j = 0; j < L; ++j) {
-                a = fmaf(x[u][j].x, qv[j].x, a);
-                a = fmaf(x[u][j].y, qv[j].y, a);
-                a = fmaf(x[u][j].z, qv[j].z, a);
-                a = fmaf(x[u][j].w, qv[j].w, a);
-            }
-            acc[u] = group_sum(a, log2g);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t row = r0 + u * rps + h;
-            const bool valid = (g == 0) && (row < r_end);
-            const uint64_t rank = make_rank(order_key_f32(acc[u]), (uint32_t)row);
-            sel.offer(my_stage, rank, valid && rank > sel.thr);
-        }
-    }
-    sel.finish(my_stage);
-    finish_workgroup<R>(sel, sm, &s_flag, ta, seg);
-}
-
-// Any d: one row per wave at a time, scalar loads strided by 64 lanes.
-template <int R>
-__global__ __launch_bounds__(kStreamThreads) void gemv_topk_generic_kernel(
-    const float *__restrict__ corpus, int64_t n, int d, const float *__restrict__ queries,
-    int64_t rows_per_wave, TreeArgs ta) {
-    constexpr int U = 4;
-    __shared__ uint64_t stage[kStreamWaves][128];
-    __shared__ uint64_t sm[kTreeEntries];
-    __shared__ int s_flag;
-    const int seg = blockIdx.y;
-    const int lane = lane_id();
-    const int wv = wave_in_group();
-    const int64_t wave = (int64_t)blockIdx.x * kStreamWaves + wv;
-    const float *__restrict__ q = queries + (int64_t)seg * d;
-    uint64_t *const my_stage = stage[wv];
-    WaveSelector<R> sel;
-    sel.init(ta.k);
-    const int64_t r_begin = wave * rows_per_wave;
-    const int64_t r_end = (r_begin + rows_per_wave < n) ? r_begin + rows_per_wave : n;
-    for (int64_t r0 = r_begin; r0 < r_end; r0 += U) {
-        float acc[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) acc[u] = 0.f;
-        for (int c = lane; c < d; c += 64) {
-            const float qc = q[c];
-#pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int64_t row = r0 + u;
-                const float x = (row < r_end) ? corpus[row * d + c] : 0.f;
-                acc[u] = fmaf(x, qc, acc[u]);
-            }
-        }
-        for (int m = 32; m >= 1; m >>= 1) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) acc[u] += __shfl_xor(acc[u], m);
-        }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t row = r0 + u;
-            const bool valid = (lane == 0) && (row < r_end);
-            const uint64_t rank = make_rank(order_key_f32(acc[u]), (uint32_t)row);
-            sel.offer(my_stage, rank, valid && rank > sel.thr);
-        }
-    }
-    sel.finish(my_stage);
-    finish_workgroup<R>(sel, sm, &s_flag, ta, seg);
-}
-
-// ---------------------------------------------------------------- raw arrays
-
-// Segment `seg` is the n-element array at base + seg * seg_stride (32-bit
-// elements).  It is read as 16-byte groups of the enclosing aligned range: group
-// t holds elements 4t - head .. 4t - head + 3, where head = (address mod 16) / 4.
-// Elements outside [0, n) are masked.  An aligned 16-byte group never crosses a
-// page, so reading the part of a group outside the array cannot fault.
-template <int DT, int R>
-__global__ __launch_bounds__(kStreamThreads) void select_topk_kernel(
-    const uint32_t *__restrict__ base, int64_t seg_stride, int64_t n, int64_t groups_per_wave, TreeArgs ta) {
-    constexpr int U = 4;
-    __shared__ uint64_t stage[kStreamWaves][128];
-    __shared__ uint64_t sm[kTreeEntries];
-    __shared__ int s_flag;
-    const int seg = blockIdx.y;
-    const int lane = lane_id();
-    const int wv = wave_in_group();
-    const int64_t wave = (int64_t)blockIdx.x * kStreamWaves + wv;
-    const uintptr_t addr = reinterpret_cast<uintptr_t>(base + seg * seg_stride);
-    const int head = (int)((addr & 15u) >> 2);
-    const uint4 *__restrict__ a4 = reinterpret_cast<const uint4 *>(addr - (uintptr_t)head * 4u);
-    const int64_t total_groups = (n + head + 3) >> 2;
-    uint64_t *const my_stage = stage[wv];
-
-    WaveSelector<R> sel;
-    sel.init(ta.k);
-    const int64_t g_begin = wave * groups_per_wave;
-    const int64_t g_end = (g_begin + groups_per_wave < total_groups) ? g_begin + groups_per_wave : total_groups;
-    for (int64_t g0 = g_begin; g0 < g_end; g0 += 64 * U) {
-        uint4 v[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t grp = g0 + u * 64 + lane;
-            v[u] = load_nt(a4 + ((grp < g_end) ? grp : g_end - 1));  // past the range: reload the last group (masked below)
-        }
-        uint32_t key[U][4];
-        bool any = false;
-        const uint32_t thr_key = rank_key(sel.thr);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-            const int64_t grp = g0 + u * 64 + lane;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                key[u][c] = (DT == 0) ? order_key_i32((int32_t)e[c]) : order_key_f32(__uint_as_float(e[c]));
-                const int64_t idx = grp * 4 + c - head;
-                const bool valid = (grp < g_end) && idx >= 0 && idx < n;
-                any |= valid && key[u][c] >= thr_key;
-            }
-        }
-        if (__ballot(any) == 0) continue;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t grp = g0 + u * 64 + lane;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int64_t idx = grp * 4 + c - head;
-                const bool valid = (grp < g_end) && idx >= 0 && idx < n;
-                const uint64_t rank = make_rank(key[u][c], (uint32_t)idx);
-                sel.offer(my_stage, rank, valid && rank > sel.thr);
-            }
-        }
-    }
-    sel.finish(my_stage);
-    finish_workgroup<R>(sel, sm, &s_flag, ta, seg);
-}
-
-// ---------------------------------------------------------------- launchers
+hipError_t launch_stream_r(int kind, int lg, int L, dim3 grid, hipStream_t s, const void *data, int64_t n, int d,
+                           int64_t seg_stride, const float *queries, int64_t per_wave, const TreeLaunch &t);
 
 bool gemv_fast_path_ok(int d) { return d % 4 == 0 && d / 4 <= 64 * 8; }
 
 int tree_fan(int kp) { return kTreeEntries / kp; }
 
-// Pick the lane-group width G (power of two <= 64) and loads per lane L (from
+// Pick the lane-group width G = 2^lg (<= 64) and loads per lane L (from
 // {1, 2, 3, 4, 6, 8}) that waste the fewest lane slots on a row, preferring wide
 // groups on ties.
 static void pick_group(int d4, int *log2g, int *L) {
@@ -400,96 +36,32 @@ static void pick_group(int d4, int *log2g, int *L) {
     *L = best_L;
 }
 
-static TreeArgs make_tree(const TreeLaunch &t) {
-    TreeArgs ta;
-    ta.tree = t.tree;
-    ta.counters = t.counters;
-    ta.seg_tree_stride = t.seg_tree_stride;
-    ta.seg_ctr_stride = t.seg_ctr_stride;
-    ta.fan = tree_fan(t.kp);
-    ta.k = t.k;
-    ta.mode = t.mode;
-    ta.out_idx = t.out_idx;
-    ta.out_val = static_cast<uint32_t *>(t.out_val);
-    ta.src = static_cast<const uint32_t *>(t.src);
-    ta.src_seg_stride = t.src_seg_stride;
-    return ta;
-}
-
-#define RT_R_CASES(MACRO) MACRO(1) MACRO(2) MACRO(4) MACRO(8) MACRO(16)
-
-template <int L>
-static hipError_t gemv_by_r(dim3 grid, hipStream_t s, const float *corpus, int64_t n, int d, int lg, const float *q,
-                            int64_t rpw, const TreeLaunch &t) {
-    const TreeArgs ta = make_tree(t);
+static hipError_t dispatch(int kind, int lg, int L, dim3 grid, hipStream_t s, const void *data, int64_t n, int d,
+                           int64_t seg_stride, const float *queries, int64_t per_wave, const TreeLaunch &t) {
     switch (t.kp / 64) {
-#define RT_CASE(RR)                                                                                                 \
-    case RR:                                                                                                        \
-        hipLaunchKernelGGL((gemv_topk_kernel<L, RR>), grid, dim3(kStreamThreads), 0, s, corpus, n, d, lg, q, rpw, ta); \
-        break;
-        RT_R_CASES(RT_CASE)
-#undef RT_CASE
-        default:
-            return hipErrorInvalidValue;
+        case 1: return launch_stream_r<1>(kind, lg, L, grid, s, data, n, d, seg_stride, queries, per_wave, t);
+        case 2: return launch_stream_r<2>(kind, lg, L, grid, s, data, n, d, seg_stride, queries, per_wave, t);
+        case 4: return launch_stream_r<4>(kind, lg, L, grid, s, data, n, d, seg_stride, queries, per_wave, t);
+        case 8: return launch_stream_r<8>(kind, lg, L, grid, s, data, n, d, seg_stride, queries, per_wave, t);
+        case 16: return launch_stream_r<16>(kind, lg, L, grid, s, data, n, d, seg_stride, queries, per_wave, t);
+        default: return hipErrorInvalidValue;
     }
-    return hipGetLastError();
 }
 
 hipError_t launch_gemv_topk(const float *corpus, int64_t n, int d, const float *queries, int segments,
                             int64_t rows_per_wave, int wgs_per_seg, const TreeLaunch &t, hipStream_t stream) {
     const dim3 grid(wgs_per_seg, segments);
-    if (!gemv_fast_path_ok(d)) {
-        const TreeArgs ta = make_tree(t);
-        switch (t.kp / 64) {
-#define RT_CASE(RR)                                                                                            \
-    case RR:                                                                                                   \
-        hipLaunchKernelGGL((gemv_topk_generic_kernel<RR>), grid, dim3(kStreamThreads), 0, stream, corpus, n, d, \
-                           queries, rows_per_wave, ta);                                                        \
-        break;
-            RT_R_CASES(RT_CASE)
-#undef RT_CASE
-            default:
-                return hipErrorInvalidValue;
-        }
-        return hipGetLastError();
-    }
+    if (!gemv_fast_path_ok(d)) return dispatch(1, 0, 0, grid, stream, corpus, n, d, 0, queries, rows_per_wave, t);
     int lg = 6, L = 8;
     pick_group(d / 4, &lg, &L);
-    switch (L) {
-        case 1: return gemv_by_r<1>(grid, stream, corpus, n, d, lg, queries, rows_per_wave, t);
-        case 2: return gemv_by_r<2>(grid, stream, corpus, n, d, lg, queries, rows_per_wave, t);
-        case 3: return gemv_by_r<3>(grid, stream, corpus, n, d, lg, queries, rows_per_wave, t);
-        case 4: return gemv_by_r<4>(grid, stream, corpus, n, d, lg, queries, rows_per_wave, t);
-        case 6: return gemv_by_r<6>(grid, stream, corpus, n, d, lg, queries, rows_per_wave, t);
-        case 8: return gemv_by_r<8>(grid, stream, corpus, n, d, lg, queries, rows_per_wave, t);
-        default: return hipErrorInvalidValue;
-    }
-}
-
-template <int DT>
-static hipError_t select_by_r(dim3 grid, hipStream_t s, const uint32_t *base, int64_t stride, int64_t n,
-                              int64_t gpw, const TreeLaunch &t) {
-    const TreeArgs ta = make_tree(t);
-    switch (t.kp / 64) {
-#define RT_CASE(RR)                                                                                                \
-    case RR:                                                                                                       \
-        hipLaunchKernelGGL((select_topk_kernel<DT, RR>), grid, dim3(kStreamThreads), 0, s, base, stride, n, gpw, ta); \
-        break;
-        RT_R_CASES(RT_CASE)
-#undef RT_CASE
-        default:
-            return hipErrorInvalidValue;
-    }
-    return hipGetLastError();
+    return dispatch(0, lg, L, grid, stream, corpus, n, d, 0, queries, rows_per_wave, t);
 }
 
 hipError_t launch_select_topk(const void *base, int64_t seg_stride, int64_t n, int dtype, int segments,
                               int64_t groups_per_wave, int wgs_per_seg, const TreeLaunch &t, hipStream_t stream) {
     const dim3 grid(wgs_per_seg, segments);
-    const uint32_t *b = static_cast<const uint32_t *>(base);
-    if (dtype == 0) return select_by_r<0>(grid, stream, b, seg_stride, n, groups_per_wave, t);
-    if (dtype == 1) return select_by_r<1>(grid, stream, b, seg_stride, n, groups_per_wave, t);
-    return hipErrorInvalidValue;
+    if (dtype != 0 && dtype != 1) return hipErrorInvalidValue;
+    return dispatch(2 + dtype, 0, 0, grid, stream, base, n, 0, seg_stride, nullptr, groups_per_wave, t);
 }
 
 __global__ void zero_u32_kernel(uint32_t *p, int64_t count) {

@@ -1,0 +1,444 @@
+// stream_topk.hpp -- exact top-K on gfx950 in one kernel launch per call.
+//
+// "GPU-Resident Top-K for Agentic RAG" (A. Banerjee), section 4: Step 2 scores
+// every corpus row by inner product, Step 3 lets each block of rows build its
+// own best-K list, Step 4 merges the per-block lists into the global best-K, and
+// only K indices and K scores leave (Step 6).  The pages launch three kernels:
+// one thread per row for scoring (uncoalesced along D), one thread per block
+// for a bubble-sort selection, and one thread for the merge.  Here a single
+// kernel does all of it:
+//
+//   1. streaming: each wavefront reads a contiguous row range with 16-byte
+//      non-temporal coalesced loads, reduces each row's dot product across a
+//      group of lanes, and feeds the scores into a register-resident best-K
+//      list (wave_topk.hpp) -- the N scores never reach HBM;
+//   2. the four waves of a workgroup merge their lists into one (LDS);
+//   3. merge tree: workgroups are grouped `fan` at a time; each workgroup stores
+//      its list, and the LAST workgroup of a group to finish (a global atomic
+//      counter per group) loads the group's lists, merges them and moves one
+//      level up; the last one at the root writes the K outputs.  Nothing waits
+//      on anything (a workgroup that is not last simply exits), and each counter
+//      is cleared by the workgroup that completes it, ready for the next call.
+//      The lists cross XCDs (each XCD has its own L2), so they are written and
+//      read with device-coherent (agent-scope) atomic stores and loads, and a
+//      workgroup waits for its stores to complete before it arrives at the
+//      counter.  A device-scope release fence would do the same job but writes
+//      back the whole L2 of the XCD; issued by every workgroup it cost ~0.2 us
+//      each, serialised (~95 us per call at 512 workgroups on MI355X).
+//
+// Exactness of the two stages: the top-K of the union of per-block top-K lists
+// is the global top-K (anything that beats an element inside its block beats it
+// globally), so the grouping is free.
+//
+// The raw-array kernel is the two-stage top-K of "CUDA Programming Model Series
+// 9: Efficient TopK" (section 2: each block reduces its share to a local top-K;
+// section 3: a second stage merges the local results), with vector loads, the
+// same register lists and the same merge tree.
+#pragma once
+#include "kernels.hpp"
+#include "wave_topk.hpp"
+
+namespace rt {
+
+struct TreeArgs {
+    uint64_t *tree;          // per segment: seg_tree_stride ranks of list storage
+    uint32_t *counters;      // per segment: seg_ctr_stride arrival counters (zero between calls)
+    int64_t seg_tree_stride;
+    int seg_ctr_stride;
+    int fan;                 // lists merged per tree node (power of two, fan * Kp <= kTreeEntries)
+    int k;
+    int mode;                // 1: write index + fp32 score from the rank; 2: index + source element
+    int32_t *out_idx;        // [segments][k]
+    uint32_t *out_val;       // [segments][k]
+    const uint32_t *src;     // mode 2: the array the ranks index into
+    int64_t src_seg_stride;
+};
+
+__device__ __forceinline__ void write_output(const TreeArgs &ta, int seg, int r, uint64_t v) {
+    const uint32_t idx = rank_index(v);
+    ta.out_idx[(int64_t)seg * ta.k + r] = (int32_t)idx;
+    ta.out_val[(int64_t)seg * ta.k + r] =
+        (ta.mode == 1) ? __float_as_uint(f32_of_order_key(rank_key(v))) : ta.src[(int64_t)seg * ta.src_seg_stride + idx];
+}
+
+// Merge `count` (1 <= count <= fan) best-first lists of 64*R ranks, stored
+// contiguously at `src`, into sm[0 .. 64*R).  Pairs of lists are merged by one
+// wave each, level by level.
+template <int R>
+__device__ __forceinline__ void merge_lists_into_lds(const uint64_t *src, int count, uint64_t *sm) {
+    constexpr int Kp = 64 * R;
+    const int lane = lane_id();
+    const int wv = wave_in_group();
+    const int nwaves = blockDim.x >> 6;
+    for (int i = threadIdx.x; i < count * Kp; i += blockDim.x)
+        sm[i] = __hip_atomic_load(&src[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    for (int s = 1; s < count; s <<= 1) {
+        for (int a = wv * 2 * s; a + s < count; a += nwaves * 2 * s) {
+            uint64_t A[R], B[R];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                A[r] = sm[a * Kp + r * 64 + lane];
+                B[r] = sm[(a + s) * Kp + r * 64 + lane];
+            }
+            list_absorb_list<R>(A, B);
+#pragma unroll
+            for (int r = 0; r < R; ++r) sm[a * Kp + r * 64 + lane] = A[r];
+        }
+        __syncthreads();
+    }
+}
+
+// Steps 2 and 3 above.  `sm` is kTreeEntries ranks of LDS; `s_flag` an int in LDS.
+template <int R>
+__device__ __forceinline__ void finish_workgroup(WaveSelector<R> &sel, uint64_t *sm, int *s_flag,
+                                                 const TreeArgs &ta, int seg) {
+    constexpr int Kp = 64 * R;
+    const int lane = lane_id();
+    const int wv = wave_in_group();
+
+    // 2. the workgroup's four wave lists -> one list in wave 0's registers.
+#pragma unroll
+    for (int r = 0; r < R; ++r) sm[wv * Kp + r * 64 + lane] = sel.L[r];
+    __syncthreads();
+    if ((wv & 1) == 0) {
+        uint64_t M[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) M[r] = sm[(wv + 1) * Kp + r * 64 + lane];
+        list_absorb_list<R>(sel.L, M);
+#pragma unroll
+        for (int r = 0; r < R; ++r) sm[wv * Kp + r * 64 + lane] = sel.L[r];
+    }
+    __syncthreads();
+    int count = gridDim.x;
+    if (wv == 0) {
+        uint64_t M[R];
+#pragma unroll
+        for (int r = 0; r < R; ++r) M[r] = sm[2 * Kp + r * 64 + lane];
+        list_absorb_list<R>(sel.L, M);
+        if (count == 1) {
+#pragma unroll
+            for (int r = 0; r < R; ++r)
+                if (r * 64 + lane < ta.k) write_output(ta, seg, r * 64 + lane, sel.L[r]);
+        }
+    }
+    if (count == 1) return;
+
+    // 3. merge tree over the workgroups of this segment.
+    uint64_t *base = ta.tree + (int64_t)seg * ta.seg_tree_stride;
+    uint32_t *ctr = ta.counters + (int64_t)seg * ta.seg_ctr_stride;
+    int node = blockIdx.x;
+    int64_t level_off = 0;
+    int ctr_off = 0;
+    if (wv == 0) {
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+            __hip_atomic_store(&base[(int64_t)node * Kp + r * 64 + lane], sel.L[r], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+    }
+    while (true) {
+        const int parent = node / ta.fan;
+        const int first = parent * ta.fan;
+        const int children = (count - first < ta.fan) ? count - first : ta.fan;
+        __builtin_amdgcn_s_waitcnt(0);  // this thread's coherent list stores have completed
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const uint32_t arrived = atomicAdd(&ctr[ctr_off + parent], 1u);
+            const int last = (int)(arrived + 1 == (uint32_t)children);
+            if (last)  // all children have arrived: clear for the next call
+                __hip_atomic_store(&ctr[ctr_off + parent], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            *s_flag = last;
+        }
+        __syncthreads();
+        if (!*s_flag) return;
+        merge_lists_into_lds<R>(base + level_off + (int64_t)first * Kp, children, sm);
+        const int up = (count + ta.fan - 1) / ta.fan;
+        if (up == 1) {
+            for (int r = threadIdx.x; r < ta.k; r += blockDim.x) write_output(ta, seg, r, sm[r]);
+            return;
+        }
+        const int64_t next_off = level_off + (int64_t)count * Kp;
+        for (int i = threadIdx.x; i < Kp; i += blockDim.x)
+            __hip_atomic_store(&base[next_off + (int64_t)parent * Kp + i], sm[i], __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        level_off = next_off;
+        ctr_off += up;
+        node = parent;
+        count = up;
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------- scoring
+
+// Rows each lane group takes per step.  Measured on MI355X at 1M x 1024: one row
+// per step with ~8 waves per CU keeps HBM near 89% of peak; larger unrolls only
+// add register pressure.  Rows of a single float4 per lane take two.
+template <int L>
+struct RowUnroll {
+    static constexpr int value = (L == 1) ? 2 : 1;
+};
+
+// A group of G = 2^LG lanes owns one row at a time; lane g of the group loads
+// float4 columns g, g+G, ..., g+(L-1)G of that row, so a row is covered by one
+// instruction per j and consecutive lanes read consecutive 16 B.  Columns past
+// the row end (when G*L > d/4) are loaded from the last column and replaced by
+// 0, so every load is unconditional.  Every row is reduced in exactly the same
+// order (per-lane FMA chain over j and the four components, then group_sum), so
+// identical rows get bit-identical scores wherever they sit, and exact ties
+// resolve by index.
+template <int LG, int L, int R>
+__global__ __launch_bounds__(kStreamThreads) void gemv_topk_kernel(
+    const float *__restrict__ corpus, int64_t n, int d, const float *__restrict__ queries,
+    int64_t rows_per_wave, TreeArgs ta) {
+    constexpr int G = 1 << LG;
+    constexpr int RPS = 64 >> LG;  // rows per lane-group pass
+    constexpr int U = RowUnroll<L>::value;
+    constexpr int STEP = RPS * U;  // rows per wave step
+    __shared__ uint64_t stage[kStreamWaves][128];
+    __shared__ uint64_t sm[kTreeEntries];
+    __shared__ int s_flag;
+
+    const int seg = blockIdx.y;
+    const int lane = lane_id();
+    const int wv = wave_in_group();
+    const int64_t wave = (int64_t)blockIdx.x * kStreamWaves + wv;
+    const int g = lane & (G - 1);
+    const int h = lane >> LG;
+    const int d4 = d >> 2;
+    const bool padded = G * L != d4;
+    const float4 *__restrict__ q4 = reinterpret_cast<const float4 *>(queries + (int64_t)seg * d);
+    uint64_t *const my_stage = stage[wv];
+
+    WaveSelector<R> sel;
+    sel.init(ta.k);
+
+    float4 qv[L];
+    int colc[L];
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+        const int col = j * G + g;
+        colc[j] = (col < d4) ? col : d4 - 1;
+        qv[j] = (col < d4) ? q4[col] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
+    const int64_t r_begin = wave * rows_per_wave;
+    const int64_t r_end = (r_begin + rows_per_wave < n) ? r_begin + rows_per_wave : n;
+    const float4 *__restrict__ base = reinterpret_cast<const float4 *>(corpus) + r_begin * d4;
+    for (int64_t r0 = r_begin; r0 < r_end; r0 += STEP, base += (int64_t)STEP * d4) {
+        const bool tail = r0 + STEP > r_end;
+        float4 x[U][L];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int rel = u * RPS + h;  // row relative to r0
+            if (tail && r0 + rel >= r_end) rel = (int)(r_end - 1 - r0);  // past the range: reload the last row
+#pragma unroll
+            for (int j = 0; j < L; ++j) x[u][j] = load_nt(base + rel * d4 + colc[j]);
+        }
+        if (padded) {
+#pragma unroll
+            for (int j = 0; j < L; ++j) {
+                if (j * G + g >= d4) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) x[u][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+                }
+            }
+        }
+        float acc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            float a = 0.f;
+#pragma unroll
+            for (int j = 0; j < L; ++j) {
+                a = fmaf(x[u][j].x, qv[j].x, a);
+                a = fmaf(x[u][j].y, qv[j].y, a);
+                a = fmaf(x[u][j].z, qv[j].z, a);
+                a = fmaf(x[u][j].w, qv[j].w, a);
+            }
+            acc[u] = group_sum(a, LG);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t row = r0 + u * RPS + h;
+            const bool valid = (g == 0) && (row < r_end);
+            const uint64_t rank = make_rank(order_key_f32(acc[u]), (uint32_t)row);
+            sel.offer(my_stage, rank, valid && rank > sel.thr);
+        }
+    }
+    sel.finish(my_stage);
+    finish_workgroup<R>(sel, sm, &s_flag, ta, seg);
+}
+
+// Any d: one row per wave at a time, scalar loads strided by 64 lanes.
+template <int R>
+__global__ __launch_bounds__(kStreamThreads) void gemv_topk_generic_kernel(
+    const float *__restrict__ corpus, int64_t n, int d, const float *__restrict__ queries,
+    int64_t rows_per_wave, TreeArgs ta) {
+    constexpr int U = 4;
+    __shared__ uint64_t stage[kStreamWaves][128];
+    __shared__ uint64_t sm[kTreeEntries];
+    __shared__ int s_flag;
+    const int seg = blockIdx.y;
+    const int lane = lane_id();
+    const int wv = wave_in_group();
+    const int64_t wave = (int64_t)blockIdx.x * kStreamWaves + wv;
+    const float *__restrict__ q = queries + (int64_t)seg * d;
+    uint64_t *const my_stage = stage[wv];
+    WaveSelector<R> sel;
+    sel.init(ta.k);
+    const int64_t r_begin = wave * rows_per_wave;
+    const int64_t r_end = (r_begin + rows_per_wave < n) ? r_begin + rows_per_wave : n;
+    for (int64_t r0 = r_begin; r0 < r_end; r0 += U) {
+        float acc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) acc[u] = 0.f;
+        for (int c = lane; c < d; c += 64) {
+            const float qc = q[c];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t row = r0 + u;
+                const float x = (row < r_end) ? corpus[row * d + c] : 0.f;
+                acc[u] = fmaf(x, qc, acc[u]);
+            }
+        }
+        for (int m = 32; m >= 1; m >>= 1) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc[u] += __shfl_xor(acc[u], m);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t row = r0 + u;
+            const bool valid = (lane == 0) && (row < r_end);
+            const uint64_t rank = make_rank(order_key_f32(acc[u]), (uint32_t)row);
+            sel.offer(my_stage, rank, valid && rank > sel.thr);
+        }
+    }
+    sel.finish(my_stage);
+    finish_workgroup<R>(sel, sm, &s_flag, ta, seg);
+}
+
+// ---------------------------------------------------------------- raw arrays
+
+// Segment `seg` is the n-element array at base + seg * seg_stride (32-bit
+// elements).  It is read as 16-byte groups of the enclosing aligned range: group
+// t holds elements 4t - head .. 4t - head + 3, where head = (address mod 16) / 4.
+// Elements outside [0, n) are masked.  An aligned 16-byte group never crosses a
+// page, so reading the part of a group outside the array cannot fault.
+template <int DT, int R>
+__global__ __launch_bounds__(kStreamThreads) void select_topk_kernel(
+    const uint32_t *__restrict__ base, int64_t seg_stride, int64_t n, int64_t groups_per_wave, TreeArgs ta) {
+    constexpr int U = 4;
+    __shared__ uint64_t stage[kStreamWaves][128];
+    __shared__ uint64_t sm[kTreeEntries];
+    __shared__ int s_flag;
+    const int seg = blockIdx.y;
+    const int lane = lane_id();
+    const int wv = wave_in_group();
+    const int64_t wave = (int64_t)blockIdx.x * kStreamWaves + wv;
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(base + seg * seg_stride);
+    const int head = (int)((addr & 15u) >> 2);
+    const uint4 *__restrict__ a4 = reinterpret_cast<const uint4 *>(addr - (uintptr_t)head * 4u);
+    const int64_t total_groups = (n + head + 3) >> 2;
+    uint64_t *const my_stage = stage[wv];
+
+    WaveSelector<R> sel;
+    sel.init(ta.k);
+    const int64_t g_begin = wave * groups_per_wave;
+    const int64_t g_end = (g_begin + groups_per_wave < total_groups) ? g_begin + groups_per_wave : total_groups;
+    for (int64_t g0 = g_begin; g0 < g_end; g0 += 64 * U) {
+        uint4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t grp = g0 + u * 64 + lane;
+            v[u] = load_nt(a4 + ((grp < g_end) ? grp : g_end - 1));  // past the range: reload the last group (masked below)
+        }
+        uint32_t key[U][4];
+        bool any = false;
+        const uint32_t thr_key = rank_key(sel.thr);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+            const int64_t grp = g0 + u * 64 + lane;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                key[u][c] = (DT == 0) ? order_key_i32((int32_t)e[c]) : order_key_f32(__uint_as_float(e[c]));
+                const int64_t idx = grp * 4 + c - head;
+                const bool valid = (grp < g_end) && idx >= 0 && idx < n;
+                any |= valid && key[u][c] >= thr_key;
+            }
+        }
+        if (__ballot(any) == 0) continue;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t grp = g0 + u * 64 + lane;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int64_t idx = grp * 4 + c - head;
+                const bool valid = (grp < g_end) && idx >= 0 && idx < n;
+                const uint64_t rank = make_rank(key[u][c], (uint32_t)idx);
+                sel.offer(my_stage, rank, valid && rank > sel.thr);
+            }
+        }
+    }
+    sel.finish(my_stage);
+    finish_workgroup<R>(sel, sm, &s_flag, ta, seg);
+}
+
+// ---------------------------------------------------------------- per-list-size launchers
+
+inline TreeArgs make_tree(const TreeLaunch &t) {
+    TreeArgs ta;
+    ta.tree = t.tree;
+    ta.counters = t.counters;
+    ta.seg_tree_stride = t.seg_tree_stride;
+    ta.seg_ctr_stride = t.seg_ctr_stride;
+    ta.fan = kTreeEntries / t.kp;
+    ta.k = t.k;
+    ta.mode = t.mode;
+    ta.out_idx = t.out_idx;
+    ta.out_val = static_cast<uint32_t *>(t.out_val);
+    ta.src = static_cast<const uint32_t *>(t.src);
+    ta.src_seg_stride = t.src_seg_stride;
+    return ta;
+}
+
+// (LG, L) pairs the planner can pick for d / 4 in [1, 512] (see pick_group).
+#define RT_GEMV_SHAPES(X) \
+    X(0, 1) X(0, 3) X(1, 1) X(1, 3) X(2, 1) X(2, 3) X(3, 1) X(3, 3) X(4, 1) X(4, 3) X(5, 1) X(5, 3) \
+    X(6, 1) X(6, 2) X(6, 3) X(6, 4) X(6, 6) X(6, 8)
+
+template <int R>
+hipError_t launch_stream_r(int kind, int lg, int L, dim3 grid, hipStream_t s, const void *data, int64_t n, int d,
+                           int64_t seg_stride, const float *queries, int64_t per_wave, const TreeLaunch &t) {
+    const TreeArgs ta = make_tree(t);
+    const float *corpus = static_cast<const float *>(data);
+    switch (kind) {
+        case 0: {  // fast scoring path
+#define RT_SHAPE(LGV, LV)                                                                                      \
+    if (lg == LGV && L == LV) {                                                                                \
+        hipLaunchKernelGGL((gemv_topk_kernel<LGV, LV, R>), grid, dim3(kStreamThreads), 0, s, corpus, n, d, queries, \
+                           per_wave, ta);                                                                      \
+        return hipGetLastError();                                                                              \
+    }
+            RT_GEMV_SHAPES(RT_SHAPE)
+#undef RT_SHAPE
+            return hipErrorInvalidValue;
+        }
+        case 1:
+            hipLaunchKernelGGL((gemv_topk_generic_kernel<R>), grid, dim3(kStreamThreads), 0, s, corpus, n, d, queries,
+                               per_wave, ta);
+            return hipGetLastError();
+        case 2:
+            hipLaunchKernelGGL((select_topk_kernel<0, R>), grid, dim3(kStreamThreads), 0, s,
+                               static_cast<const uint32_t *>(data), seg_stride, n, per_wave, ta);
+            return hipGetLastError();
+        case 3:
+            hipLaunchKernelGGL((select_topk_kernel<1, R>), grid, dim3(kStreamThreads), 0, s,
+                               static_cast<const uint32_t *>(data), seg_stride, n, per_wave, ta);
+            return hipGetLastError();
+        default:
+            return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace rt
