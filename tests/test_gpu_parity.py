@@ -115,6 +115,37 @@ def test_batched_exact_arithmetic(eng):
     assert np.array_equal(g_sc.astype(np.float64), o_sc)
 
 
+@pytest.mark.parametrize("n,k", [(20_000, 1024), (100_000, 129), (70_000, 700)])
+def test_batched_large_k_all_equal_scores(eng, n, k):
+    """Every score equal: the k-th key's bin holds the whole row, so the radix
+    selector's candidates exceed its LDS sort (and, for n > 65536, its candidate
+    buffer) and the exact whole-row selection must return indices 0..k-1."""
+    d = 64
+    corpus = np.zeros((n, d), np.float32)
+    corpus[:, 0] = 1.0
+    qs = np.zeros((4, d), np.float32)
+    qs[:, 0] = np.array([0.5, 0.25, 2.0, 1.0], np.float32)
+    g_idx, g_sc = _search(eng, corpus, qs, k)
+    for qi in range(4):
+        assert list(g_idx[qi]) == list(range(k)), qi
+        assert np.all(g_sc[qi] == qs[qi, 0])
+
+
+def test_batched_large_k_ties_and_tail(eng):
+    """A crowded k-th bin with exact integer ties, followed by the normal radix
+    path on the next call (the counters and histograms must have been cleared)."""
+    corpus = workloads.small_int_matrix(30_000, 32, lo=-1, hi=1, config_id=9)
+    qs = workloads.small_int_matrix(8, 32, lo=-1, hi=1, config_id=9, stream=1)
+    for k in (1024, 300):
+        g_idx, g_sc = _search(eng, corpus, qs, k)
+        o_idx, o_sc = oracle.search(corpus, qs, k)
+        assert np.array_equal(g_idx, o_idx), k
+        assert np.array_equal(g_sc.astype(np.float64), o_sc), k
+    gauss = workloads.gaussian_rows(50_000, 256, config_id=10)
+    gq = workloads.gaussian_rows(8, 256, config_id=10, stream=1)
+    _check_against_oracle(eng, gauss, gq, 500)
+
+
 def test_deterministic_repeat(eng):
     corpus = workloads.gaussian_rows(60_000, 768, config_id=12)
     qs = workloads.gaussian_rows(4, 768, config_id=12, stream=1)
