@@ -38,6 +38,25 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "queries/s + p50 latency at N=1M,D=1024,K∈{8,32,100}; % of HBM peak"
 
 
+def measured_traffic():
+    """HBM bytes per launch of the scan kernel from the committed PMC summary,
+    if it was taken on the current kernel sources (else None)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemv_topk_1m_x_1024_traffic.json")
+    try:
+        with open(path) as f:
+            data = json.load(f)
+        h = hashlib.sha256()
+        for src in data["kernel_sources"]:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        if h.hexdigest() != data["kernel_sources_sha256"]:
+            return None
+        return float(data["traffic_bytes_per_launch"]["mean over K=8,32,100"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def pct(a, p):
     return float(np.percentile(np.asarray(a), p))
 
@@ -188,7 +207,9 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
                    "n": n, "d": d, "ks": list(ks), "queries_per_step": len(ks)},
         "per_k": per_k,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": measured_traffic() if (n, d, ks) == (1_000_000, 1024, (8, 32, 100)) else None,
+                     "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, profiles/)",
                      "kernel": "gemv_topk_kernel (fused scoring, per-wave top-K lists and merge tree)",
                      "bytes_per_launch": corpus_bytes, "avg_launch_us": avg_ms * 1e3},
         "input_gen_s": gen_s,
