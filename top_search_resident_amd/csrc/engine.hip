@@ -28,9 +28,10 @@ constexpr int64_t kMaxWgsPerSeg = 2048;
 constexpr int64_t kRadixCandCap = int64_t(1) << 16;
 // Lists longer than this use the radix selector on materialised batch scores.
 constexpr int kMaxListForBatch = 128;
-// Streaming waves per CU the planner aims for: about 8 keeps HBM near its
-// measured ceiling at 1M x 1024 on MI355X.
-constexpr int64_t kWavesPerCu = 8;
+// Streaming waves per CU the planner aims for (measured on MI355X): about 8 for
+// the scorer (1M x 1024), 16 for raw-array selection (1e8 int32).
+constexpr int64_t kScoreWavesPerCu = 8;
+constexpr int64_t kSelectWavesPerCu = 16;
 
 int kp_for(int k) {
     int kp = 64;
@@ -44,20 +45,21 @@ struct Plan {
 };
 
 // Split `units` (rows or 16-byte groups) of each of `segments` segments over
-// waves: at least `min_per_wave` units per wave, about kWavesPerCu waves per CU
+// waves: at least `min_per_wave` units per wave, about waves_per_cu waves per CU
 // in total, and the merge tree (<= 2 lists per workgroup) must fit its storage.
-Plan plan_stream(int64_t units, int segments, int kp, int64_t min_per_wave, int num_cus) {
-    int64_t target = (int64_t)num_cus * kWavesPerCu / segments;
-    if (target < rt::kStreamWaves) target = rt::kStreamWaves;
+Plan plan_stream(int64_t units, int segments, int kp, int64_t min_per_wave, int num_cus, int64_t waves_per_cu,
+                 int waves_per_wg) {
+    int64_t target = (int64_t)num_cus * waves_per_cu / segments;
+    if (target < waves_per_wg) target = waves_per_wg;
     int64_t waves = (units + min_per_wave - 1) / min_per_wave;
     if (waves > target) waves = target;
     if (waves < 1) waves = 1;
-    int64_t wgs = (waves + rt::kStreamWaves - 1) / rt::kStreamWaves;
+    int64_t wgs = (waves + waves_per_wg - 1) / waves_per_wg;
     const int64_t cap = kTreeRanks / ((int64_t)segments * 2 * kp);
     if (wgs > cap) wgs = cap;
     if (wgs > kMaxWgsPerSeg) wgs = kMaxWgsPerSeg;
     if (wgs < 1) wgs = 1;
-    waves = wgs * rt::kStreamWaves;
+    waves = wgs * waves_per_wg;
     Plan p;
     p.wgs = (int)wgs;
     p.per_wave = (units + waves - 1) / waves;
@@ -295,7 +297,7 @@ rt_status search_resident(rt_engine *e, const float *queries, int32_t q, int32_t
         if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[3], s);
         if (kp <= kMaxListForBatch) {
             // each wave streams at least 1024 scores (256 groups of 4)
-            const Plan p = plan_stream((n + 3) / 4, q, kp, 256, e->num_cus);
+            const Plan p = plan_stream((n + 3) / 4, q, kp, 256, e->num_cus, kSelectWavesPerCu, rt::select_waves(kp));
             const rt::TreeLaunch t = tree_for(e, p, kp, k, 1, out_idx, out_scores, nullptr, 0);
             if (err == hipSuccess) err = rt::launch_select_topk(e->scores, ld, n, 1, q, p.per_wave, p.wgs, t, s);
         } else if (err == hipSuccess) {
@@ -312,7 +314,7 @@ rt_status search_resident(rt_engine *e, const float *queries, int32_t q, int32_t
             err = rt::launch_radix_topk(e->scores, ld, n, q, k, wgs, sc, out_idx, out_scores, s);
         }
     } else if (err == hipSuccess) {
-        const Plan p = plan_stream(n, q, kp, 32, e->num_cus);
+        const Plan p = plan_stream(n, q, kp, 32, e->num_cus, kScoreWavesPerCu, rt::kStreamWaves);
         const rt::TreeLaunch t = tree_for(e, p, kp, k, 1, out_idx, out_scores, nullptr, 0);
         err = rt::launch_gemv_topk(e->corpus, n, d, queries, q, p.per_wave, p.wgs, t, s);
     }
@@ -335,7 +337,7 @@ rt_status topk_select(rt_engine *e, const void *values, int32_t dtype, int64_t n
     e->had_batch_kernel = false;
     if (err == hipSuccess) err = prologue(e, s);
     const int64_t head = (int64_t)((reinterpret_cast<uintptr_t>(values) & 15u) >> 2);
-    const Plan p = plan_stream((n + head + 3) / 4, 1, kp, 256, e->num_cus);
+    const Plan p = plan_stream((n + head + 3) / 4, 1, kp, 256, e->num_cus, kSelectWavesPerCu, rt::select_waves(kp));
     const rt::TreeLaunch t = tree_for(e, p, kp, k, 2, out_idx, out_values, values, 0);
     if (err == hipSuccess) err = rt::launch_select_topk(values, 0, n, dtype, 1, p.per_wave, p.wgs, t, s);
     if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[1], s);

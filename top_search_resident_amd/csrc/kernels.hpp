@@ -9,6 +9,9 @@ namespace rt {
 // Workgroup shape of the streaming kernels: 4 waves of 64 lanes.
 constexpr int kStreamWaves = 4;
 constexpr int kStreamThreads = kStreamWaves * 64;
+// Raw-array selection runs 16-wave workgroups that share a certified bound in
+// LDS (all 16 lists must fit the merge LDS, so only for lists <= 256 entries).
+constexpr int select_waves(int kp) { return kp <= 256 ? 16 : 4; }
 // LDS ranks a workgroup uses to merge lists in the merge tree (32 KiB); a tree
 // node merges kTreeEntries / Kp lists.
 constexpr int kTreeEntries = 4096;

@@ -61,18 +61,14 @@ __device__ __forceinline__ void write_output(const TreeArgs &ta, int seg, int r,
         (ta.mode == 1) ? __float_as_uint(f32_of_order_key(rank_key(v))) : ta.src[(int64_t)seg * ta.src_seg_stride + idx];
 }
 
-// Merge `count` (1 <= count <= fan) best-first lists of 64*R ranks, stored
-// contiguously at `src`, into sm[0 .. 64*R).  Pairs of lists are merged by one
-// wave each, level by level.
+// Merge `count` best-first lists of 64*R ranks held contiguously in LDS at sm
+// into sm[0 .. 64*R).  Pairs of lists are merged by one wave each, level by level.
 template <int R>
-__device__ __forceinline__ void merge_lists_into_lds(const uint64_t *src, int count, uint64_t *sm) {
+__device__ __forceinline__ void merge_lds_lists(uint64_t *sm, int count) {
     constexpr int Kp = 64 * R;
     const int lane = lane_id();
     const int wv = wave_in_group();
     const int nwaves = blockDim.x >> 6;
-    for (int i = threadIdx.x; i < count * Kp; i += blockDim.x)
-        sm[i] = __hip_atomic_load(&src[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
     for (int s = 1; s < count; s <<= 1) {
         for (int a = wv * 2 * s; a + s < count; a += nwaves * 2 * s) {
             uint64_t A[R], B[R];
@@ -89,6 +85,17 @@ __device__ __forceinline__ void merge_lists_into_lds(const uint64_t *src, int co
     }
 }
 
+// Load `count` (1 <= count <= fan) lists stored contiguously at `src` (written
+// by other workgroups, possibly on other XCDs) and merge them into sm[0 .. 64*R).
+template <int R>
+__device__ __forceinline__ void merge_lists_into_lds(const uint64_t *src, int count, uint64_t *sm) {
+    constexpr int Kp = 64 * R;
+    for (int i = threadIdx.x; i < count * Kp; i += blockDim.x)
+        sm[i] = __hip_atomic_load(&src[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    merge_lds_lists<R>(sm, count);
+}
+
 // Steps 2 and 3 above.  `sm` is kTreeEntries ranks of LDS; `s_flag` an int in LDS.
 template <int R>
 __device__ __forceinline__ void finish_workgroup(WaveSelector<R> &sel, uint64_t *sm, int *s_flag,
@@ -97,32 +104,17 @@ __device__ __forceinline__ void finish_workgroup(WaveSelector<R> &sel, uint64_t 
     const int lane = lane_id();
     const int wv = wave_in_group();
 
-    // 2. the workgroup's four wave lists -> one list in wave 0's registers.
+    // 2. the workgroup's wave lists -> one list in sm[0 .. Kp) (blockDim / 64
+    //    waves; blockDim / 64 * Kp <= kTreeEntries).
 #pragma unroll
     for (int r = 0; r < R; ++r) sm[wv * Kp + r * 64 + lane] = sel.L[r];
     __syncthreads();
-    if ((wv & 1) == 0) {
-        uint64_t M[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) M[r] = sm[(wv + 1) * Kp + r * 64 + lane];
-        list_absorb_list<R>(sel.L, M);
-#pragma unroll
-        for (int r = 0; r < R; ++r) sm[wv * Kp + r * 64 + lane] = sel.L[r];
-    }
-    __syncthreads();
+    merge_lds_lists<R>(sm, blockDim.x >> 6);
     int count = gridDim.x;
-    if (wv == 0) {
-        uint64_t M[R];
-#pragma unroll
-        for (int r = 0; r < R; ++r) M[r] = sm[2 * Kp + r * 64 + lane];
-        list_absorb_list<R>(sel.L, M);
-        if (count == 1) {
-#pragma unroll
-            for (int r = 0; r < R; ++r)
-                if (r * 64 + lane < ta.k) write_output(ta, seg, r * 64 + lane, sel.L[r]);
-        }
+    if (count == 1) {
+        for (int r = threadIdx.x; r < ta.k; r += blockDim.x) write_output(ta, seg, r, sm[r]);
+        return;
     }
-    if (count == 1) return;
 
     // 3. merge tree over the workgroups of this segment.
     uint64_t *base = ta.tree + (int64_t)seg * ta.seg_tree_stride;
@@ -130,12 +122,8 @@ __device__ __forceinline__ void finish_workgroup(WaveSelector<R> &sel, uint64_t 
     int node = blockIdx.x;
     int64_t level_off = 0;
     int ctr_off = 0;
-    if (wv == 0) {
-#pragma unroll
-        for (int r = 0; r < R; ++r)
-            __hip_atomic_store(&base[(int64_t)node * Kp + r * 64 + lane], sel.L[r], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-    }
+    for (int i = threadIdx.x; i < Kp; i += blockDim.x)
+        __hip_atomic_store(&base[(int64_t)node * Kp + i], sm[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     while (true) {
         const int parent = node / ta.fan;
         const int first = parent * ta.fan;
@@ -324,17 +312,18 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_topk_generic_kernel(
 // t holds elements 4t - head .. 4t - head + 3, where head = (address mod 16) / 4.
 // Elements outside [0, n) are masked.  An aligned 16-byte group never crosses a
 // page, so reading the part of a group outside the array cannot fault.
-template <int DT, int R>
-__global__ __launch_bounds__(kStreamThreads) void select_topk_kernel(
+template <int DT, int R, int W>
+__global__ __launch_bounds__(W * 64) void select_topk_kernel(
     const uint32_t *__restrict__ base, int64_t seg_stride, int64_t n, int64_t groups_per_wave, TreeArgs ta) {
-    constexpr int U = 4;
-    __shared__ uint64_t stage[kStreamWaves][128];
+    constexpr int U = 2;  // 2 x 16 B per lane per step, loads one step ahead (measured best at 1e8 int32)
+    __shared__ uint64_t stage[W][128];
     __shared__ uint64_t sm[kTreeEntries];
+    __shared__ uint64_t wg_thr;  // largest k-th entry any wave of the workgroup has published
     __shared__ int s_flag;
     const int seg = blockIdx.y;
     const int lane = lane_id();
     const int wv = wave_in_group();
-    const int64_t wave = (int64_t)blockIdx.x * kStreamWaves + wv;
+    const int64_t wave = (int64_t)blockIdx.x * W + wv;
     const uintptr_t addr = reinterpret_cast<uintptr_t>(base + seg * seg_stride);
     const int head = (int)((addr & 15u) >> 2);
     const uint4 *__restrict__ a4 = reinterpret_cast<const uint4 *>(addr - (uintptr_t)head * 4u);
@@ -343,17 +332,37 @@ __global__ __launch_bounds__(kStreamThreads) void select_topk_kernel(
 
     WaveSelector<R> sel;
     sel.init(ta.k);
+    if (threadIdx.x == 0) wg_thr = 0ull;
+    __syncthreads();
     const int64_t g_begin = wave * groups_per_wave;
     const int64_t g_end = (g_begin + groups_per_wave < total_groups) ? g_begin + groups_per_wave : total_groups;
+    // Loads run one step ahead of the filtering.  Groups past the range reload
+    // the last group (masked below).
+    uint4 nv[U];
+    if (g_begin < g_end) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t grp = g_begin + u * 64 + lane;
+            nv[u] = load_nt(a4 + ((grp < g_end) ? grp : g_end - 1));
+        }
+    }
     for (int64_t g0 = g_begin; g0 < g_end; g0 += 64 * U) {
         uint4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t grp = g0 + u * 64 + lane;
-            v[u] = load_nt(a4 + ((grp < g_end) ? grp : g_end - 1));  // past the range: reload the last group (masked below)
+        for (int u = 0; u < U; ++u) v[u] = nv[u];
+        if (g0 + 64 * U < g_end) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t grp = g0 + 64 * U + u * 64 + lane;
+                nv[u] = load_nt(a4 + ((grp < g_end) ? grp : g_end - 1));
+            }
         }
+        // Every element of an interior step is in range: no group past g_end, no
+        // element before the array start or past its end.
+        const bool interior = (g0 + 64 * U <= g_end) && (g0 > 0 || head == 0) && ((g0 + 64 * U) * 4 - head <= n);
         uint32_t key[U][4];
-        bool any = false;
+        uint32_t mx = 0;
+        sel.sync_shared(&wg_thr);
         const uint32_t thr_key = rank_key(sel.thr);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -362,25 +371,33 @@ __global__ __launch_bounds__(kStreamThreads) void select_topk_kernel(
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 key[u][c] = (DT == 0) ? order_key_i32((int32_t)e[c]) : order_key_f32(__uint_as_float(e[c]));
-                const int64_t idx = grp * 4 + c - head;
-                const bool valid = (grp < g_end) && idx >= 0 && idx < n;
-                any |= valid && key[u][c] >= thr_key;
+                bool valid = true;
+                if (!interior) {
+                    const int64_t idx = grp * 4 + c - head;
+                    valid = (grp < g_end) && idx >= 0 && idx < n;
+                }
+                mx = (valid && key[u][c] > mx) ? key[u][c] : mx;
             }
         }
-        if (__ballot(any) == 0) continue;
+        // A key below the threshold's key can never enter the list (key ties go
+        // to the exact rank test).  Most steps stop here; in the others only the
+        // element slots that hold a candidate pay for the exact test.
+        if (__ballot(mx >= thr_key) == 0) continue;
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int64_t grp = g0 + u * 64 + lane;
+            const int64_t idx0 = (g0 + u * 64 + lane) * 4 - head;
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-                const int64_t idx = grp * 4 + c - head;
-                const bool valid = (grp < g_end) && idx >= 0 && idx < n;
+                const int64_t idx = idx0 + c;
+                const bool valid = interior || ((g0 + u * 64 + lane < g_end) && idx >= 0 && idx < n);
+                const bool maybe = valid && key[u][c] >= rank_key(sel.thr);
+                if (__ballot(maybe) == 0) continue;
                 const uint64_t rank = make_rank(key[u][c], (uint32_t)idx);
-                sel.offer(my_stage, rank, valid && rank > sel.thr);
+                sel.offer(my_stage, rank, maybe && rank > sel.thr, &wg_thr);
             }
         }
     }
-    sel.finish(my_stage);
+    sel.finish(my_stage, &wg_thr);
     finish_workgroup<R>(sel, sm, &s_flag, ta, seg);
 }
 
@@ -429,12 +446,12 @@ hipError_t launch_stream_r(int kind, int lg, int L, dim3 grid, hipStream_t s, co
                                per_wave, ta);
             return hipGetLastError();
         case 2:
-            hipLaunchKernelGGL((select_topk_kernel<0, R>), grid, dim3(kStreamThreads), 0, s,
-                               static_cast<const uint32_t *>(data), seg_stride, n, per_wave, ta);
+            hipLaunchKernelGGL((select_topk_kernel<0, R, select_waves(64 * R)>), grid, dim3(64 * select_waves(64 * R)), 0,
+                               s, static_cast<const uint32_t *>(data), seg_stride, n, per_wave, ta);
             return hipGetLastError();
         case 3:
-            hipLaunchKernelGGL((select_topk_kernel<1, R>), grid, dim3(kStreamThreads), 0, s,
-                               static_cast<const uint32_t *>(data), seg_stride, n, per_wave, ta);
+            hipLaunchKernelGGL((select_topk_kernel<1, R, select_waves(64 * R)>), grid, dim3(64 * select_waves(64 * R)), 0,
+                               s, static_cast<const uint32_t *>(data), seg_stride, n, per_wave, ta);
             return hipGetLastError();
         default:
             return hipErrorInvalidValue;

@@ -47,10 +47,56 @@ __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 // Index of this thread's wave in its workgroup, as a wave-uniform value.
 __device__ __forceinline__ int wave_in_group() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
+// Exchange with lane ^ M.  Measured lane semantics on gfx950: quad_perm covers
+// M = 1, 2; v_permlane16_swap / v_permlane32_swap with both operands the same
+// register return the two halves of the swap, so lanes pick the half that came
+// from lane ^ 16 (^ 32); M = 4, 8 use ds_bpermute.
+template <int M>
+__device__ __forceinline__ uint32_t xor_u32(uint32_t v) {
+    if constexpr (M == 1) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+    } else if constexpr (M == 2) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+    } else if constexpr (M == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (__lane_id() & 16) ? r[0] : r[1];
+    } else if constexpr (M == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+        return (__lane_id() & 32) ? r[0] : r[1];
+    } else {
+        return (uint32_t)__shfl_xor((int)v, M);
+    }
+}
+
+template <int M>
+__device__ __forceinline__ uint64_t xor_u64(uint64_t v) {
+    const uint32_t lo = xor_u32<M>((uint32_t)v);
+    const uint32_t hi = xor_u32<M>((uint32_t)(v >> 32));
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Lane 63 - l: the row mirror (l ^ 15) composed with the 16- and 32-lane swaps.
+__device__ __forceinline__ uint64_t reverse_u64(uint64_t v) {
+    uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x140, 0xF, 0xF, false);
+    uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), 0x140, 0xF, 0xF, false);
+    lo = xor_u32<16>(lo);
+    hi = xor_u32<16>(hi);
+    lo = xor_u32<32>(lo);
+    hi = xor_u32<32>(hi);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+// Runtime-mask form for loops the compiler fully unrolls (the switch folds).
 __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-    const int lo = __shfl_xor((int)(uint32_t)v, m);
-    const int hi = __shfl_xor((int)(uint32_t)(v >> 32), m);
-    return ((uint64_t)(uint32_t)hi << 32) | (uint64_t)(uint32_t)lo;
+    switch (m) {
+        case 1: return xor_u64<1>(v);
+        case 2: return xor_u64<2>(v);
+        case 4: return xor_u64<4>(v);
+        case 8: return xor_u64<8>(v);
+        case 16: return xor_u64<16>(v);
+        case 32: return xor_u64<32>(v);
+        default: return v;
+    }
 }
 
 __device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
@@ -177,7 +223,7 @@ __device__ __forceinline__ void bitonic_merge_desc(uint64_t (&L)[R]) {
 // sequence keeps the best half and is bitonic.
 template <int R>
 __device__ __forceinline__ void list_absorb64(uint64_t (&L)[R], uint64_t batch_desc) {
-    const uint64_t asc = shfl_xor_u64(batch_desc, 63);  // lane l gets batch[63 - l]
+    const uint64_t asc = reverse_u64(batch_desc);  // lane l gets batch[63 - l]
     L[R - 1] = umax64(L[R - 1], asc);
     bitonic_merge_desc<R>(L);
 }
@@ -186,7 +232,7 @@ __device__ __forceinline__ void list_absorb64(uint64_t (&L)[R], uint64_t batch_d
 template <int R>
 __device__ __forceinline__ void list_absorb_list(uint64_t (&L)[R], const uint64_t (&M)[R]) {
 #pragma unroll
-    for (int r = 0; r < R; ++r) L[r] = umax64(L[r], shfl_xor_u64(M[R - 1 - r], 63));
+    for (int r = 0; r < R; ++r) L[r] = umax64(L[r], reverse_u64(M[R - 1 - r]));
     bitonic_merge_desc<R>(L);
 }
 
@@ -209,27 +255,32 @@ __device__ __forceinline__ uint64_t list_entry(const uint64_t (&L)[R], int j) {
 
 // Per-wave streaming selector.  Candidates are appended to a 128-entry LDS
 // staging buffer private to the wave; every 64 of them are sorted and absorbed
-// into the register list.  `thr` is the list's k-th entry (0 until the list holds
-// k real entries): k already-seen elements reach or beat it, so anything at or
-// below it can never enter the top-k and is not offered.  The staging buffer is
+// into the register list.  `thr` is a certified bound: some set of k
+// already-seen elements all reach or beat it, so anything at or below it can
+// never enter the top-k and is not offered.  It is the list's k-th entry (0
+// until the list holds k real entries), raised -- when the workgroup shares a
+// bound in LDS (`wg_thr`, non-null) -- to the largest k-th entry any wave of
+// the workgroup has published.  The staging buffer and the shared bound are
 // passed to each call (not stored) so the compiler keeps LDS addressing and
 // keeps the list in registers.
 template <int R>
 struct WaveSelector {
     uint64_t L[R];
-    uint64_t thr;  // wave-uniform
-    int pending;   // wave-uniform
+    uint64_t thr;        // wave-uniform
+    uint64_t published;  // wave-uniform: last value this wave put into *wg_thr
+    int pending;         // wave-uniform
     int k;
 
     __device__ __forceinline__ void init(int k_) {
 #pragma unroll
         for (int r = 0; r < R; ++r) L[r] = 0;
         thr = 0;
+        published = 0;
         pending = 0;
         k = k_;
     }
 
-    __device__ __forceinline__ void absorb_stage_front(uint64_t *__restrict__ stage, int count) {
+    __device__ __forceinline__ void absorb_stage_front(uint64_t *__restrict__ stage, int count, uint64_t *wg_thr) {
         const int lane = lane_id();
         wave_lds_sync();
         uint64_t x = (lane < count) ? stage[lane] : 0ull;
@@ -237,17 +288,28 @@ struct WaveSelector {
         list_absorb64<R>(L, x);
         const uint64_t kth = list_entry<R>(L, k - 1);
         if (kth > thr) thr = kth;
+        if (wg_thr != nullptr && kth > published) {
+            published = kth;
+            if (lane == 0) __hip_atomic_fetch_max(wg_thr, kth, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        }
+    }
+
+    // Raise thr to the workgroup's shared bound.
+    __device__ __forceinline__ void sync_shared(const uint64_t *wg_thr) {
+        const uint64_t g = *(volatile const uint64_t *)wg_thr;
+        if (g > thr) thr = g;
     }
 
     // Offer one rank per lane; `take` must already include rank > thr.
-    __device__ __forceinline__ void offer(uint64_t *__restrict__ stage, uint64_t rank, bool take) {
+    __device__ __forceinline__ void offer(uint64_t *__restrict__ stage, uint64_t rank, bool take,
+                                          uint64_t *wg_thr = nullptr) {
         const uint64_t m = __ballot(take);
         if (m == 0) return;
         const int lane = lane_id();
         if (take) stage[pending + lanes_below(m)] = rank;
         pending += __popcll(m);
         if (pending >= 64) {
-            absorb_stage_front(stage, 64);
+            absorb_stage_front(stage, 64, wg_thr);
             const int rest = pending - 64;
             uint64_t t = 0;
             if (lane < rest) t = stage[64 + lane];
@@ -257,8 +319,8 @@ struct WaveSelector {
         }
     }
 
-    __device__ __forceinline__ void finish(uint64_t *__restrict__ stage) {
-        if (pending > 0) absorb_stage_front(stage, pending);
+    __device__ __forceinline__ void finish(uint64_t *__restrict__ stage, uint64_t *wg_thr = nullptr) {
+        if (pending > 0) absorb_stage_front(stage, pending, wg_thr);
         pending = 0;
     }
 };
