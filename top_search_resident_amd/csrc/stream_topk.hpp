@@ -85,44 +85,26 @@ __device__ __forceinline__ void merge_lds_lists(uint64_t *sm, int count) {
     }
 }
 
-// Load `count` (1 <= count <= fan) lists stored contiguously at `src` (written
-// by other workgroups, possibly on other XCDs) and merge them into sm[0 .. 64*R).
-template <int R>
-__device__ __forceinline__ void merge_lists_into_lds(const uint64_t *src, int count, uint64_t *sm) {
-    constexpr int Kp = 64 * R;
-    for (int i = threadIdx.x; i < count * Kp; i += blockDim.x)
-        sm[i] = __hip_atomic_load(&src[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __syncthreads();
-    merge_lds_lists<R>(sm, count);
-}
+// LDS words the merges use besides the lists.
+struct MergeScratch {
+    int flag;
+};
 
-// Steps 2 and 3 above.  `sm` is kTreeEntries ranks of LDS; `s_flag` an int in LDS.
-template <int R>
-__device__ __forceinline__ void finish_workgroup(WaveSelector<R> &sel, uint64_t *sm, int *s_flag,
-                                                 const TreeArgs &ta, int seg) {
+// Step 3: a merge tree.  Workgroups are grouped `fan` at a time; the last of a
+// group to arrive loads the first k entries of the group's lists (the rest of
+// each list cannot matter), merges them and moves one level up; the last one at
+// the root writes the outputs.
+template <int R, int NT>
+__device__ __forceinline__ void tree_finish(uint64_t *sm, MergeScratch *ms, const TreeArgs &ta, int seg) {
     constexpr int Kp = 64 * R;
-    const int lane = lane_id();
-    const int wv = wave_in_group();
-
-    // 2. the workgroup's wave lists -> one list in sm[0 .. Kp) (blockDim / 64
-    //    waves; blockDim / 64 * Kp <= kTreeEntries).
-#pragma unroll
-    for (int r = 0; r < R; ++r) sm[wv * Kp + r * 64 + lane] = sel.L[r];
-    __syncthreads();
-    merge_lds_lists<R>(sm, blockDim.x >> 6);
+    const int k = ta.k;
     int count = gridDim.x;
-    if (count == 1) {
-        for (int r = threadIdx.x; r < ta.k; r += blockDim.x) write_output(ta, seg, r, sm[r]);
-        return;
-    }
-
-    // 3. merge tree over the workgroups of this segment.
     uint64_t *base = ta.tree + (int64_t)seg * ta.seg_tree_stride;
     uint32_t *ctr = ta.counters + (int64_t)seg * ta.seg_ctr_stride;
     int node = blockIdx.x;
     int64_t level_off = 0;
     int ctr_off = 0;
-    for (int i = threadIdx.x; i < Kp; i += blockDim.x)
+    for (int i = threadIdx.x; i < k; i += NT)
         __hip_atomic_store(&base[(int64_t)node * Kp + i], sm[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     while (true) {
         const int parent = node / ta.fan;
@@ -135,18 +117,22 @@ __device__ __forceinline__ void finish_workgroup(WaveSelector<R> &sel, uint64_t 
             const int last = (int)(arrived + 1 == (uint32_t)children);
             if (last)  // all children have arrived: clear for the next call
                 __hip_atomic_store(&ctr[ctr_off + parent], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            *s_flag = last;
+            ms->flag = last;
         }
         __syncthreads();
-        if (!*s_flag) return;
-        merge_lists_into_lds<R>(base + level_off + (int64_t)first * Kp, children, sm);
+        if (!ms->flag) return;
+        const uint64_t *src = base + level_off + (int64_t)first * Kp;
+        for (int i = threadIdx.x; i < children * Kp; i += NT)
+            sm[i] = ((i & (Kp - 1)) < k) ? __hip_atomic_load(&src[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+        __syncthreads();
+        merge_lds_lists<R>(sm, children);
         const int up = (count + ta.fan - 1) / ta.fan;
         if (up == 1) {
-            for (int r = threadIdx.x; r < ta.k; r += blockDim.x) write_output(ta, seg, r, sm[r]);
+            for (int r = threadIdx.x; r < k; r += NT) write_output(ta, seg, r, sm[r]);
             return;
         }
         const int64_t next_off = level_off + (int64_t)count * Kp;
-        for (int i = threadIdx.x; i < Kp; i += blockDim.x)
+        for (int i = threadIdx.x; i < k; i += NT)
             __hip_atomic_store(&base[next_off + (int64_t)parent * Kp + i], sm[i], __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         level_off = next_off;
@@ -155,6 +141,27 @@ __device__ __forceinline__ void finish_workgroup(WaveSelector<R> &sel, uint64_t 
         count = up;
         __syncthreads();
     }
+}
+
+// Steps 2 and 3 above.  `sm` is kTreeEntries ranks of LDS; NT the workgroup size.
+template <int R, int NT>
+__device__ __forceinline__ void finish_workgroup(WaveSelector<R> &sel, uint64_t *sm, MergeScratch *ms,
+                                                 const TreeArgs &ta, int seg) {
+    constexpr int Kp = 64 * R;
+    const int lane = lane_id();
+    const int wv = wave_in_group();
+
+    // 2. the workgroup's wave lists -> one list in sm[0 .. Kp) (NT / 64 * Kp <= kTreeEntries).
+#pragma unroll
+    for (int r = 0; r < R; ++r) sm[wv * Kp + r * 64 + lane] = sel.L[r];
+    __syncthreads();
+    merge_lds_lists<R>(sm, NT / 64);
+    if (gridDim.x == 1) {
+        for (int r = threadIdx.x; r < ta.k; r += NT) write_output(ta, seg, r, sm[r]);
+        return;
+    }
+    // 3. across the workgroups of this segment.
+    tree_finish<R, NT>(sm, ms, ta, seg);
 }
 
 // ---------------------------------------------------------------- scoring
@@ -185,7 +192,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_topk_kernel(
     constexpr int STEP = RPS * U;  // rows per wave step
     __shared__ uint64_t stage[kStreamWaves][128];
     __shared__ uint64_t sm[kTreeEntries];
-    __shared__ int s_flag;
+    __shared__ MergeScratch ms;
 
     const int seg = blockIdx.y;
     const int lane = lane_id();
@@ -254,7 +261,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_topk_kernel(
         }
     }
     sel.finish(my_stage);
-    finish_workgroup<R>(sel, sm, &s_flag, ta, seg);
+    finish_workgroup<R, kStreamThreads>(sel, sm, &ms, ta, seg);
 }
 
 // Any d: one row per wave at a time, scalar loads strided by 64 lanes.
@@ -265,7 +272,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_topk_generic_kernel(
     constexpr int U = 4;
     __shared__ uint64_t stage[kStreamWaves][128];
     __shared__ uint64_t sm[kTreeEntries];
-    __shared__ int s_flag;
+    __shared__ MergeScratch ms;
     const int seg = blockIdx.y;
     const int lane = lane_id();
     const int wv = wave_in_group();
@@ -302,10 +309,16 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_topk_generic_kernel(
         }
     }
     sel.finish(my_stage);
-    finish_workgroup<R>(sel, sm, &s_flag, ta, seg);
+    finish_workgroup<R, kStreamThreads>(sel, sm, &ms, ta, seg);
 }
 
 // ---------------------------------------------------------------- raw arrays
+
+// Compile-time flag selecting the masked (edge) form of a filtering step.
+template <bool B>
+struct EdgeTag {
+    static constexpr bool value = B;
+};
 
 // Segment `seg` is the n-element array at base + seg * seg_stride (32-bit
 // elements).  It is read as 16-byte groups of the enclosing aligned range: group
@@ -316,17 +329,22 @@ template <int DT, int R, int W>
 __global__ __launch_bounds__(W * 64) void select_topk_kernel(
     const uint32_t *__restrict__ base, int64_t seg_stride, int64_t n, int64_t groups_per_wave, TreeArgs ta) {
     constexpr int U = 2;  // 2 x 16 B per lane per step, loads one step ahead (measured best at 1e8 int32)
+    constexpr int kBootM = (R <= 8) ? R : 8;  // keys per lane behind the first step's bound
     __shared__ uint64_t stage[W][128];
     __shared__ uint64_t sm[kTreeEntries];
     __shared__ uint64_t wg_thr;  // largest k-th entry any wave of the workgroup has published
-    __shared__ int s_flag;
+    __shared__ MergeScratch ms;
     const int seg = blockIdx.y;
     const int lane = lane_id();
     const int wv = wave_in_group();
     const int64_t wave = (int64_t)blockIdx.x * W + wv;
-    const uintptr_t addr = reinterpret_cast<uintptr_t>(base + seg * seg_stride);
-    const int head = (int)((addr & 15u) >> 2);
-    const uint4 *__restrict__ a4 = reinterpret_cast<const uint4 *>(addr - (uintptr_t)head * 4u);
+    // The array may start anywhere; loads are 16-byte groups from the aligned
+    // address at or below its start, `head` elements early.  The pointer is
+    // formed from the kernel argument (not from an integer) so that the loads
+    // stay global loads, which LDS waits do not have to drain.
+    const uint32_t *const seg_base = base + seg * seg_stride;
+    const int head = (int)((reinterpret_cast<uintptr_t>(seg_base) & 15u) >> 2);
+    const uint4 *__restrict__ a4 = reinterpret_cast<const uint4 *>(seg_base - head);
     const int64_t total_groups = (n + head + 3) >> 2;
     uint64_t *const my_stage = stage[wv];
 
@@ -336,8 +354,70 @@ __global__ __launch_bounds__(W * 64) void select_topk_kernel(
     __syncthreads();
     const int64_t g_begin = wave * groups_per_wave;
     const int64_t g_end = (g_begin + groups_per_wave < total_groups) ? g_begin + groups_per_wave : total_groups;
+
+    // One step: U groups of 4 elements per lane.  EDGE steps mask elements
+    // outside [0, n) and groups past g_end; interior steps skip those tests.
+    auto step = [&](int64_t g0, const uint4 (&v)[U], auto edge_tag) {
+        constexpr bool EDGE = decltype(edge_tag)::value;
+        uint32_t key[U][4];
+        uint32_t mx = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                key[u][c] = (DT == 0) ? order_key_i32((int32_t)e[c]) : order_key_f32(__uint_as_float(e[c]));
+                if constexpr (EDGE) {
+                    const int64_t grp = g0 + u * 64 + lane;
+                    const int64_t idx = grp * 4 + c - head;
+                    if (!(grp < g_end && idx >= 0 && idx < n)) key[u][c] = 0;  // below every threshold key but 0
+                }
+                mx = key[u][c] > mx ? key[u][c] : mx;
+            }
+        }
+        // First step of the wave: start from a certified bound instead of an
+        // empty list.  Each lane's M-th largest key km has M elements at or
+        // above it; the q-th largest km over the wave (q = ceil(k / M) <= 64)
+        // then has q * M >= k elements at or above it, so no element with a
+        // smaller key can be in the top k.  Masked slots hold key 0 and only
+        // weaken the bound.
+        if constexpr (kBootM > 0) {
+            if (g0 == g_begin) {
+                static_assert(U * 4 == 8, "bootstrap reads eight keys per lane");
+                const uint32_t flat[8] = {key[0][0], key[0][1], key[0][2], key[0][3],
+                                          key[1][0], key[1][1], key[1][2], key[1][3]};
+                const int q = (ta.k + kBootM - 1) / kBootM;
+                if (q <= 64) {
+                    const uint32_t sorted = wave_sort64_desc_u32(mth_largest8<kBootM>(flat));
+                    const uint32_t kk = (uint32_t)__builtin_amdgcn_readlane((int)sorted, q - 1);
+                    const uint64_t boot = ((uint64_t)kk << 32) - 1;  // keeps every key >= kk
+                    if (kk != 0 && boot > sel.thr) sel.thr = boot;
+                }
+            }
+        }
+        sel.sync_shared(&wg_thr);
+        const uint32_t thr_key = rank_key(sel.thr);
+        // A key below the threshold's key can never enter the list (key ties go
+        // to the exact rank test).  Most steps stop here; in the others only the
+        // element slots that hold a candidate pay for the exact test.
+        if (__ballot(mx >= thr_key) == 0) return;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t grp = g0 + u * 64 + lane;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const int64_t idx = grp * 4 + c - head;
+                bool maybe = key[u][c] >= rank_key(sel.thr);
+                if constexpr (EDGE) maybe = maybe && grp < g_end && idx >= 0 && idx < n;
+                if (__ballot(maybe) == 0) continue;
+                const uint64_t rank = make_rank(key[u][c], (uint32_t)idx);
+                sel.offer(my_stage, rank, maybe && rank > sel.thr, &wg_thr);
+            }
+        }
+    };
+
     // Loads run one step ahead of the filtering.  Groups past the range reload
-    // the last group (masked below).
+    // the last group (masked in edge steps).
     uint4 nv[U];
     if (g_begin < g_end) {
 #pragma unroll
@@ -360,45 +440,13 @@ __global__ __launch_bounds__(W * 64) void select_topk_kernel(
         // Every element of an interior step is in range: no group past g_end, no
         // element before the array start or past its end.
         const bool interior = (g0 + 64 * U <= g_end) && (g0 > 0 || head == 0) && ((g0 + 64 * U) * 4 - head <= n);
-        uint32_t key[U][4];
-        uint32_t mx = 0;
-        sel.sync_shared(&wg_thr);
-        const uint32_t thr_key = rank_key(sel.thr);
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const uint32_t e[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-            const int64_t grp = g0 + u * 64 + lane;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                key[u][c] = (DT == 0) ? order_key_i32((int32_t)e[c]) : order_key_f32(__uint_as_float(e[c]));
-                bool valid = true;
-                if (!interior) {
-                    const int64_t idx = grp * 4 + c - head;
-                    valid = (grp < g_end) && idx >= 0 && idx < n;
-                }
-                mx = (valid && key[u][c] > mx) ? key[u][c] : mx;
-            }
-        }
-        // A key below the threshold's key can never enter the list (key ties go
-        // to the exact rank test).  Most steps stop here; in the others only the
-        // element slots that hold a candidate pay for the exact test.
-        if (__ballot(mx >= thr_key) == 0) continue;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t idx0 = (g0 + u * 64 + lane) * 4 - head;
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                const int64_t idx = idx0 + c;
-                const bool valid = interior || ((g0 + u * 64 + lane < g_end) && idx >= 0 && idx < n);
-                const bool maybe = valid && key[u][c] >= rank_key(sel.thr);
-                if (__ballot(maybe) == 0) continue;
-                const uint64_t rank = make_rank(key[u][c], (uint32_t)idx);
-                sel.offer(my_stage, rank, maybe && rank > sel.thr, &wg_thr);
-            }
-        }
+        if (interior)
+            step(g0, v, EdgeTag<false>{});
+        else
+            step(g0, v, EdgeTag<true>{});
     }
     sel.finish(my_stage, &wg_thr);
-    finish_workgroup<R>(sel, sm, &s_flag, ta, seg);
+    finish_workgroup<R, W * 64>(sel, sm, &ms, ta, seg);
 }
 
 // ---------------------------------------------------------------- per-list-size launchers

@@ -47,10 +47,13 @@ __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 // Index of this thread's wave in its workgroup, as a wave-uniform value.
 __device__ __forceinline__ int wave_in_group() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
 
-// Exchange with lane ^ M.  Measured lane semantics on gfx950: quad_perm covers
-// M = 1, 2; v_permlane16_swap / v_permlane32_swap with both operands the same
-// register return the two halves of the swap, so lanes pick the half that came
-// from lane ^ 16 (^ 32); M = 4, 8 use ds_bpermute.
+// Exchange with lane ^ M, without an LDS round trip.  Measured lane semantics on
+// gfx950: quad_perm covers M = 1, 2; for M = 4, 8 a lane whose bit M is clear
+// reads lane + M (DPP row_shl:M, never crossing its 16-lane row for such a
+// lane) and one whose bit is set reads lane - M (row_shr:M);
+// v_permlane16_swap / v_permlane32_swap with both operands the same register
+// return the two halves of the swap, so lanes pick the half that came from
+// lane ^ 16 (^ 32).
 template <int M>
 __device__ __forceinline__ uint32_t xor_u32(uint32_t v) {
     if constexpr (M == 1) {
@@ -64,7 +67,10 @@ __device__ __forceinline__ uint32_t xor_u32(uint32_t v) {
         const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
         return (__lane_id() & 32) ? r[0] : r[1];
     } else {
-        return (uint32_t)__shfl_xor((int)v, M);
+        static_assert(M == 4 || M == 8, "lane exchange distance");
+        const uint32_t up = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x100 + M, 0xF, 0xF, false);
+        const uint32_t down = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x110 + M, 0xF, 0xF, false);
+        return (__lane_id() & M) ? down : up;
     }
 }
 
@@ -191,6 +197,63 @@ __device__ __forceinline__ uint64_t wave_sort64_desc(uint64_t x) {
     return x;
 }
 
+// Bitonic sort of 64 keys (one per lane), largest first.
+__device__ __forceinline__ uint32_t wave_sort64_desc_u32(uint32_t x) {
+    const int lane = lane_id();
+#pragma unroll
+    for (int k = 2; k <= 64; k <<= 1) {
+#pragma unroll
+        for (int j = k >> 1; j > 0; j >>= 1) {
+            uint32_t y;
+            switch (j) {
+                case 1: y = xor_u32<1>(x); break;
+                case 2: y = xor_u32<2>(x); break;
+                case 4: y = xor_u32<4>(x); break;
+                case 8: y = xor_u32<8>(x); break;
+                case 16: y = xor_u32<16>(x); break;
+                default: y = xor_u32<32>(x); break;
+            }
+            const bool desc_seg = (lane & k) == 0;
+            const bool lower = (lane & j) == 0;
+            x = (lower == desc_seg) ? max(x, y) : min(x, y);
+        }
+    }
+    return x;
+}
+
+// The M-th largest (M = 1, 2, 4 or 8) of eight keys.
+template <int M>
+__device__ __forceinline__ uint32_t mth_largest8(const uint32_t (&in)[8]) {
+    uint32_t a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = in[i];
+    if constexpr (M == 1) {
+        uint32_t m = a[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) m = max(m, a[i]);
+        return m;
+    } else {
+        // bitonic sorting network on 8 registers, largest first
+#pragma unroll
+        for (int k = 2; k <= 8; k <<= 1) {
+#pragma unroll
+            for (int j = k >> 1; j > 0; j >>= 1) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int p = i ^ j;
+                    if (p > i) {
+                        const bool desc = (i & k) == 0;
+                        const uint32_t hi = max(a[i], a[p]), lo = min(a[i], a[p]);
+                        a[i] = desc ? hi : lo;
+                        a[p] = desc ? lo : hi;
+                    }
+                }
+            }
+        }
+        return a[M - 1];
+    }
+}
+
 // Sort a bitonic sequence of 64*R ranks (entry j = lane j%64 of register j/64)
 // into best-first order.
 template <int R>
@@ -263,6 +326,9 @@ __device__ __forceinline__ uint64_t list_entry(const uint64_t (&L)[R], int j) {
 // the workgroup has published.  The staging buffer and the shared bound are
 // passed to each call (not stored) so the compiler keeps LDS addressing and
 // keeps the list in registers.
+// 64-bit word in LDS (address space 3).
+typedef __attribute__((address_space(3))) uint64_t lds_u64;
+
 template <int R>
 struct WaveSelector {
     uint64_t L[R];
@@ -290,13 +356,18 @@ struct WaveSelector {
         if (kth > thr) thr = kth;
         if (wg_thr != nullptr && kth > published) {
             published = kth;
-            if (lane == 0) __hip_atomic_fetch_max(wg_thr, kth, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+            if (lane == 0)
+                __hip_atomic_fetch_max((lds_u64 *)(wg_thr), kth, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_WORKGROUP);
         }
     }
 
-    // Raise thr to the workgroup's shared bound.
+    // Raise thr to the workgroup's shared bound.  The bound lives in LDS; the
+    // load is made through an LDS-qualified pointer so that it waits on LDS
+    // traffic only, never on the wave's outstanding HBM loads.
     __device__ __forceinline__ void sync_shared(const uint64_t *wg_thr) {
-        const uint64_t g = *(volatile const uint64_t *)wg_thr;
+        const uint64_t g = __hip_atomic_load((const lds_u64 *)(wg_thr), __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_WORKGROUP);
         if (g > thr) thr = g;
     }
 
