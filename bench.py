@@ -284,7 +284,7 @@ def run_batched(args, torch, eng, corpus, qhost, qdev, ks, name, gen_s):
             "per_k": per_k,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                         "kernel": "mfma_scores_kernel", "bytes_per_launch": corpus_bytes,
+                         "kernel": "mfma_scores_fixed_kernel" if d in (256, 384, 512, 768, 1024) else "mfma_scores_kernel", "bytes_per_launch": corpus_bytes,
                          "avg_launch_us": float(np.mean(all_mf)) * 1e3},
             "input_gen_s": gen_s}
     if not args.no_cpu_baseline:

@@ -15,7 +15,8 @@ constexpr int select_waves(int kp) { return kp <= 256 ? 16 : 4; }
 // LDS ranks a workgroup uses to merge lists in the merge tree (32 KiB); a tree
 // node merges kTreeEntries / Kp lists.
 constexpr int kTreeEntries = 4096;
-// Batched scoring: one 512-thread workgroup per CU, 32 queries x 64 rows per wave tile.
+// Batched scoring: one workgroup per CU (512 threads for a runtime depth, 1024 for
+// the compile-time depths), 32 queries x 32 rows per wave tile.
 constexpr int kMfmaThreads = 512;
 constexpr int kMfmaMaxQ = 32;
 constexpr int kMfmaMaxD = 1024;

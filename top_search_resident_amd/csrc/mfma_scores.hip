@@ -6,18 +6,22 @@
 // queries as missing (section 9); with a batch the corpus is read from HBM once
 // for all queries and the arithmetic runs on v_mfma_f32_32x32x2_f32.
 //
-// Tiling.  One workgroup of kMfmaThreads per CU stages the whole (zero-padded)
-// 32 x d query block in LDS (row stride d + 4 floats to spread LDS banks).  Each
-// wave owns tiles of 32 corpus rows and produces one 32 x 32 output tile
-// (queries x rows) with v_mfma_f32_32x32x2_f32.  For an MFMA step the query
-// operand lane l holds Q[l % 32][c] and the corpus operand lane l holds
-// C[row0 + l % 32][c], with the column c = c0 + 16 (l / 32) + 4 i + e for step
-// (i, e); so per 32 columns each lane issues four 16-byte corpus loads covering
-// 64 contiguous bytes of its row, and the two lane halves cover the row's full
-// 128-byte line.  Loads run two 32-column chunks ahead of the multiplies.  The
-// loads are ordinary (cached): a line is consumed by four successive load
-// instructions, and the non-temporal hint made it miss again (measured 1.7x
-// slower on MI355X).
+// Tiling.  One workgroup per CU stages the whole 32 x d query block in LDS,
+// zero-padded to a whole number of pipeline rounds of 32 columns (row stride
+// padded by 4 floats to spread LDS banks).  Each wave owns tiles of 32 corpus
+// rows and produces one 32 x 32 output tile (queries x rows) with
+// v_mfma_f32_32x32x2_f32.  For an MFMA step the query operand lane l holds
+// Q[l % 32][c] and the corpus operand lane l holds C[row0 + l % 32][c], with the
+// column c = c0 + 16 (l / 32) + 4 i + e for step (i, e); so per 32 columns each
+// lane issues four 16-byte corpus loads covering 64 contiguous bytes of its row,
+// and the two lane halves cover the row's full 128-byte line.  Loads run KPF
+// 32-column chunks ahead of the multiplies.  Every load is unconditional:
+// addresses past the row end are clamped and their values replaced by zero
+// afterwards, rows past n read the last row.  (Predicated loads become
+// exec-masked branches, across which the compiler can only wait for all
+// outstanding loads, which serialises the pipeline.)  The loads are ordinary
+// (cached): a line is consumed by four successive load instructions, and the
+// non-temporal hint made it miss again (measured 1.7x slower on MI355X).
 // Output element (query, row) of a 32x32 tile sits in lane row % 32 + 32 *
 // ((query / 4) % 2), register (query % 4) + 4 * (query / 8); rows are stored
 // contiguously per query (S row stride ld), so each store is 128 B per half-wave.
@@ -27,22 +31,124 @@ namespace rt {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ float4 ld4_or_zero(const float *p, bool ok) {
-    return ok ? *reinterpret_cast<const float4 *>(p) : make_float4(0.f, 0.f, 0.f, 0.f);
-}
-
 __device__ __forceinline__ float comp(const float4 &v, int e) {
     return e == 0 ? v.x : (e == 1 ? v.y : (e == 2 ? v.z : v.w));
 }
 
-constexpr int kPrefetch = 2;  // 32-column chunks loaded ahead of the multiplies
+// Runtime-depth kernel: chunks of 32 columns loaded ahead of the multiplies and
+// independent accumulators (the workgroup size is kMfmaThreads).
+constexpr int kMfmaPrefetch = 2;
+constexpr int kMfmaAcc = 2;
 
-__global__ __launch_bounds__(kMfmaThreads) void mfma_scores_kernel(
-    const float *__restrict__ corpus, int64_t n, int d, const float *__restrict__ queries, int q,
-    float *__restrict__ scores, int64_t ld, int64_t tiles_per_wave) {
+// Columns the kernel walks for depth d: whole rounds of kpf chunks.
+constexpr int mfma_cols(int d, int kpf) { return ((d + 32 * kpf - 1) / (32 * kpf)) * (32 * kpf); }
+
+// KPF: chunks loaded ahead; NT: workgroup size; ACC: independent accumulators
+// (chunk j accumulates into acc[j % ACC], summed at the end).
+template <int KPF, int NT, int ACC>
+__global__ __launch_bounds__(NT) void mfma_scores_kernel(const float *__restrict__ corpus, int64_t n, int d,
+                                                         const float *__restrict__ queries, int q,
+                                                         float *__restrict__ scores, int64_t ld,
+                                                         int64_t tiles_per_wave) {
+    static_assert(KPF % ACC == 0, "each ring slot feeds one accumulator");
     extern __shared__ float qs[];
-    const int dp = d + 4;
-    for (int i = threadIdx.x; i < kMfmaMaxQ * d; i += blockDim.x) {
+    const int nchunks = (d + 31) / 32;
+    const int nck = (nchunks + KPF - 1) / KPF * KPF;  // chunks walked: whole pipeline rounds
+    const int dpad = nck * 32;
+    const int dp = dpad + 4;
+    for (int i = threadIdx.x; i < kMfmaMaxQ * dpad; i += NT) {
+        const int r = i / dpad, c = i - r * dpad;
+        qs[r * dp + c] = (r < q && c < d) ? queries[(int64_t)r * d + c] : 0.f;
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int wv = threadIdx.x >> 6;
+    const int m = lane & 31;
+    const int kk = lane >> 5;
+    const int64_t wave = (int64_t)blockIdx.x * (NT / 64) + wv;
+    const int64_t tiles = (n + 31) / 32;
+    const int64_t t_begin = wave * tiles_per_wave;
+    const int64_t t_end = (t_begin + tiles_per_wave < tiles) ? t_begin + tiles_per_wave : tiles;
+    const float *qrow = qs + m * dp + 16 * kk;
+
+    for (int64_t t = t_begin; t < t_end; ++t) {
+        const int64_t row0 = t * 32;
+        const bool valid = row0 + m < n;
+        const float *p = corpus + (valid ? row0 + m : n - 1) * (int64_t)d;
+        auto load_chunk = [&](int chunk, float4(&dst)[4]) {
+            chunk = chunk < nchunks ? chunk : nchunks - 1;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int col = chunk * 32 + 16 * kk + 4 * i;
+                dst[i] = *reinterpret_cast<const float4 *>(p + (col < d ? col : d - 4));
+            }
+        };
+        floatx16 acc[ACC];
+#pragma unroll
+        for (int h = 0; h < ACC; ++h)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[h][v] = 0.f;
+        float4 buf[KPF][4];
+#pragma unroll
+        for (int s = 0; s < KPF; ++s) load_chunk(s, buf[s]);
+        // Slot s of the ring always holds chunk ci + s: it is consumed in place
+        // and then refilled with chunk ci + s + KPF, so no register is copied
+        // while a load into it may still be in flight.
+        for (int ci = 0; ci < nck; ci += KPF) {
+#pragma unroll
+            for (int s = 0; s < KPF; ++s) {
+                const int c0 = (ci + s) * 32;
+                float4 a[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const float4 *>(qrow + c0 + 4 * i);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    // Columns past d hold clamped (real) data: select zero there
+                    // (a select, not a branch) so the zero query padding
+                    // multiplies zeros, whatever the data.
+                    const bool in_row = c0 + 16 * kk + 4 * i < d;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        acc[s % ACC] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                            comp(a[i], e), in_row ? comp(buf[s][i], e) : 0.f, acc[s % ACC], 0, 0, 0);
+                }
+                load_chunk(ci + s + KPF, buf[s]);
+                // keep the refill here: left alone, the scheduler sinks it down
+                // to its use KPF chunks later, which serialises the loads
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int h = 1; h < ACC; ++h)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[0][v] += acc[h][v];
+        if (valid) {
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int qi = 8 * (v >> 2) + 4 * kk + (v & 3);
+                if (qi < q) scores[(int64_t)qi * ld + row0 + m] = acc[0][v];
+            }
+        }
+    }
+}
+
+// The same tile loop for a depth of exactly d = 32 NCK known at compile time:
+// the chunk loop is unrolled, so within a tile every wait for a ring slot is a
+// counted wait for that slot's own loads (a loop-carried slot can only be
+// waited for with all loads), the column offsets are load immediates with no
+// clamping or masking, and the refills of a tile's last chunks already fetch
+// the next tile's first chunks (one pipeline across the wave's tiles).
+template <int NCK, int KPF, int NT, int ACC>
+__global__ __launch_bounds__(NT) void mfma_scores_fixed_kernel(const float *__restrict__ corpus, int64_t n,
+                                                               const float *__restrict__ queries, int q,
+                                                               float *__restrict__ scores, int64_t ld,
+                                                               int64_t tiles_per_wave) {
+    static_assert(KPF <= NCK && NCK % ACC == 0, "pipeline shape");
+    constexpr int d = NCK * 32;
+    constexpr int dp = d + 4;
+    extern __shared__ float qs[];
+    for (int i = threadIdx.x; i < kMfmaMaxQ * d; i += NT) {
         const int r = i / d, c = i - r * d;
         qs[r * dp + c] = (r < q) ? queries[(int64_t)r * d + c] : 0.f;
     }
@@ -52,80 +158,115 @@ __global__ __launch_bounds__(kMfmaThreads) void mfma_scores_kernel(
     const int wv = threadIdx.x >> 6;
     const int m = lane & 31;
     const int kk = lane >> 5;
-    const int64_t wave = (int64_t)blockIdx.x * (kMfmaThreads / 64) + wv;
+    const int64_t wave = (int64_t)blockIdx.x * (NT / 64) + wv;
     const int64_t tiles = (n + 31) / 32;
     const int64_t t_begin = wave * tiles_per_wave;
     const int64_t t_end = (t_begin + tiles_per_wave < tiles) ? t_begin + tiles_per_wave : tiles;
+    if (t_begin >= t_end) return;
     const float *qrow = qs + m * dp + 16 * kk;
-    const int nchunks = (d + 31) / 32;
-
+    auto row_of = [&](int64_t t) {
+        const int64_t row = t * 32 + m;
+        return corpus + (row < n ? row : n - 1) * (int64_t)d + 16 * kk;
+    };
+    auto load_chunk = [&](const float *p, int chunk, float4(&dst)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[i] = *reinterpret_cast<const float4 *>(p + chunk * 32 + 4 * i);
+    };
+    const float *p = row_of(t_begin);
+    float4 buf[KPF][4];
+#pragma unroll
+    for (int s = 0; s < KPF; ++s) load_chunk(p, s, buf[s]);
     for (int64_t t = t_begin; t < t_end; ++t) {
-        const int64_t row0 = t * 32;
-        const bool valid = row0 + m < n;
-        // rows past the end load the last row (their outputs are not stored)
-        const float *p = corpus + (valid ? row0 + m : n - 1) * (int64_t)d + 16 * kk;
-        floatx16 acc;
+        const float *pn = (t + 1 < t_end) ? row_of(t + 1) : p;  // past the last tile: reload (cached)
+        // The query operands are the same for every tile; an opaque per-tile
+        // offset keeps the compiler from hoisting all NCK chunks of them into
+        // registers (hundreds of VGPRs) instead of reading LDS chunk by chunk.
+        int qoff = 0;
+        asm volatile("" : "+v"(qoff));
+        const float *qt = qrow + qoff;
+        floatx16 acc[ACC];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-        float4 buf[kPrefetch][4];
+        for (int h = 0; h < ACC; ++h)
 #pragma unroll
-        for (int s = 0; s < kPrefetch; ++s) {
+            for (int v = 0; v < 16; ++v) acc[h][v] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NCK; ++j) {
+            const int s = j % KPF;
+            float4 a[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const float4 *>(qt + j * 32 + 4 * i);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int col = s * 32 + 16 * kk + 4 * i;
-                buf[s][i] = ld4_or_zero(p + s * 32 + 4 * i, s < nchunks && col < d);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc[j % ACC] = __builtin_amdgcn_mfma_f32_32x32x2f32(comp(a[i], e), comp(buf[s][i], e),
+                                                                        acc[j % ACC], 0, 0, 0);
             }
+            if (j + KPF < NCK)
+                load_chunk(p, j + KPF, buf[s]);
+            else
+                load_chunk(pn, j + KPF - NCK, buf[s]);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        for (int ci = 0; ci < nchunks; ci += kPrefetch) {
 #pragma unroll
-            for (int s = 0; s < kPrefetch; ++s) {
-                const int chunk = ci + s;
-                if (chunk < nchunks) {
-                    const int c0 = chunk * 32;
-                    float4 cur[4];
+        for (int h = 1; h < ACC; ++h)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) cur[i] = buf[s][i];
-                    const int cn = c0 + kPrefetch * 32;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        buf[s][i] = ld4_or_zero(p + cn + 4 * i, chunk + kPrefetch < nchunks && cn + 16 * kk + 4 * i < d);
-                    float4 a[4];
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) a[i] = ld4_or_zero(qrow + c0 + 4 * i, c0 + 16 * kk + 4 * i < d);
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            acc = __builtin_amdgcn_mfma_f32_32x32x2f32(comp(a[i], e), comp(cur[i], e), acc, 0, 0, 0);
-                    }
-                }
-            }
-        }
-        if (valid) {
+            for (int v = 0; v < 16; ++v) acc[0][v] += acc[h][v];
+        const int64_t row0 = t * 32;
+        if (row0 + m < n) {
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
                 const int qi = 8 * (v >> 2) + 4 * kk + (v & 3);
-                if (qi < q) scores[(int64_t)qi * ld + row0 + m] = acc[v];
+                if (qi < q) scores[(int64_t)qi * ld + row0 + m] = acc[0][v];
             }
         }
+        p = pn;
     }
 }
 
-static size_t mfma_lds_bytes(int d) { return (size_t)kMfmaMaxQ * (d + 4) * sizeof(float); }
+static size_t mfma_lds_bytes(int d, int kpf) { return (size_t)kMfmaMaxQ * (mfma_cols(d, kpf) + 4) * sizeof(float); }
+
+// Depths with a compile-time kernel (d = 32 * NCK); others take the runtime loop.
+#define RT_MFMA_FIXED(X) X(8) X(12) X(16) X(24) X(32)
+constexpr int kFixedPrefetch = 2;
+constexpr int kFixedThreads = 1024;
+constexpr int kFixedAcc = 2;
 
 hipError_t prepare_mfma_scores() {
-    return hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_scores_kernel),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)mfma_lds_bytes(kMfmaMaxD));
+    hipError_t err = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&mfma_scores_kernel<kMfmaPrefetch, kMfmaThreads, kMfmaAcc>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)mfma_lds_bytes(kMfmaMaxD, kMfmaPrefetch));
+#define RT_PREP(NCK)                                                                                              \
+    if (err == hipSuccess)                                                                                        \
+        err = hipFuncSetAttribute(                                                                                \
+            reinterpret_cast<const void *>(&mfma_scores_fixed_kernel<NCK, kFixedPrefetch, kFixedThreads, kFixedAcc>), \
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)mfma_lds_bytes(NCK * 32, 1));
+    RT_MFMA_FIXED(RT_PREP)
+#undef RT_PREP
+    return err;
 }
 
 hipError_t launch_mfma_scores(const float *corpus, int64_t n, int d, const float *queries, int q, float *scores,
                               int64_t ld, int num_cus, hipStream_t stream) {
     const int64_t tiles = (n + 31) / 32;
-    const int64_t waves = (int64_t)num_cus * (kMfmaThreads / 64);
-    const int64_t tiles_per_wave = (tiles + waves - 1) / waves;
-    const int64_t blocks = (tiles + tiles_per_wave * (kMfmaThreads / 64) - 1) / (tiles_per_wave * (kMfmaThreads / 64));
-    hipLaunchKernelGGL(mfma_scores_kernel, dim3((unsigned)blocks), dim3(kMfmaThreads), mfma_lds_bytes(d), stream,
-                       corpus, n, d, queries, q, scores, ld, tiles_per_wave);
+#define RT_FIXED(NCK)                                                                                          \
+    if (d == NCK * 32) {                                                                                       \
+        constexpr int w = kFixedThreads / 64;                                                                  \
+        const int64_t tpw = (tiles + (int64_t)num_cus * w - 1) / ((int64_t)num_cus * w);                       \
+        const int64_t blocks = (tiles + tpw * w - 1) / (tpw * w);                                              \
+        hipLaunchKernelGGL((mfma_scores_fixed_kernel<NCK, kFixedPrefetch, kFixedThreads, kFixedAcc>),          \
+                           dim3((unsigned)blocks), dim3(kFixedThreads), mfma_lds_bytes(d, 1), stream, corpus, n, \
+                           queries, q, scores, ld, tpw);                                                       \
+        return hipGetLastError();                                                                              \
+    }
+    RT_MFMA_FIXED(RT_FIXED)
+#undef RT_FIXED
+    constexpr int w = kMfmaThreads / 64;
+    const int64_t tiles_per_wave = (tiles + (int64_t)num_cus * w - 1) / ((int64_t)num_cus * w);
+    const int64_t blocks = (tiles + tiles_per_wave * w - 1) / (tiles_per_wave * w);
+    hipLaunchKernelGGL((mfma_scores_kernel<kMfmaPrefetch, kMfmaThreads, kMfmaAcc>), dim3((unsigned)blocks),
+                       dim3(kMfmaThreads), mfma_lds_bytes(d, kMfmaPrefetch), stream, corpus, n, d, queries, q, scores,
+                       ld, tiles_per_wave);
     return hipGetLastError();
 }
 
