@@ -115,11 +115,11 @@ def test_batched_exact_arithmetic(eng):
     assert np.array_equal(g_sc.astype(np.float64), o_sc)
 
 
-@pytest.mark.parametrize("n,k", [(20_000, 1024), (100_000, 129), (70_000, 700)])
+@pytest.mark.parametrize("n,k", [(20_000, 1024), (100_000, 129), (70_000, 700), (200_000, 64)])
 def test_batched_large_k_all_equal_scores(eng, n, k):
-    """Every score equal: the k-th key's bin holds the whole row, so the radix
-    selector's candidates exceed its LDS sort (and, for n > 65536, its candidate
-    buffer) and the exact whole-row selection must return indices 0..k-1."""
+    """Every score equal: every tile maximum reaches the bound, so the kept
+    scores (and, for n > 131072, the tile list) overflow LDS and the exact
+    whole-row selection must return indices 0..k-1."""
     d = 64
     corpus = np.zeros((n, d), np.float32)
     corpus[:, 0] = 1.0
@@ -132,8 +132,8 @@ def test_batched_large_k_all_equal_scores(eng, n, k):
 
 
 def test_batched_large_k_ties_and_tail(eng):
-    """A crowded k-th bin with exact integer ties, followed by the normal radix
-    path on the next call (the counters and histograms must have been cleared)."""
+    """Exact integer ties crowding the k-th score, then ordinary Gaussian rows on
+    the next call."""
     corpus = workloads.small_int_matrix(30_000, 32, lo=-1, hi=1, config_id=9)
     qs = workloads.small_int_matrix(8, 32, lo=-1, hi=1, config_id=9, stream=1)
     for k in (1024, 300):
@@ -144,6 +144,41 @@ def test_batched_large_k_ties_and_tail(eng):
     gauss = workloads.gaussian_rows(50_000, 256, config_id=10)
     gq = workloads.gaussian_rows(8, 256, config_id=10, stream=1)
     _check_against_oracle(eng, gauss, gq, 500)
+
+
+def test_batched_fewer_tiles_than_k(eng):
+    """n = 1000 rows make 32 tiles, fewer than k: no tile bound, every score kept."""
+    corpus = workloads.gaussian_rows(1_000, 256, config_id=21)
+    qs = workloads.gaussian_rows(5, 256, config_id=21, stream=1)
+    for k in (100, 1000):
+        _check_against_oracle(eng, corpus, qs, k)
+
+
+def test_batched_outlier_tile(eng):
+    """One row far above the rest puts the largest tile maximum more than an
+    octave above the k-th, outside the first histogram window: the bound comes
+    from the two plain digit passes instead."""
+    corpus = workloads.gaussian_rows(40_000, 128, config_id=22)
+    corpus[12_345] *= 64.0
+    qs = workloads.gaussian_rows(6, 128, config_id=22, stream=1)
+    qs[:, :] = np.abs(qs)  # every query favours the scaled row's positive entries
+    corpus[12_345] = np.abs(corpus[12_345])
+    for k in (50, 700):
+        g_idx, _, o_idx, _ = _check_against_oracle(eng, corpus, qs, k)
+        assert np.all(g_idx[:, 0] == 12_345)
+
+
+def test_batched_ragged_last_tile(eng):
+    """The best rows sit in the last, partial tile (n = 32 m + 7): its maximum
+    must cover only rows below n."""
+    n = 32 * 900 + 7
+    corpus = workloads.gaussian_rows(n, 256, config_id=23)
+    qs = workloads.gaussian_rows(4, 256, config_id=23, stream=1)
+    for qi in range(4):
+        corpus[n - 1 - qi] = qs[qi] * np.float32(3.0)
+    for k in (1, 10, 130):
+        g_idx, _, _, _ = _check_against_oracle(eng, corpus, qs, k)
+        assert np.all(g_idx[:, 0] == np.array([n - 1, n - 2, n - 3, n - 4]))
 
 
 def test_deterministic_repeat(eng):

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(HERE, "libresident_topk.so")
 SOURCES = ["engine.hip", "stream_topk.hip", "mfma_scores.hip",
-           "radix_topk.hip", "stream_r1.hip", "stream_r2.hip", "stream_r4.hip", "stream_r8.hip", "stream_r16.hip"]
+           "batch_select.hip", "stream_r1.hip", "stream_r2.hip", "stream_r4.hip", "stream_r8.hip", "stream_r16.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

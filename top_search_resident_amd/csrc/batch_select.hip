@@ -1,0 +1,423 @@
+// batch_select.hip -- exact top-K of materialised batch score rows (gfx950).
+//
+// Batched retrieval writes each query's scores to a row of S and, per query,
+// the largest score of every 32-row tile (mfma_scores.hip).  The pages score
+// one query at a time and select with one lane per block ("GPU-Resident Top-K
+// for Agentic RAG", section 4 Steps 3-4; section 9 and the K = 100 rows of the
+// section 5 table show that selector collapsing as K grows).  Here K tiles
+// whose maxima reach a value B hold K distinct scores >= B, so the K-th score
+// is >= B: one workgroup per query pins the K-th largest tile maximum to a
+// narrow bin, reads only the tiles that reach its lower edge (about K tiles),
+// keeps their scores at or above it and sorts those.  If too many tiles or
+// scores qualify (many equal scores), the workgroup selects exactly over the
+// whole row instead: three histogram passes pin the K-th largest key digit by
+// digit, then it collects the keys above it and the lowest-index ties.
+//
+// Ranks are the same (key << 32 | ~index) packing as wave_topk.hpp, so the
+// order -- larger score first, exact ties to the lower index -- is the pages'
+// comparator (section 3, "Problem B").
+#include "kernels.hpp"
+#include "wave_topk.hpp"
+
+namespace rt {
+
+constexpr int kDigitBins = 2048;       // 11-bit digits
+constexpr int kBatchSelectThreads = 1024;
+constexpr int kSortCap = 8192;    // candidates sorted in LDS (64 KiB)
+
+__device__ __forceinline__ uint32_t row_key(uint32_t bits) { return order_key_f32(__uint_as_float(bits)); }
+
+// ---------------------------------------------------------------- helpers
+
+// Inclusive prefix sum of one value per thread over the workgroup (LDS scratch
+// `buf` of blockDim entries).  Returns this thread's inclusive sum.
+__device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, uint32_t *buf) {
+    const int t = threadIdx.x;
+    buf[t] = v;
+    __syncthreads();
+    for (int off = 1; off < (int)blockDim.x; off <<= 1) {
+        const uint32_t add = (t >= off) ? buf[t - off] : 0u;
+        __syncthreads();
+        buf[t] += add;
+        __syncthreads();
+    }
+    const uint32_t r = buf[t];
+    __syncthreads();
+    return r;
+}
+
+// Sort sm[0 .. M) best-first with the kBatchSelectThreads threads of the
+// workgroup (M a power of two in [64, kSortCap]).  Bitonic network on
+// registers: the first min(M, 1024) threads hold E = M / 1024 (at least one)
+// elements, element r * 1024 + t in thread t.  Exchanges with a partner in the
+// same wave go through DPP / permlane, partners in the same thread are register
+// swaps, and only partners in another wave go through LDS (for M = 2048, 14 of
+// the 66 steps) -- instead of one LDS round trip and barrier per step.
+template <int M>
+__device__ __forceinline__ void block_sort_desc_m(uint64_t *sm) {
+    constexpr int NT = kBatchSelectThreads;
+    constexpr int ACT = M < NT ? M : NT;  // active threads (whole waves)
+    constexpr int E = M / ACT;
+    const int t = threadIdx.x;
+    const bool active = t < ACT;
+    uint64_t x[E];
+#pragma unroll
+    for (int r = 0; r < E; ++r) x[r] = active ? sm[r * ACT + t] : 0ull;
+    __syncthreads();
+#pragma unroll
+    for (int k2 = 2; k2 <= M; k2 <<= 1) {
+#pragma unroll
+        for (int j = k2 >> 1; j > 0; j >>= 1) {
+            if (j >= ACT) {  // partner in this thread: register r ^ (j / ACT)
+                const int jr = j / ACT;
+#pragma unroll
+                for (int r = 0; r < E; ++r) {
+                    if ((r & jr) == 0) {
+                        const int p = r | jr;
+                        const bool desc = (((r * ACT) + t) & k2) == 0;
+                        const uint64_t hi = umax64(x[r], x[p]), lo = umin64(x[r], x[p]);
+                        x[r] = desc ? hi : lo;
+                        x[p] = desc ? lo : hi;
+                    }
+                }
+            } else if (j >= 64) {  // partner in another wave: through LDS
+                if (active) {
+#pragma unroll
+                    for (int r = 0; r < E; ++r) sm[r * ACT + t] = x[r];
+                }
+                __syncthreads();
+                if (active) {
+#pragma unroll
+                    for (int r = 0; r < E; ++r) {
+                        const uint64_t y = sm[r * ACT + (t ^ j)];
+                        const bool desc = (((r * ACT) + t) & k2) == 0;
+                        const bool lower = (t & j) == 0;
+                        x[r] = (lower == desc) ? umax64(x[r], y) : umin64(x[r], y);
+                    }
+                }
+                __syncthreads();
+            } else if (active) {  // partner in this wave
+#pragma unroll
+                for (int r = 0; r < E; ++r) {
+                    const uint64_t y = shfl_xor_u64(x[r], j);
+                    const bool desc = (((r * ACT) + t) & k2) == 0;
+                    const bool lower = (t & j) == 0;
+                    x[r] = (lower == desc) ? umax64(x[r], y) : umin64(x[r], y);
+                }
+            }
+        }
+    }
+    if (active) {
+#pragma unroll
+        for (int r = 0; r < E; ++r) sm[r * ACT + t] = x[r];
+    }
+    __syncthreads();
+}
+
+// Sort sm[0 .. m) best-first, m a power of two in [64, kSortCap].
+__device__ __forceinline__ void block_sort_desc(uint64_t *sm, int m) {
+    switch (m) {
+        case 64: block_sort_desc_m<64>(sm); break;
+        case 128: block_sort_desc_m<128>(sm); break;
+        case 256: block_sort_desc_m<256>(sm); break;
+        case 512: block_sort_desc_m<512>(sm); break;
+        case 1024: block_sort_desc_m<1024>(sm); break;
+        case 2048: block_sort_desc_m<2048>(sm); break;
+        case 4096: block_sort_desc_m<4096>(sm); break;
+        default: block_sort_desc_m<8192>(sm); break;
+    }
+}
+
+struct SelectOut {
+    int k;
+    int32_t *out_idx;  // [segments][k]
+    uint32_t *out_val; // [segments][k], fp32 scores from the ranks
+};
+
+__device__ __forceinline__ void write_result(const SelectOut &o, int seg, int r, uint64_t v) {
+    o.out_idx[(int64_t)seg * o.k + r] = (int32_t)rank_index(v);
+    o.out_val[(int64_t)seg * o.k + r] = __float_as_uint(f32_of_order_key(rank_key(v)));
+}
+
+// Exact top-k of one whole row by one workgroup: pin the k-th largest key with
+// three histogram passes (11 + 11 + 10 bits), then collect every key above it
+// and, in index order, the lowest-index elements equal to it.
+__device__ void select_row_exactly(const uint32_t *row, int64_t n, const SelectOut &o, int seg, uint64_t *sm,
+                                   uint32_t *sh, uint32_t *scan_buf, uint32_t *s_vals) {
+    uint32_t prefix = 0, pmask = 0;
+    uint32_t need = (uint32_t)o.k;  // how many of the remaining keys to take from the top
+    const int shifts[3] = {21, 10, 0};
+    const int widths[3] = {11, 11, 10};
+    for (int pass = 0; pass < 3; ++pass) {
+        const int sh_bits = shifts[pass];
+        const uint32_t dmask = (1u << widths[pass]) - 1u;
+        for (int b = threadIdx.x; b < kDigitBins; b += blockDim.x) sh[b] = 0u;
+        __syncthreads();
+        for (int64_t e = threadIdx.x; e < n; e += blockDim.x) {
+            const uint32_t key = row_key(row[e]);
+            if ((key & pmask) == prefix) atomicAdd(&sh[(key >> sh_bits) & dmask], 1u);
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            uint32_t cum = 0;
+            int digit = 0;
+            for (int b = (int)dmask; b >= 0; --b) {
+                if (cum + sh[b] >= need) {
+                    digit = b;
+                    break;
+                }
+                cum += sh[b];
+            }
+            s_vals[0] = prefix | ((uint32_t)digit << sh_bits);
+            s_vals[1] = need - cum;
+        }
+        __syncthreads();
+        prefix = s_vals[0];
+        need = s_vals[1];
+        pmask |= dmask << sh_bits;
+        __syncthreads();
+    }
+    const uint32_t T = prefix;         // the k-th largest key
+    const uint32_t ties = need;        // how many keys equal to T belong to the top-k
+    if (threadIdx.x == 0) s_vals[2] = 0u;
+    __syncthreads();
+    for (int64_t e = threadIdx.x; e < n; e += blockDim.x) {
+        const uint32_t key = row_key(row[e]);
+        if (key > T) sm[atomicAdd(&s_vals[2], 1u)] = make_rank(key, (uint32_t)e);
+    }
+    __syncthreads();
+    uint32_t taken = 0;  // ties collected so far, identical in every thread
+    for (int64_t c0 = 0; c0 < n && taken < ties; c0 += blockDim.x) {
+        const int64_t e = c0 + threadIdx.x;
+        const bool eq = e < n && row_key(row[e]) == T;
+        const uint32_t incl = block_inclusive_scan(eq ? 1u : 0u, scan_buf);
+        const uint32_t ordinal = taken + incl - (eq ? 1u : 0u);
+        if (eq && ordinal < ties) sm[o.k - ties + ordinal] = make_rank(T, (uint32_t)e);
+        taken += scan_buf[blockDim.x - 1];  // the chunk's total: the last thread's inclusive sum
+        __syncthreads();
+    }
+    int m = 64;
+    while (m < o.k) m <<= 1;
+    for (int i = o.k + threadIdx.x; i < m; i += blockDim.x) sm[i] = 0ull;
+    __syncthreads();
+    block_sort_desc(sm, m);
+    for (int r = threadIdx.x; r < o.k; r += blockDim.x) write_result(o, seg, r, sm[r]);
+}
+
+// ---------------------------------------------------------------- tile-bounded selection
+
+// Top-k of score rows that come with per-tile maxima (tmax[row][tile] = largest
+// score among elements 32 tile .. 32 tile + 31).  K tiles whose maxima reach a
+// value B hold K distinct elements >= B, so the k-th largest score is >= B and
+// every element of the top k lies in a tile whose maximum is >= B.  One
+// workgroup per row:
+//   1. histograms of the tile-maximum keys pin the k-th largest one to a bin
+//      (see below); B is the lower edge of that bin, so at least k tiles
+//      reach it;
+//   2. the tiles whose maximum reaches B are listed (about k of them for
+//      i.i.d. scores), their scores read, and those >= B kept in LDS;
+//   3. the kept ranks are sorted in LDS and the best k written.
+// A row with fewer than k tiles keeps every element; if the tile list or the
+// kept ranks overflow LDS (many equal scores), the row is selected exactly by
+// select_row_exactly instead.
+constexpr int kTileListCap = 4096;
+
+// Call f(i, in_range, key) for tile maxima i = 0 .. tiles - 1, thread by thread
+// in blocks of 16 per thread whose loads are all issued before any is used.
+// Every lane calls f the same number of times (f may use wave ballots).  The
+// loads are unconditional (clamped index) and all keys are formed before any
+// f runs: a load or a use inside a branch makes the compiler wait for every
+// outstanding load there.
+template <typename F>
+__device__ __forceinline__ void scan_tiles(const uint32_t *tm, int64_t tiles, F &&f) {
+    constexpr int U = 16;
+    for (int64_t i0 = 0; i0 < tiles; i0 += (int64_t)U * blockDim.x) {
+        uint32_t kv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = i0 + (int64_t)u * blockDim.x + threadIdx.x;
+            kv[u] = tm[i < tiles ? i : tiles - 1];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) kv[u] = row_key(kv[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int64_t i = i0 + (int64_t)u * blockDim.x + threadIdx.x;
+            f(i, i < tiles, kv[u]);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBatchSelectThreads) void tile_bound_select_kernel(const uint32_t *__restrict__ rows,
+                                                                              int64_t ld, int64_t n,
+                                                                              const uint32_t *__restrict__ tmax,
+                                                                              int64_t tld, SelectOut o) {
+    __shared__ uint64_t sm[kSortCap];
+    __shared__ uint32_t sh[kDigitBins];
+    __shared__ uint32_t scan_buf[kBatchSelectThreads];
+    __shared__ uint32_t tl[kTileListCap];
+    __shared__ uint32_t s_vals[4];
+    const int seg = blockIdx.y;
+    const int t = threadIdx.x;
+    const int lane = lane_id();
+    const uint32_t *row = rows + (int64_t)seg * ld;
+    const uint32_t *tm = tmax + (int64_t)seg * tld;
+    const int64_t tiles = (n + 31) / 32;
+
+    // 1. the bound.  Tile maxima crowd into a few top-11-bit bins, so the
+    //    first try histograms a window just below the largest tile maximum in
+    //    2048 bins of 2^12 key units (2^23 units: one octave for fp32),
+    //    counting only keys inside it: few keys, spread out, few LDS
+    //    collisions.  If fewer than k keys fall inside, two plain 11-bit
+    //    passes over all keys pin the top 22 bits instead.
+    uint32_t bound = 0;
+    if (tiles >= o.k) {
+        uint32_t top = 0;
+        scan_tiles(tm, tiles, [&](int64_t, bool ok, uint32_t key) {
+            if (ok) top = max(top, key);
+        });
+        for (int off = 32; off >= 1; off >>= 1) top = max(top, (uint32_t)__shfl_xor((int)top, off));
+        if (t == 0) s_vals[0] = 0u;
+        for (int b = t; b < kDigitBins; b += blockDim.x) sh[b] = 0u;
+        __syncthreads();
+        if (lane == 0) atomicMax(&s_vals[0], top);
+        __syncthreads();
+        top = s_vals[0] >> 12;  // window: key >> 12 in (top - 2048, top]
+        scan_tiles(tm, tiles, [&](int64_t, bool ok, uint32_t key) {
+            const uint32_t dist = top - (key >> 12);
+            if (ok && dist < (uint32_t)kDigitBins) atomicAdd(&sh[dist], 1u);
+        });
+        __syncthreads();
+        // lowest window bin (distance from the top) whose prefix count reaches k
+        const uint32_t c0 = sh[2 * t], c1 = sh[2 * t + 1];
+        const uint32_t incl = block_inclusive_scan(c0 + c1, scan_buf);
+        const uint32_t before = incl - c0 - c1;
+        if (t == 0) s_vals[1] = 0xffffffffu;
+        __syncthreads();
+        if (before < (uint32_t)o.k && incl >= (uint32_t)o.k)
+            s_vals[1] = (before + c0 >= (uint32_t)o.k) ? (uint32_t)(2 * t) : (uint32_t)(2 * t + 1);
+        __syncthreads();
+        const uint32_t dist = s_vals[1];
+        if (dist != 0xffffffffu) {
+            bound = (top - dist) << 12;
+        } else {
+            uint32_t prefix = 0, pmask = 0, need = (uint32_t)o.k;
+            for (int pass = 0; pass < 2; ++pass) {
+                const int shift = pass == 0 ? 21 : 10;
+                for (int b = t; b < kDigitBins; b += blockDim.x) sh[b] = 0u;
+                __syncthreads();
+                scan_tiles(tm, tiles, [&](int64_t, bool ok, uint32_t key) {
+                    if (ok && (key & pmask) == prefix) atomicAdd(&sh[(key >> shift) & (kDigitBins - 1)], 1u);
+                });
+                __syncthreads();
+                // highest digit whose suffix count reaches `need`: thread t
+                // owns digits 2047 - 2t and 2046 - 2t, a prefix sum gives
+                // suffix counts
+                const uint32_t hi = sh[kDigitBins - 1 - 2 * t];
+                const uint32_t lo = sh[kDigitBins - 2 - 2 * t];
+                const uint32_t incl2 = block_inclusive_scan(hi + lo, scan_buf);
+                const uint32_t before2 = incl2 - hi - lo;
+                if (before2 < need && incl2 >= need) {
+                    const bool in_hi = before2 + hi >= need;
+                    s_vals[0] = (uint32_t)(kDigitBins - (in_hi ? 1 : 2) - 2 * t);
+                    s_vals[1] = in_hi ? before2 : before2 + hi;  // keys above the digit
+                }
+                __syncthreads();
+                prefix |= s_vals[0] << shift;
+                need -= s_vals[1];
+                pmask |= (uint32_t)(kDigitBins - 1) << shift;
+                __syncthreads();
+            }
+            bound = prefix;
+        }
+    }
+
+    // 2. tiles reaching the bound, then their elements >= bound
+    if (t == 0) {
+        s_vals[2] = 0u;  // listed tiles
+        s_vals[3] = 0u;  // kept ranks
+    }
+    __syncthreads();
+    scan_tiles(tm, tiles, [&](int64_t i, bool ok, uint32_t key) {
+        const bool take = ok && key >= bound;
+        const uint64_t m = __ballot(take);
+        if (m == 0) return;
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&s_vals[2], (uint32_t)__popcll(m));
+        base = (uint32_t)__shfl(base, 0);
+        const uint32_t pos = base + (uint32_t)lanes_below(m);
+        if (take && pos < (uint32_t)kTileListCap) tl[pos] = (uint32_t)i;
+    });
+    __syncthreads();
+    const uint32_t listed = s_vals[2];
+    bool overflow = listed > (uint32_t)kTileListCap;
+    if (!overflow) {
+        // half-wave h takes listed tiles h, h + 32, ...; lane l of it element
+        // l.  Sixteen tiles' loads are issued before any is used, and each
+        // wave reserves its kept slots with one LDS atomic per round.
+        constexpr int kGatherUnroll = 16;
+        const int half = t >> 5;
+        const int l = t & 31;
+        const int halves = blockDim.x >> 5;
+        for (uint32_t j0 = 0; j0 < listed; j0 += (uint32_t)(halves * kGatherUnroll)) {
+            uint32_t key[kGatherUnroll];
+            int64_t e[kGatherUnroll];
+#pragma unroll
+            for (int u = 0; u < kGatherUnroll; ++u) {
+                const uint32_t j = j0 + (uint32_t)(u * halves + half);
+                e[u] = (j < listed) ? (int64_t)tl[j < (uint32_t)kTileListCap ? j : 0u] * 32 + l : n;
+                key[u] = row[e[u] < n ? e[u] : n - 1];  // unconditional load (see scan_tiles)
+            }
+#pragma unroll
+            for (int u = 0; u < kGatherUnroll; ++u) key[u] = row_key(key[u]);
+            uint64_t mk[kGatherUnroll];
+            uint32_t total = 0;
+#pragma unroll
+            for (int u = 0; u < kGatherUnroll; ++u) {
+                mk[u] = __ballot(e[u] < n && key[u] >= bound);
+                total += (uint32_t)__popcll(mk[u]);
+            }
+            if (total == 0) continue;
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&s_vals[3], total);
+            base = (uint32_t)__shfl(base, 0);
+#pragma unroll
+            for (int u = 0; u < kGatherUnroll; ++u) {
+                const uint32_t pos = base + (uint32_t)lanes_below(mk[u]);
+                if (((mk[u] >> lane) & 1ull) && pos < (uint32_t)kSortCap)
+                    sm[pos] = make_rank(key[u], (uint32_t)e[u]);
+                base += (uint32_t)__popcll(mk[u]);
+            }
+        }
+        __syncthreads();
+        overflow = s_vals[3] > (uint32_t)kSortCap;
+    }
+    if (overflow) {
+        __syncthreads();
+        select_row_exactly(row, n, o, seg, sm, sh, scan_buf, s_vals);
+        return;
+    }
+
+    // 3. sort what was kept (at least k ranks) and write the best k
+    const int kept = (int)s_vals[3];
+    int msz = 64;
+    while (msz < kept) msz <<= 1;
+    for (int i = kept + t; i < msz; i += blockDim.x) sm[i] = 0ull;
+    __syncthreads();
+    block_sort_desc(sm, msz);
+    for (int r = t; r < o.k; r += blockDim.x) write_result(o, seg, r, sm[r]);
+}
+
+hipError_t launch_tile_bound_select(const float *rows, int64_t ld, int64_t n, const float *tmax, int64_t tld,
+                                    int segments, int k, int32_t *out_idx, float *out_scores, hipStream_t stream) {
+    SelectOut o;
+    o.k = k;
+    o.out_idx = out_idx;
+    o.out_val = reinterpret_cast<uint32_t *>(out_scores);
+    hipLaunchKernelGGL(tile_bound_select_kernel, dim3(1, segments), dim3(kBatchSelectThreads), 0, stream,
+                       reinterpret_cast<const uint32_t *>(rows), ld, n, reinterpret_cast<const uint32_t *>(tmax),
+                       tld, o);
+    return hipGetLastError();
+}
+
+}  // namespace rt

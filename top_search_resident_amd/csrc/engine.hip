@@ -24,10 +24,6 @@ constexpr int32_t kMaxQ = 32;
 constexpr int64_t kTreeRanks = int64_t(1) << 23;
 // Most streaming workgroups per segment (bounds the counter array).
 constexpr int64_t kMaxWgsPerSeg = 2048;
-// Large-K radix selector: candidate capacity per query row.
-constexpr int64_t kRadixCandCap = int64_t(1) << 16;
-// Lists longer than this use the radix selector on materialised batch scores.
-constexpr int kMaxListForBatch = 128;
 // Streaming waves per CU the planner aims for (measured on MI355X): about 8 for
 // the scorer (1M x 1024), 16 for raw-array selection (1e8 int32).
 constexpr int64_t kScoreWavesPerCu = 8;
@@ -78,10 +74,10 @@ struct rt_engine {
     int32_t resident_d = 0;
     float *corpus = nullptr;
     float *scores = nullptr;  // batched scores, max_q x roundup(max_n, 64); only when max_q > 1
+    float *tmax = nullptr;    // per-query maxima of 32-row score tiles, max_q x tile_ld; only when max_q > 1
+    int64_t tile_ld = 0;
     uint64_t *tree = nullptr;       // kTreeRanks merge-tree ranks
     uint32_t *counters = nullptr;   // kMaxQ x kMaxWgsPerSeg arrival counters
-    uint32_t *radix_u32 = nullptr;  // kMaxQ x (2048 + 2): histograms, candidate counts, arrivals
-    uint64_t *radix_cand = nullptr; // kMaxQ x kRadixCandCap candidate ranks (batched engines only)
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
     bool profiling = false;
     bool had_batch_kernel = false;
@@ -154,10 +150,9 @@ void rt_engine_destroy(rt_engine *e) {
     (void)hipDeviceSynchronize();
     (void)hipFree(e->corpus);
     (void)hipFree(e->scores);
+    (void)hipFree(e->tmax);
     (void)hipFree(e->tree);
     (void)hipFree(e->counters);
-    (void)hipFree(e->radix_u32);
-    (void)hipFree(e->radix_cand);
     for (auto &ev : e->ev)
         if (ev) (void)hipEventDestroy(ev);
     (void)hipSetDevice(prev);
@@ -203,17 +198,16 @@ rt_status rt_engine_create(int64_t max_n, int32_t max_d, int32_t max_k, int32_t 
     bool ok = alloc(reinterpret_cast<void **>(&e->corpus), sizeof(float) * (size_t)max_n * (size_t)max_d) &&
               alloc(reinterpret_cast<void **>(&e->tree), sizeof(uint64_t) * (size_t)kTreeRanks) &&
               alloc(reinterpret_cast<void **>(&e->counters), sizeof(uint32_t) * (size_t)(kMaxQ * kMaxWgsPerSeg));
+    e->tile_ld = ((max_n + 31) / 32 + 63) / 64 * 64;
     if (ok && max_q > 1)
         ok = alloc(reinterpret_cast<void **>(&e->scores), sizeof(float) * (size_t)max_q * (size_t)ld) &&
-             alloc(reinterpret_cast<void **>(&e->radix_u32), sizeof(uint32_t) * (size_t)kMaxQ * (2048 + 2)) &&
-             alloc(reinterpret_cast<void **>(&e->radix_cand), sizeof(uint64_t) * (size_t)kMaxQ * kRadixCandCap);
+             alloc(reinterpret_cast<void **>(&e->tmax), sizeof(float) * (size_t)max_q * (size_t)e->tile_ld);
     if (!ok) {
         rt_engine_destroy(e);
         (void)hipSetDevice(prev);
         return RT_ENOMEM;
     }
     err = hipMemset(e->counters, 0, sizeof(uint32_t) * (size_t)(kMaxQ * kMaxWgsPerSeg));
-    if (err == hipSuccess && e->radix_u32) err = hipMemset(e->radix_u32, 0, sizeof(uint32_t) * (size_t)kMaxQ * (2048 + 2));
     if (err == hipSuccess) err = rt::prepare_mfma_scores();
     for (int i = 0; i < 4 && err == hipSuccess; ++i) err = hipEventCreate(&e->ev[i]);
     if (err == hipSuccess) err = hipDeviceSynchronize();
@@ -268,7 +262,6 @@ static hipError_t prologue(rt_engine *e, hipStream_t s) {
     hipError_t err = hipSuccess;
     if (e->dirty) {
         err = rt::launch_zero_counters(e->counters, (int64_t)kMaxQ * kMaxWgsPerSeg, s);
-        if (err == hipSuccess && e->radix_u32) err = rt::launch_zero_counters(e->radix_u32, (int64_t)kMaxQ * (2048 + 2), s);
         if (err != hipSuccess) return err;
         e->dirty = false;
     }
@@ -293,26 +286,10 @@ rt_status search_resident(rt_engine *e, const float *queries, int32_t q, int32_t
     if (err == hipSuccess) err = prologue(e, s);
     if (err == hipSuccess && batched) {
         const int64_t ld = (n + 63) / 64 * 64;
-        err = rt::launch_mfma_scores(e->corpus, n, d, queries, q, e->scores, ld, e->num_cus, s);
+        err = rt::launch_mfma_scores(e->corpus, n, d, queries, q, e->scores, ld, e->tmax, e->tile_ld, e->num_cus, s);
         if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[3], s);
-        if (kp <= kMaxListForBatch) {
-            // each wave streams at least 1024 scores (256 groups of 4)
-            const Plan p = plan_stream((n + 3) / 4, q, kp, 256, e->num_cus, kSelectWavesPerCu, rt::select_waves(kp));
-            const rt::TreeLaunch t = tree_for(e, p, kp, k, 1, out_idx, out_scores, nullptr, 0);
-            if (err == hipSuccess) err = rt::launch_select_topk(e->scores, ld, n, 1, q, p.per_wave, p.wgs, t, s);
-        } else if (err == hipSuccess) {
-            rt::RadixScratch sc;
-            sc.hist = e->radix_u32;
-            sc.count = e->radix_u32 + (size_t)kMaxQ * 2048;
-            sc.arrive = sc.count + kMaxQ;
-            sc.cand = e->radix_cand;
-            sc.cand_cap = kRadixCandCap;
-            int wgs = (int)(2 * (int64_t)e->num_cus / q);
-            const int64_t by_size = (n + 8191) / 8192;  // at least ~8K scores per workgroup
-            if (wgs > by_size) wgs = (int)by_size;
-            if (wgs < 1) wgs = 1;
-            err = rt::launch_radix_topk(e->scores, ld, n, q, k, wgs, sc, out_idx, out_scores, s);
-        }
+        if (err == hipSuccess)
+            err = rt::launch_tile_bound_select(e->scores, ld, n, e->tmax, e->tile_ld, q, k, out_idx, out_scores, s);
     } else if (err == hipSuccess) {
         const Plan p = plan_stream(n, q, kp, 32, e->num_cus, kScoreWavesPerCu, rt::kStreamWaves);
         const rt::TreeLaunch t = tree_for(e, p, kp, k, 1, out_idx, out_scores, nullptr, 0);

@@ -54,23 +54,16 @@ hipError_t launch_select_topk(const void *base, int64_t seg_stride, int64_t n, i
 // Clear merge-tree counters after a failed launch left them in an unknown state.
 hipError_t launch_zero_counters(uint32_t *counters, int64_t count, hipStream_t stream);
 
-// Scratch of the large-K radix selector (all counters zero between calls).
-struct RadixScratch {
-    uint32_t *hist;     // [segments][2048] key-prefix histograms
-    uint32_t *count;    // [segments] candidate counts
-    uint32_t *arrive;   // [segments] workgroup arrival counters
-    uint64_t *cand;     // [segments][cand_cap] candidate ranks
-    int64_t cand_cap;
-};
-
-// Exact top-k (k <= 1024) of each of `segments` fp32 rows of n scores, ld apart,
-// via key-prefix histograms (two launches); writes index + score per row.
-hipError_t launch_radix_topk(const float *rows, int64_t ld, int64_t n, int segments, int k, int wgs_per_seg,
-                             const RadixScratch &sc, int32_t *out_idx, float *out_scores, hipStream_t stream);
-
 // Batched inner products S[q][row] (row stride ld) on MFMA; q <= 32, d % 4 == 0, d <= 1024.
+// Also writes, per query, the largest score of every 32-row tile:
+// tmax[query * tld + tile], tile = row / 32.
 hipError_t prepare_mfma_scores();
 hipError_t launch_mfma_scores(const float *corpus, int64_t n, int d, const float *queries, int q,
-                              float *scores, int64_t ld, int num_cus, hipStream_t stream);
+                              float *scores, int64_t ld, float *tmax, int64_t tld, int num_cus, hipStream_t stream);
+
+// Exact top-k (k <= 1024) of each of `segments` fp32 score rows (ld apart) given
+// their 32-element tile maxima (tld apart); writes index + score per row.
+hipError_t launch_tile_bound_select(const float *rows, int64_t ld, int64_t n, const float *tmax, int64_t tld,
+                                    int segments, int k, int32_t *out_idx, float *out_scores, hipStream_t stream);
 
 }  // namespace rt

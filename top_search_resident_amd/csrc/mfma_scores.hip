@@ -22,10 +22,15 @@
 // outstanding loads, which serialises the pipeline.)  The loads are ordinary
 // (cached): a line is consumed by four successive load instructions, and the
 // non-temporal hint made it miss again (measured 1.7x slower on MI355X).
-// Output element (query, row) of a 32x32 tile sits in lane row % 32 + 32 *
-// ((query / 4) % 2), register (query % 4) + 4 * (query / 8); rows are stored
-// contiguously per query (S row stride ld), so each store is 128 B per half-wave.
+// The corpus rows are the MFMA's first (M) operand and the queries its second
+// (N), so the 32 x 32 output tile (rows x queries) has element (row, query) in
+// lane query % 32 + 32 * ((row / 4) % 2), register (row % 4) + 4 * (row / 8):
+// each lane holds sixteen rows of one query, four runs of four consecutive
+// rows, stored as four 16-byte stores into that query's score row (row stride
+// ld), and the tile's maximum per query is an in-register maximum plus one
+// exchange between the lane halves.
 #include "kernels.hpp"
+#include "wave_topk.hpp"
 
 namespace rt {
 
@@ -43,12 +48,46 @@ constexpr int kMfmaAcc = 2;
 // Columns the kernel walks for depth d: whole rounds of kpf chunks.
 constexpr int mfma_cols(int d, int kpf) { return ((d + 32 * kpf - 1) / (32 * kpf)) * (32 * kpf); }
 
+// Store a finished tile (rows row0 .. row0 + 31 x queries) and, per query, the
+// largest of its valid scores into tmax[query][tile].  Lane (query j = lane %
+// 32, half h = lane / 32) holds rows 8 g + 4 h + c in register 4 g + c.
+__device__ __forceinline__ void store_tile(const floatx16 &acc, int64_t t, int64_t n, int q, int lane,
+                                           float *__restrict__ scores, int64_t ld, float *__restrict__ tmax,
+                                           int64_t tld) {
+    const int j = lane & 31;
+    const int h = lane >> 5;
+    const int64_t row0 = t * 32;
+    const bool has_q = j < q;
+    float *srow = scores + (int64_t)j * ld + row0 + 4 * h;
+    float mx = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+        const int64_t r = row0 + 8 * g + 4 * h;  // first row of this run of four
+        const float4 v = make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+        if (r + 3 < n) {
+            if (has_q) *reinterpret_cast<float4 *>(srow + 8 * g) = v;
+            mx = fmaxf(mx, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                if (r + c < n) {
+                    if (has_q) srow[8 * g + c] = acc[4 * g + c];
+                    mx = fmaxf(mx, acc[4 * g + c]);
+                }
+            }
+        }
+    }
+    mx = fmaxf(mx, __uint_as_float(xor_u32<32>(__float_as_uint(mx))));
+    if (h == 0 && has_q) tmax[(int64_t)j * tld + t] = mx;
+}
+
 // KPF: chunks loaded ahead; NT: workgroup size; ACC: independent accumulators
 // (chunk j accumulates into acc[j % ACC], summed at the end).
 template <int KPF, int NT, int ACC>
 __global__ __launch_bounds__(NT) void mfma_scores_kernel(const float *__restrict__ corpus, int64_t n, int d,
                                                          const float *__restrict__ queries, int q,
                                                          float *__restrict__ scores, int64_t ld,
+                                                         float *__restrict__ tmax, int64_t tld,
                                                          int64_t tiles_per_wave) {
     static_assert(KPF % ACC == 0, "each ring slot feeds one accumulator");
     extern __shared__ float qs[];
@@ -63,7 +102,7 @@ __global__ __launch_bounds__(NT) void mfma_scores_kernel(const float *__restrict
     __syncthreads();
 
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    const int wv = wave_in_group();  // wave-uniform: the tile loop runs on scalar registers
     const int m = lane & 31;
     const int kk = lane >> 5;
     const int64_t wave = (int64_t)blockIdx.x * (NT / 64) + wv;
@@ -111,7 +150,7 @@ __global__ __launch_bounds__(NT) void mfma_scores_kernel(const float *__restrict
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
                         acc[s % ACC] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                            comp(a[i], e), in_row ? comp(buf[s][i], e) : 0.f, acc[s % ACC], 0, 0, 0);
+                            in_row ? comp(buf[s][i], e) : 0.f, comp(a[i], e), acc[s % ACC], 0, 0, 0);
                 }
                 load_chunk(ci + s + KPF, buf[s]);
                 // keep the refill here: left alone, the scheduler sinks it down
@@ -123,13 +162,7 @@ __global__ __launch_bounds__(NT) void mfma_scores_kernel(const float *__restrict
         for (int h = 1; h < ACC; ++h)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[0][v] += acc[h][v];
-        if (valid) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int qi = 8 * (v >> 2) + 4 * kk + (v & 3);
-                if (qi < q) scores[(int64_t)qi * ld + row0 + m] = acc[0][v];
-            }
-        }
+        store_tile(acc[0], t, n, q, lane, scores, ld, tmax, tld);
     }
 }
 
@@ -143,6 +176,7 @@ template <int NCK, int KPF, int NT, int ACC>
 __global__ __launch_bounds__(NT) void mfma_scores_fixed_kernel(const float *__restrict__ corpus, int64_t n,
                                                                const float *__restrict__ queries, int q,
                                                                float *__restrict__ scores, int64_t ld,
+                                                               float *__restrict__ tmax, int64_t tld,
                                                                int64_t tiles_per_wave) {
     static_assert(KPF <= NCK && NCK % ACC == 0, "pipeline shape");
     constexpr int d = NCK * 32;
@@ -155,7 +189,7 @@ __global__ __launch_bounds__(NT) void mfma_scores_fixed_kernel(const float *__re
     __syncthreads();
 
     const int lane = threadIdx.x & 63;
-    const int wv = threadIdx.x >> 6;
+    const int wv = wave_in_group();  // wave-uniform: the tile loop runs on scalar registers
     const int m = lane & 31;
     const int kk = lane >> 5;
     const int64_t wave = (int64_t)blockIdx.x * (NT / 64) + wv;
@@ -199,7 +233,7 @@ __global__ __launch_bounds__(NT) void mfma_scores_fixed_kernel(const float *__re
             for (int i = 0; i < 4; ++i) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    acc[j % ACC] = __builtin_amdgcn_mfma_f32_32x32x2f32(comp(a[i], e), comp(buf[s][i], e),
+                    acc[j % ACC] = __builtin_amdgcn_mfma_f32_32x32x2f32(comp(buf[s][i], e), comp(a[i], e),
                                                                         acc[j % ACC], 0, 0, 0);
             }
             if (j + KPF < NCK)
@@ -212,14 +246,7 @@ __global__ __launch_bounds__(NT) void mfma_scores_fixed_kernel(const float *__re
         for (int h = 1; h < ACC; ++h)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[0][v] += acc[h][v];
-        const int64_t row0 = t * 32;
-        if (row0 + m < n) {
-#pragma unroll
-            for (int v = 0; v < 16; ++v) {
-                const int qi = 8 * (v >> 2) + 4 * kk + (v & 3);
-                if (qi < q) scores[(int64_t)qi * ld + row0 + m] = acc[0][v];
-            }
-        }
+        store_tile(acc[0], t, n, q, lane, scores, ld, tmax, tld);
         p = pn;
     }
 }
@@ -247,7 +274,7 @@ hipError_t prepare_mfma_scores() {
 }
 
 hipError_t launch_mfma_scores(const float *corpus, int64_t n, int d, const float *queries, int q, float *scores,
-                              int64_t ld, int num_cus, hipStream_t stream) {
+                              int64_t ld, float *tmax, int64_t tld, int num_cus, hipStream_t stream) {
     const int64_t tiles = (n + 31) / 32;
 #define RT_FIXED(NCK)                                                                                          \
     if (d == NCK * 32) {                                                                                       \
@@ -256,7 +283,7 @@ hipError_t launch_mfma_scores(const float *corpus, int64_t n, int d, const float
         const int64_t blocks = (tiles + tpw * w - 1) / (tpw * w);                                              \
         hipLaunchKernelGGL((mfma_scores_fixed_kernel<NCK, kFixedPrefetch, kFixedThreads, kFixedAcc>),          \
                            dim3((unsigned)blocks), dim3(kFixedThreads), mfma_lds_bytes(d, 1), stream, corpus, n, \
-                           queries, q, scores, ld, tpw);                                                       \
+                           queries, q, scores, ld, tmax, tld, tpw);                                                       \
         return hipGetLastError();                                                                              \
     }
     RT_MFMA_FIXED(RT_FIXED)
@@ -266,7 +293,7 @@ hipError_t launch_mfma_scores(const float *corpus, int64_t n, int d, const float
     const int64_t blocks = (tiles + tiles_per_wave * w - 1) / (tiles_per_wave * w);
     hipLaunchKernelGGL((mfma_scores_kernel<kMfmaPrefetch, kMfmaThreads, kMfmaAcc>), dim3((unsigned)blocks),
                        dim3(kMfmaThreads), mfma_lds_bytes(d, kMfmaPrefetch), stream, corpus, n, d, queries, q, scores,
-                       ld, tiles_per_wave);
+                       ld, tmax, tld, tiles_per_wave);
     return hipGetLastError();
 }
 
