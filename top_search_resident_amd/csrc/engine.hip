@@ -24,8 +24,9 @@ constexpr int32_t kMaxQ = 32;
 constexpr int64_t kTreeRanks = int64_t(1) << 23;
 // Most streaming workgroups per segment (bounds the counter array).
 constexpr int64_t kMaxWgsPerSeg = 2048;
-// Streaming waves per CU the planner aims for (measured on MI355X): about 8 for
-// the scorer (1M x 1024), 16 for raw-array selection (1e8 int32).
+// Streaming waves per CU the planner aims for (measured on MI355X): 8 for the
+// scorer -- one 8-wave workgroup per CU beat 4-wave pairs and 16 waves per CU
+// from 10k x 384 to 1M x 1024 -- and 16 for raw-array selection (1e8 int32).
 constexpr int64_t kScoreWavesPerCu = 8;
 constexpr int64_t kSelectWavesPerCu = 16;
 
@@ -291,7 +292,7 @@ rt_status search_resident(rt_engine *e, const float *queries, int32_t q, int32_t
         if (err == hipSuccess)
             err = rt::launch_tile_bound_select(e->scores, ld, n, e->tmax, e->tile_ld, q, k, out_idx, out_scores, s);
     } else if (err == hipSuccess) {
-        const Plan p = plan_stream(n, q, kp, 32, e->num_cus, kScoreWavesPerCu, rt::kStreamWaves);
+        const Plan p = plan_stream(n, q, kp, 32, e->num_cus, kScoreWavesPerCu, rt::gemv_waves(kp));
         const rt::TreeLaunch t = tree_for(e, p, kp, k, 1, out_idx, out_scores, nullptr, 0);
         err = rt::launch_gemv_topk(e->corpus, n, d, queries, q, p.per_wave, p.wgs, t, s);
     }

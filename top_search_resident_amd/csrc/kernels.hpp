@@ -6,9 +6,12 @@
 
 namespace rt {
 
-// Workgroup shape of the streaming kernels: 4 waves of 64 lanes.
-constexpr int kStreamWaves = 4;
-constexpr int kStreamThreads = kStreamWaves * 64;
+// Workgroup shape of the scoring kernels: kGemvWaves waves of 64 lanes for
+// lists of up to 256 entries (a merge-tree node merges its lists with all the
+// workgroup's waves), 4 waves for longer lists (all wave lists must fit the
+// merge LDS).
+constexpr int kGemvWaves = 8;
+constexpr int gemv_waves(int kp) { return kp <= 256 ? kGemvWaves : 4; }
 // Raw-array selection runs 16-wave workgroups that share a certified bound in
 // LDS (all 16 lists must fit the merge LDS, so only for lists <= 256 entries).
 constexpr int select_waves(int kp) { return kp <= 256 ? 16 : 4; }

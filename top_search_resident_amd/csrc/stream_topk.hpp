@@ -62,7 +62,10 @@ __device__ __forceinline__ void write_output(const TreeArgs &ta, int seg, int r,
 }
 
 // Merge `count` best-first lists of 64*R ranks held contiguously in LDS at sm
-// into sm[0 .. 64*R).  Pairs of lists are merged by one wave each, level by level.
+// into sm[0 .. 64*R).  Pairs of lists are merged by one wave each, level by
+// level.  A merge is bound by instruction issue (running several pairs side by
+// side in one wave measured slower), so merge throughput is the number of
+// waves of the workgroup.
 template <int R>
 __device__ __forceinline__ void merge_lds_lists(uint64_t *sm, int count) {
     constexpr int Kp = 64 * R;
@@ -121,9 +124,23 @@ __device__ __forceinline__ void tree_finish(uint64_t *sm, MergeScratch *ms, cons
         }
         __syncthreads();
         if (!ms->flag) return;
+        // All of a thread's loads are issued before any is stored to LDS (a
+        // loop of load-then-store pays one device round trip per entry).
         const uint64_t *src = base + level_off + (int64_t)first * Kp;
-        for (int i = threadIdx.x; i < children * Kp; i += NT)
-            sm[i] = ((i & (Kp - 1)) < k) ? __hip_atomic_load(&src[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+        constexpr int E = kTreeEntries / NT;
+        uint64_t v[E];
+#pragma unroll
+        for (int u = 0; u < E; ++u) {
+            const int i = u * NT + threadIdx.x;
+            v[u] = (i < children * Kp && (i & (Kp - 1)) < k)
+                       ? __hip_atomic_load(&src[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                       : 0ull;
+        }
+#pragma unroll
+        for (int u = 0; u < E; ++u) {
+            const int i = u * NT + threadIdx.x;
+            if (i < children * Kp) sm[i] = v[u];
+        }
         __syncthreads();
         merge_lds_lists<R>(sm, children);
         const int up = (count + ta.fan - 1) / ta.fan;
@@ -183,21 +200,22 @@ struct RowUnroll {
 // identical rows get bit-identical scores wherever they sit, and exact ties
 // resolve by index.
 template <int LG, int L, int R>
-__global__ __launch_bounds__(kStreamThreads) void gemv_topk_kernel(
+__global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_topk_kernel(
     const float *__restrict__ corpus, int64_t n, int d, const float *__restrict__ queries,
     int64_t rows_per_wave, TreeArgs ta) {
     constexpr int G = 1 << LG;
     constexpr int RPS = 64 >> LG;  // rows per lane-group pass
     constexpr int U = RowUnroll<L>::value;
     constexpr int STEP = RPS * U;  // rows per wave step
-    __shared__ uint64_t stage[kStreamWaves][128];
+    constexpr int W = gemv_waves(64 * R);
+    __shared__ uint64_t stage[W][128];
     __shared__ uint64_t sm[kTreeEntries];
     __shared__ MergeScratch ms;
 
     const int seg = blockIdx.y;
     const int lane = lane_id();
     const int wv = wave_in_group();
-    const int64_t wave = (int64_t)blockIdx.x * kStreamWaves + wv;
+    const int64_t wave = (int64_t)blockIdx.x * W + wv;
     const int g = lane & (G - 1);
     const int h = lane >> LG;
     const int d4 = d >> 2;
@@ -261,22 +279,23 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_topk_kernel(
         }
     }
     sel.finish(my_stage);
-    finish_workgroup<R, kStreamThreads>(sel, sm, &ms, ta, seg);
+    finish_workgroup<R, W * 64>(sel, sm, &ms, ta, seg);
 }
 
 // Any d: one row per wave at a time, scalar loads strided by 64 lanes.
 template <int R>
-__global__ __launch_bounds__(kStreamThreads) void gemv_topk_generic_kernel(
+__global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_topk_generic_kernel(
     const float *__restrict__ corpus, int64_t n, int d, const float *__restrict__ queries,
     int64_t rows_per_wave, TreeArgs ta) {
     constexpr int U = 4;
-    __shared__ uint64_t stage[kStreamWaves][128];
+    constexpr int W = gemv_waves(64 * R);
+    __shared__ uint64_t stage[W][128];
     __shared__ uint64_t sm[kTreeEntries];
     __shared__ MergeScratch ms;
     const int seg = blockIdx.y;
     const int lane = lane_id();
     const int wv = wave_in_group();
-    const int64_t wave = (int64_t)blockIdx.x * kStreamWaves + wv;
+    const int64_t wave = (int64_t)blockIdx.x * W + wv;
     const float *__restrict__ q = queries + (int64_t)seg * d;
     uint64_t *const my_stage = stage[wv];
     WaveSelector<R> sel;
@@ -309,7 +328,7 @@ __global__ __launch_bounds__(kStreamThreads) void gemv_topk_generic_kernel(
         }
     }
     sel.finish(my_stage);
-    finish_workgroup<R, kStreamThreads>(sel, sm, &ms, ta, seg);
+    finish_workgroup<R, W * 64>(sel, sm, &ms, ta, seg);
 }
 
 // ---------------------------------------------------------------- raw arrays
@@ -481,7 +500,7 @@ hipError_t launch_stream_r(int kind, int lg, int L, dim3 grid, hipStream_t s, co
         case 0: {  // fast scoring path
 #define RT_SHAPE(LGV, LV)                                                                                      \
     if (lg == LGV && L == LV) {                                                                                \
-        hipLaunchKernelGGL((gemv_topk_kernel<LGV, LV, R>), grid, dim3(kStreamThreads), 0, s, corpus, n, d, queries, \
+        hipLaunchKernelGGL((gemv_topk_kernel<LGV, LV, R>), grid, dim3(64 * gemv_waves(64 * R)), 0, s, corpus, n, d, queries, \
                            per_wave, ta);                                                                      \
         return hipGetLastError();                                                                              \
     }
@@ -490,7 +509,7 @@ hipError_t launch_stream_r(int kind, int lg, int L, dim3 grid, hipStream_t s, co
             return hipErrorInvalidValue;
         }
         case 1:
-            hipLaunchKernelGGL((gemv_topk_generic_kernel<R>), grid, dim3(kStreamThreads), 0, s, corpus, n, d, queries,
+            hipLaunchKernelGGL((gemv_topk_generic_kernel<R>), grid, dim3(64 * gemv_waves(64 * R)), 0, s, corpus, n, d, queries,
                                per_wave, ta);
             return hipGetLastError();
         case 2:
