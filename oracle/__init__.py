@@ -39,9 +39,13 @@ class Oracle:
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_scores.argtypes = [_ptr, _c_i64, _c_i64, _ptr, _ptr]
         lib.oracle_search.argtypes = [_ptr, _c_i64, _c_i64, _ptr, _c_i64, _c_i64, _ptr, _ptr]
+        lib.oracle_cosine_scores.argtypes = [_ptr, _c_i64, _c_i64, _ptr, _ptr]
+        lib.oracle_search_metric.argtypes = [_ptr, _c_i64, _c_i64, _ptr, _c_i64, _c_i64, ctypes.c_int32,
+                                             _ptr, _ptr]
         lib.oracle_topk_i32.argtypes = [_ptr, _c_i64, _c_i64, _ptr, _ptr]
         lib.oracle_topk_f32.argtypes = [_ptr, _c_i64, _c_i64, _ptr, _ptr]
-        for f in (lib.oracle_scores, lib.oracle_search, lib.oracle_topk_i32, lib.oracle_topk_f32):
+        for f in (lib.oracle_scores, lib.oracle_search, lib.oracle_topk_i32, lib.oracle_topk_f32,
+                  lib.oracle_cosine_scores, lib.oracle_search_metric):
             f.restype = ctypes.c_int
         self.lib = lib
 
@@ -61,8 +65,22 @@ class Oracle:
             raise RuntimeError(f"oracle_scores failed ({rc})")
         return out
 
-    def search(self, corpus, queries, k):
-        """Exact top-k by inner product for each query.
+    def cosine_scores(self, corpus, query):
+        """fp64 cosine similarity of every corpus row with one query, shape (n,);
+        -inf where a norm is zero."""
+        corpus = np.ascontiguousarray(corpus, dtype=np.float32)
+        query = np.ascontiguousarray(query, dtype=np.float32).reshape(-1)
+        n, d = corpus.shape
+        if query.shape[0] != d:
+            raise ValueError("query length must equal corpus width")
+        out = np.empty(n, dtype=np.float64)
+        rc = self.lib.oracle_cosine_scores(_ptr_of(corpus), n, d, _ptr_of(query), _ptr_of(out))
+        if rc:
+            raise RuntimeError(f"oracle_cosine_scores failed ({rc})")
+        return out
+
+    def search(self, corpus, queries, k, metric=0):
+        """Exact top-k for each query; metric 0 = inner product, 1 = cosine.
 
         Returns (idx int32 [q, k], score float64 [q, k]), best-first, ties by
         lower index."""
@@ -76,8 +94,12 @@ class Oracle:
             raise ValueError("query width must equal corpus width")
         idx = np.empty((q, k), dtype=np.int32)
         sc = np.empty((q, k), dtype=np.float64)
-        rc = self.lib.oracle_search(_ptr_of(corpus), n, d, _ptr_of(queries), q, k,
-                                    _ptr_of(idx), _ptr_of(sc))
+        if metric == 0:
+            rc = self.lib.oracle_search(_ptr_of(corpus), n, d, _ptr_of(queries), q, k,
+                                        _ptr_of(idx), _ptr_of(sc))
+        else:
+            rc = self.lib.oracle_search_metric(_ptr_of(corpus), n, d, _ptr_of(queries), q, k, int(metric),
+                                               _ptr_of(idx), _ptr_of(sc))
         if rc:
             raise RuntimeError(f"oracle_search failed ({rc})")
         return idx, sc
@@ -116,8 +138,12 @@ def scores(corpus, query):
     return default().scores(corpus, query)
 
 
-def search(corpus, queries, k):
-    return default().search(corpus, queries, k)
+def search(corpus, queries, k, metric=0):
+    return default().search(corpus, queries, k, metric)
+
+
+def cosine_scores(corpus, query):
+    return default().cosine_scores(corpus, query)
 
 
 def topk(values, k):

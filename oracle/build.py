@@ -14,7 +14,7 @@ LIBRARY = os.path.join(HERE, "liboracle.so")
 
 def build(source=SOURCE, out=LIBRARY, extra_cflags=(), quiet=False):
     cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c11", "-Wall", "-Wextra",
-           *extra_cflags, "-o", out + ".tmp", source]
+           *extra_cflags, "-o", out + ".tmp", source, "-lm"]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("oracle build failed:\n" + " ".join(cmd) + "\n" + res.stderr)

@@ -24,6 +24,12 @@
  *    best-first (section 4 "Step 4": results come back best-first; the method is
  *    exact brute force, section 6).
  *
+ *  - Cosine mode (same article, section 4 "Step 2", the cosine branch of the
+ *    scoring kernel; section 7 on the two metrics): the inner product divided by
+ *    the product of the query's and the row's L2 norms, and -inf when that
+ *    product is not positive (a zero row or a zero query).  Norms are the square
+ *    root of the fp64 sum of squares taken in ascending d.
+ *
  *  - Plain top-K over a raw int32 / fp32 array: the K largest values, ties to
  *    the lower index ("CUDA Programming Model Series 9: Efficient TopK, two-stage
  *    reduction kernel design", section 1 and 2.1 state the largest-K task; the tie
@@ -39,6 +45,7 @@
  * on the thread count.  Sorting uses the C library qsort with a total-order
  * comparator, so its output is unique.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -113,14 +120,34 @@ int oracle_scores(const float *corpus, int64_t n, int64_t d, const float *query,
 }
 
 /*
- * For each of the q queries (row-major q x d), score all n corpus rows, sort all
- * (score, index) pairs by "better" and write the first k: indices to
- * out_idx[qi*k + r], fp64 scores to out_score[qi*k + r].
- * Returns 0 on success, 1 on bad arguments, 2 if memory runs out.
+ * Cosine scores: scores[i] = <row i, query> / (|query| |row i|), or -inf when
+ * |query| |row i| is not positive.  The inner products are oracle_scores'.
  */
-int oracle_search(const float *corpus, int64_t n, int64_t d, const float *queries, int64_t q,
-                  int64_t k, int32_t *out_idx, double *out_score) {
-    if (n < 1 || d < 1 || q < 1 || k < 1 || k > n) return 1;
+int oracle_cosine_scores(const float *corpus, int64_t n, int64_t d, const float *query, double *scores) {
+    if (n < 0 || d < 1 || (n > 0 && (!corpus || !query || !scores))) return 1;
+    int rc = oracle_scores(corpus, n, d, query, scores);
+    if (rc) return rc;
+    double q_sq = 0.0;
+    for (int64_t c = 0; c < d; ++c) q_sq += (double)query[c] * (double)query[c];
+    const double q_norm = sqrt(q_sq);
+    int64_t i;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < n; ++i) {
+        const float *row = corpus + i * d;
+        double r_sq = 0.0;
+        for (int64_t c = 0; c < d; ++c) r_sq += (double)row[c] * (double)row[c];
+        const double denom = q_norm * sqrt(r_sq);
+        scores[i] = (denom > 0.0) ? scores[i] / denom : -INFINITY;
+    }
+    return 0;
+}
+
+/*
+ * As oracle_search, with metric 0 = inner product, 1 = cosine.
+ */
+int oracle_search_metric(const float *corpus, int64_t n, int64_t d, const float *queries, int64_t q,
+                         int64_t k, int32_t metric, int32_t *out_idx, double *out_score) {
+    if (n < 1 || d < 1 || q < 1 || k < 1 || k > n || metric < 0 || metric > 1) return 1;
     if (!corpus || !queries || !out_idx || !out_score) return 1;
     double *scores = (double *)malloc(sizeof(double) * (size_t)n);
     scored_row *rows = (scored_row *)malloc(sizeof(scored_row) * (size_t)n);
@@ -130,7 +157,10 @@ int oracle_search(const float *corpus, int64_t n, int64_t d, const float *querie
         return 2;
     }
     for (int64_t qi = 0; qi < q; ++qi) {
-        oracle_scores(corpus, n, d, queries + qi * d, scores);
+        if (metric == 1)
+            oracle_cosine_scores(corpus, n, d, queries + qi * d, scores);
+        else
+            oracle_scores(corpus, n, d, queries + qi * d, scores);
         for (int64_t i = 0; i < n; ++i) {
             rows[i].score = scores[i];
             rows[i].index = i;
@@ -144,6 +174,17 @@ int oracle_search(const float *corpus, int64_t n, int64_t d, const float *querie
     free(scores);
     free(rows);
     return 0;
+}
+
+/*
+ * For each of the q queries (row-major q x d), score all n corpus rows by inner
+ * product, sort all (score, index) pairs by "better" and write the first k:
+ * indices to out_idx[qi*k + r], fp64 scores to out_score[qi*k + r].
+ * Returns 0 on success, 1 on bad arguments, 2 if memory runs out.
+ */
+int oracle_search(const float *corpus, int64_t n, int64_t d, const float *queries, int64_t q,
+                  int64_t k, int32_t *out_idx, double *out_score) {
+    return oracle_search_metric(corpus, n, d, queries, q, k, 0, out_idx, out_score);
 }
 
 /* K largest of an int32 array, ties to the lower index; values widened to int64. */

@@ -11,7 +11,9 @@ the oracle disagrees with something the pages or the mathematics fix:
   top-K;
 * hand-worked fixtures in ``tests/golden/hand_worked.json``;
 * invariants (sortedness, distinctness, completeness), permutation invariance,
-  and the exactness of the two-stage (per-block then merge) decomposition.
+  and the exactness of the two-stage (per-block then merge) decomposition;
+* cosine mode: exact rationals on integer vectors with integer norms, scale
+  invariance, the zero-norm rule, and a 50-digit decimal evaluation.
 
 ``tests/test_oracle_mutants.py`` plants plausible mistakes in copies of the
 oracle and checks that at least one of these pins fails for each.
@@ -269,6 +271,94 @@ def pin_two_stage_decomposition(o, seed=20):
         assert [s for s, _ in pool[:k]] == list(g_sc[0]), trial
 
 
+# ------------------------------------------------------------------ cosine mode
+
+def _norm_vectors():
+    """Integer vectors of length 4 whose L2 norms are integers, with every sign
+    pattern and a few coordinate orders."""
+    base = [(1, 2, 2, 0), (2, 3, 6, 0), (1, 4, 8, 0), (4, 4, 7, 0), (2, 6, 9, 0), (6, 6, 7, 0),
+            (3, 4, 12, 0), (0, 0, 0, 5), (1, 1, 1, 1), (2, 2, 1, 4), (0, 3, 4, 0), (2, 4, 5, 6)]
+    out = []
+    for v in base:
+        for signs in ((1, 1, 1, 1), (-1, 1, -1, 1), (1, -1, 1, -1), (-1, -1, -1, -1)):
+            for perm in ((0, 1, 2, 3), (3, 2, 1, 0), (1, 3, 0, 2)):
+                out.append(tuple(signs[i] * v[perm[i]] for i in range(4)))
+    return sorted(set(out))
+
+
+def pin_cosine_pythagorean_exact(o):
+    """Integer vectors with integer norms make the cosine an exact rational
+    dot / (|q| |r|); the oracle's fp64 value is its correctly rounded quotient,
+    and the order (with its exact ties) is the rank-counting order."""
+    vecs = _norm_vectors()
+    corpus = np.array(vecs, np.float32)
+    norms = [round(float(np.sqrt(sum(x * x for x in v)))) for v in vecs]
+    assert all(sum(x * x for x in v) == nv * nv for v, nv in zip(vecs, norms))
+    n = len(vecs)
+    for qi in (0, 7, 19, 33, 50):
+        q = vecs[qi % n]
+        nq = norms[qi % n]
+        exact = [Fraction(sum(a * b for a, b in zip(v, q)), nv * nq) for v, nv in zip(vecs, norms)]
+        got = o.cosine_scores(corpus, np.array(q, np.float32))
+        for i in range(n):
+            assert got[i] == float(exact[i]), (qi, i, got[i], exact[i])
+        rank = [sum(1 for j in range(n) if _better(exact[j], j, exact[i], i)) for i in range(n)]
+        by_rank = [None] * n
+        for i, r in enumerate(rank):
+            by_rank[r] = i
+        for k in (1, 5, n):
+            idx, _ = o.search(corpus, np.array([q], np.float32), k, metric=1)
+            assert list(idx[0]) == by_rank[:k], (qi, k)
+
+
+def pin_cosine_scale_invariance(o, seed=31):
+    """Cosine ignores positive scale: rows and query multiplied by powers of two
+    (exact in fp32) give bit-identical scores; a negated row gives the negated
+    score."""
+    rng = np.random.default_rng(seed)
+    corpus = rng.standard_normal((30, 13)).astype(np.float32)
+    q = rng.standard_normal(13).astype(np.float32)
+    base = o.cosine_scores(corpus, q)
+    scale = np.float32(2.0) ** rng.integers(-20, 21, size=30).astype(np.float32)
+    scaled = corpus * scale[:, None]
+    assert np.array_equal(o.cosine_scores(scaled, q * np.float32(2.0 ** -7)), base)
+    assert np.array_equal(o.cosine_scores(-corpus, q), -base)
+    assert np.all(np.abs(base) <= 1.0)
+
+
+def pin_cosine_zero_norms(o):
+    """A zero row scores -inf and ranks below every finite score (zero rows among
+    themselves by index); a zero query makes every score -inf, so the answer is
+    indices 0 .. k-1."""
+    corpus = np.array([[0, 0, 0], [1, 0, 0], [0, 0, 0], [-1, 0, 0], [0, 2, 0]], np.float32)
+    q = np.array([1, 0, 0], np.float32)
+    sc = o.cosine_scores(corpus, q)
+    assert sc[0] == -np.inf and sc[2] == -np.inf
+    assert list(sc[[1, 3, 4]]) == [1.0, -1.0, 0.0]
+    idx, _ = o.search(corpus, q[None, :], 5, metric=1)
+    assert list(idx[0]) == [1, 4, 3, 0, 2]
+    idx, sc = o.search(corpus, np.zeros((1, 3), np.float32), 3, metric=1)
+    assert list(idx[0]) == [0, 1, 2] and np.all(sc == -np.inf)
+
+
+def pin_cosine_decimal(o, seed=32):
+    """On small random inputs the oracle agrees with a 50-digit decimal
+    evaluation of dot / (|q| |r|) to within its own fp64 rounding bound."""
+    from decimal import Decimal, getcontext
+    getcontext().prec = 50
+    rng = np.random.default_rng(seed)
+    for n, d in ((12, 5), (7, 40)):
+        corpus = rng.standard_normal((n, d)).astype(np.float32)
+        q = rng.standard_normal(d).astype(np.float32)
+        got = o.cosine_scores(corpus, q)
+        dq = [Decimal(float(x)) for x in q]
+        qn = sum(x * x for x in dq).sqrt()
+        for i in range(n):
+            dr = [Decimal(float(x)) for x in corpus[i]]
+            exact = sum(a * b for a, b in zip(dr, dq)) / (sum(x * x for x in dr).sqrt() * qn)
+            assert abs(Decimal(got[i]) - exact) <= Decimal((d + 8) * 2.0 ** -52), (n, d, i)
+
+
 ALL_PINS = [
     pin_scores_exact_rational,
     pin_search_rank_counting,
@@ -282,4 +372,8 @@ ALL_PINS = [
     pin_invariants,
     pin_permutation_invariance,
     pin_two_stage_decomposition,
+    pin_cosine_pythagorean_exact,
+    pin_cosine_scale_invariance,
+    pin_cosine_zero_norms,
+    pin_cosine_decimal,
 ]

@@ -2,7 +2,8 @@
 
 Each mutant is a copy of ``oracle/oracle.c`` with one plausible mistake planted
 in it (a dropped term, a flipped order or tie rule, a transposed operand, an
-overflowing int32 comparison, fp32 accumulation, lost value bits).  The copy is
+overflowing int32 comparison, fp32 accumulation, lost value bits, four cosine-norm
+mistakes).  The copy is
 compiled in a temporary directory; at least one pin must fail against it.  The
 real oracle is never modified.
 """
@@ -28,6 +29,11 @@ MUTANTS = {
     "value_bits_lost": ("memcpy(&out_val[r], &values[items[r].index], sizeof(float));",
                         "out_val[r] = items[r].value + 0.0f;"),
     "wrong_query_index": ("(double)query[c]", "(double)query[d - 1 - c]"),
+    "cosine_no_query_norm": ("const double denom = q_norm * sqrt(r_sq);", "const double denom = sqrt(r_sq);"),
+    "cosine_squared_norms": ("const double q_norm = sqrt(q_sq);", "const double q_norm = q_sq;"),
+    "cosine_zero_norm_scores_zero": ("scores[i] / denom : -INFINITY;", "scores[i] / denom : 0.0;"),
+    "cosine_row_norm_uses_query": ("r_sq += (double)row[c] * (double)row[c];",
+                                   "r_sq += (double)row[c] * (double)query[c];"),
 }
 
 
