@@ -78,7 +78,7 @@ def cpu_model():
     return "unknown"
 
 
-def time_search(eng, torch, qdev, ks, steps, warmup, profile=True):
+def time_search(eng, torch, qdev, ks, steps, warmup, profile=True, metric="dot"):
     """Sequential single queries; returns per-K lists of host latency (us),
     whole-call device time and streaming-kernel time (ms)."""
     n_q = qdev.shape[0]
@@ -87,7 +87,7 @@ def time_search(eng, torch, qdev, ks, steps, warmup, profile=True):
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         for k in ks:
-            eng.search_resident(qdev[i % n_q:i % n_q + 1], k, *outs[k], stream=stream)
+            eng.search_resident(qdev[i % n_q:i % n_q + 1], k, *outs[k], stream=stream, metric=metric)
     torch.cuda.synchronize()
     eng.profile(profile)
     lat = {k: [] for k in ks}
@@ -99,7 +99,7 @@ def time_search(eng, torch, qdev, ks, steps, warmup, profile=True):
         q = qdev[i % n_q:i % n_q + 1]
         for k in ks:
             s = time.perf_counter_ns()
-            eng.search_resident(q, k, *outs[k], stream=stream)
+            eng.search_resident(q, k, *outs[k], stream=stream, metric=metric)
             stream.synchronize()
             lat[k].append((time.perf_counter_ns() - s) / 1e3)
             if profile:
@@ -112,7 +112,7 @@ def time_search(eng, torch, qdev, ks, steps, warmup, profile=True):
     return wall, lat, part, merge
 
 
-def time_end_to_end(eng, torch, qhost, ks, reps):
+def time_end_to_end(eng, torch, qhost, ks, reps, metric="dot"):
     """Pages-style interval: pinned query H->D, search, K idx + K scores D->H."""
     d = qhost.shape[1]
     pin_q = torch.empty((1, d), dtype=torch.float32).pin_memory()
@@ -129,7 +129,7 @@ def time_end_to_end(eng, torch, qhost, ks, reps):
             pin_q.copy_(torch.from_numpy(qhost[r % qhost.shape[0]:r % qhost.shape[0] + 1]))
             s = time.perf_counter_ns()
             qdev.copy_(pin_q, non_blocking=True)
-            eng.search_resident(qdev, k, oi, os_, stream=stream)
+            eng.search_resident(qdev, k, oi, os_, stream=stream, metric=metric)
             hi.copy_(oi, non_blocking=True)
             hs.copy_(os_, non_blocking=True)
             stream.synchronize()
@@ -138,7 +138,7 @@ def time_end_to_end(eng, torch, qhost, ks, reps):
     return res
 
 
-def cpu_baseline_retrieval(corpus, qhost, kmax, gpu_results, budget_s, max_queries):
+def cpu_baseline_retrieval(corpus, qhost, kmax, gpu_results, budget_s, max_queries, metric="dot"):
     """Time the oracle on a bounded sample and check the GPU answers of the same
     queries against it."""
     import oracle
@@ -148,15 +148,17 @@ def cpu_baseline_retrieval(corpus, qhost, kmax, gpu_results, budget_s, max_queri
     nq = 0
     for qi in range(min(max_queries, qhost.shape[0])):
         s = time.perf_counter()
-        o_idx, o_sc = oracle.search(corpus, qhost[qi:qi + 1], kmax)
+        o_idx, o_sc = oracle.search(corpus, qhost[qi:qi + 1], kmax, metric=1 if metric == "cosine" else 0)
         times.append(time.perf_counter() - s)
         for k, (g_idx, g_sc) in gpu_results.items():
-            check_retrieval(g_idx[qi], g_sc[qi], o_idx[0, :k], o_sc[0, :k], corpus, qhost[qi], oracle)
+            check_retrieval(g_idx[qi], g_sc[qi], o_idx[0, :k], o_sc[0, :k], corpus, qhost[qi], oracle,
+                            metric=metric)
         nq += 1
         if time.perf_counter() - t_start > budget_s:
             break
     return {"value": nq / sum(times), "unit": "queries/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"first {nq} queries of the workload at K={kmax} (smaller K are prefixes), fp64 dots + full sort; "
+            "sample": f"first {nq} queries of the workload at K={kmax} (smaller K are prefixes), fp64 "
+                      f"{'cosines' if metric == 'cosine' else 'dots'} + full sort; "
                       f"GPU answers of the same queries checked against it (R1-R4)",
             "host_cores": host_cores(), "cpu_model": cpu_model(), "parity": "ok"}
 
@@ -178,10 +180,12 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
     if batch > 1:
         return run_batched(args, torch, eng, corpus, qhost, qdev, ks, name, gen_s)
 
-    wall, lat, part, merge = time_search(eng, torch, qdev, ks, args.steps, args.warmup)
+    wall, lat, part, merge = time_search(eng, torch, qdev, ks, args.steps, args.warmup, metric=args.metric)
     nq = args.steps * len(ks)
     qps = nq / wall
-    corpus_bytes = n * d * 4 + d * 4
+    # algorithmic bytes per launch: the corpus and the query, plus the rows'
+    # norms for the cosine metric
+    corpus_bytes = n * d * 4 + d * 4 + (n * 4 if args.metric == "cosine" else 0)
     per_k = {}
     all_part = []
     for k in ks:
@@ -198,24 +202,27 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
     avg_ms = float(np.mean(all_part))
     achieved = corpus_bytes / (avg_ms * 1e-3) / 1e9
     line = {
-        "metric": METRIC if name == "c3_1m_1024" else f"queries/s + p50 latency ({name})",
+        "metric": (METRIC if (name, args.metric) == ("c3_1m_1024", "dot")
+                   else f"queries/s + p50 latency ({name}, {args.metric})"),
         "value": qps, "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{name}: resident {n} x {d} fp32 corpus (Gaussian, L2-normalised rows), "
-                               f"sequential single queries, K in {list(ks)}; one step = one query per K",
-                   "n": n, "d": d, "ks": list(ks), "queries_per_step": len(ks)},
+                               f"sequential single queries, K in {list(ks)}; one step = one query per K"
+                               + ("; cosine metric" if args.metric == "cosine" else ""),
+                   "n": n, "d": d, "ks": list(ks), "queries_per_step": len(ks), "metric": args.metric},
         "per_k": per_k,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": measured_traffic() if (n, d, ks) == (1_000_000, 1024, (8, 32, 100)) else None,
+                     "traffic": (measured_traffic()
+                                 if (n, d, ks, args.metric) == (1_000_000, 1024, (8, 32, 100), "dot") else None),
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, profiles/)",
                      "kernel": "gemv_topk_kernel (fused scoring, per-wave top-K lists and merge tree)",
                      "bytes_per_launch": corpus_bytes, "avg_launch_us": avg_ms * 1e3},
         "input_gen_s": gen_s,
     }
     if args.e2e_reps:
-        line["end_to_end_pcie"] = time_end_to_end(eng, torch, qhost, ks, args.e2e_reps)
+        line["end_to_end_pcie"] = time_end_to_end(eng, torch, qhost, ks, args.e2e_reps, metric=args.metric)
     if not args.no_cpu_baseline:
         sample = min(args.cpu_queries, qhost.shape[0])
         gpu_res = {}
@@ -223,11 +230,12 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
             gi = np.empty((sample, k), np.int32)
             gs = np.empty((sample, k), np.float32)
             for qi in range(sample):
-                a, b = eng.search_resident(qdev[qi:qi + 1], k)
+                a, b = eng.search_resident(qdev[qi:qi + 1], k, metric=args.metric)
                 torch.cuda.synchronize()
                 gi[qi], gs[qi] = a.cpu().numpy()[0], b.cpu().numpy()[0]
             gpu_res[k] = (gi, gs)
-        line["cpu_baseline"] = cpu_baseline_retrieval(corpus, qhost, max(ks), gpu_res, args.cpu_budget, sample)
+        line["cpu_baseline"] = cpu_baseline_retrieval(corpus, qhost, max(ks), gpu_res, args.cpu_budget, sample,
+                                                      metric=args.metric)
     eng.close()
     return line
 
@@ -240,7 +248,7 @@ def run_batched(args, torch, eng, corpus, qhost, qdev, ks, name, gen_s):
                 torch.empty((q, k), dtype=torch.float32, device="cuda")) for k in ks}
     for _ in range(args.warmup):
         for k in ks:
-            eng.search_resident(qdev, k, *outs[k], stream=stream)
+            eng.search_resident(qdev, k, *outs[k], stream=stream, metric=args.metric)
     torch.cuda.synchronize()
     eng.profile(True)
     lat = {k: [] for k in ks}
@@ -251,7 +259,7 @@ def run_batched(args, torch, eng, corpus, qhost, qdev, ks, name, gen_s):
     for _ in range(args.steps):
         for k in ks:
             s = time.perf_counter_ns()
-            eng.search_resident(qdev, k, *outs[k], stream=stream)
+            eng.search_resident(qdev, k, *outs[k], stream=stream, metric=args.metric)
             stream.synchronize()
             lat[k].append((time.perf_counter_ns() - s) / 1e3)
             total, mfma, sel = eng.profile_read()
@@ -260,7 +268,7 @@ def run_batched(args, torch, eng, corpus, qhost, qdev, ks, name, gen_s):
             mf[k].append(mfma)
     wall = time.perf_counter() - t0
     eng.profile(False)
-    corpus_bytes = n * d * 4 + q * d * 4
+    corpus_bytes = n * d * 4 + q * d * 4 + (n * 4 if args.metric == "cosine" else 0)
     flops = 2.0 * n * d * q
     per_k = {}
     for k in ks:
@@ -275,12 +283,12 @@ def run_batched(args, torch, eng, corpus, qhost, qdev, ks, name, gen_s):
                          "mfma_kernel_tflops": flops / (mfma_ms * 1e-3) / 1e12}
     all_mf = np.concatenate([np.asarray(mf[k]) for k in ks])
     achieved = corpus_bytes / (float(np.mean(all_mf)) * 1e-3) / 1e9
-    line = {"metric": f"queries/s ({name})", "value": q * args.steps * len(ks) / wall, "unit": "queries/s",
+    line = {"metric": f"queries/s ({name}{', cosine' if args.metric == 'cosine' else ''})", "value": q * args.steps * len(ks) / wall, "unit": "queries/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
             "vs_baseline": None, "dtype": "f32", "data": "synthetic",
             "config": {"workload": f"{name}: batch of {q} queries vs resident {n} x {d} fp32, K in {list(ks)}",
-                       "n": n, "d": d, "q": q, "ks": list(ks)},
+                       "n": n, "d": d, "q": q, "ks": list(ks), "metric": args.metric},
             "per_k": per_k,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": achieved / HBM_PEAK_GBS, "traffic": None,
@@ -291,14 +299,14 @@ def run_batched(args, torch, eng, corpus, qhost, qdev, ks, name, gen_s):
         import oracle
         from tests.gpu_util import check_retrieval
         kmax = max(ks)
-        gi, gs = eng.search_resident(qdev, kmax)
+        gi, gs = eng.search_resident(qdev, kmax, metric=args.metric)
         torch.cuda.synchronize()
         gi, gs = gi.cpu().numpy(), gs.cpu().numpy()
         s = time.perf_counter()
-        o_idx, o_sc = oracle.search(corpus, qhost, kmax)
+        o_idx, o_sc = oracle.search(corpus, qhost, kmax, metric=1 if args.metric == "cosine" else 0)
         el = time.perf_counter() - s
         for qi in range(q):
-            check_retrieval(gi[qi], gs[qi], o_idx[qi], o_sc[qi], corpus, qhost[qi], oracle)
+            check_retrieval(gi[qi], gs[qi], o_idx[qi], o_sc[qi], corpus, qhost[qi], oracle, metric=args.metric)
         line["cpu_baseline"] = {"value": q / el, "unit": "queries/s", "cores": oracle.num_threads(),
                                 "kind": "oracle", "sample": f"the full batch of {q} queries at K={kmax}",
                                 "host_cores": host_cores(), "cpu_model": cpu_model(), "parity": "ok"}
@@ -392,6 +400,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c3_1m_1024")
+    ap.add_argument("--metric", default="dot", choices=("dot", "cosine"),
+                    help="similarity for the retrieval workloads (the headline line is the inner product)")
     ap.add_argument("--num-queries", type=int, default=1000)
     ap.add_argument("--cpu-queries", type=int, default=40)
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time in cpu_baseline")

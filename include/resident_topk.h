@@ -55,6 +55,11 @@ typedef enum {
 
 typedef enum { RT_DTYPE_INT32 = 0, RT_DTYPE_FLOAT32 = 1 } rt_dtype;
 
+/* Similarity used by search_resident_metric ("GPU-Resident Top-K for Agentic
+ * RAG", section 4, Step 2: the scoring kernel computes an inner product and,
+ * with cosine enabled, divides it by the query's and the row's L2 norms). */
+typedef enum { RT_METRIC_DOT = 0, RT_METRIC_COSINE = 1 } rt_metric;
+
 /*
  * Create an engine on HIP device `device` and allocate, once, everything later
  * calls need, sized for the worst case: a corpus of max_n x max_d fp32, results
@@ -76,8 +81,10 @@ void rt_engine_destroy(rt_engine *e);
  * Copy an n x d row-major fp32 corpus into the engine's device memory and make
  * it the resident corpus, replacing any previous one ("GPU-Resident Top-K for
  * Agentic RAG", section 4, Step 1).  `corpus` may be host or device memory
- * (hipMemcpyDefault); the caller keeps ownership.  Synchronous: when it returns
- * RT_OK the copy is complete.  RT_EINVAL if e or corpus is NULL, n < 1,
+ * (hipMemcpyDefault); the caller keeps ownership.  The L2 norm of every row is
+ * computed on the device as part of the upload (for the cosine metric; section
+ * 4, Step 2 keeps a precomputed per-row norm).  Synchronous: when it returns
+ * RT_OK the copy and the norms are complete.  RT_EINVAL if e or corpus is NULL, n < 1,
  * n > max_n, d < 1 or d > max_d (the pages return "invalid value" for
  * N > max_n or D > max_d).  On failure the previous corpus stays resident
  * unless the copy itself failed (RT_EHIP), in which case no corpus is resident.
@@ -97,6 +104,22 @@ rt_status upload_corpus_rowmajor(rt_engine *e, const float *corpus, int64_t n, i
  */
 rt_status search_resident(rt_engine *e, const float *queries, int32_t q, int32_t k,
                           int32_t *out_idx, float *out_scores, void *stream);
+
+/*
+ * search_resident with a choice of similarity ("GPU-Resident Top-K for Agentic
+ * RAG", section 4, Step 2, and section 7 on dot product versus cosine):
+ *   RT_METRIC_DOT     score = <row, query> (exactly search_resident);
+ *   RT_METRIC_COSINE  score = <row, query> / (|query| |row|), computed in fp32
+ *                     from the inner product, the row's L2 norm (computed at
+ *                     upload) and the query's L2 norm (computed on the device
+ *                     per call); -inf when |query| |row| is not positive (a
+ *                     zero row or a zero query), so such rows rank last and,
+ *                     among themselves, by lower index.
+ * Arguments, layouts, ordering and errors are those of search_resident, plus
+ * RT_EINVAL for an unknown metric.
+ */
+rt_status search_resident_metric(rt_engine *e, const float *queries, int32_t q, int32_t k, int32_t metric,
+                                 int32_t *out_idx, float *out_scores, void *stream);
 
 /*
  * Plain top-k of a raw device array, no scoring ("CUDA Programming Model
@@ -149,6 +172,8 @@ rt_status rt_check_create(int64_t max_n, int32_t max_d, int32_t max_k, int32_t m
 rt_status rt_check_upload(int64_t max_n, int32_t max_d, const void *corpus, int64_t n, int32_t d);
 rt_status rt_check_search(int32_t max_k, int32_t max_q, int64_t resident_n, const void *queries,
                           int32_t q, int32_t k, const void *out_idx, const void *out_scores);
+rt_status rt_check_search_metric(int32_t max_k, int32_t max_q, int64_t resident_n, const void *queries,
+                                 int32_t q, int32_t k, int32_t metric, const void *out_idx, const void *out_scores);
 rt_status rt_check_select(int32_t max_k, const void *values, int32_t dtype, int64_t n, int32_t k,
                           const void *out_idx, const void *out_values);
 

@@ -12,10 +12,17 @@ SCALE_FLOOR = 0.01
 
 
 def _rel_ok(g, o, tol=REL_TOL, scale=None):
+    """|g - o| <= tol * max(|o|, SCALE_FLOOR * scale); infinite values (the
+    cosine metric's -inf for a zero norm) must be equal."""
+    g = np.asarray(g, dtype=np.float64)
+    o = np.asarray(o, dtype=np.float64)
     den = np.abs(o)
     if scale is not None:
         den = np.maximum(den, SCALE_FLOOR * scale)
-    return np.abs(g - o) <= tol * np.maximum(den, 1e-30)
+    with np.errstate(invalid="ignore"):
+        close = np.abs(g - o) <= tol * np.maximum(den, 1e-30)
+    inf = np.isinf(g) | np.isinf(o)
+    return np.where(inf, g == o, close)
 
 
 def cs_bound(rows, query):
@@ -23,8 +30,24 @@ def cs_bound(rows, query):
     return np.linalg.norm(rows.astype(np.float64), axis=1) * np.linalg.norm(query.astype(np.float64))
 
 
-def check_retrieval(g_idx, g_sc, o_idx, o_sc, corpus, query, oracle_mod, tol=REL_TOL):
-    """Float retrieval acceptance for one query.
+def oracle_scores(oracle_mod, rows, query, metric="dot"):
+    """The oracle's fp64 scores of `rows` for one query under `metric`."""
+    if metric == "cosine":
+        return oracle_mod.cosine_scores(rows, query)
+    return oracle_mod.scores(rows, query)
+
+
+def score_scale(rows, query, metric="dot"):
+    """Largest |score| each row can have: |x| |q| for the inner product, 1 for
+    cosine."""
+    if metric == "cosine":
+        return np.ones(rows.shape[0])
+    return cs_bound(rows, query)
+
+
+def check_retrieval(g_idx, g_sc, o_idx, o_sc, corpus, query, oracle_mod, tol=REL_TOL, metric="dot"):
+    """Float retrieval acceptance for one query under `metric` ("dot" or
+    "cosine").
 
     R1  the GPU list is sorted under the comparator on its own fp32 scores;
     R2  each GPU score is within tol of the oracle's score of the same row and
@@ -46,9 +69,9 @@ def check_retrieval(g_idx, g_sc, o_idx, o_sc, corpus, query, oracle_mod, tol=REL
         a, b = g_sc[j], g_sc[j + 1]
         assert a > b or (a == b and g_idx[j] < g_idx[j + 1]), f"not sorted at {j}"
     # R2
-    o_of_g = oracle_mod.scores(corpus[g_idx], query)
-    scale_g = cs_bound(corpus[g_idx], query)
-    scale_o = cs_bound(corpus[o_idx.astype(np.int64)], query)
+    o_of_g = oracle_scores(oracle_mod, corpus[g_idx], query, metric)
+    scale_g = score_scale(corpus[g_idx], query, metric)
+    scale_o = score_scale(corpus[o_idx.astype(np.int64)], query, metric)
     assert np.all(_rel_ok(g_sc.astype(np.float64), o_of_g, tol, scale_g)), \
         "score differs from the oracle's score of that row"
     assert np.all(_rel_ok(g_sc.astype(np.float64), o_sc, tol, np.maximum(scale_g, scale_o))), \
@@ -57,7 +80,7 @@ def check_retrieval(g_idx, g_sc, o_idx, o_sc, corpus, query, oracle_mod, tol=REL
     diff = np.setxor1d(g_idx, o_idx.astype(np.int64))
     if diff.size:
         o_k = o_sc[-1]
-        o_diff = oracle_mod.scores(corpus[diff], query)
+        o_diff = oracle_scores(oracle_mod, corpus[diff], query, metric)
         assert np.all(_rel_ok(o_diff, np.full_like(o_diff, o_k), tol, scale_o[-1])), \
             f"index sets differ away from the k-th boundary: {diff[:8]}"
 

@@ -76,6 +76,16 @@ def test_check_search(lib):
         assert lib.rt_check_search(128, 32, 1000, args[0], 1, 8, args[1], args[2]) == EINVAL
 
 
+def test_check_search_metric(lib):
+    for metric in (_lib.RT_METRIC_DOT, _lib.RT_METRIC_COSINE):
+        assert lib.rt_check_search_metric(128, 32, 1000, P, 1, 8, metric, P, P) == OK
+        assert lib.rt_check_search_metric(128, 32, 7, P, 1, 8, metric, P, P) == EINVAL   # k > n
+        assert lib.rt_check_search_metric(128, 32, 0, P, 1, 8, metric, P, P) == ESTATE   # nothing resident
+        assert lib.rt_check_search_metric(128, 32, 1000, NULL, 1, 8, metric, P, P) == EINVAL
+    for metric in (-1, 2, 99):
+        assert lib.rt_check_search_metric(128, 32, 1000, P, 1, 8, metric, P, P) == EINVAL
+
+
 def test_check_select(lib):
     assert lib.rt_check_select(64, P, 0, 1000, 50, P, P) == OK
     assert lib.rt_check_select(64, P, 1, 1000, 50, P, P) == OK
@@ -90,6 +100,7 @@ def test_check_select(lib):
 def test_entry_points_reject_null_engine(lib):
     assert lib.upload_corpus_rowmajor(NULL, P, 10, 4) == EINVAL
     assert lib.search_resident(NULL, P, 1, 1, P, P, NULL) == EINVAL
+    assert lib.search_resident_metric(NULL, P, 1, 1, 1, P, P, NULL) == EINVAL
     assert lib.topk_select(NULL, P, 0, 10, 1, P, P, NULL) == EINVAL
     assert lib.rt_profile_enable(NULL, 1) == EINVAL
     assert lib.rt_last_hip_error(NULL) == 0

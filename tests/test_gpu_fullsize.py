@@ -111,3 +111,32 @@ def test_batched_500k():
         for k in w["ks"]:
             for qi in range(qs.shape[0]):
                 check_retrieval(res[k][0][qi], res[k][1][qi], o_idx[qi, :k], o_sc[qi, :k], corpus, qs[qi], oracle)
+
+
+def test_cosine_1m():
+    """The cosine metric at the large single-query size, rows rescaled by
+    log-normal factors (so each row's norm matters), in the launch configuration
+    the benchmark times with --metric cosine."""
+    name = "c3_1m_1024"
+    print(f"[fullsize] {name} cosine: generating inputs", flush=True)
+    corpus, qs = workloads.retrieval_inputs(name, queries=24)
+    rng = np.random.default_rng(77)
+    corpus *= np.exp(rng.standard_normal(corpus.shape[0])).astype(np.float32)[:, None]
+    qs *= np.float32(3.0)
+    n, d = corpus.shape
+    ks = workloads.WORKLOADS[name]["ks"]
+    with ResidentTopK(n, d, max(ks), 1) as eng:
+        eng.upload_corpus_rowmajor(corpus)
+        qdev = torch.from_numpy(qs).cuda()
+        print(f"[fullsize] {name} cosine: oracle for 2 queries", flush=True)
+        o_idx, o_sc = oracle.search(corpus, qs[:2], max(ks), metric=1)
+        for k in ks:
+            for qi in range(qs.shape[0]):
+                i, s = eng.search_resident(qdev[qi:qi + 1], k, metric="cosine")
+                g_idx, g_sc = i.cpu().numpy()[0], s.cpu().numpy()[0]
+                _sorted_distinct(g_idx, g_sc)
+                o_rows = oracle.cosine_scores(corpus[g_idx.astype(np.int64)], qs[qi])
+                assert np.all(np.abs(g_sc.astype(np.float64) - o_rows) <= REL_TOL * np.maximum(np.abs(o_rows), 0.01))
+                if qi < 2:
+                    check_retrieval(g_idx, g_sc, o_idx[qi, :k], o_sc[qi, :k], corpus, qs[qi], oracle,
+                                    metric="cosine")

@@ -14,7 +14,7 @@ library is not built.
 import ctypes
 
 from . import _lib
-from ._lib import ResidentTopKError, RT_DTYPE_FLOAT32, RT_DTYPE_INT32
+from ._lib import ResidentTopKError, RT_DTYPE_FLOAT32, RT_DTYPE_INT32, RT_METRIC_COSINE, RT_METRIC_DOT
 
 __all__ = ["ResidentTopK", "ResidentTopKError"]
 
@@ -92,11 +92,15 @@ class ResidentTopK:
         _check(st, "upload_corpus_rowmajor", self._h)
         self._keep = corpus  # not needed after the synchronous copy; kept only until the next upload
 
-    def search_resident(self, queries, k, out_idx=None, out_scores=None, stream=None):
-        """Exact top-k by inner product.  queries: device fp32 [q, d] or [d].
+    def search_resident(self, queries, k, out_idx=None, out_scores=None, stream=None, metric="dot"):
+        """Exact top-k by inner product (metric="dot") or cosine similarity
+        (metric="cosine").  queries: device fp32 [q, d] or [d].
         Returns (idx int32 [q, k], scores fp32 [q, k]) on the device, best-first;
         enqueued on `stream` (default: torch's current stream)."""
         torch = _torch()
+        metrics = {"dot": RT_METRIC_DOT, "cosine": RT_METRIC_COSINE}
+        if metric not in metrics:
+            raise ValueError(f"metric must be one of {sorted(metrics)}")
         if queries.dim() == 1:
             queries = queries.view(1, -1)
         if queries.dtype != torch.float32 or not queries.is_cuda or not queries.is_contiguous():
@@ -110,9 +114,9 @@ class ResidentTopK:
             raise TypeError("out_idx must be int32 and out_scores float32")
         if out_idx.numel() < q * k or out_scores.numel() < q * k:
             raise ValueError("output buffers are too small")
-        st = self._lib.search_resident(self._h, ctypes.c_void_p(queries.data_ptr()), int(q), int(k),
-                                       ctypes.c_void_p(out_idx.data_ptr()),
-                                       ctypes.c_void_p(out_scores.data_ptr()), _stream_handle(stream))
+        st = self._lib.search_resident_metric(self._h, ctypes.c_void_p(queries.data_ptr()), int(q), int(k),
+                                              metrics[metric], ctypes.c_void_p(out_idx.data_ptr()),
+                                              ctypes.c_void_p(out_scores.data_ptr()), _stream_handle(stream))
         _check(st, "search_resident", self._h)
         return out_idx, out_scores
 

@@ -10,13 +10,14 @@ LIBRARY = os.path.join(HERE, "libresident_topk.so")
 
 RT_OK, RT_EINVAL, RT_ESTATE, RT_ENOMEM, RT_EHIP = 0, 1, 2, 3, 4
 RT_DTYPE_INT32, RT_DTYPE_FLOAT32 = 0, 1
+RT_METRIC_DOT, RT_METRIC_COSINE = 0, 1
 
 # Every symbol include/resident_topk.h declares.
 EXPORTS = (
     "rt_engine_create", "rt_engine_destroy", "upload_corpus_rowmajor", "search_resident",
-    "topk_select", "rt_status_string", "rt_last_hip_error", "rt_profile_enable",
+    "search_resident_metric", "topk_select", "rt_status_string", "rt_last_hip_error", "rt_profile_enable",
     "rt_profile_read", "rt_engine_info", "rt_check_create", "rt_check_upload",
-    "rt_check_search", "rt_check_select",
+    "rt_check_search", "rt_check_search_metric", "rt_check_select",
 )
 
 _lib = None
@@ -51,6 +52,7 @@ def load():
         "rt_engine_destroy": ([vp], None),
         "upload_corpus_rowmajor": ([vp, vp, i64, i32], ctypes.c_int),
         "search_resident": ([vp, vp, i32, i32, vp, vp, vp], ctypes.c_int),
+        "search_resident_metric": ([vp, vp, i32, i32, i32, vp, vp, vp], ctypes.c_int),
         "topk_select": ([vp, vp, i32, i64, i32, vp, vp, vp], ctypes.c_int),
         "rt_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "rt_last_hip_error": ([vp], i32),
@@ -60,6 +62,7 @@ def load():
         "rt_check_create": ([i64, i32, i32, i32], ctypes.c_int),
         "rt_check_upload": ([i64, i32, vp, i64, i32], ctypes.c_int),
         "rt_check_search": ([i32, i32, i64, vp, i32, i32, vp, vp], ctypes.c_int),
+        "rt_check_search_metric": ([i32, i32, i64, vp, i32, i32, i32, vp, vp], ctypes.c_int),
         "rt_check_select": ([i32, vp, i32, i64, i32, vp, vp], ctypes.c_int),
     }
     for name, (args, res) in sig.items():

@@ -74,6 +74,7 @@ struct rt_engine {
     int64_t resident_n = 0;
     int32_t resident_d = 0;
     float *corpus = nullptr;
+    float *rnorm = nullptr;   // L2 norm of every resident row (cosine metric), roundup(max_n, 64) floats
     float *scores = nullptr;  // batched scores, max_q x roundup(max_n, 64); only when max_q > 1
     float *tmax = nullptr;    // per-query maxima of 32-row score tiles, max_q x tile_ld; only when max_q > 1
     int64_t tile_ld = 0;
@@ -133,6 +134,12 @@ rt_status rt_check_search(int32_t max_k, int32_t max_q, int64_t resident_n, cons
     return RT_OK;
 }
 
+rt_status rt_check_search_metric(int32_t max_k, int32_t max_q, int64_t resident_n, const void *queries,
+                                 int32_t q, int32_t k, int32_t metric, const void *out_idx, const void *out_scores) {
+    if (metric != RT_METRIC_DOT && metric != RT_METRIC_COSINE) return RT_EINVAL;
+    return rt_check_search(max_k, max_q, resident_n, queries, q, k, out_idx, out_scores);
+}
+
 rt_status rt_check_select(int32_t max_k, const void *values, int32_t dtype, int64_t n, int32_t k,
                           const void *out_idx, const void *out_values) {
     if (values == nullptr || out_idx == nullptr || out_values == nullptr) return RT_EINVAL;
@@ -150,6 +157,7 @@ void rt_engine_destroy(rt_engine *e) {
     (void)hipSetDevice(e->device);
     (void)hipDeviceSynchronize();
     (void)hipFree(e->corpus);
+    (void)hipFree(e->rnorm);
     (void)hipFree(e->scores);
     (void)hipFree(e->tmax);
     (void)hipFree(e->tree);
@@ -197,6 +205,7 @@ rt_status rt_engine_create(int64_t max_n, int32_t max_d, int32_t max_k, int32_t 
     };
     const int64_t ld = (max_n + 63) / 64 * 64;
     bool ok = alloc(reinterpret_cast<void **>(&e->corpus), sizeof(float) * (size_t)max_n * (size_t)max_d) &&
+              alloc(reinterpret_cast<void **>(&e->rnorm), sizeof(float) * (size_t)ld) &&
               alloc(reinterpret_cast<void **>(&e->tree), sizeof(uint64_t) * (size_t)kTreeRanks) &&
               alloc(reinterpret_cast<void **>(&e->counters), sizeof(uint32_t) * (size_t)(kMaxQ * kMaxWgsPerSeg));
     e->tile_ld = ((max_n + 31) / 32 + 63) / 64 * 64;
@@ -209,6 +218,7 @@ rt_status rt_engine_create(int64_t max_n, int32_t max_d, int32_t max_k, int32_t 
         return RT_ENOMEM;
     }
     err = hipMemset(e->counters, 0, sizeof(uint32_t) * (size_t)(kMaxQ * kMaxWgsPerSeg));
+    if (err == hipSuccess) err = hipMemset(e->rnorm, 0, sizeof(float) * (size_t)ld);
     if (err == hipSuccess) err = rt::prepare_mfma_scores();
     for (int i = 0; i < 4 && err == hipSuccess; ++i) err = hipEventCreate(&e->ev[i]);
     if (err == hipSuccess) err = hipDeviceSynchronize();
@@ -231,6 +241,9 @@ rt_status upload_corpus_rowmajor(rt_engine *e, const float *corpus, int64_t n, i
     hipError_t err = hipSetDevice(e->device);
     if (err == hipSuccess)
         err = hipMemcpy(e->corpus, corpus, sizeof(float) * (size_t)n * (size_t)d, hipMemcpyDefault);
+    // The rows' L2 norms for the cosine metric, computed once per upload.
+    if (err == hipSuccess) err = rt::launch_row_norms(e->corpus, n, d, e->rnorm, e->num_cus, nullptr);
+    if (err == hipSuccess) err = hipDeviceSynchronize();
     (void)hipSetDevice(prev);
     if (err != hipSuccess) {
         e->resident_n = 0;
@@ -270,10 +283,11 @@ static hipError_t prologue(rt_engine *e, hipStream_t s) {
     return err;
 }
 
-rt_status search_resident(rt_engine *e, const float *queries, int32_t q, int32_t k, int32_t *out_idx,
-                          float *out_scores, void *stream) {
+rt_status search_resident_metric(rt_engine *e, const float *queries, int32_t q, int32_t k, int32_t metric,
+                                 int32_t *out_idx, float *out_scores, void *stream) {
     if (!e) return RT_EINVAL;
-    rt_status st = rt_check_search(e->max_k, e->max_q, e->resident_n, queries, q, k, out_idx, out_scores);
+    rt_status st =
+        rt_check_search_metric(e->max_k, e->max_q, e->resident_n, queries, q, k, metric, out_idx, out_scores);
     if (st != RT_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     int prev = 0;
@@ -282,24 +296,31 @@ rt_status search_resident(rt_engine *e, const float *queries, int32_t q, int32_t
     const int64_t n = e->resident_n;
     const int d = e->resident_d;
     const int kp = kp_for(k);
+    const float *rnorm = (metric == RT_METRIC_COSINE) ? e->rnorm : nullptr;
     const bool batched = q > 1 && e->scores != nullptr && d % 4 == 0 && d <= rt::kMfmaMaxD;
     e->had_batch_kernel = batched;
     if (err == hipSuccess) err = prologue(e, s);
     if (err == hipSuccess && batched) {
         const int64_t ld = (n + 63) / 64 * 64;
-        err = rt::launch_mfma_scores(e->corpus, n, d, queries, q, e->scores, ld, e->tmax, e->tile_ld, e->num_cus, s);
+        err = rt::launch_mfma_scores(e->corpus, n, d, queries, q, rnorm, e->scores, ld, e->tmax, e->tile_ld,
+                                     e->num_cus, s);
         if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[3], s);
         if (err == hipSuccess)
             err = rt::launch_tile_bound_select(e->scores, ld, n, e->tmax, e->tile_ld, q, k, out_idx, out_scores, s);
     } else if (err == hipSuccess) {
         const Plan p = plan_stream(n, q, kp, 32, e->num_cus, kScoreWavesPerCu, rt::gemv_waves(kp));
         const rt::TreeLaunch t = tree_for(e, p, kp, k, 1, out_idx, out_scores, nullptr, 0);
-        err = rt::launch_gemv_topk(e->corpus, n, d, queries, q, p.per_wave, p.wgs, t, s);
+        err = rt::launch_gemv_topk(e->corpus, n, d, queries, rnorm, q, p.per_wave, p.wgs, t, s);
     }
     if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[1], s);
     (void)hipSetDevice(prev);
     if (err != hipSuccess) return hip_fail(e, err);
     return RT_OK;
+}
+
+rt_status search_resident(rt_engine *e, const float *queries, int32_t q, int32_t k, int32_t *out_idx,
+                          float *out_scores, void *stream) {
+    return search_resident_metric(e, queries, q, k, RT_METRIC_DOT, out_idx, out_scores, stream);
 }
 
 rt_status topk_select(rt_engine *e, const void *values, int32_t dtype, int64_t n, int32_t k, int32_t *out_idx,

@@ -46,8 +46,13 @@ int tree_fan(int kp);
 bool gemv_fast_path_ok(int d);
 
 // Fused scoring + selection + merge for `segments` queries; grid (wgs_per_seg, segments).
-hipError_t launch_gemv_topk(const float *corpus, int64_t n, int d, const float *queries, int segments,
-                            int64_t rows_per_wave, int wgs_per_seg, const TreeLaunch &t, hipStream_t stream);
+// rnorm == nullptr: inner product; otherwise cosine, rnorm[i] = |row i|.
+hipError_t launch_gemv_topk(const float *corpus, int64_t n, int d, const float *queries, const float *rnorm,
+                            int segments, int64_t rows_per_wave, int wgs_per_seg, const TreeLaunch &t,
+                            hipStream_t stream);
+
+// rnorm[i] = L2 norm of corpus row i (fp64 sum of squares, rounded to fp32).
+hipError_t launch_row_norms(const float *corpus, int64_t n, int d, float *rnorm, int num_cus, hipStream_t stream);
 
 // Selection + merge over `segments` raw 32-bit arrays (dtype 0 = int32, 1 = fp32)
 // of n elements, seg_stride elements apart.
@@ -59,10 +64,12 @@ hipError_t launch_zero_counters(uint32_t *counters, int64_t count, hipStream_t s
 
 // Batched inner products S[q][row] (row stride ld) on MFMA; q <= 32, d % 4 == 0, d <= 1024.
 // Also writes, per query, the largest score of every 32-row tile:
-// tmax[query * tld + tile], tile = row / 32.
+// tmax[query * tld + tile], tile = row / 32.  rnorm != nullptr selects cosine
+// scores (rnorm[i] = |row i|, readable up to a multiple of 4 rows past n).
 hipError_t prepare_mfma_scores();
 hipError_t launch_mfma_scores(const float *corpus, int64_t n, int d, const float *queries, int q,
-                              float *scores, int64_t ld, float *tmax, int64_t tld, int num_cus, hipStream_t stream);
+                              const float *rnorm, float *scores, int64_t ld, float *tmax, int64_t tld, int num_cus,
+                              hipStream_t stream);
 
 // Exact top-k (k <= 1024) of each of `segments` fp32 score rows (ld apart) given
 // their 32-element tile maxima (tld apart); writes index + score per row.

@@ -50,14 +50,27 @@ constexpr int mfma_cols(int d, int kpf) { return ((d + 32 * kpf - 1) / (32 * kpf
 
 // Store a finished tile (rows row0 .. row0 + 31 x queries) and, per query, the
 // largest of its valid scores into tmax[query][tile].  Lane (query j = lane %
-// 32, half h = lane / 32) holds rows 8 g + 4 h + c in register 4 g + c.
-__device__ __forceinline__ void store_tile(const floatx16 &acc, int64_t t, int64_t n, int q, int lane,
+// 32, half h = lane / 32) holds rows 8 g + 4 h + c in register 4 g + c.  With
+// COS each inner product is first turned into a cosine with the query's norm
+// qn and the rows' norms rn[g] (rows 8 g + 4 h .. + 3).
+template <bool COS>
+__device__ __forceinline__ void store_tile(const floatx16 &acc_in, int64_t t, int64_t n, int q, int lane,
                                            float *__restrict__ scores, int64_t ld, float *__restrict__ tmax,
-                                           int64_t tld) {
+                                           int64_t tld, const float4 (&rn)[4], float qn) {
     const int j = lane & 31;
     const int h = lane >> 5;
     const int64_t row0 = t * 32;
     const bool has_q = j < q;
+    floatx16 acc = acc_in;
+    if constexpr (COS) {
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            acc[4 * g + 0] = cosine_of(acc[4 * g + 0], qn, rn[g].x);
+            acc[4 * g + 1] = cosine_of(acc[4 * g + 1], qn, rn[g].y);
+            acc[4 * g + 2] = cosine_of(acc[4 * g + 2], qn, rn[g].z);
+            acc[4 * g + 3] = cosine_of(acc[4 * g + 3], qn, rn[g].w);
+        }
+    }
     float *srow = scores + (int64_t)j * ld + row0 + 4 * h;
     float mx = -INFINITY;
 #pragma unroll
@@ -81,16 +94,36 @@ __device__ __forceinline__ void store_tile(const floatx16 &acc, int64_t t, int64
     if (h == 0 && has_q) tmax[(int64_t)j * tld + t] = mx;
 }
 
+// Row norms a lane needs for tile t (rows 32 t + 8 g + 4 h .. + 3, g = 0..3).
+__device__ __forceinline__ void load_tile_norms(const float *__restrict__ rnorm, int64_t t, int lane,
+                                                float4 (&rn)[4]) {
+    const float *p = rnorm + t * 32 + 4 * (lane >> 5);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) rn[g] = *reinterpret_cast<const float4 *>(p + 8 * g);
+}
+
+// Per-query L2 norms of the staged query block (row stride dp in LDS), one wave
+// per query, into qn[0 .. 32).
+__device__ __forceinline__ void stage_query_norms(const float *qs, int dp, int d, float *qn) {
+    const int nw = blockDim.x >> 6;
+    for (int j = wave_in_group(); j < kMfmaMaxQ; j += nw) {
+        const float v = wave_l2_norm(qs + j * dp, d);
+        if (lane_id() == 0) qn[j] = v;
+    }
+}
+
 // KPF: chunks loaded ahead; NT: workgroup size; ACC: independent accumulators
 // (chunk j accumulates into acc[j % ACC], summed at the end).
-template <int KPF, int NT, int ACC>
+template <int KPF, int NT, int ACC, bool COS>
 __global__ __launch_bounds__(NT) void mfma_scores_kernel(const float *__restrict__ corpus, int64_t n, int d,
                                                          const float *__restrict__ queries, int q,
+                                                         const float *__restrict__ rnorm,
                                                          float *__restrict__ scores, int64_t ld,
                                                          float *__restrict__ tmax, int64_t tld,
                                                          int64_t tiles_per_wave) {
     static_assert(KPF % ACC == 0, "each ring slot feeds one accumulator");
     extern __shared__ float qs[];
+    __shared__ float qn_s[kMfmaMaxQ];
     const int nchunks = (d + 31) / 32;
     const int nck = (nchunks + KPF - 1) / KPF * KPF;  // chunks walked: whole pipeline rounds
     const int dpad = nck * 32;
@@ -100,6 +133,12 @@ __global__ __launch_bounds__(NT) void mfma_scores_kernel(const float *__restrict
         qs[r * dp + c] = (r < q && c < d) ? queries[(int64_t)r * d + c] : 0.f;
     }
     __syncthreads();
+    float qn = 0.f;
+    if constexpr (COS) {
+        stage_query_norms(qs, dp, d, qn_s);
+        __syncthreads();
+        qn = qn_s[threadIdx.x & 31];
+    }
 
     const int lane = threadIdx.x & 63;
     const int wv = wave_in_group();  // wave-uniform: the tile loop runs on scalar registers
@@ -114,6 +153,8 @@ __global__ __launch_bounds__(NT) void mfma_scores_kernel(const float *__restrict
     for (int64_t t = t_begin; t < t_end; ++t) {
         const int64_t row0 = t * 32;
         const bool valid = row0 + m < n;
+        float4 rn[4];
+        if constexpr (COS) load_tile_norms(rnorm, t, lane, rn);
         const float *p = corpus + (valid ? row0 + m : n - 1) * (int64_t)d;
         auto load_chunk = [&](int chunk, float4(&dst)[4]) {
             chunk = chunk < nchunks ? chunk : nchunks - 1;
@@ -162,7 +203,7 @@ __global__ __launch_bounds__(NT) void mfma_scores_kernel(const float *__restrict
         for (int h = 1; h < ACC; ++h)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[0][v] += acc[h][v];
-        store_tile(acc[0], t, n, q, lane, scores, ld, tmax, tld);
+        store_tile<COS>(acc[0], t, n, q, lane, scores, ld, tmax, tld, rn, qn);
     }
 }
 
@@ -172,9 +213,10 @@ __global__ __launch_bounds__(NT) void mfma_scores_kernel(const float *__restrict
 // waited for with all loads), the column offsets are load immediates with no
 // clamping or masking, and the refills of a tile's last chunks already fetch
 // the next tile's first chunks (one pipeline across the wave's tiles).
-template <int NCK, int KPF, int NT, int ACC>
+template <int NCK, int KPF, int NT, int ACC, bool COS>
 __global__ __launch_bounds__(NT) void mfma_scores_fixed_kernel(const float *__restrict__ corpus, int64_t n,
                                                                const float *__restrict__ queries, int q,
+                                                               const float *__restrict__ rnorm,
                                                                float *__restrict__ scores, int64_t ld,
                                                                float *__restrict__ tmax, int64_t tld,
                                                                int64_t tiles_per_wave) {
@@ -182,11 +224,18 @@ __global__ __launch_bounds__(NT) void mfma_scores_fixed_kernel(const float *__re
     constexpr int d = NCK * 32;
     constexpr int dp = d + 4;
     extern __shared__ float qs[];
+    __shared__ float qn_s[kMfmaMaxQ];
     for (int i = threadIdx.x; i < kMfmaMaxQ * d; i += NT) {
         const int r = i / d, c = i - r * d;
         qs[r * dp + c] = (r < q) ? queries[(int64_t)r * d + c] : 0.f;
     }
     __syncthreads();
+    float qn = 0.f;
+    if constexpr (COS) {
+        stage_query_norms(qs, dp, d, qn_s);
+        __syncthreads();
+        qn = qn_s[threadIdx.x & 31];
+    }
 
     const int lane = threadIdx.x & 63;
     const int wv = wave_in_group();  // wave-uniform: the tile loop runs on scalar registers
@@ -218,6 +267,8 @@ __global__ __launch_bounds__(NT) void mfma_scores_fixed_kernel(const float *__re
         int qoff = 0;
         asm volatile("" : "+v"(qoff));
         const float *qt = qrow + qoff;
+        float4 rn[4];
+        if constexpr (COS) load_tile_norms(rnorm, t, lane, rn);
         floatx16 acc[ACC];
 #pragma unroll
         for (int h = 0; h < ACC; ++h)
@@ -246,7 +297,7 @@ __global__ __launch_bounds__(NT) void mfma_scores_fixed_kernel(const float *__re
         for (int h = 1; h < ACC; ++h)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[0][v] += acc[h][v];
-        store_tile(acc[0], t, n, q, lane, scores, ld, tmax, tld);
+        store_tile<COS>(acc[0], t, n, q, lane, scores, ld, tmax, tld, rn, qn);
         p = pn;
     }
 }
@@ -259,42 +310,59 @@ constexpr int kFixedPrefetch = 2;
 constexpr int kFixedThreads = 1024;
 constexpr int kFixedAcc = 2;
 
-hipError_t prepare_mfma_scores() {
+template <bool COS>
+static hipError_t prepare_metric() {
     hipError_t err = hipFuncSetAttribute(
-        reinterpret_cast<const void *>(&mfma_scores_kernel<kMfmaPrefetch, kMfmaThreads, kMfmaAcc>),
+        reinterpret_cast<const void *>(&mfma_scores_kernel<kMfmaPrefetch, kMfmaThreads, kMfmaAcc, COS>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)mfma_lds_bytes(kMfmaMaxD, kMfmaPrefetch));
-#define RT_PREP(NCK)                                                                                              \
-    if (err == hipSuccess)                                                                                        \
-        err = hipFuncSetAttribute(                                                                                \
-            reinterpret_cast<const void *>(&mfma_scores_fixed_kernel<NCK, kFixedPrefetch, kFixedThreads, kFixedAcc>), \
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)mfma_lds_bytes(NCK * 32, 1));
+#define RT_PREP(NCK)                                                                                          \
+    if (err == hipSuccess)                                                                                    \
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(                                             \
+                                      &mfma_scores_fixed_kernel<NCK, kFixedPrefetch, kFixedThreads, kFixedAcc, COS>), \
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)mfma_lds_bytes(NCK * 32, 1));
     RT_MFMA_FIXED(RT_PREP)
 #undef RT_PREP
     return err;
 }
 
-hipError_t launch_mfma_scores(const float *corpus, int64_t n, int d, const float *queries, int q, float *scores,
-                              int64_t ld, float *tmax, int64_t tld, int num_cus, hipStream_t stream) {
+hipError_t prepare_mfma_scores() {
+    hipError_t err = prepare_metric<false>();
+    if (err == hipSuccess) err = prepare_metric<true>();
+    return err;
+}
+
+template <bool COS>
+static hipError_t launch_metric(const float *corpus, int64_t n, int d, const float *queries, int q,
+                                const float *rnorm, float *scores, int64_t ld, float *tmax, int64_t tld, int num_cus,
+                                hipStream_t stream) {
     const int64_t tiles = (n + 31) / 32;
-#define RT_FIXED(NCK)                                                                                          \
-    if (d == NCK * 32) {                                                                                       \
-        constexpr int w = kFixedThreads / 64;                                                                  \
-        const int64_t tpw = (tiles + (int64_t)num_cus * w - 1) / ((int64_t)num_cus * w);                       \
-        const int64_t blocks = (tiles + tpw * w - 1) / (tpw * w);                                              \
-        hipLaunchKernelGGL((mfma_scores_fixed_kernel<NCK, kFixedPrefetch, kFixedThreads, kFixedAcc>),          \
+#define RT_FIXED(NCK)                                                                                            \
+    if (d == NCK * 32) {                                                                                         \
+        constexpr int w = kFixedThreads / 64;                                                                    \
+        const int64_t tpw = (tiles + (int64_t)num_cus * w - 1) / ((int64_t)num_cus * w);                         \
+        const int64_t blocks = (tiles + tpw * w - 1) / (tpw * w);                                                \
+        hipLaunchKernelGGL((mfma_scores_fixed_kernel<NCK, kFixedPrefetch, kFixedThreads, kFixedAcc, COS>),       \
                            dim3((unsigned)blocks), dim3(kFixedThreads), mfma_lds_bytes(d, 1), stream, corpus, n, \
-                           queries, q, scores, ld, tmax, tld, tpw);                                                       \
-        return hipGetLastError();                                                                              \
+                           queries, q, rnorm, scores, ld, tmax, tld, tpw);                                       \
+        return hipGetLastError();                                                                                \
     }
     RT_MFMA_FIXED(RT_FIXED)
 #undef RT_FIXED
     constexpr int w = kMfmaThreads / 64;
     const int64_t tiles_per_wave = (tiles + (int64_t)num_cus * w - 1) / ((int64_t)num_cus * w);
     const int64_t blocks = (tiles + tiles_per_wave * w - 1) / (tiles_per_wave * w);
-    hipLaunchKernelGGL((mfma_scores_kernel<kMfmaPrefetch, kMfmaThreads, kMfmaAcc>), dim3((unsigned)blocks),
-                       dim3(kMfmaThreads), mfma_lds_bytes(d, kMfmaPrefetch), stream, corpus, n, d, queries, q, scores,
-                       ld, tmax, tld, tiles_per_wave);
+    hipLaunchKernelGGL((mfma_scores_kernel<kMfmaPrefetch, kMfmaThreads, kMfmaAcc, COS>), dim3((unsigned)blocks),
+                       dim3(kMfmaThreads), mfma_lds_bytes(d, kMfmaPrefetch), stream, corpus, n, d, queries, q, rnorm,
+                       scores, ld, tmax, tld, tiles_per_wave);
     return hipGetLastError();
+}
+
+hipError_t launch_mfma_scores(const float *corpus, int64_t n, int d, const float *queries, int q,
+                              const float *rnorm, float *scores, int64_t ld, float *tmax, int64_t tld, int num_cus,
+                              hipStream_t stream) {
+    if (rnorm != nullptr)
+        return launch_metric<true>(corpus, n, d, queries, q, rnorm, scores, ld, tmax, tld, num_cus, stream);
+    return launch_metric<false>(corpus, n, d, queries, q, nullptr, scores, ld, tmax, tld, num_cus, stream);
 }
 
 }  // namespace rt

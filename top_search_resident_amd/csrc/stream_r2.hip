@@ -1,7 +1,10 @@
-// stream_r2.hip -- streaming top-K kernels with 128-entry lists (see stream_topk.hpp).
+// stream_r2.hip -- inner-product scoring and raw-array selection kernels with
+// 128-entry lists (see stream_topk.hpp).
 #include "stream_topk.hpp"
 
 namespace rt {
-template hipError_t launch_stream_r<2>(int, int, int, dim3, hipStream_t, const void *, int64_t, int, int64_t,
-                                         const float *, int64_t, const TreeLaunch &);
+template hipError_t launch_gemv_r<2, false>(bool, int, int, dim3, hipStream_t, const float *, int64_t, int,
+                                           const float *, const float *, int64_t, const TreeLaunch &);
+template hipError_t launch_select_r<2>(int, dim3, hipStream_t, const void *, int64_t, int64_t, int64_t,
+                                        const TreeLaunch &);
 }  // namespace rt

@@ -199,10 +199,13 @@ struct RowUnroll {
 // order (per-lane FMA chain over j and the four components, then group_sum), so
 // identical rows get bit-identical scores wherever they sit, and exact ties
 // resolve by index.
-template <int LG, int L, int R>
+// COS selects the cosine metric: each wave computes the query's norm once, the
+// rows' norms (rnorm, computed at upload) are loaded with the rows, and each
+// dot product becomes cosine_of(dot, |q|, |row|) before it is ranked.
+template <int LG, int L, int R, bool COS>
 __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_topk_kernel(
     const float *__restrict__ corpus, int64_t n, int d, const float *__restrict__ queries,
-    int64_t rows_per_wave, TreeArgs ta) {
+    const float *__restrict__ rnorm, int64_t rows_per_wave, TreeArgs ta) {
     constexpr int G = 1 << LG;
     constexpr int RPS = 64 >> LG;  // rows per lane-group pass
     constexpr int U = RowUnroll<L>::value;
@@ -226,6 +229,9 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_topk_kernel(
     WaveSelector<R> sel;
     sel.init(ta.k);
 
+    float qnorm = 0.f;
+    if constexpr (COS) qnorm = wave_l2_norm(queries + (int64_t)seg * d, d);
+
     float4 qv[L];
     int colc[L];
 #pragma unroll
@@ -241,12 +247,14 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_topk_kernel(
     for (int64_t r0 = r_begin; r0 < r_end; r0 += STEP, base += (int64_t)STEP * d4) {
         const bool tail = r0 + STEP > r_end;
         float4 x[U][L];
+        float rn[U];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             int rel = u * RPS + h;  // row relative to r0
             if (tail && r0 + rel >= r_end) rel = (int)(r_end - 1 - r0);  // past the range: reload the last row
 #pragma unroll
             for (int j = 0; j < L; ++j) x[u][j] = load_nt(base + rel * d4 + colc[j]);
+            if constexpr (COS) rn[u] = rnorm[r0 + rel];
         }
         if (padded) {
 #pragma unroll
@@ -269,6 +277,7 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_topk_kernel(
                 a = fmaf(x[u][j].w, qv[j].w, a);
             }
             acc[u] = group_sum(a, LG);
+            if constexpr (COS) acc[u] = cosine_of(acc[u], qnorm, rn[u]);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -283,10 +292,10 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_topk_kernel(
 }
 
 // Any d: one row per wave at a time, scalar loads strided by 64 lanes.
-template <int R>
+template <int R, bool COS>
 __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_topk_generic_kernel(
     const float *__restrict__ corpus, int64_t n, int d, const float *__restrict__ queries,
-    int64_t rows_per_wave, TreeArgs ta) {
+    const float *__restrict__ rnorm, int64_t rows_per_wave, TreeArgs ta) {
     constexpr int U = 4;
     constexpr int W = gemv_waves(64 * R);
     __shared__ uint64_t stage[W][128];
@@ -298,6 +307,8 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_topk_generic_ker
     const int64_t wave = (int64_t)blockIdx.x * W + wv;
     const float *__restrict__ q = queries + (int64_t)seg * d;
     uint64_t *const my_stage = stage[wv];
+    float qnorm = 0.f;
+    if constexpr (COS) qnorm = wave_l2_norm(q, d);
     WaveSelector<R> sel;
     sel.init(ta.k);
     const int64_t r_begin = wave * rows_per_wave;
@@ -318,6 +329,13 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_topk_generic_ker
         for (int m = 32; m >= 1; m >>= 1) {
 #pragma unroll
             for (int u = 0; u < U; ++u) acc[u] += __shfl_xor(acc[u], m);
+        }
+        if constexpr (COS) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t row = r0 + u;
+                acc[u] = cosine_of(acc[u], qnorm, rnorm[row < r_end ? row : r_end - 1]);
+            }
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -491,38 +509,42 @@ inline TreeArgs make_tree(const TreeLaunch &t) {
     X(0, 1) X(0, 3) X(1, 1) X(1, 3) X(2, 1) X(2, 3) X(3, 1) X(3, 3) X(4, 1) X(4, 3) X(5, 1) X(5, 3) \
     X(6, 1) X(6, 2) X(6, 3) X(6, 4) X(6, 6) X(6, 8)
 
-template <int R>
-hipError_t launch_stream_r(int kind, int lg, int L, dim3 grid, hipStream_t s, const void *data, int64_t n, int d,
-                           int64_t seg_stride, const float *queries, int64_t per_wave, const TreeLaunch &t) {
+// Scoring launcher for lists of 64*R entries: the vector kernel of shape (lg, L)
+// when `fast`, else the scalar kernel; COS selects the cosine metric (rnorm then
+// holds the corpus rows' L2 norms).
+template <int R, bool COS>
+hipError_t launch_gemv_r(bool fast, int lg, int L, dim3 grid, hipStream_t s, const float *corpus, int64_t n, int d,
+                         const float *queries, const float *rnorm, int64_t per_wave, const TreeLaunch &t) {
     const TreeArgs ta = make_tree(t);
-    const float *corpus = static_cast<const float *>(data);
-    switch (kind) {
-        case 0: {  // fast scoring path
-#define RT_SHAPE(LGV, LV)                                                                                      \
-    if (lg == LGV && L == LV) {                                                                                \
-        hipLaunchKernelGGL((gemv_topk_kernel<LGV, LV, R>), grid, dim3(64 * gemv_waves(64 * R)), 0, s, corpus, n, d, queries, \
-                           per_wave, ta);                                                                      \
-        return hipGetLastError();                                                                              \
+    const dim3 block(64 * gemv_waves(64 * R));
+    if (!fast) {
+        hipLaunchKernelGGL((gemv_topk_generic_kernel<R, COS>), grid, block, 0, s, corpus, n, d, queries, rnorm,
+                           per_wave, ta);
+        return hipGetLastError();
     }
-            RT_GEMV_SHAPES(RT_SHAPE)
+#define RT_SHAPE(LGV, LV)                                                                                     \
+    if (lg == LGV && L == LV) {                                                                               \
+        hipLaunchKernelGGL((gemv_topk_kernel<LGV, LV, R, COS>), grid, block, 0, s, corpus, n, d, queries, rnorm, \
+                           per_wave, ta);                                                                     \
+        return hipGetLastError();                                                                             \
+    }
+    RT_GEMV_SHAPES(RT_SHAPE)
 #undef RT_SHAPE
-            return hipErrorInvalidValue;
-        }
-        case 1:
-            hipLaunchKernelGGL((gemv_topk_generic_kernel<R>), grid, dim3(64 * gemv_waves(64 * R)), 0, s, corpus, n, d, queries,
-                               per_wave, ta);
-            return hipGetLastError();
-        case 2:
-            hipLaunchKernelGGL((select_topk_kernel<0, R, select_waves(64 * R)>), grid, dim3(64 * select_waves(64 * R)), 0,
-                               s, static_cast<const uint32_t *>(data), seg_stride, n, per_wave, ta);
-            return hipGetLastError();
-        case 3:
-            hipLaunchKernelGGL((select_topk_kernel<1, R, select_waves(64 * R)>), grid, dim3(64 * select_waves(64 * R)), 0,
-                               s, static_cast<const uint32_t *>(data), seg_stride, n, per_wave, ta);
-            return hipGetLastError();
-        default:
-            return hipErrorInvalidValue;
-    }
+    return hipErrorInvalidValue;
+}
+
+// Raw-array selection launcher for lists of 64*R entries (dtype 0 = int32, 1 = fp32).
+template <int R>
+hipError_t launch_select_r(int dtype, dim3 grid, hipStream_t s, const void *data, int64_t n, int64_t seg_stride,
+                           int64_t per_wave, const TreeLaunch &t) {
+    const TreeArgs ta = make_tree(t);
+    constexpr int W = select_waves(64 * R);
+    const uint32_t *base = static_cast<const uint32_t *>(data);
+    if (dtype == 0)
+        hipLaunchKernelGGL((select_topk_kernel<0, R, W>), grid, dim3(64 * W), 0, s, base, seg_stride, n, per_wave, ta);
+    else
+        hipLaunchKernelGGL((select_topk_kernel<1, R, W>), grid, dim3(64 * W), 0, s, base, seg_stride, n, per_wave, ta);
+    return hipGetLastError();
 }
 
 }  // namespace rt

@@ -168,6 +168,31 @@ __device__ __forceinline__ float group_sum(float v, int log2g) {
     return v;
 }
 
+// L2 norm of the d floats at v, computed by one whole wave: lane l sums the
+// squares of elements l, l + 64, ... in fp64 (each fp32 square is exact in
+// fp64), the 64 partial sums are added by a fixed butterfly, and the fp64
+// square root is rounded to fp32 once.  Every wave that calls it on the same
+// data gets the same bits, and every lane returns the result.
+__device__ __forceinline__ float wave_l2_norm(const float *__restrict__ v, int64_t d) {
+    double s = 0.0;
+    for (int64_t c = lane_id(); c < d; c += kWave) {
+        const double x = (double)v[c];
+        s = fma(x, x, s);
+    }
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+    return (float)sqrt(s);
+}
+
+// Cosine score from an inner product: acc / (|q| |x|), or -inf when that
+// product of norms is not positive (a zero row or a zero query) -- the pages'
+// cosine branch of the scoring kernel, in fp32 ("GPU-Resident Top-K for Agentic
+// RAG", section 4, Step 2).
+__device__ __forceinline__ float cosine_of(float acc, float qnorm, float rnorm) {
+    const float den = qnorm * rnorm;
+    return den > 0.f ? acc / den : -INFINITY;
+}
+
 // Number of set bits of `mask` below this lane.
 __device__ __forceinline__ int lanes_below(uint64_t mask) {
     return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),

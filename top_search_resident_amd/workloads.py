@@ -89,6 +89,16 @@ def gaussian_rows(n, d, config_id, stream=STREAM_CORPUS, normalise=True, out=Non
     return out
 
 
+def scaled_rows(n, d, config_id, stream=STREAM_CORPUS, sigma=1.0):
+    """n x d fp32 rows: iid N(0,1) entries, each row multiplied by its own
+    log-normal factor exp(sigma * N(0,1)), so row lengths vary widely (inputs for
+    the cosine metric, whose ranking then differs from the inner product's)."""
+    rows = gaussian_rows(n, d, config_id, stream, normalise=False)
+    scale = np.exp(sigma * _rng(config_id, stream, 1 << 20).standard_normal(n)).astype(np.float32)
+    rows *= scale[:, None]
+    return rows
+
+
 def retrieval_inputs(name, n=None, d=None, queries=None):
     """(corpus fp32 [n, d], queries fp32 [q, d]) for a retrieval workload.
 
