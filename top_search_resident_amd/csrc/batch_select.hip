@@ -16,6 +16,7 @@
 // Ranks are the same (key << 32 | ~index) packing as wave_topk.hpp, so the
 // order -- larger score first, exact ties to the lower index -- is the pages'
 // comparator (section 3, "Problem B").
+#include "block_sort.hpp"
 #include "kernels.hpp"
 #include "wave_topk.hpp"
 
@@ -46,86 +47,9 @@ __device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, uint32_t *b
     return r;
 }
 
-// Sort sm[0 .. M) best-first with the kBatchSelectThreads threads of the
-// workgroup (M a power of two in [64, kSortCap]).  Bitonic network on
-// registers: the first min(M, 1024) threads hold E = M / 1024 (at least one)
-// elements, element r * 1024 + t in thread t.  Exchanges with a partner in the
-// same wave go through DPP / permlane, partners in the same thread are register
-// swaps, and only partners in another wave go through LDS (for M = 2048, 14 of
-// the 66 steps) -- instead of one LDS round trip and barrier per step.
-template <int M>
-__device__ __forceinline__ void block_sort_desc_m(uint64_t *sm) {
-    constexpr int NT = kBatchSelectThreads;
-    constexpr int ACT = M < NT ? M : NT;  // active threads (whole waves)
-    constexpr int E = M / ACT;
-    const int t = threadIdx.x;
-    const bool active = t < ACT;
-    uint64_t x[E];
-#pragma unroll
-    for (int r = 0; r < E; ++r) x[r] = active ? sm[r * ACT + t] : 0ull;
-    __syncthreads();
-#pragma unroll
-    for (int k2 = 2; k2 <= M; k2 <<= 1) {
-#pragma unroll
-        for (int j = k2 >> 1; j > 0; j >>= 1) {
-            if (j >= ACT) {  // partner in this thread: register r ^ (j / ACT)
-                const int jr = j / ACT;
-#pragma unroll
-                for (int r = 0; r < E; ++r) {
-                    if ((r & jr) == 0) {
-                        const int p = r | jr;
-                        const bool desc = (((r * ACT) + t) & k2) == 0;
-                        const uint64_t hi = umax64(x[r], x[p]), lo = umin64(x[r], x[p]);
-                        x[r] = desc ? hi : lo;
-                        x[p] = desc ? lo : hi;
-                    }
-                }
-            } else if (j >= 64) {  // partner in another wave: through LDS
-                if (active) {
-#pragma unroll
-                    for (int r = 0; r < E; ++r) sm[r * ACT + t] = x[r];
-                }
-                __syncthreads();
-                if (active) {
-#pragma unroll
-                    for (int r = 0; r < E; ++r) {
-                        const uint64_t y = sm[r * ACT + (t ^ j)];
-                        const bool desc = (((r * ACT) + t) & k2) == 0;
-                        const bool lower = (t & j) == 0;
-                        x[r] = (lower == desc) ? umax64(x[r], y) : umin64(x[r], y);
-                    }
-                }
-                __syncthreads();
-            } else if (active) {  // partner in this wave
-#pragma unroll
-                for (int r = 0; r < E; ++r) {
-                    const uint64_t y = shfl_xor_u64(x[r], j);
-                    const bool desc = (((r * ACT) + t) & k2) == 0;
-                    const bool lower = (t & j) == 0;
-                    x[r] = (lower == desc) ? umax64(x[r], y) : umin64(x[r], y);
-                }
-            }
-        }
-    }
-    if (active) {
-#pragma unroll
-        for (int r = 0; r < E; ++r) sm[r * ACT + t] = x[r];
-    }
-    __syncthreads();
-}
-
 // Sort sm[0 .. m) best-first, m a power of two in [64, kSortCap].
 __device__ __forceinline__ void block_sort_desc(uint64_t *sm, int m) {
-    switch (m) {
-        case 64: block_sort_desc_m<64>(sm); break;
-        case 128: block_sort_desc_m<128>(sm); break;
-        case 256: block_sort_desc_m<256>(sm); break;
-        case 512: block_sort_desc_m<512>(sm); break;
-        case 1024: block_sort_desc_m<1024>(sm); break;
-        case 2048: block_sort_desc_m<2048>(sm); break;
-        case 4096: block_sort_desc_m<4096>(sm); break;
-        default: block_sort_desc_m<8192>(sm); break;
-    }
+    block_sort_desc_any<kBatchSelectThreads, kSortCap>(sm, m);
 }
 
 struct SelectOut {

@@ -11,12 +11,16 @@ namespace rt {
 // workgroup's waves), 4 waves for longer lists (all wave lists must fit the
 // merge LDS).
 constexpr int kGemvWaves = 8;
+// Rows per wave up to which the scorer loads two steps ahead (below, every
+// step of a short range would pay a full memory latency; above, the chip is
+// bandwidth-bound and lookahead only adds outstanding requests).
+constexpr int64_t kGemvLookaheadRows = 128;
 constexpr int gemv_waves(int kp) { return kp <= 256 ? kGemvWaves : 4; }
 // Raw-array selection runs 16-wave workgroups that share a certified bound in
 // LDS (all 16 lists must fit the merge LDS, so only for lists <= 256 entries).
 constexpr int select_waves(int kp) { return kp <= 256 ? 16 : 4; }
 // LDS ranks a workgroup uses to merge lists in the merge tree (32 KiB); a tree
-// node merges kTreeEntries / Kp lists.
+// node merges kTreeEntries / tree_stride(k, Kp) lists.
 constexpr int kTreeEntries = 4096;
 // Batched scoring: one workgroup per CU (512 threads for a runtime depth, 1024 for
 // the compile-time depths), 32 queries x 32 rows per wave tile.
@@ -39,8 +43,11 @@ struct TreeLaunch {
     int64_t src_seg_stride;    // mode 2: elements between segments of src
 };
 
-// Lists merged per tree node for list length kp.
-int tree_fan(int kp);
+// Entries between consecutive lists in the merge tree for top-k with lists of
+// kp entries: the smallest power of two >= k when k <= 32 (only the first k
+// entries of a list matter), else kp.  A tree node merges kTreeEntries / stride
+// lists.
+int tree_stride(int k, int kp);
 
 // Fast inner-product path: d % 4 == 0 and d / 4 <= 64 * 8.
 bool gemv_fast_path_ok(int d);

@@ -24,7 +24,12 @@ RT_EXTERN_R(16)
 
 bool gemv_fast_path_ok(int d) { return d % 4 == 0 && d / 4 <= 64 * 8; }
 
-int tree_fan(int kp) { return kTreeEntries / kp; }
+int tree_stride(int k, int kp) {
+    if (k > kWave / 2) return kp;
+    int kc = 1;
+    while (kc < k) kc <<= 1;
+    return kc;
+}
 
 // Pick the lane-group width G = 2^lg (<= 64) and loads per lane L (from
 // {1, 2, 3, 4, 6, 8}) that waste the fewest lane slots on a row, preferring wide

@@ -45,7 +45,8 @@ struct TreeArgs {
     uint32_t *counters;      // per segment: seg_ctr_stride arrival counters (zero between calls)
     int64_t seg_tree_stride;
     int seg_ctr_stride;
-    int fan;                 // lists merged per tree node (power of two, fan * Kp <= kTreeEntries)
+    int fan;                 // lists merged per tree node (power of two, fan * kc <= kTreeEntries)
+    int kc;                  // list stride in the tree: smallest power of two >= k if k <= 32, else Kp
     int k;
     int mode;                // 1: write index + fp32 score from the rank; 2: index + source element
     int32_t *out_idx;        // [segments][k]
@@ -88,19 +89,88 @@ __device__ __forceinline__ void merge_lds_lists(uint64_t *sm, int count) {
     }
 }
 
+// Merge `count` best-first lists of KC entries each (KC a power of two <= 64)
+// held at sm[c * KC ..] into sm[0 .. KC): the best KC of their union.  Rounds
+// of pairwise merges, one barrier per round; a pair is merged by a group of KC
+// lanes (lane i takes the larger of A[i] and B[KC - 1 - i], which leaves the
+// best KC of A and B as a bitonic sequence, then log2(KC) exchange steps sort
+// it), so a wave merges 64 / KC pairs at once.  Only the first k <= KC entries
+// of a list ever matter, so short lists are merged as short lists.
+// One exchange step of a bitonic merge at lane distance J (i = lane within the
+// group): the lower lane keeps the larger rank.
+template <int J>
+__device__ __forceinline__ uint64_t merge_step(uint64_t x, int i) {
+    return cmpx64(x, xor_u64<J>(x), (i & J) == 0);
+}
+
+// Sort a bitonic sequence held by groups of KC lanes (one rank per lane) into
+// best-first order: steps at distances KC/2, ..., 1, spelled out so that every
+// lane exchange is a fixed DPP / permlane move.
+template <int KC>
+__device__ __forceinline__ uint64_t group_bitonic_merge(uint64_t x, int i) {
+    if constexpr (KC >= 64) x = merge_step<32>(x, i);
+    if constexpr (KC >= 32) x = merge_step<16>(x, i);
+    if constexpr (KC >= 16) x = merge_step<8>(x, i);
+    if constexpr (KC >= 8) x = merge_step<4>(x, i);
+    if constexpr (KC >= 4) x = merge_step<2>(x, i);
+    if constexpr (KC >= 2) x = merge_step<1>(x, i);
+    return x;
+}
+
+template <int KC>
+__device__ __forceinline__ void merge_short_lists_t(uint64_t *sm, int count) {
+    constexpr int PER_WAVE = kWave / KC;
+    const int lane = lane_id();
+    const int i = lane & (KC - 1);
+    const int slots = (int)(blockDim.x >> 6) * PER_WAVE;
+    const int slot = wave_in_group() * PER_WAVE + lane / KC;
+    for (int s = 1; s < count; s <<= 1) {
+        const int pairs = (count - s + 2 * s - 1) / (2 * s);  // lists a = 0, 2s, ... with a + s < count
+        for (int p0 = 0; p0 < pairs; p0 += slots) {
+            const int p = p0 + slot;
+            // Groups without a pair read list 0 (any in-range address) and
+            // do not write.
+            const bool active = p < pairs;
+            const int a = active ? p * 2 * s : 0;
+            const int b = active ? a + s : 0;
+            uint64_t x = umax64(sm[a * KC + i], sm[b * KC + (KC - 1 - i)]);
+            x = group_bitonic_merge<KC>(x, i);
+            if (active) sm[a * KC + i] = x;
+        }
+        __syncthreads();
+    }
+}
+
+__device__ __forceinline__ void merge_short_lists(uint64_t *sm, int count, int kc) {
+    switch (kc) {
+        case 1: merge_short_lists_t<1>(sm, count); break;
+        case 2: merge_short_lists_t<2>(sm, count); break;
+        case 4: merge_short_lists_t<4>(sm, count); break;
+        case 8: merge_short_lists_t<8>(sm, count); break;
+        case 16: merge_short_lists_t<16>(sm, count); break;
+        case 32: merge_short_lists_t<32>(sm, count); break;
+        default: merge_short_lists_t<64>(sm, count); break;
+    }
+}
+
 // LDS words the merges use besides the lists.
 struct MergeScratch {
     int flag;
 };
 
-// Step 3: a merge tree.  Workgroups are grouped `fan` at a time; the last of a
-// group to arrive loads the first k entries of the group's lists (the rest of
-// each list cannot matter), merges them and moves one level up; the last one at
-// the root writes the outputs.
+// Step 3: a merge tree.  Each workgroup stores the first k entries of its list,
+// kc entries apart (kc = the smallest power of two >= k for k <= 32, else the
+// list length Kp); workgroups are grouped `fan` = kTreeEntries / kc at a time,
+// and the last of a group to arrive (a global arrival counter) loads the
+// group's lists, merges them and moves one level up; the last one at the root
+// writes the outputs.  Lists of up to 32 entries are merged as short lists
+// (merge_short_lists: faster than full 64-entry merges from 64 lists up, and
+// the short stride makes the fan wider, e.g. one level of up to 512 lists for
+// k <= 8), longer ones with the register networks (merge_lds_lists).
 template <int R, int NT>
 __device__ __forceinline__ void tree_finish(uint64_t *sm, MergeScratch *ms, const TreeArgs &ta, int seg) {
-    constexpr int Kp = 64 * R;
     const int k = ta.k;
+    const int kc = ta.kc;
     int count = gridDim.x;
     uint64_t *base = ta.tree + (int64_t)seg * ta.seg_tree_stride;
     uint32_t *ctr = ta.counters + (int64_t)seg * ta.seg_ctr_stride;
@@ -108,7 +178,7 @@ __device__ __forceinline__ void tree_finish(uint64_t *sm, MergeScratch *ms, cons
     int64_t level_off = 0;
     int ctr_off = 0;
     for (int i = threadIdx.x; i < k; i += NT)
-        __hip_atomic_store(&base[(int64_t)node * Kp + i], sm[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&base[(int64_t)node * kc + i], sm[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     while (true) {
         const int parent = node / ta.fan;
         const int first = parent * ta.fan;
@@ -126,31 +196,34 @@ __device__ __forceinline__ void tree_finish(uint64_t *sm, MergeScratch *ms, cons
         if (!ms->flag) return;
         // All of a thread's loads are issued before any is stored to LDS (a
         // loop of load-then-store pays one device round trip per entry).
-        const uint64_t *src = base + level_off + (int64_t)first * Kp;
+        const uint64_t *src = base + level_off + (int64_t)first * kc;
         constexpr int E = kTreeEntries / NT;
         uint64_t v[E];
 #pragma unroll
         for (int u = 0; u < E; ++u) {
             const int i = u * NT + threadIdx.x;
-            v[u] = (i < children * Kp && (i & (Kp - 1)) < k)
+            v[u] = (i < children * kc && (i & (kc - 1)) < k)
                        ? __hip_atomic_load(&src[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                        : 0ull;
         }
 #pragma unroll
         for (int u = 0; u < E; ++u) {
             const int i = u * NT + threadIdx.x;
-            if (i < children * Kp) sm[i] = v[u];
+            if (i < children * kc) sm[i] = v[u];
         }
         __syncthreads();
-        merge_lds_lists<R>(sm, children);
+        if (kc < kWave)
+            merge_short_lists(sm, children, kc);
+        else
+            merge_lds_lists<R>(sm, children);
         const int up = (count + ta.fan - 1) / ta.fan;
         if (up == 1) {
             for (int r = threadIdx.x; r < k; r += NT) write_output(ta, seg, r, sm[r]);
             return;
         }
-        const int64_t next_off = level_off + (int64_t)count * Kp;
+        const int64_t next_off = level_off + (int64_t)count * kc;
         for (int i = threadIdx.x; i < k; i += NT)
-            __hip_atomic_store(&base[next_off + (int64_t)parent * Kp + i], sm[i], __ATOMIC_RELAXED,
+            __hip_atomic_store(&base[next_off + (int64_t)parent * kc + i], sm[i], __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         level_off = next_off;
         ctr_off += up;
@@ -183,9 +256,8 @@ __device__ __forceinline__ void finish_workgroup(WaveSelector<R> &sel, uint64_t 
 
 // ---------------------------------------------------------------- scoring
 
-// Rows each lane group takes per step.  Measured on MI355X at 1M x 1024: one row
-// per step with ~8 waves per CU keeps HBM near 89% of peak; larger unrolls only
-// add register pressure.  Rows of a single float4 per lane take two.
+// Rows each lane group takes per step: one, or two for rows of a single float4
+// per lane.
 template <int L>
 struct RowUnroll {
     static constexpr int value = (L == 1) ? 2 : 1;
@@ -199,10 +271,20 @@ struct RowUnroll {
 // order (per-lane FMA chain over j and the four components, then group_sum), so
 // identical rows get bit-identical scores wherever they sit, and exact ties
 // resolve by index.
+// Loads: with P = 0 a step issues its loads and consumes them at once, so a
+// wave has one step in flight -- best when each wave streams hundreds of rows
+// and the chip is bandwidth-bound (measured on MI355X at 1M x 1024: any
+// lookahead costs 1-2%).  With P > 0 loads run P steps ahead: slot s of a ring
+// of P register sets holds step i + s; it is consumed in place and refilled
+// with step i + s + P, so every wait is a counted wait for one slot's loads --
+// best when each wave has only tens of rows and every step would otherwise pay
+// a full memory latency (50k x 768: 42 -> 34 us).  Rows past the wave's range
+// are loaded from its last row (cached) and never offered, so no load is
+// predicated.
 // COS selects the cosine metric: each wave computes the query's norm once, the
 // rows' norms (rnorm, computed at upload) are loaded with the rows, and each
 // dot product becomes cosine_of(dot, |q|, |row|) before it is ranked.
-template <int LG, int L, int R, bool COS>
+template <int LG, int L, int R, bool COS, int P>
 __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_topk_kernel(
     const float *__restrict__ corpus, int64_t n, int d, const float *__restrict__ queries,
     const float *__restrict__ rnorm, int64_t rows_per_wave, TreeArgs ta) {
@@ -210,6 +292,7 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_topk_kernel(
     constexpr int RPS = 64 >> LG;  // rows per lane-group pass
     constexpr int U = RowUnroll<L>::value;
     constexpr int STEP = RPS * U;  // rows per wave step
+    constexpr int SLOTS = P > 0 ? P : 1;
     constexpr int W = gemv_waves(64 * R);
     __shared__ uint64_t stage[W][128];
     __shared__ uint64_t sm[kTreeEntries];
@@ -222,7 +305,6 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_topk_kernel(
     const int g = lane & (G - 1);
     const int h = lane >> LG;
     const int d4 = d >> 2;
-    const bool padded = G * L != d4;
     const float4 *__restrict__ q4 = reinterpret_cast<const float4 *>(queries + (int64_t)seg * d);
     uint64_t *const my_stage = stage[wv];
 
@@ -232,59 +314,93 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_topk_kernel(
     float qnorm = 0.f;
     if constexpr (COS) qnorm = wave_l2_norm(queries + (int64_t)seg * d, d);
 
+    // Columns past the row end (G * L > d / 4) load the last column; their bits
+    // are and-ed with a zero mask (a plain select or branch on a loaded register
+    // makes the compiler wait for every outstanding load first).
     float4 qv[L];
     int colc[L];
+    uint32_t cmask[L];
 #pragma unroll
     for (int j = 0; j < L; ++j) {
         const int col = j * G + g;
         colc[j] = (col < d4) ? col : d4 - 1;
+        cmask[j] = (col < d4) ? 0xffffffffu : 0u;
         qv[j] = (col < d4) ? q4[col] : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 
     const int64_t r_begin = wave * rows_per_wave;
     const int64_t r_end = (r_begin + rows_per_wave < n) ? r_begin + rows_per_wave : n;
-    const float4 *__restrict__ base = reinterpret_cast<const float4 *>(corpus) + r_begin * d4;
-    for (int64_t r0 = r_begin; r0 < r_end; r0 += STEP, base += (int64_t)STEP * d4) {
-        const bool tail = r0 + STEP > r_end;
-        float4 x[U][L];
-        float rn[U];
+    if (r_begin < r_end) {
+        const float4 *__restrict__ c4 = reinterpret_cast<const float4 *>(corpus);
+        const int64_t last = r_end - 1;
+        float4 x[SLOTS][U][L];
+        float rn[SLOTS][U];
+        // Fill slot s with the rows of the step starting at row r0.
+        auto load_step = [&](int s, int64_t r0) {
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int rel = u * RPS + h;  // row relative to r0
-            if (tail && r0 + rel >= r_end) rel = (int)(r_end - 1 - r0);  // past the range: reload the last row
+            for (int u = 0; u < U; ++u) {
+                int64_t row = r0 + u * RPS + h;
+                row = row < last ? row : last;
+                const float4 *p = c4 + row * d4;
 #pragma unroll
-            for (int j = 0; j < L; ++j) x[u][j] = load_nt(base + rel * d4 + colc[j]);
-            if constexpr (COS) rn[u] = rnorm[r0 + rel];
-        }
-        if (padded) {
+                for (int j = 0; j < L; ++j) x[s][u][j] = load_nt(p + colc[j]);
+                if constexpr (COS) rn[s][u] = rnorm[row];
+            }
+        };
+        // Score the rows of slot s (step starting at row rs) and offer them;
+        // with P > 0 the slot is refilled with step rs + P * STEP first.
+        auto consume = [&](int s, int64_t rs) {
+            float acc[U];
 #pragma unroll
-            for (int j = 0; j < L; ++j) {
-                if (j * G + g >= d4) {
+            for (int u = 0; u < U; ++u) {
+                float a = 0.f;
 #pragma unroll
-                    for (int u = 0; u < U; ++u) x[u][j] = make_float4(0.f, 0.f, 0.f, 0.f);
+                for (int j = 0; j < L; ++j) {
+                    float4 v = x[s][u][j];
+                    if constexpr (G * L > 4) {  // a shape that can be padded
+                        v.x = __uint_as_float(__float_as_uint(v.x) & cmask[j]);
+                        v.y = __uint_as_float(__float_as_uint(v.y) & cmask[j]);
+                        v.z = __uint_as_float(__float_as_uint(v.z) & cmask[j]);
+                        v.w = __uint_as_float(__float_as_uint(v.w) & cmask[j]);
+                    }
+                    a = fmaf(v.x, qv[j].x, a);
+                    a = fmaf(v.y, qv[j].y, a);
+                    a = fmaf(v.z, qv[j].z, a);
+                    a = fmaf(v.w, qv[j].w, a);
                 }
+                acc[u] = group_sum(a, LG);
+                if constexpr (COS) acc[u] = cosine_of(acc[u], qnorm, rn[s][u]);
             }
-        }
-        float acc[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            float a = 0.f;
-#pragma unroll
-            for (int j = 0; j < L; ++j) {
-                a = fmaf(x[u][j].x, qv[j].x, a);
-                a = fmaf(x[u][j].y, qv[j].y, a);
-                a = fmaf(x[u][j].z, qv[j].z, a);
-                a = fmaf(x[u][j].w, qv[j].w, a);
+            if constexpr (P > 0) {
+                load_step(s, rs + P * STEP);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            acc[u] = group_sum(a, LG);
-            if constexpr (COS) acc[u] = cosine_of(acc[u], qnorm, rn[u]);
-        }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int64_t row = r0 + u * RPS + h;
-            const bool valid = (g == 0) && (row < r_end);
-            const uint64_t rank = make_rank(order_key_f32(acc[u]), (uint32_t)row);
-            sel.offer(my_stage, rank, valid && rank > sel.thr);
+            for (int u = 0; u < U; ++u) {
+                const int64_t row = rs + u * RPS + h;
+                const bool valid = (g == 0) && (row < r_end);
+                const uint64_t rank = make_rank(order_key_f32(acc[u]), (uint32_t)row);
+                sel.offer(my_stage, rank, valid && rank > sel.thr);
+            }
+        };
+        if constexpr (P == 0) {
+            for (int64_t r0 = r_begin; r0 < r_end; r0 += STEP) {
+                load_step(0, r0);
+                consume(0, r0);
+            }
+        } else {
+            // The prologue must issue the slots in ring order, as the loop
+            // refills them: the wait for slot s at the loop head is computed
+            // for the worse of the two orders.
+#pragma unroll
+            for (int s = 0; s < P; ++s) {
+                load_step(s, r_begin + s * STEP);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            for (int64_t r0 = r_begin; r0 < r_end; r0 += P * STEP) {
+#pragma unroll
+                for (int s = 0; s < P; ++s) consume(s, r0 + s * STEP);
+            }
         }
     }
     sel.finish(my_stage);
@@ -494,7 +610,8 @@ inline TreeArgs make_tree(const TreeLaunch &t) {
     ta.counters = t.counters;
     ta.seg_tree_stride = t.seg_tree_stride;
     ta.seg_ctr_stride = t.seg_ctr_stride;
-    ta.fan = kTreeEntries / t.kp;
+    ta.kc = tree_stride(t.k, t.kp);
+    ta.fan = kTreeEntries / ta.kc;
     ta.k = t.k;
     ta.mode = t.mode;
     ta.out_idx = t.out_idx;
@@ -515,6 +632,8 @@ inline TreeArgs make_tree(const TreeLaunch &t) {
 template <int R, bool COS>
 hipError_t launch_gemv_r(bool fast, int lg, int L, dim3 grid, hipStream_t s, const float *corpus, int64_t n, int d,
                          const float *queries, const float *rnorm, int64_t per_wave, const TreeLaunch &t) {
+    // Lookahead only for short row ranges per wave (see gemv_topk_kernel).
+    const bool ahead = per_wave <= kGemvLookaheadRows;
     const TreeArgs ta = make_tree(t);
     const dim3 block(64 * gemv_waves(64 * R));
     if (!fast) {
@@ -522,11 +641,15 @@ hipError_t launch_gemv_r(bool fast, int lg, int L, dim3 grid, hipStream_t s, con
                            per_wave, ta);
         return hipGetLastError();
     }
-#define RT_SHAPE(LGV, LV)                                                                                     \
-    if (lg == LGV && L == LV) {                                                                               \
-        hipLaunchKernelGGL((gemv_topk_kernel<LGV, LV, R, COS>), grid, block, 0, s, corpus, n, d, queries, rnorm, \
-                           per_wave, ta);                                                                     \
-        return hipGetLastError();                                                                             \
+#define RT_SHAPE(LGV, LV)                                                                                      \
+    if (lg == LGV && L == LV) {                                                                                \
+        if (ahead)                                                                                             \
+            hipLaunchKernelGGL((gemv_topk_kernel<LGV, LV, R, COS, 2>), grid, block, 0, s, corpus, n, d, queries, \
+                               rnorm, per_wave, ta);                                                           \
+        else                                                                                                   \
+            hipLaunchKernelGGL((gemv_topk_kernel<LGV, LV, R, COS, 0>), grid, block, 0, s, corpus, n, d, queries, \
+                               rnorm, per_wave, ta);                                                           \
+        return hipGetLastError();                                                                              \
     }
     RT_GEMV_SHAPES(RT_SHAPE)
 #undef RT_SHAPE

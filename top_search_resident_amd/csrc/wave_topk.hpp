@@ -127,6 +127,20 @@ __device__ __forceinline__ uint4 load_nt(const uint4 *p) {
 __device__ __forceinline__ uint64_t umax64(uint64_t a, uint64_t b) { return a > b ? a : b; }
 __device__ __forceinline__ uint64_t umin64(uint64_t a, uint64_t b) { return a > b ? b : a; }
 
+// One side of a compare-exchange: the larger of x and its partner y when
+// keep_max, else the smaller.  Written as a single compare and a select: the
+// form "keep_max ? max(x, y) : min(x, y)" compiles to two compares under
+// exec-masked branches, which made every exchange step of the sorting
+// networks several times slower.
+__device__ __forceinline__ uint64_t cmpx64(uint64_t x, uint64_t y, bool keep_max) {
+    const bool x_wins = (x > y) == keep_max;
+    return x_wins ? x : y;
+}
+__device__ __forceinline__ uint32_t cmpx32(uint32_t x, uint32_t y, bool keep_max) {
+    const bool x_wins = (x > y) == keep_max;
+    return x_wins ? x : y;
+}
+
 // Cross-lane moves through DPP (no LDS round trip).  Controls: quad_perm
 // [1,0,3,2] and [2,3,0,1] swap neighbours at distance 1 and 2; row_half_mirror
 // reverses each 8-lane half-row and row_mirror each 16-lane row.
@@ -171,13 +185,26 @@ __device__ __forceinline__ float group_sum(float v, int log2g) {
 // L2 norm of the d floats at v, computed by one whole wave: lane l sums the
 // squares of elements l, l + 64, ... in fp64 (each fp32 square is exact in
 // fp64), the 64 partial sums are added by a fixed butterfly, and the fp64
-// square root is rounded to fp32 once.  Every wave that calls it on the same
+// square root is rounded to fp32 once.  Loads are issued eight at a time from
+// clamped addresses (out-of-range elements count as zero), so a wave waits for
+// one memory latency per 512 elements.  Every wave that calls it on the same
 // data gets the same bits, and every lane returns the result.
 __device__ __forceinline__ float wave_l2_norm(const float *__restrict__ v, int64_t d) {
+    constexpr int B = 8;
     double s = 0.0;
-    for (int64_t c = lane_id(); c < d; c += kWave) {
-        const double x = (double)v[c];
-        s = fma(x, x, s);
+    const int lane = lane_id();
+    for (int64_t cb = 0; cb < d; cb += kWave * B) {
+        float x[B];
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            const int64_t c = cb + i * kWave + lane;
+            x[i] = v[c < d ? c : d - 1];
+        }
+#pragma unroll
+        for (int i = 0; i < B; ++i) {
+            const double y = (cb + i * kWave + lane < d) ? (double)x[i] : 0.0;
+            s = fma(y, y, s);
+        }
     }
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
@@ -216,7 +243,7 @@ __device__ __forceinline__ uint64_t wave_sort64_desc(uint64_t x) {
             const uint64_t y = shfl_xor_u64(x, j);
             const bool desc_seg = (lane & k) == 0;
             const bool lower = (lane & j) == 0;
-            x = (lower == desc_seg) ? umax64(x, y) : umin64(x, y);
+            x = cmpx64(x, y, lower == desc_seg);
         }
     }
     return x;
@@ -240,7 +267,7 @@ __device__ __forceinline__ uint32_t wave_sort64_desc_u32(uint32_t x) {
             }
             const bool desc_seg = (lane & k) == 0;
             const bool lower = (lane & j) == 0;
-            x = (lower == desc_seg) ? max(x, y) : min(x, y);
+            x = cmpx32(x, y, lower == desc_seg);
         }
     }
     return x;
@@ -301,7 +328,7 @@ __device__ __forceinline__ void bitonic_merge_desc(uint64_t (&L)[R]) {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
             const uint64_t y = shfl_xor_u64(L[r], j);
-            L[r] = lower ? umax64(L[r], y) : umin64(L[r], y);
+            L[r] = cmpx64(L[r], y, lower);
         }
     }
 }
