@@ -179,6 +179,8 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
 
     if batch > 1:
         return run_batched(args, torch, eng, corpus, qhost, qdev, ks, name, gen_s)
+    if args.streams > 1:
+        return run_concurrent(args, torch, eng, corpus, qhost, qdev, ks, name, gen_s)
 
     wall, lat, part, merge = time_search(eng, torch, qdev, ks, args.steps, args.warmup, metric=args.metric)
     nq = args.steps * len(ks)
@@ -236,6 +238,52 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
             gpu_res[k] = (gi, gs)
         line["cpu_baseline"] = cpu_baseline_retrieval(corpus, qhost, max(ks), gpu_res, args.cpu_budget, sample,
                                                       metric=args.metric)
+    eng.close()
+    return line
+
+
+def run_concurrent(args, torch, eng, corpus, qhost, qdev, ks, name, gen_s):
+    """S engines sharing the resident corpus, one stream each (several agents
+    querying one corpus): every step issues, on each stream, one query per K,
+    and then waits for all streams."""
+    n, d = corpus.shape
+    S = args.streams
+    engines = [eng] + [eng.shared() for _ in range(S - 1)]
+    streams = [torch.cuda.Stream() for _ in range(S)]
+    outs = [{k: (torch.empty((1, k), dtype=torch.int32, device="cuda"),
+                 torch.empty((1, k), dtype=torch.float32, device="cuda")) for k in ks} for _ in range(S)]
+    n_q = qdev.shape[0]
+
+    def step(i):
+        for e in range(S):
+            q = qdev[(i * S + e) % n_q:(i * S + e) % n_q + 1]
+            for k in ks:
+                engines[e].search_resident(q, k, *outs[e][k], stream=streams[e], metric=args.metric)
+
+    torch.cuda.synchronize()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    lat = []
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        s0 = time.perf_counter_ns()
+        step(i)
+        for st in streams:
+            st.synchronize()
+        lat.append((time.perf_counter_ns() - s0) / 1e3)
+    wall = time.perf_counter() - t0
+    nq = args.steps * S * len(ks)
+    line = {"metric": f"queries/s with {S} concurrent streams ({name}, {args.metric})", "value": nq / wall,
+            "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": f"{name}: {S} engines sharing one resident {n} x {d} fp32 corpus, one stream "
+                                   f"each; a step = one query per K on every stream, then wait for all",
+                       "n": n, "d": d, "ks": list(ks), "streams": S, "metric": args.metric},
+            "step_p50_us": pct(lat, 50), "step_p99_us": pct(lat, 99), "input_gen_s": gen_s}
+    for e in engines[1:]:
+        e.close()
     eng.close()
     return line
 
@@ -402,6 +450,8 @@ def main():
     ap.add_argument("--workload", default="c3_1m_1024")
     ap.add_argument("--metric", default="dot", choices=("dot", "cosine"),
                     help="similarity for the retrieval workloads (the headline line is the inner product)")
+    ap.add_argument("--streams", type=int, default=1,
+                    help="single-query workloads: engines sharing the corpus, one stream each, searching concurrently")
     ap.add_argument("--num-queries", type=int, default=1000)
     ap.add_argument("--cpu-queries", type=int, default=40)
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time in cpu_baseline")

@@ -29,7 +29,9 @@
  *   - Argument errors are detected on the host before anything is enqueued;
  *     outputs are then left untouched.
  *   - One engine runs one search or select at a time: calls on one engine that
- *     overlap on different streams race on the engine's scratch memory.
+ *     overlap on different streams race on the engine's scratch memory.  For
+ *     concurrent searches use several engines sharing one corpus
+ *     (rt_engine_create_shared).
  *   - Results are best-first.  Indices are int32 (0-based row / element
  *     positions), so n is limited to 2^31 - 1.
  *   - Inputs must be NaN-free; the comparator does not order NaN.
@@ -73,8 +75,27 @@ typedef enum { RT_METRIC_DOT = 0, RT_METRIC_COSINE = 1 } rt_metric;
 rt_status rt_engine_create(int64_t max_n, int32_t max_d, int32_t max_k, int32_t max_q,
                            int32_t device, rt_engine **out);
 
-/* Free every device buffer of the engine (waits for its pending work).  NULL is
- * ignored. */
+/*
+ * Create an engine that searches the same resident corpus as `other` without a
+ * copy: the corpus and its row norms are shared (reference-counted: they stay
+ * allocated until the last engine sharing them is destroyed, in any order),
+ * while the new engine has scratch memory of its own (merge tree, counters,
+ * batch buffers, timing events), sized for results up to max_k and batches up
+ * to max_q.  Searches and selects on different engines may therefore run at
+ * the same time on different streams -- several agents querying one corpus
+ * concurrently, the use case of "GPU-Resident Top-K for Agentic RAG" (section
+ * 1: many micro-agents, each retrieving top-K from the same corpus; section 9
+ * lists query concurrency within one engine as missing).  An upload through any of the sharing engines
+ * replaces the corpus for all of them; the caller must not upload while a
+ * search on any of them is in flight.
+ * Limits as rt_engine_create (1 <= max_k <= 1024, 1 <= max_q <= 32); the
+ * device is other's.  RT_EINVAL for NULL arguments or limits out of range,
+ * RT_ENOMEM / RT_EHIP if the scratch cannot be allocated (then *out = NULL).
+ */
+rt_status rt_engine_create_shared(rt_engine *other, int32_t max_k, int32_t max_q, rt_engine **out);
+
+/* Free the engine's own device buffers, and the resident corpus if no other
+ * engine shares it (waits for pending work on the device).  NULL is ignored. */
 void rt_engine_destroy(rt_engine *e);
 
 /*

@@ -106,4 +106,5 @@ def test_entry_points_reject_null_engine(lib):
     assert lib.rt_last_hip_error(NULL) == 0
     out = ctypes.c_void_p()
     assert lib.rt_engine_create(0, 8, 8, 1, 0, ctypes.byref(out)) == EINVAL and not out.value
+    assert lib.rt_engine_create_shared(NULL, 8, 1, ctypes.byref(out)) == EINVAL and not out.value
     lib.rt_engine_destroy(NULL)  # ignored

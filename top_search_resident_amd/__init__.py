@@ -41,14 +41,26 @@ class ResidentTopK:
     """One engine: owns all device memory for a resident corpus of up to
     max_n x max_d fp32 rows, top-k up to max_k, batches up to max_q queries."""
 
-    def __init__(self, max_n, max_d, max_k=128, max_q=1, device=0):
+    def __init__(self, max_n, max_d, max_k=128, max_q=1, device=0, _share=None):
         self._lib = _lib.load()
         self._h = ctypes.c_void_p()
-        st = self._lib.rt_engine_create(int(max_n), int(max_d), int(max_k), int(max_q), int(device),
-                                        ctypes.byref(self._h))
-        _check(st, "rt_engine_create")
+        if _share is None:
+            st = self._lib.rt_engine_create(int(max_n), int(max_d), int(max_k), int(max_q), int(device),
+                                            ctypes.byref(self._h))
+            _check(st, "rt_engine_create")
+        else:
+            st = self._lib.rt_engine_create_shared(_share._h, int(max_k), int(max_q), ctypes.byref(self._h))
+            _check(st, "rt_engine_create_shared")
         self.device = int(device)
         self.max_n, self.max_d, self.max_k, self.max_q = int(max_n), int(max_d), int(max_k), int(max_q)
+
+    def shared(self, max_k=None, max_q=None):
+        """A new engine that searches this engine's resident corpus (no copy) with
+        scratch memory of its own, so the two can search concurrently on
+        different streams.  The corpus stays allocated until every engine that
+        shares it is closed."""
+        return ResidentTopK(self.max_n, self.max_d, self.max_k if max_k is None else max_k,
+                            self.max_q if max_q is None else max_q, self.device, _share=self)
 
     # -- lifecycle ---------------------------------------------------------
     def close(self):

@@ -14,7 +14,7 @@ RT_METRIC_DOT, RT_METRIC_COSINE = 0, 1
 
 # Every symbol include/resident_topk.h declares.
 EXPORTS = (
-    "rt_engine_create", "rt_engine_destroy", "upload_corpus_rowmajor", "search_resident",
+    "rt_engine_create", "rt_engine_create_shared", "rt_engine_destroy", "upload_corpus_rowmajor", "search_resident",
     "search_resident_metric", "topk_select", "rt_status_string", "rt_last_hip_error", "rt_profile_enable",
     "rt_profile_read", "rt_engine_info", "rt_check_create", "rt_check_upload",
     "rt_check_search", "rt_check_search_metric", "rt_check_select",
@@ -49,6 +49,7 @@ def load():
     vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
     sig = {
         "rt_engine_create": ([i64, i32, i32, i32, i32, ctypes.POINTER(vp)], ctypes.c_int),
+        "rt_engine_create_shared": ([vp, i32, i32, ctypes.POINTER(vp)], ctypes.c_int),
         "rt_engine_destroy": ([vp], None),
         "upload_corpus_rowmajor": ([vp, vp, i64, i32], ctypes.c_int),
         "search_resident": ([vp, vp, i32, i32, vp, vp, vp], ctypes.c_int),

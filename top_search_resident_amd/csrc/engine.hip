@@ -9,6 +9,7 @@
 // kernels of stream_topk.hip and mfma_scores.hip.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <new>
 
 #include "../../include/resident_topk.h"
@@ -66,15 +67,24 @@ Plan plan_stream(int64_t units, int segments, int kp, int64_t min_per_wave, int 
 
 }  // namespace
 
+// The resident corpus and its row norms.  Engines created with
+// rt_engine_create_shared point at the same one; it is freed with the last of
+// them.
+struct rt_resident {
+    std::atomic<int> refs{1};
+    int64_t max_n = 0;
+    int32_t max_d = 0;
+    int64_t n = 0;            // resident rows (0: nothing uploaded)
+    int32_t d = 0;
+    float *corpus = nullptr;  // max_n x max_d fp32
+    float *rnorm = nullptr;   // L2 norm of every resident row (cosine metric), roundup(max_n, 64) floats
+};
+
 struct rt_engine {
     int device = 0;
     int num_cus = 0;
-    int64_t max_n = 0;
-    int32_t max_d = 0, max_k = 0, max_q = 0;
-    int64_t resident_n = 0;
-    int32_t resident_d = 0;
-    float *corpus = nullptr;
-    float *rnorm = nullptr;   // L2 norm of every resident row (cosine metric), roundup(max_n, 64) floats
+    rt_resident *res = nullptr;
+    int32_t max_k = 0, max_q = 0;
     float *scores = nullptr;  // batched scores, max_q x roundup(max_n, 64); only when max_q > 1
     float *tmax = nullptr;    // per-query maxima of 32-row score tiles, max_q x tile_ld; only when max_q > 1
     int64_t tile_ld = 0;
@@ -156,16 +166,53 @@ void rt_engine_destroy(rt_engine *e) {
     (void)hipGetDevice(&prev);
     (void)hipSetDevice(e->device);
     (void)hipDeviceSynchronize();
-    (void)hipFree(e->corpus);
-    (void)hipFree(e->rnorm);
     (void)hipFree(e->scores);
     (void)hipFree(e->tmax);
     (void)hipFree(e->tree);
     (void)hipFree(e->counters);
     for (auto &ev : e->ev)
         if (ev) (void)hipEventDestroy(ev);
+    if (e->res && e->res->refs.fetch_sub(1) == 1) {
+        (void)hipFree(e->res->corpus);
+        (void)hipFree(e->res->rnorm);
+        delete e->res;
+    }
     (void)hipSetDevice(prev);
     delete e;
+}
+
+static bool dev_alloc(void **p, size_t bytes) {
+    if (hipMalloc(p, bytes) != hipSuccess) {
+        (void)hipGetLastError();
+        return false;
+    }
+    return true;
+}
+
+// Allocate and initialise an engine's own scratch (everything but the resident
+// corpus) on the current device; e->res, device, max_k and max_q are set.
+static rt_status setup_scratch(rt_engine *e) {
+    hipError_t err = hipDeviceGetAttribute(&e->num_cus, hipDeviceAttributeMultiprocessorCount, e->device);
+    if (err != hipSuccess || e->num_cus < 1) e->num_cus = 256;
+    (void)hipGetLastError();
+    const int64_t max_n = e->res->max_n;
+    const int64_t ld = (max_n + 63) / 64 * 64;
+    e->tile_ld = ((max_n + 31) / 32 + 63) / 64 * 64;
+    bool ok = dev_alloc(reinterpret_cast<void **>(&e->tree), sizeof(uint64_t) * (size_t)kTreeRanks) &&
+              dev_alloc(reinterpret_cast<void **>(&e->counters), sizeof(uint32_t) * (size_t)(kMaxQ * kMaxWgsPerSeg));
+    if (ok && e->max_q > 1)
+        ok = dev_alloc(reinterpret_cast<void **>(&e->scores), sizeof(float) * (size_t)e->max_q * (size_t)ld) &&
+             dev_alloc(reinterpret_cast<void **>(&e->tmax), sizeof(float) * (size_t)e->max_q * (size_t)e->tile_ld);
+    if (!ok) return RT_ENOMEM;
+    err = hipMemset(e->counters, 0, sizeof(uint32_t) * (size_t)(kMaxQ * kMaxWgsPerSeg));
+    if (err == hipSuccess) err = rt::prepare_mfma_scores();
+    for (int i = 0; i < 4 && err == hipSuccess; ++i) err = hipEventCreate(&e->ev[i]);
+    if (err == hipSuccess) err = hipDeviceSynchronize();
+    if (err != hipSuccess) {
+        (void)hipGetLastError();
+        return RT_EHIP;
+    }
+    return RT_OK;
 }
 
 rt_status rt_engine_create(int64_t max_n, int32_t max_d, int32_t max_k, int32_t max_q, int32_t device,
@@ -180,53 +227,64 @@ rt_status rt_engine_create(int64_t max_n, int32_t max_d, int32_t max_k, int32_t 
         return device < 0 ? RT_EINVAL : RT_EHIP;
     }
     rt_engine *e = new (std::nothrow) rt_engine();
-    if (!e) return RT_ENOMEM;
+    rt_resident *r = new (std::nothrow) rt_resident();
+    if (!e || !r) {
+        delete e;
+        delete r;
+        return RT_ENOMEM;
+    }
     e->device = device;
-    e->max_n = max_n;
-    e->max_d = max_d;
     e->max_k = max_k;
     e->max_q = max_q;
+    e->res = r;
+    r->max_n = max_n;
+    r->max_d = max_d;
     int prev = 0;
     (void)hipGetDevice(&prev);
     hipError_t err = hipSetDevice(device);
     if (err != hipSuccess) {
-        delete e;
+        rt_engine_destroy(e);
         return hip_fail(nullptr, err);
     }
-    err = hipDeviceGetAttribute(&e->num_cus, hipDeviceAttributeMultiprocessorCount, device);
-    if (err != hipSuccess || e->num_cus < 1) e->num_cus = 256;
-
-    auto alloc = [&](void **p, size_t bytes) -> bool {
-        if (hipMalloc(p, bytes) != hipSuccess) {
-            (void)hipGetLastError();
-            return false;
-        }
-        return true;
-    };
     const int64_t ld = (max_n + 63) / 64 * 64;
-    bool ok = alloc(reinterpret_cast<void **>(&e->corpus), sizeof(float) * (size_t)max_n * (size_t)max_d) &&
-              alloc(reinterpret_cast<void **>(&e->rnorm), sizeof(float) * (size_t)ld) &&
-              alloc(reinterpret_cast<void **>(&e->tree), sizeof(uint64_t) * (size_t)kTreeRanks) &&
-              alloc(reinterpret_cast<void **>(&e->counters), sizeof(uint32_t) * (size_t)(kMaxQ * kMaxWgsPerSeg));
-    e->tile_ld = ((max_n + 31) / 32 + 63) / 64 * 64;
-    if (ok && max_q > 1)
-        ok = alloc(reinterpret_cast<void **>(&e->scores), sizeof(float) * (size_t)max_q * (size_t)ld) &&
-             alloc(reinterpret_cast<void **>(&e->tmax), sizeof(float) * (size_t)max_q * (size_t)e->tile_ld);
-    if (!ok) {
-        rt_engine_destroy(e);
-        (void)hipSetDevice(prev);
-        return RT_ENOMEM;
-    }
-    err = hipMemset(e->counters, 0, sizeof(uint32_t) * (size_t)(kMaxQ * kMaxWgsPerSeg));
-    if (err == hipSuccess) err = hipMemset(e->rnorm, 0, sizeof(float) * (size_t)ld);
-    if (err == hipSuccess) err = rt::prepare_mfma_scores();
-    for (int i = 0; i < 4 && err == hipSuccess; ++i) err = hipEventCreate(&e->ev[i]);
-    if (err == hipSuccess) err = hipDeviceSynchronize();
+    st = (dev_alloc(reinterpret_cast<void **>(&r->corpus), sizeof(float) * (size_t)max_n * (size_t)max_d) &&
+          dev_alloc(reinterpret_cast<void **>(&r->rnorm), sizeof(float) * (size_t)ld))
+             ? RT_OK
+             : RT_ENOMEM;
+    if (st == RT_OK && hipMemset(r->rnorm, 0, sizeof(float) * (size_t)ld) != hipSuccess) st = RT_EHIP;
+    if (st == RT_OK) st = setup_scratch(e);
     (void)hipSetDevice(prev);
-    if (err != hipSuccess) {
+    if (st != RT_OK) {
         rt_engine_destroy(e);
         (void)hipGetLastError();
-        return RT_EHIP;
+        return st;
+    }
+    *out = e;
+    return RT_OK;
+}
+
+rt_status rt_engine_create_shared(rt_engine *other, int32_t max_k, int32_t max_q, rt_engine **out) {
+    if (out == nullptr) return RT_EINVAL;
+    *out = nullptr;
+    if (other == nullptr) return RT_EINVAL;
+    rt_status st = rt_check_create(other->res->max_n, other->res->max_d, max_k, max_q);
+    if (st != RT_OK) return st;
+    rt_engine *e = new (std::nothrow) rt_engine();
+    if (!e) return RT_ENOMEM;
+    e->device = other->device;
+    e->max_k = max_k;
+    e->max_q = max_q;
+    e->res = other->res;
+    e->res->refs.fetch_add(1);
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    hipError_t err = hipSetDevice(e->device);
+    st = (err == hipSuccess) ? setup_scratch(e) : RT_EHIP;
+    (void)hipSetDevice(prev);
+    if (st != RT_OK) {
+        rt_engine_destroy(e);
+        (void)hipGetLastError();
+        return st;
     }
     *out = e;
     return RT_OK;
@@ -234,24 +292,25 @@ rt_status rt_engine_create(int64_t max_n, int32_t max_d, int32_t max_k, int32_t 
 
 rt_status upload_corpus_rowmajor(rt_engine *e, const float *corpus, int64_t n, int32_t d) {
     if (!e) return RT_EINVAL;
-    rt_status st = rt_check_upload(e->max_n, e->max_d, corpus, n, d);
+    rt_resident *r = e->res;
+    rt_status st = rt_check_upload(r->max_n, r->max_d, corpus, n, d);
     if (st != RT_OK) return st;
     int prev = 0;
     (void)hipGetDevice(&prev);
     hipError_t err = hipSetDevice(e->device);
     if (err == hipSuccess)
-        err = hipMemcpy(e->corpus, corpus, sizeof(float) * (size_t)n * (size_t)d, hipMemcpyDefault);
+        err = hipMemcpy(r->corpus, corpus, sizeof(float) * (size_t)n * (size_t)d, hipMemcpyDefault);
     // The rows' L2 norms for the cosine metric, computed once per upload.
-    if (err == hipSuccess) err = rt::launch_row_norms(e->corpus, n, d, e->rnorm, e->num_cus, nullptr);
+    if (err == hipSuccess) err = rt::launch_row_norms(r->corpus, n, d, r->rnorm, e->num_cus, nullptr);
     if (err == hipSuccess) err = hipDeviceSynchronize();
     (void)hipSetDevice(prev);
     if (err != hipSuccess) {
-        e->resident_n = 0;
-        e->resident_d = 0;
+        r->n = 0;
+        r->d = 0;
         return hip_fail(e, err);
     }
-    e->resident_n = n;
-    e->resident_d = d;
+    r->n = n;
+    r->d = d;
     return RT_OK;
 }
 
@@ -287,22 +346,23 @@ rt_status search_resident_metric(rt_engine *e, const float *queries, int32_t q, 
                                  int32_t *out_idx, float *out_scores, void *stream) {
     if (!e) return RT_EINVAL;
     rt_status st =
-        rt_check_search_metric(e->max_k, e->max_q, e->resident_n, queries, q, k, metric, out_idx, out_scores);
+        rt_check_search_metric(e->max_k, e->max_q, e->res->n, queries, q, k, metric, out_idx, out_scores);
     if (st != RT_OK) return st;
     hipStream_t s = static_cast<hipStream_t>(stream);
     int prev = 0;
     (void)hipGetDevice(&prev);
     hipError_t err = hipSetDevice(e->device);
-    const int64_t n = e->resident_n;
-    const int d = e->resident_d;
+    const int64_t n = e->res->n;
+    const int d = e->res->d;
+    const float *corpus = e->res->corpus;
     const int kp = kp_for(k);
-    const float *rnorm = (metric == RT_METRIC_COSINE) ? e->rnorm : nullptr;
+    const float *rnorm = (metric == RT_METRIC_COSINE) ? e->res->rnorm : nullptr;
     const bool batched = q > 1 && e->scores != nullptr && d % 4 == 0 && d <= rt::kMfmaMaxD;
     e->had_batch_kernel = batched;
     if (err == hipSuccess) err = prologue(e, s);
     if (err == hipSuccess && batched) {
         const int64_t ld = (n + 63) / 64 * 64;
-        err = rt::launch_mfma_scores(e->corpus, n, d, queries, q, rnorm, e->scores, ld, e->tmax, e->tile_ld,
+        err = rt::launch_mfma_scores(corpus, n, d, queries, q, rnorm, e->scores, ld, e->tmax, e->tile_ld,
                                      e->num_cus, s);
         if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[3], s);
         if (err == hipSuccess)
@@ -310,7 +370,7 @@ rt_status search_resident_metric(rt_engine *e, const float *queries, int32_t q, 
     } else if (err == hipSuccess) {
         const Plan p = plan_stream(n, q, kp, 32, e->num_cus, kScoreWavesPerCu, rt::gemv_waves(kp));
         const rt::TreeLaunch t = tree_for(e, p, kp, k, 1, out_idx, out_scores, nullptr, 0);
-        err = rt::launch_gemv_topk(e->corpus, n, d, queries, rnorm, q, p.per_wave, p.wgs, t, s);
+        err = rt::launch_gemv_topk(corpus, n, d, queries, rnorm, q, p.per_wave, p.wgs, t, s);
     }
     if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[1], s);
     (void)hipSetDevice(prev);
@@ -369,12 +429,12 @@ rt_status rt_profile_read(rt_engine *e, float *ms3) {
 
 rt_status rt_engine_info(const rt_engine *e, int64_t *out7) {
     if (!e || !out7) return RT_EINVAL;
-    out7[0] = e->max_n;
-    out7[1] = e->max_d;
+    out7[0] = e->res->max_n;
+    out7[1] = e->res->max_d;
     out7[2] = e->max_k;
     out7[3] = e->max_q;
-    out7[4] = e->resident_n;
-    out7[5] = e->resident_d;
+    out7[4] = e->res->n;
+    out7[5] = e->res->d;
     out7[6] = e->device;
     return RT_OK;
 }
