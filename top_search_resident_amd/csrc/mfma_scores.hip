@@ -259,6 +259,12 @@ __global__ __launch_bounds__(NT) void mfma_scores_fixed_kernel(const float *__re
     float4 buf[KPF][4];
 #pragma unroll
     for (int s = 0; s < KPF; ++s) load_chunk(p, s, buf[s]);
+    // Query operands of the chunk being multiplied; the next chunk's are read
+    // from LDS before this chunk's MFMAs are issued, so the MFMAs never wait
+    // on an LDS read issued just before them.
+    float4 acur[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acur[i] = *reinterpret_cast<const float4 *>(qrow + 4 * i);
     for (int64_t t = t_begin; t < t_end; ++t) {
         const float *pn = (t + 1 < t_end) ? row_of(t + 1) : p;  // past the last tile: reload (cached)
         // The query operands are the same for every tile; an opaque per-tile
@@ -277,14 +283,16 @@ __global__ __launch_bounds__(NT) void mfma_scores_fixed_kernel(const float *__re
 #pragma unroll
         for (int j = 0; j < NCK; ++j) {
             const int s = j % KPF;
-            float4 a[4];
+            const int jn = (j + 1 < NCK) ? j + 1 : 0;  // the next tile starts again at chunk 0
+            float4 anext[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) a[i] = *reinterpret_cast<const float4 *>(qt + j * 32 + 4 * i);
+            for (int i = 0; i < 4; ++i) anext[i] = *reinterpret_cast<const float4 *>(qt + jn * 32 + 4 * i);
+            __builtin_amdgcn_sched_barrier(0);  // issue them before this chunk's MFMAs
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    acc[j % ACC] = __builtin_amdgcn_mfma_f32_32x32x2f32(comp(buf[s][i], e), comp(a[i], e),
+                    acc[j % ACC] = __builtin_amdgcn_mfma_f32_32x32x2f32(comp(buf[s][i], e), comp(acur[i], e),
                                                                         acc[j % ACC], 0, 0, 0);
             }
             if (j + KPF < NCK)
@@ -292,6 +300,8 @@ __global__ __launch_bounds__(NT) void mfma_scores_fixed_kernel(const float *__re
             else
                 load_chunk(pn, j + KPF - NCK, buf[s]);
             __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acur[i] = anext[i];
         }
 #pragma unroll
         for (int h = 1; h < ACC; ++h)
