@@ -78,16 +78,22 @@ def cpu_model():
     return "unknown"
 
 
-def time_search(eng, torch, qdev, ks, steps, warmup, profile=True, metric="dot"):
+def time_search(eng, torch, qdev, ks, steps, warmup, profile=True, metric="dot", filtered=False):
     """Sequential single queries; returns per-K lists of host latency (us),
-    whole-call device time and streaming-kernel time (ms)."""
+    whole-call device time and streaming-kernel time (ms) (with `filtered`: the
+    bf16 pass time in place of the streaming-kernel time)."""
+    def search(q, k, oi, os_, stream):
+        if filtered:
+            return eng.search_resident_filtered(q, k, oi, os_, stream=stream)
+        return eng.search_resident(q, k, oi, os_, stream=stream, metric=metric)
+
     n_q = qdev.shape[0]
     outs = {k: (torch.empty((1, k), dtype=torch.int32, device="cuda"),
                 torch.empty((1, k), dtype=torch.float32, device="cuda")) for k in ks}
     stream = torch.cuda.current_stream()
     for i in range(warmup):
         for k in ks:
-            eng.search_resident(qdev[i % n_q:i % n_q + 1], k, *outs[k], stream=stream, metric=metric)
+            search(qdev[i % n_q:i % n_q + 1], k, *outs[k], stream)
     torch.cuda.synchronize()
     eng.profile(profile)
     lat = {k: [] for k in ks}
@@ -99,12 +105,12 @@ def time_search(eng, torch, qdev, ks, steps, warmup, profile=True, metric="dot")
         q = qdev[i % n_q:i % n_q + 1]
         for k in ks:
             s = time.perf_counter_ns()
-            eng.search_resident(q, k, *outs[k], stream=stream, metric=metric)
+            search(q, k, *outs[k], stream)
             stream.synchronize()
             lat[k].append((time.perf_counter_ns() - s) / 1e3)
             if profile:
-                total, _, kern = eng.profile_read()
-                part[k].append(kern)
+                total, first, kern = eng.profile_read()
+                part[k].append(first if filtered else kern)
                 merge[k].append(total)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -112,7 +118,7 @@ def time_search(eng, torch, qdev, ks, steps, warmup, profile=True, metric="dot")
     return wall, lat, part, merge
 
 
-def time_end_to_end(eng, torch, qhost, ks, reps, metric="dot"):
+def time_end_to_end(eng, torch, qhost, ks, reps, metric="dot", filtered=False):
     """Pages-style interval: pinned query H->D, search, K idx + K scores D->H."""
     d = qhost.shape[1]
     pin_q = torch.empty((1, d), dtype=torch.float32).pin_memory()
@@ -129,7 +135,10 @@ def time_end_to_end(eng, torch, qhost, ks, reps, metric="dot"):
             pin_q.copy_(torch.from_numpy(qhost[r % qhost.shape[0]:r % qhost.shape[0] + 1]))
             s = time.perf_counter_ns()
             qdev.copy_(pin_q, non_blocking=True)
-            eng.search_resident(qdev, k, oi, os_, stream=stream, metric=metric)
+            if filtered:
+                eng.search_resident_filtered(qdev, k, oi, os_, stream=stream)
+            else:
+                eng.search_resident(qdev, k, oi, os_, stream=stream, metric=metric)
             hi.copy_(oi, non_blocking=True)
             hs.copy_(os_, non_blocking=True)
             stream.synchronize()
@@ -182,12 +191,20 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
     if args.streams > 1:
         return run_concurrent(args, torch, eng, corpus, qhost, qdev, ks, name, gen_s)
 
-    wall, lat, part, merge = time_search(eng, torch, qdev, ks, args.steps, args.warmup, metric=args.metric)
+    if args.filtered:
+        eng.enable_filtered()
+    wall, lat, part, merge = time_search(eng, torch, qdev, ks, args.steps, args.warmup, metric=args.metric,
+                                         filtered=args.filtered)
     nq = args.steps * len(ks)
     qps = nq / wall
-    # algorithmic bytes per launch: the corpus and the query, plus the rows'
-    # norms for the cosine metric
-    corpus_bytes = n * d * 4 + d * 4 + (n * 4 if args.metric == "cosine" else 0)
+    # algorithmic bytes per launch of the dominant kernel: the corpus and the
+    # query, plus the rows' norms for the cosine metric; for the filtered search
+    # the bf16 pass: the bf16 corpus, the rows' norms and the upper bounds it
+    # writes
+    if args.filtered:
+        corpus_bytes = n * d * 2 + d * 4 + n * 4 + n * 4
+    else:
+        corpus_bytes = n * d * 4 + d * 4 + (n * 4 if args.metric == "cosine" else 0)
     per_k = {}
     all_part = []
     for k in ks:
@@ -204,27 +221,34 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
     avg_ms = float(np.mean(all_part))
     achieved = corpus_bytes / (avg_ms * 1e-3) / 1e9
     line = {
-        "metric": (METRIC if (name, args.metric) == ("c3_1m_1024", "dot")
-                   else f"queries/s + p50 latency ({name}, {args.metric})"),
+        "metric": (METRIC if (name, args.metric, args.filtered) == ("c3_1m_1024", "dot", False)
+                   else f"queries/s + p50 latency ({name}, {'bf16-filtered exact ' if args.filtered else ''}"
+                        f"{args.metric})"),
         "value": qps, "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "f32", "data": "synthetic",
         "config": {"workload": f"{name}: resident {n} x {d} fp32 corpus (Gaussian, L2-normalised rows), "
                                f"sequential single queries, K in {list(ks)}; one step = one query per K"
-                               + ("; cosine metric" if args.metric == "cosine" else ""),
-                   "n": n, "d": d, "ks": list(ks), "queries_per_step": len(ks), "metric": args.metric},
+                               + ("; cosine metric" if args.metric == "cosine" else "")
+                               + ("; bf16-filtered exact search (answers identical to the fp32 scan)"
+                                  if args.filtered else ""),
+                   "n": n, "d": d, "ks": list(ks), "queries_per_step": len(ks), "metric": args.metric,
+                   "filtered": bool(args.filtered)},
         "per_k": per_k,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
                      "traffic": (measured_traffic()
-                                 if (n, d, ks, args.metric) == (1_000_000, 1024, (8, 32, 100), "dot") else None),
+                                 if (n, d, ks, args.metric, args.filtered) == (1_000_000, 1024, (8, 32, 100), "dot", False)
+                                 else None),
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, profiles/)",
-                     "kernel": "gemv_topk_kernel (fused scoring, per-wave top-K lists and merge tree)",
+                     "kernel": ("gemv_bound_kernel (bf16 pass of the filtered search)" if args.filtered else
+                                "gemv_topk_kernel (fused scoring, per-wave top-K lists and merge tree)"),
                      "bytes_per_launch": corpus_bytes, "avg_launch_us": avg_ms * 1e3},
         "input_gen_s": gen_s,
     }
     if args.e2e_reps:
-        line["end_to_end_pcie"] = time_end_to_end(eng, torch, qhost, ks, args.e2e_reps, metric=args.metric)
+        line["end_to_end_pcie"] = time_end_to_end(eng, torch, qhost, ks, args.e2e_reps, metric=args.metric,
+                                                  filtered=args.filtered)
     if not args.no_cpu_baseline:
         sample = min(args.cpu_queries, qhost.shape[0])
         gpu_res = {}
@@ -232,7 +256,10 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
             gi = np.empty((sample, k), np.int32)
             gs = np.empty((sample, k), np.float32)
             for qi in range(sample):
-                a, b = eng.search_resident(qdev[qi:qi + 1], k, metric=args.metric)
+                if args.filtered:
+                    a, b = eng.search_resident_filtered(qdev[qi:qi + 1], k)
+                else:
+                    a, b = eng.search_resident(qdev[qi:qi + 1], k, metric=args.metric)
                 torch.cuda.synchronize()
                 gi[qi], gs[qi] = a.cpu().numpy()[0], b.cpu().numpy()[0]
             gpu_res[k] = (gi, gs)
@@ -450,6 +477,8 @@ def main():
     ap.add_argument("--workload", default="c3_1m_1024")
     ap.add_argument("--metric", default="dot", choices=("dot", "cosine"),
                     help="similarity for the retrieval workloads (the headline line is the inner product)")
+    ap.add_argument("--filtered", action="store_true",
+                    help="single-query workloads: search_resident_filtered (bf16 pass + exact fp32 re-rank)")
     ap.add_argument("--streams", type=int, default=1,
                     help="single-query workloads: engines sharing the corpus, one stream each, searching concurrently")
     ap.add_argument("--num-queries", type=int, default=1000)

@@ -143,6 +143,35 @@ rt_status search_resident_metric(rt_engine *e, const float *queries, int32_t q, 
                                  int32_t *out_idx, float *out_scores, void *stream);
 
 /*
+ * Prepare an engine for search_resident_filtered: allocate, once, a bf16 copy
+ * of the resident corpus (max_n x max_d x 2 bytes, shared by every engine that
+ * shares the corpus, refreshed by each upload) and this engine's scratch for
+ * the filtered search (4 x max_q x roundup(max_n, 64) bytes of row bounds).
+ * Like rt_engine_create, it allocates: call it at set-up, not per query.
+ * RT_EINVAL for NULL, RT_ENOMEM if the memory is not available.
+ */
+rt_status rt_enable_filtered(rt_engine *e);
+
+/*
+ * Exact top-k by inner product, the same answer as search_resident (indices,
+ * order and fp32 scores, bit for bit), reading the fp32 rows only where they
+ * can matter.  "Reduced-precision storage with exact re-rank": a first pass
+ * scores every row from the bf16 copy (half the bytes) and bounds the
+ * difference to the fp32 score from the rounding to bf16 and the fp32
+ * summation error of both sums (with the rows' and the query's L2 norms,
+ * Cauchy-Schwarz); the k-th largest lower bound T is certified to be at most
+ * the k-th largest fp32 score, so only rows whose upper bound reaches T are
+ * scored in fp32 by the second pass -- with the plain path's arithmetic -- and
+ * ranked.  Arguments, layouts and errors as search_resident; RT_ESTATE also
+ * when rt_enable_filtered was not called on this engine.  If the depth is not
+ * a multiple of 8 or above 2048, or a corpus value is not finite in bf16, the
+ * call runs the plain fp32 scan instead (same answer).  Inner product only.
+ * Asynchronous on `stream`.
+ */
+rt_status search_resident_filtered(rt_engine *e, const float *queries, int32_t q, int32_t k,
+                                   int32_t *out_idx, float *out_scores, void *stream);
+
+/*
  * Plain top-k of a raw device array, no scoring ("CUDA Programming Model
  * Series 9: Efficient TopK", sections 2-3: two-stage selection).
  *   values     device, n elements of `dtype` (RT_DTYPE_INT32 or
@@ -169,9 +198,10 @@ int32_t rt_last_hip_error(const rt_engine *e);
  * Kernel timing for measurement.  While enabled (on != 0), every search or
  * select records HIP events on its stream around its kernels; after the stream
  * has finished, rt_profile_read returns the last call's device times in
- * milliseconds: [0] = the whole call, [1] = the batched scoring kernel (0 when
- * the call had none), [2] = the streaming top-K kernel (scoring or raw-array
- * selection, per-block lists and the merge tree), i.e. [0] - [1].  The events
+ * milliseconds: [0] = the whole call, [1] = its first kernel when it ran two
+ * (the batched scoring kernel of a batch, the bf16 pass of a filtered search;
+ * 0 otherwise), [2] = the rest (the streaming top-K kernel: scoring or
+ * raw-array selection, per-block lists and the merge tree), i.e. [0] - [1].  The events
  * are created by rt_engine_create.  RT_EINVAL on NULL arguments.
  */
 rt_status rt_profile_enable(rt_engine *e, int32_t on);

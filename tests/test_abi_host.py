@@ -101,6 +101,8 @@ def test_entry_points_reject_null_engine(lib):
     assert lib.upload_corpus_rowmajor(NULL, P, 10, 4) == EINVAL
     assert lib.search_resident(NULL, P, 1, 1, P, P, NULL) == EINVAL
     assert lib.search_resident_metric(NULL, P, 1, 1, 1, P, P, NULL) == EINVAL
+    assert lib.search_resident_filtered(NULL, P, 1, 1, P, P, NULL) == EINVAL
+    assert lib.rt_enable_filtered(NULL) == EINVAL
     assert lib.topk_select(NULL, P, 0, 10, 1, P, P, NULL) == EINVAL
     assert lib.rt_profile_enable(NULL, 1) == EINVAL
     assert lib.rt_last_hip_error(NULL) == 0

@@ -132,6 +132,35 @@ class ResidentTopK:
         _check(st, "search_resident", self._h)
         return out_idx, out_scores
 
+    def enable_filtered(self):
+        """Allocate the bf16 copy of the corpus and this engine's scratch for
+        search_resident_filtered (once, at set-up)."""
+        _check(self._lib.rt_enable_filtered(self._h), "rt_enable_filtered", self._h)
+
+    def search_resident_filtered(self, queries, k, out_idx=None, out_scores=None, stream=None):
+        """Exact inner-product top-k (the same answer as search_resident) that
+        reads a bf16 copy of the corpus first and the fp32 rows only where their
+        certified score bounds reach the k-th lower bound."""
+        torch = _torch()
+        if queries.dim() == 1:
+            queries = queries.view(1, -1)
+        if queries.dtype != torch.float32 or not queries.is_cuda or not queries.is_contiguous():
+            raise TypeError("queries must be a contiguous float32 CUDA tensor")
+        q = queries.shape[0]
+        if out_idx is None:
+            out_idx = torch.empty((q, k), dtype=torch.int32, device=queries.device)
+        if out_scores is None:
+            out_scores = torch.empty((q, k), dtype=torch.float32, device=queries.device)
+        if out_idx.dtype != torch.int32 or out_scores.dtype != torch.float32:
+            raise TypeError("out_idx must be int32 and out_scores float32")
+        if out_idx.numel() < q * k or out_scores.numel() < q * k:
+            raise ValueError("output buffers are too small")
+        st = self._lib.search_resident_filtered(self._h, ctypes.c_void_p(queries.data_ptr()), int(q), int(k),
+                                                ctypes.c_void_p(out_idx.data_ptr()),
+                                                ctypes.c_void_p(out_scores.data_ptr()), _stream_handle(stream))
+        _check(st, "search_resident_filtered", self._h)
+        return out_idx, out_scores
+
     def topk_select(self, values, k, out_idx=None, out_values=None, stream=None):
         """Top-k of a raw device int32/fp32 1-D tensor, ties to the lower position.
         Returns (idx int32 [k], values [k]) on the device, best-first."""

@@ -15,7 +15,7 @@ RT_METRIC_DOT, RT_METRIC_COSINE = 0, 1
 # Every symbol include/resident_topk.h declares.
 EXPORTS = (
     "rt_engine_create", "rt_engine_create_shared", "rt_engine_destroy", "upload_corpus_rowmajor", "search_resident",
-    "search_resident_metric", "topk_select", "rt_status_string", "rt_last_hip_error", "rt_profile_enable",
+    "search_resident_metric", "rt_enable_filtered", "search_resident_filtered", "topk_select", "rt_status_string", "rt_last_hip_error", "rt_profile_enable",
     "rt_profile_read", "rt_engine_info", "rt_check_create", "rt_check_upload",
     "rt_check_search", "rt_check_search_metric", "rt_check_select",
 )
@@ -54,6 +54,8 @@ def load():
         "upload_corpus_rowmajor": ([vp, vp, i64, i32], ctypes.c_int),
         "search_resident": ([vp, vp, i32, i32, vp, vp, vp], ctypes.c_int),
         "search_resident_metric": ([vp, vp, i32, i32, i32, vp, vp, vp], ctypes.c_int),
+        "rt_enable_filtered": ([vp], ctypes.c_int),
+        "search_resident_filtered": ([vp, vp, i32, i32, vp, vp, vp], ctypes.c_int),
         "topk_select": ([vp, vp, i32, i64, i32, vp, vp, vp], ctypes.c_int),
         "rt_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "rt_last_hip_error": ([vp], i32),

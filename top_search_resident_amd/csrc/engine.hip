@@ -9,6 +9,8 @@
 // kernels of stream_topk.hip and mfma_scores.hip.
 #include <hip/hip_runtime.h>
 
+#include <math.h>
+
 #include <atomic>
 #include <new>
 
@@ -78,6 +80,9 @@ struct rt_resident {
     int32_t d = 0;
     float *corpus = nullptr;  // max_n x max_d fp32
     float *rnorm = nullptr;   // L2 norm of every resident row (cosine metric), roundup(max_n, 64) floats
+    uint16_t *corpus16 = nullptr;  // bf16 copy, max_n x max_d (after rt_enable_filtered)
+    uint32_t *bad16 = nullptr;     // set by the conversion when a value is not finite in bf16
+    bool copy16_ok = false;        // the bf16 copy matches the resident corpus and is usable
 };
 
 struct rt_engine {
@@ -90,6 +95,8 @@ struct rt_engine {
     int64_t tile_ld = 0;
     uint64_t *tree = nullptr;       // kTreeRanks merge-tree ranks
     uint32_t *counters = nullptr;   // kMaxQ x kMaxWgsPerSeg arrival counters
+    float *ubuf = nullptr;          // filtered search: max_q x roundup(max_n, 64) upper bounds
+    float *thr = nullptr;           // filtered search: max_q thresholds
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
     bool profiling = false;
     bool had_batch_kernel = false;
@@ -170,11 +177,15 @@ void rt_engine_destroy(rt_engine *e) {
     (void)hipFree(e->tmax);
     (void)hipFree(e->tree);
     (void)hipFree(e->counters);
+    (void)hipFree(e->ubuf);
+    (void)hipFree(e->thr);
     for (auto &ev : e->ev)
         if (ev) (void)hipEventDestroy(ev);
     if (e->res && e->res->refs.fetch_sub(1) == 1) {
         (void)hipFree(e->res->corpus);
         (void)hipFree(e->res->rnorm);
+        (void)hipFree(e->res->corpus16);
+        (void)hipFree(e->res->bad16);
         delete e->res;
     }
     (void)hipSetDevice(prev);
@@ -290,6 +301,18 @@ rt_status rt_engine_create_shared(rt_engine *other, int32_t max_k, int32_t max_q
     return RT_OK;
 }
 
+// Rebuild the bf16 copy of the resident rows (synchronous); *ok tells whether
+// every value is finite in bf16, so that the filtered search's bounds hold.
+static hipError_t refresh_copy16(rt_resident *r, int64_t n, int32_t d, int num_cus, bool *ok) {
+    *ok = false;
+    hipError_t err = hipMemset(r->bad16, 0, sizeof(uint32_t));
+    if (err == hipSuccess) err = rt::launch_to_bf16(r->corpus, r->corpus16, n * (int64_t)d, r->bad16, num_cus, nullptr);
+    uint32_t bad = 1;
+    if (err == hipSuccess) err = hipMemcpy(&bad, r->bad16, sizeof(uint32_t), hipMemcpyDeviceToHost);
+    if (err == hipSuccess) *ok = (bad == 0);
+    return err;
+}
+
 rt_status upload_corpus_rowmajor(rt_engine *e, const float *corpus, int64_t n, int32_t d) {
     if (!e) return RT_EINVAL;
     rt_resident *r = e->res;
@@ -300,8 +323,12 @@ rt_status upload_corpus_rowmajor(rt_engine *e, const float *corpus, int64_t n, i
     hipError_t err = hipSetDevice(e->device);
     if (err == hipSuccess)
         err = hipMemcpy(r->corpus, corpus, sizeof(float) * (size_t)n * (size_t)d, hipMemcpyDefault);
-    // The rows' L2 norms for the cosine metric, computed once per upload.
+    // The rows' L2 norms for the cosine metric and the filtered search,
+    // computed once per upload.
     if (err == hipSuccess) err = rt::launch_row_norms(r->corpus, n, d, r->rnorm, e->num_cus, nullptr);
+    r->copy16_ok = false;
+    bool ok16 = false;
+    if (err == hipSuccess && r->corpus16) err = refresh_copy16(r, n, d, e->num_cus, &ok16);
     if (err == hipSuccess) err = hipDeviceSynchronize();
     (void)hipSetDevice(prev);
     if (err != hipSuccess) {
@@ -311,7 +338,42 @@ rt_status upload_corpus_rowmajor(rt_engine *e, const float *corpus, int64_t n, i
     }
     r->n = n;
     r->d = d;
+    r->copy16_ok = ok16;
     return RT_OK;
+}
+
+rt_status rt_enable_filtered(rt_engine *e) {
+    if (!e) return RT_EINVAL;
+    rt_resident *r = e->res;
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    hipError_t err = hipSetDevice(e->device);
+    rt_status st = RT_OK;
+    const int64_t ld = (r->max_n + 63) / 64 * 64;
+    if (err == hipSuccess && !r->corpus16) {
+        if (!dev_alloc(reinterpret_cast<void **>(&r->corpus16),
+                       sizeof(uint16_t) * (size_t)r->max_n * (size_t)r->max_d) ||
+            !dev_alloc(reinterpret_cast<void **>(&r->bad16), sizeof(uint32_t))) {
+            (void)hipFree(r->corpus16);
+            r->corpus16 = nullptr;
+            st = RT_ENOMEM;
+        } else if (r->n > 0) {
+            bool ok16 = false;
+            err = refresh_copy16(r, r->n, r->d, e->num_cus, &ok16);
+            if (err == hipSuccess) r->copy16_ok = ok16;
+        }
+    }
+    if (err == hipSuccess && st == RT_OK && !e->ubuf) {
+        if (!dev_alloc(reinterpret_cast<void **>(&e->ubuf), sizeof(float) * (size_t)e->max_q * (size_t)ld) ||
+            !dev_alloc(reinterpret_cast<void **>(&e->thr), sizeof(float) * (size_t)e->max_q)) {
+            (void)hipFree(e->ubuf);
+            e->ubuf = nullptr;
+            st = RT_ENOMEM;
+        }
+    }
+    (void)hipSetDevice(prev);
+    if (err != hipSuccess) return hip_fail(e, err);
+    return st;
 }
 
 static rt::TreeLaunch tree_for(rt_engine *e, const Plan &p, int kp, int k, int mode, int32_t *out_idx,
@@ -381,6 +443,45 @@ rt_status search_resident_metric(rt_engine *e, const float *queries, int32_t q, 
 rt_status search_resident(rt_engine *e, const float *queries, int32_t q, int32_t k, int32_t *out_idx,
                           float *out_scores, void *stream) {
     return search_resident_metric(e, queries, q, k, RT_METRIC_DOT, out_idx, out_scores, stream);
+}
+
+rt_status search_resident_filtered(rt_engine *e, const float *queries, int32_t q, int32_t k, int32_t *out_idx,
+                                   float *out_scores, void *stream) {
+    if (!e) return RT_EINVAL;
+    rt_status st = rt_check_search(e->max_k, e->max_q, e->res->n, queries, q, k, out_idx, out_scores);
+    if (st != RT_OK) return st;
+    if (!e->ubuf) return RT_ESTATE;  // rt_enable_filtered was not called on this engine
+    rt_resident *r = e->res;
+    const int64_t n = r->n;
+    const int d = r->d;
+    if (!r->copy16_ok || !rt::filtered_search_ok(d))  // same answer through the plain scan
+        return search_resident_metric(e, queries, q, k, RT_METRIC_DOT, out_idx, out_scores, stream);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    hipError_t err = hipSetDevice(e->device);
+    const int kp = kp_for(k);
+    e->had_batch_kernel = false;
+    if (err == hipSuccess) err = prologue(e, s);
+    if (err == hipSuccess) {
+        const Plan p1 = plan_stream(n, q, kp, 32, e->num_cus, kScoreWavesPerCu, rt::gemv_waves(kp));
+        const Plan p2 = plan_stream(n, q, kp, 512, e->num_cus, kScoreWavesPerCu, rt::gemv_waves(kp));
+        const rt::TreeLaunch t1 = tree_for(e, p1, kp, k, 3, nullptr, e->thr, nullptr, 0);
+        const rt::TreeLaunch t2 = tree_for(e, p2, kp, k, 1, out_idx, out_scores, nullptr, 0);
+        rt::FilterLaunch f;
+        f.cb = rt::filter_bound_factor(d);
+        f.delta = ldexpf((float)d, -126);
+        f.ubuf = e->ubuf;
+        f.uld = (r->max_n + 63) / 64 * 64;
+        f.thr = e->thr;
+        e->had_batch_kernel = e->profiling;
+        err = rt::launch_filtered_search(r->corpus, r->corpus16, r->rnorm, n, d, queries, q, p1.per_wave, p1.wgs, t1,
+                                         p2.per_wave, p2.wgs, t2, f, e->profiling ? e->ev[3] : nullptr, s);
+    }
+    if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[1], s);
+    (void)hipSetDevice(prev);
+    if (err != hipSuccess) return hip_fail(e, err);
+    return RT_OK;
 }
 
 rt_status topk_select(rt_engine *e, const void *values, int32_t dtype, int64_t n, int32_t k, int32_t *out_idx,

@@ -1,0 +1,308 @@
+// filter_topk.hpp -- exact inner-product top-K that reads a bf16 copy of the
+// corpus first and the fp32 rows only where they can matter (gfx950).
+//
+// "GPU-Resident Top-K for Agentic RAG" (A. Banerjee) scores every row in fp32
+// (section 4, Step 2); the scan is bound by reading N x D x 4 bytes.  With a
+// bf16 copy of the corpus resident as well, a first pass reads half the bytes:
+// for row i it computes a_i = sum_j bf16(x_ij) q_j in fp32 and a bound e_i with
+// |a_i - s_i| <= e_i, where s_i is the fp32 score the plain path computes.
+// The bound follows from the rounding of x to bf16 (relative 2^-9) and from
+// the fp32 summation error of both sums (gamma_D = D u / (1 - D u) times the
+// sum of |terms|), with sum_j |x_ij q_j| <= |x_i| |q| (Cauchy-Schwarz):
+//     e_i = |x_i| |q| (2^-9 + gamma_D (2 + 2^-9)), rounded up (host: cb),
+// plus d 2^-126 max(|q|, 1), which covers the absolute rounding of subnormal
+// values and products.  The first pass finds T, the k-th largest lower bound
+// a_i - e_i (k rows have s_i >= T), and stores every upper bound a_i + e_i.  Any row with a_i + e_i < T has s_i < T <= the k-th
+// largest s, so the top-k by s lies among the rows with a_i + e_i >= T: the
+// second pass re-scores exactly those rows in fp32 with the plain path's
+// arithmetic (lane_chain + group_sum) and selects among them.  The answer is
+// the plain path's answer, bit for bit.  For Gaussian unit rows at 1M x 1024
+// the band [T - 2 e, T] holds about a hundred rows, so the second pass reads
+// ~4 MB of bounds and a few hundred fp32 rows.
+#pragma once
+#include "stream_topk.hpp"
+
+namespace rt {
+
+// Extra arguments of the two passes.
+struct FilterArgs {
+    float cb;        // bound factor: e_i = cb |q| |x_i| + delta
+    float delta;     // absolute slack for subnormal values, times max(|q|, 1)
+    float *ubuf;     // [segments][uld] upper bounds a_i + e_i (pass 1 writes, pass 2 reads)
+    int64_t uld;
+    float *thr;      // [segments] T, the k-th largest lower bound (written by pass 1's tree)
+};
+
+// bf16 -> fp32 of the two halves of a 32-bit word.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Pass 1.  Lane-group layout as gemv_topk_kernel, over 16-byte blocks of 8 bf16
+// (d8 = d / 8 blocks per row): lane g of a group of G = 2^LG lanes owns blocks
+// g, g + G, ... (L loads).  Loads always run ahead (P = 2 or 4 steps): a bf16
+// step carries half the bytes of an fp32 one, and with loads at use the pass
+// reached only 4.7 TB/s at 1M x 1024 (432 us; 326 us with P = 2, 320 us with
+// P = 4, measured on MI355X).  Per row: a (fp32 FMA chain per lane, group_sum), the
+// bound e, the upper bound written to ubuf, the lower bound ranked by the wave
+// selectors; the merge tree's root writes the k-th lower bound to thr[seg].
+template <int LG, int L, int R, int P>
+__global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_bound_kernel(
+    const uint16_t *__restrict__ corpus16, int64_t n, int d, const float *__restrict__ queries,
+    const float *__restrict__ rnorm, int64_t rows_per_wave, TreeArgs ta, FilterArgs fa) {
+    constexpr int G = 1 << LG;
+    constexpr int RPS = 64 >> LG;
+    constexpr int U = RowUnroll<L>::value;
+    constexpr int STEP = RPS * U;
+    constexpr int SLOTS = P > 0 ? P : 1;
+    constexpr int W = gemv_waves(64 * R);
+    __shared__ uint64_t stage[W][128];
+    __shared__ uint64_t sm[kTreeEntries];
+    __shared__ MergeScratch ms;
+
+    const int seg = blockIdx.y;
+    const int lane = lane_id();
+    const int wv = wave_in_group();
+    const int64_t wave = (int64_t)blockIdx.x * W + wv;
+    const int g = lane & (G - 1);
+    const int h = lane >> LG;
+    const int d8 = d >> 3;
+    const float *qrow = queries + (int64_t)seg * d;
+    uint64_t *const my_stage = stage[wv];
+    float *const ub = fa.ubuf + (int64_t)seg * fa.uld;
+
+    WaveSelector<R> sel;
+    sel.init(ta.k);
+    const float qnorm = wave_l2_norm(qrow, d);
+    const float eq = fa.cb * qnorm;
+    const float dl = fa.delta * fmaxf(qnorm, 1.f);
+
+    // The eight query values of each of this lane's blocks; blocks past the row
+    // end load the last block and are and-ed with a zero mask.
+    float4 qa[L], qb[L];
+    int colc[L];
+    uint32_t cmask[L];
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+        const int col = j * G + g;
+        const bool in = col < d8;
+        colc[j] = in ? col : d8 - 1;
+        cmask[j] = in ? 0xffffffffu : 0u;
+        const float4 *q4 = reinterpret_cast<const float4 *>(qrow) + 2 * colc[j];
+        qa[j] = in ? q4[0] : make_float4(0.f, 0.f, 0.f, 0.f);
+        qb[j] = in ? q4[1] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
+    const int64_t r_begin = wave * rows_per_wave;
+    const int64_t r_end = (r_begin + rows_per_wave < n) ? r_begin + rows_per_wave : n;
+    if (r_begin < r_end) {
+        const uint4 *__restrict__ c16 = reinterpret_cast<const uint4 *>(corpus16);
+        const int64_t last = r_end - 1;
+        uint4 x[SLOTS][U][L];
+        float rn[SLOTS][U];
+        auto load_step = [&](int s, int64_t r0) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                int64_t row = r0 + u * RPS + h;
+                row = row < last ? row : last;
+                const uint4 *p = c16 + row * d8;
+#pragma unroll
+                for (int j = 0; j < L; ++j) x[s][u][j] = load_nt(p + colc[j]);
+                rn[s][u] = rnorm[row];
+            }
+        };
+        auto consume = [&](int s, int64_t rs) {
+            float lo[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                float a = 0.f;
+#pragma unroll
+                for (int j = 0; j < L; ++j) {
+                    uint4 v = x[s][u][j];
+                    v.x &= cmask[j];
+                    v.y &= cmask[j];
+                    v.z &= cmask[j];
+                    v.w &= cmask[j];
+                    a = fmaf(bf16_lo(v.x), qa[j].x, a);
+                    a = fmaf(bf16_hi(v.x), qa[j].y, a);
+                    a = fmaf(bf16_lo(v.y), qa[j].z, a);
+                    a = fmaf(bf16_hi(v.y), qa[j].w, a);
+                    a = fmaf(bf16_lo(v.z), qb[j].x, a);
+                    a = fmaf(bf16_hi(v.z), qb[j].y, a);
+                    a = fmaf(bf16_lo(v.w), qb[j].z, a);
+                    a = fmaf(bf16_hi(v.w), qb[j].w, a);
+                }
+                a = group_sum(a, LG);
+                const float e = fmaf(eq, rn[s][u], dl);
+                const int64_t row = rs + u * RPS + h;
+                if (g == 0 && row < r_end) ub[row] = a + e;
+                lo[u] = a - e;
+            }
+            if constexpr (P > 0) {
+                load_step(s, rs + P * STEP);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t row = rs + u * RPS + h;
+                const bool valid = (g == 0) && (row < r_end);
+                const uint64_t rank = make_rank(order_key_f32(lo[u]), (uint32_t)row);
+                sel.offer(my_stage, rank, valid && rank > sel.thr);
+            }
+        };
+        if constexpr (P == 0) {
+            for (int64_t r0 = r_begin; r0 < r_end; r0 += STEP) {
+                load_step(0, r0);
+                consume(0, r0);
+            }
+        } else {
+#pragma unroll
+            for (int s = 0; s < P; ++s) {
+                load_step(s, r_begin + s * STEP);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            for (int64_t r0 = r_begin; r0 < r_end; r0 += P * STEP) {
+#pragma unroll
+                for (int s = 0; s < P; ++s) consume(s, r0 + s * STEP);
+            }
+        }
+    }
+    sel.finish(my_stage);
+    finish_workgroup<R, W * 64>(sel, sm, &ms, ta, seg);
+}
+
+// Pass 2.  A wave takes rows_per_wave rows in blocks of 64: every lane reads one
+// upper bound (eight blocks' bounds are loaded at once), a ballot lists the rows
+// reaching T, and the wave's lane groups score those rows -- RPS of them at a
+// time -- exactly as gemv_topk_kernel does (lane_chain + group_sum with the same
+// shape), then offer them to the selectors.  Rows below T are never read.
+template <int LG, int L, int R>
+__global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_filtered_kernel(
+    const float *__restrict__ corpus, int64_t n, int d, const float *__restrict__ queries,
+    int64_t rows_per_wave, TreeArgs ta, FilterArgs fa) {
+    constexpr int G = 1 << LG;
+    constexpr int RPS = 64 >> LG;
+    constexpr int NB = 8;  // blocks of 64 bounds loaded at once
+    constexpr int W = gemv_waves(64 * R);
+    __shared__ uint64_t stage[W][128];
+    __shared__ uint64_t sm[kTreeEntries];
+    __shared__ MergeScratch ms;
+
+    const int seg = blockIdx.y;
+    const int lane = lane_id();
+    const int wv = wave_in_group();
+    const int64_t wave = (int64_t)blockIdx.x * W + wv;
+    const int g = lane & (G - 1);
+    const int h = lane >> LG;
+    const int d4 = d >> 2;
+    const float4 *__restrict__ q4 = reinterpret_cast<const float4 *>(queries + (int64_t)seg * d);
+    const float4 *__restrict__ c4 = reinterpret_cast<const float4 *>(corpus);
+    const float *__restrict__ ub = fa.ubuf + (int64_t)seg * fa.uld;
+    uint64_t *const my_stage = stage[wv];
+
+    WaveSelector<R> sel;
+    sel.init(ta.k);
+    const float T = fa.thr[seg];
+
+    float4 qv[L];
+    int colc[L];
+    uint32_t cmask[L];
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+        const int col = j * G + g;
+        colc[j] = (col < d4) ? col : d4 - 1;
+        cmask[j] = (col < d4) ? 0xffffffffu : 0u;
+        qv[j] = (col < d4) ? q4[col] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
+    const int64_t r_begin = wave * rows_per_wave;
+    const int64_t r_end = (r_begin + rows_per_wave < n) ? r_begin + rows_per_wave : n;
+    for (int64_t b0 = r_begin; b0 < r_end; b0 += (int64_t)NB * 64) {
+        float uu[NB];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int64_t row = b0 + b * 64 + lane;
+            uu[b] = ub[row < r_end ? row : r_end - 1];
+        }
+#pragma unroll
+        for (int b = 0; b < NB; ++b) {
+            const int64_t row0 = b0 + b * 64;
+            uint64_t m = __ballot(row0 + lane < r_end && uu[b] >= T);
+            while (m != 0) {  // wave-uniform
+                // group h takes the h-th remaining candidate
+                int mine = -1;
+#pragma unroll
+                for (int i = 0; i < RPS; ++i) {
+                    if (m != 0) {
+                        const int bit = __builtin_ctzll(m);
+                        m &= m - 1;
+                        if (i == h) mine = bit;
+                    }
+                }
+                const int64_t row = row0 + (mine >= 0 ? mine : 0);
+                float4 x[L];
+#pragma unroll
+                for (int j = 0; j < L; ++j) x[j] = c4[row * d4 + colc[j]];
+                const float s = group_sum(lane_chain<G, L>(x, qv, cmask), LG);
+                const bool valid = (g == 0) && (mine >= 0);
+                const uint64_t rank = make_rank(order_key_f32(s), (uint32_t)row);
+                sel.offer(my_stage, rank, valid && rank > sel.thr);
+            }
+        }
+    }
+    sel.finish(my_stage);
+    finish_workgroup<R, W * 64>(sel, sm, &ms, ta, seg);
+}
+
+inline FilterArgs make_filter(const FilterLaunch &f) {
+    FilterArgs fa;
+    fa.cb = f.cb;
+    fa.delta = f.delta;
+    fa.ubuf = f.ubuf;
+    fa.uld = f.uld;
+    fa.thr = f.thr;
+    return fa;
+}
+
+// Launchers for lists of 64*R entries (shapes as RT_GEMV_SHAPES; pass 1 over
+// 8-element bf16 blocks, pass 2 over float4 columns).
+// `ahead`: short row ranges per wave (two steps ahead), else four.
+template <int R>
+hipError_t launch_bound_r(int lg, int L, bool ahead, dim3 grid, hipStream_t s, const uint16_t *corpus16, int64_t n,
+                          int d, const float *queries, const float *rnorm, int64_t per_wave, const TreeLaunch &t,
+                          const FilterLaunch &f) {
+    const TreeArgs ta = make_tree(t);
+    const FilterArgs fa = make_filter(f);
+    const dim3 block(64 * gemv_waves(64 * R));
+#define RT_SHAPE(LGV, LV)                                                                                         \
+    if (lg == LGV && L == LV) {                                                                                   \
+        if (ahead)                                                                                                \
+            hipLaunchKernelGGL((gemv_bound_kernel<LGV, LV, R, 2>), grid, block, 0, s, corpus16, n, d, queries,    \
+                               rnorm, per_wave, ta, fa);                                                          \
+        else                                                                                                      \
+            hipLaunchKernelGGL((gemv_bound_kernel<LGV, LV, R, 4>), grid, block, 0, s, corpus16, n, d, queries,    \
+                               rnorm, per_wave, ta, fa);                                                          \
+        return hipGetLastError();                                                                                 \
+    }
+    RT_GEMV_SHAPES(RT_SHAPE)
+#undef RT_SHAPE
+    return hipErrorInvalidValue;
+}
+
+template <int R>
+hipError_t launch_filtered_r(int lg, int L, dim3 grid, hipStream_t s, const float *corpus, int64_t n, int d,
+                             const float *queries, int64_t per_wave, const TreeLaunch &t, const FilterLaunch &f) {
+    const TreeArgs ta = make_tree(t);
+    const FilterArgs fa = make_filter(f);
+    const dim3 block(64 * gemv_waves(64 * R));
+#define RT_SHAPE(LGV, LV)                                                                                         \
+    if (lg == LGV && L == LV) {                                                                                   \
+        hipLaunchKernelGGL((gemv_filtered_kernel<LGV, LV, R>), grid, block, 0, s, corpus, n, d, queries,          \
+                           per_wave, ta, fa);                                                                     \
+        return hipGetLastError();                                                                                 \
+    }
+    RT_GEMV_SHAPES(RT_SHAPE)
+#undef RT_SHAPE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace rt

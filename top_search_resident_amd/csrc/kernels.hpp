@@ -36,12 +36,44 @@ struct TreeLaunch {
     int seg_ctr_stride;        // >= workgroups_per_segment
     int kp;                    // list length: power of two in [64, 1024], >= k
     int k;
-    int mode;                  // 1: search (index + fp32 score); 2: select (index + source element)
+    int mode;                  // 1: search (index + fp32 score); 2: select (index + source element);
+                               // 3: only the k-th entry's fp32 value (to out_val[segment])
     int32_t *out_idx;          // [segments][k]
     void *out_val;             // [segments][k] 32-bit values
     const void *src;           // mode 2: the selected-from array
     int64_t src_seg_stride;    // mode 2: elements between segments of src
 };
+
+// The bf16-filtered exact search (filter_topk.hpp): bound factor and scratch.
+struct FilterLaunch {
+    float cb;        // e_i = cb |q| |x_i| + delta bounds |bf16 score - fp32 score|
+    float delta;
+    float *ubuf;     // [segments][uld] upper bounds, written by pass 1
+    int64_t uld;
+    float *thr;      // [segments] k-th largest lower bound, written by pass 1
+};
+
+// Bound factor cb for depth d (fp64 on the host, rounded up; see filter_topk.hpp).
+float filter_bound_factor(int d);
+// Depths the filtered search handles: d % 8 == 0 and the fp32 fast-path shapes.
+bool filtered_search_ok(int d);
+// Lane-group shape (G = 2^log2g lanes, L 16-byte loads per lane) for rows of
+// `blocks` 16-byte blocks (blocks <= 512).
+void pick_gemv_shape(int blocks, int *log2g, int *L);
+
+// Exact top-k by inner product for `segments` queries through the bf16 copy
+// (pass 1: bounds and the threshold) and the fp32 rows that reach it (pass 2).
+// d % 8 == 0.  Grids (wgs1 or wgs2, segments).  `between` (may be null) is
+// recorded on the stream after pass 1.
+hipError_t launch_filtered_search(const float *corpus, const uint16_t *corpus16, const float *rnorm, int64_t n,
+                                  int d, const float *queries, int segments, int64_t rows_per_wave1, int wgs1,
+                                  const TreeLaunch &t1, int64_t rows_per_wave2, int wgs2, const TreeLaunch &t2,
+                                  const FilterLaunch &f, hipEvent_t between, hipStream_t stream);
+
+// corpus16[i] = bf16 of corpus[i] (round to nearest even), i < count; *bad is set
+// to 1 if any value is not finite or rounds to infinity (the caller clears it).
+hipError_t launch_to_bf16(const float *corpus, uint16_t *corpus16, int64_t count, uint32_t *bad, int num_cus,
+                          hipStream_t stream);
 
 // Entries between consecutive lists in the merge tree for top-k with lists of
 // kp entries: the smallest power of two >= k when k <= 32 (only the first k

@@ -32,9 +32,9 @@ int tree_stride(int k, int kp) {
 }
 
 // Pick the lane-group width G = 2^lg (<= 64) and loads per lane L (from
-// {1, 2, 3, 4, 6, 8}) that waste the fewest lane slots on a row, preferring wide
-// groups on ties.
-static void pick_group(int d4, int *log2g, int *L) {
+// {1, 2, 3, 4, 6, 8}) that waste the fewest lane slots on a row of d4 16-byte
+// blocks, preferring wide groups on ties.
+void pick_gemv_shape(int d4, int *log2g, int *L) {
     static const int Ls[6] = {1, 2, 3, 4, 6, 8};
     int best_waste = 1 << 30, best_lg = 6, best_L = 8;
     for (int lg = 6; lg >= 0; --lg) {
@@ -74,7 +74,7 @@ hipError_t launch_gemv_topk(const float *corpus, int64_t n, int d, const float *
     const dim3 grid(wgs_per_seg, segments);
     const bool fast = gemv_fast_path_ok(d);
     int lg = 6, L = 8;
-    if (fast) pick_group(d / 4, &lg, &L);
+    if (fast) pick_gemv_shape(d / 4, &lg, &L);
     if (rnorm != nullptr)
         return dispatch_gemv<true>(fast, lg, L, grid, stream, corpus, n, d, queries, rnorm, rows_per_wave, t);
     return dispatch_gemv<false>(fast, lg, L, grid, stream, corpus, n, d, queries, nullptr, rows_per_wave, t);

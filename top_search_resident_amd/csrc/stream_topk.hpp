@@ -48,7 +48,8 @@ struct TreeArgs {
     int fan;                 // lists merged per tree node (power of two, fan * kc <= kTreeEntries)
     int kc;                  // list stride in the tree: smallest power of two >= k if k <= 32, else Kp
     int k;
-    int mode;                // 1: write index + fp32 score from the rank; 2: index + source element
+    int mode;                // 1: index + fp32 score from the rank; 2: index + source element;
+                             // 3: only the k-th entry's fp32 value, to out_val[seg]
     int32_t *out_idx;        // [segments][k]
     uint32_t *out_val;       // [segments][k]
     const uint32_t *src;     // mode 2: the array the ranks index into
@@ -56,6 +57,10 @@ struct TreeArgs {
 };
 
 __device__ __forceinline__ void write_output(const TreeArgs &ta, int seg, int r, uint64_t v) {
+    if (ta.mode == 3) {  // only the k-th entry's value, as fp32
+        if (r == ta.k - 1) ta.out_val[seg] = __float_as_uint(f32_of_order_key(rank_key(v)));
+        return;
+    }
     const uint32_t idx = rank_index(v);
     ta.out_idx[(int64_t)seg * ta.k + r] = (int32_t)idx;
     ta.out_val[(int64_t)seg * ta.k + r] =
@@ -256,6 +261,34 @@ __device__ __forceinline__ void finish_workgroup(WaveSelector<R> &sel, uint64_t 
 
 // ---------------------------------------------------------------- scoring
 
+// Per-lane part of an fp32 row's inner product: the FMA chain over this lane's
+// L float4 columns (components x, y, z, w, in order), columns past the row end
+// masked to zero (their bits are and-ed with a zero mask: a select or branch on
+// a loaded register makes the compiler wait for every outstanding load first).
+// group_sum of it over the row's lane group is the row's score.  Every kernel
+// that scores fp32 rows with a lane-group shape goes through this function, so
+// they all compute the same bits for the same row.
+template <int G, int L>
+__device__ __forceinline__ float lane_chain(const float4 (&x)[L], const float4 (&qv)[L],
+                                            const uint32_t (&cmask)[L]) {
+    float a = 0.f;
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+        float4 v = x[j];
+        if constexpr (G * L > 4) {  // a shape that can be padded
+            v.x = __uint_as_float(__float_as_uint(v.x) & cmask[j]);
+            v.y = __uint_as_float(__float_as_uint(v.y) & cmask[j]);
+            v.z = __uint_as_float(__float_as_uint(v.z) & cmask[j]);
+            v.w = __uint_as_float(__float_as_uint(v.w) & cmask[j]);
+        }
+        a = fmaf(v.x, qv[j].x, a);
+        a = fmaf(v.y, qv[j].y, a);
+        a = fmaf(v.z, qv[j].z, a);
+        a = fmaf(v.w, qv[j].w, a);
+    }
+    return a;
+}
+
 // Rows each lane group takes per step: one, or two for rows of a single float4
 // per lane.
 template <int L>
@@ -353,22 +386,7 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_topk_kernel(
             float acc[U];
 #pragma unroll
             for (int u = 0; u < U; ++u) {
-                float a = 0.f;
-#pragma unroll
-                for (int j = 0; j < L; ++j) {
-                    float4 v = x[s][u][j];
-                    if constexpr (G * L > 4) {  // a shape that can be padded
-                        v.x = __uint_as_float(__float_as_uint(v.x) & cmask[j]);
-                        v.y = __uint_as_float(__float_as_uint(v.y) & cmask[j]);
-                        v.z = __uint_as_float(__float_as_uint(v.z) & cmask[j]);
-                        v.w = __uint_as_float(__float_as_uint(v.w) & cmask[j]);
-                    }
-                    a = fmaf(v.x, qv[j].x, a);
-                    a = fmaf(v.y, qv[j].y, a);
-                    a = fmaf(v.z, qv[j].z, a);
-                    a = fmaf(v.w, qv[j].w, a);
-                }
-                acc[u] = group_sum(a, LG);
+                acc[u] = group_sum(lane_chain<G, L>(x[s][u], qv, cmask), LG);
                 if constexpr (COS) acc[u] = cosine_of(acc[u], qnorm, rn[s][u]);
             }
             if constexpr (P > 0) {
