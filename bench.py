@@ -19,6 +19,11 @@ cpu_baseline: the CPU oracle (fp64 dots + full sort) timed on this host's cores
 on a bounded sample of the same queries; the same sample's GPU answers are
 checked against it (R1-R4) before the line is printed.
 
+filtered_exact: the same queries through search_resident_filtered (a bf16 copy
+scanned first, fp32 rows re-scored only where certified bounds reach the k-th
+lower bound); its answers are checked to equal the plain scan's bit for bit
+before it is timed.  Reported beside `value`, which stays the plain fp32 scan.
+
 Other workloads (--workload): c1_10k_384, c2_50k_768, c2_100k_768,
 c4_1e8_int32, c5_q32_500k_768 -- parity-test configurations, available for
 measurement; the default line is c3_1m_1024.
@@ -249,6 +254,8 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
     if args.e2e_reps:
         line["end_to_end_pcie"] = time_end_to_end(eng, torch, qhost, ks, args.e2e_reps, metric=args.metric,
                                                   filtered=args.filtered)
+    if not args.filtered and args.metric == "dot" and not args.no_filtered_leg and d % 8 == 0:
+        line["filtered_exact"] = filtered_leg(args, torch, eng, qdev, ks, n, d)
     if not args.no_cpu_baseline:
         sample = min(args.cpu_queries, qhost.shape[0])
         gpu_res = {}
@@ -267,6 +274,33 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
                                                       metric=args.metric)
     eng.close()
     return line
+
+
+def filtered_leg(args, torch, eng, qdev, ks, n, d):
+    """The same queries through search_resident_filtered (bf16 pass + exact fp32
+    re-rank of the rows whose bounds reach the k-th lower bound): its answers are
+    first checked to be identical, bit for bit, to the plain scan's on a sample,
+    then timed like the plain scan."""
+    eng.enable_filtered()
+    for qi in range(min(5, qdev.shape[0])):
+        for k in ks:
+            a = eng.search_resident(qdev[qi:qi + 1], k)
+            b = eng.search_resident_filtered(qdev[qi:qi + 1], k)
+            torch.cuda.synchronize()
+            if not (torch.equal(a[0], b[0]) and torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))):
+                raise SystemExit(f"filtered search differs from the plain scan (query {qi}, k {k})")
+    steps = min(args.steps, 300)
+    wall, lat, part, merge = time_search(eng, torch, qdev, ks, steps, args.warmup, filtered=True)
+    pass1_bytes = n * d * 2 + d * 4 + n * 4 + n * 4  # bf16 rows, query, row norms, upper bounds written
+    p1 = float(np.mean(np.concatenate([np.asarray(part[k]) for k in ks])))
+    return {"value": steps * len(ks) / wall, "unit": "queries/s", "steps": steps,
+            "identical_to_fp32_scan": True,
+            "per_k": {str(k): {"p50_us": pct(lat[k], 50), "p99_us": pct(lat[k], 99),
+                               "device_p50_us": pct(np.asarray(merge[k]) * 1e3, 50),
+                               "bf16_pass_avg_us": float(np.mean(part[k]) * 1e3)} for k in ks},
+            "bf16_pass": {"kernel": "gemv_bound_kernel", "bytes_per_launch": pass1_bytes,
+                          "avg_launch_us": p1 * 1e3, "achieved_gbs": pass1_bytes / (p1 * 1e-3) / 1e9,
+                          "frac_of_hbm_peak": pass1_bytes / (p1 * 1e-3) / 1e9 / HBM_PEAK_GBS}}
 
 
 def run_concurrent(args, torch, eng, corpus, qhost, qdev, ks, name, gen_s):
@@ -479,6 +513,8 @@ def main():
                     help="similarity for the retrieval workloads (the headline line is the inner product)")
     ap.add_argument("--filtered", action="store_true",
                     help="single-query workloads: search_resident_filtered (bf16 pass + exact fp32 re-rank)")
+    ap.add_argument("--no-filtered-leg", action="store_true",
+                    help="skip the extra timing of search_resident_filtered on single-query workloads")
     ap.add_argument("--streams", type=int, default=1,
                     help="single-query workloads: engines sharing the corpus, one stream each, searching concurrently")
     ap.add_argument("--num-queries", type=int, default=1000)

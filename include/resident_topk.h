@@ -228,6 +228,20 @@ rt_status rt_check_search_metric(int32_t max_k, int32_t max_q, int64_t resident_
 rt_status rt_check_select(int32_t max_k, const void *values, int32_t dtype, int64_t n, int32_t k,
                           const void *out_idx, const void *out_values);
 
+/*
+ * The two constants of search_resident_filtered's bound for depth d, host-only
+ * (no GPU needed): out2 = [cb, delta], where a row x with bf16 score a and
+ * fp32 score s satisfies |a - s| <= cb |q| |x| + delta max(|q|, 1).
+ * cb = (2^-8 + gamma_d (2 + 2^-8)) (1 + 2^-10), rounded up to fp32, with
+ * gamma_d = d 2^-24 / (1 - d 2^-24): bf16 keeps 8 significant bits, so
+ * rounding to nearest changes an element by at most 2^-8 of its magnitude, and
+ * gamma_d bounds the fp32 summation error of each sum relative to the sum of
+ * |terms| <= |q| |x| (Cauchy-Schwarz); the factor (1 + 2^-10) absorbs the fp32
+ * rounding of the bound itself.  delta = 4 d 2^-126 covers values and partial
+ * results below 2^-126.  RT_EINVAL for d < 1 or a NULL out2.
+ */
+rt_status rt_filter_bounds(int32_t d, float *out2);
+
 #ifdef __cplusplus
 }
 #endif

@@ -116,6 +116,55 @@ def test_filtered_bf16_overflow_falls_back(eng):
     _both(eng, corpus, q, 16)
 
 
+def test_filtered_worst_case_rounding(eng):
+    """Every element of row 700 sits halfway between two bf16 values, with the
+    rounding lowering every product (bf16 score 15.625, fp32 score 15.875, a
+    shortfall of 2^-8 of sum |x q|); row 300 is exact in bf16 and scores 15.8125.
+    A bound on the bf16 rounding below 2^-8 would exclude row 700, the answer."""
+    d = 64
+    corpus = workloads.gaussian_rows(5_000, d, config_id=580)
+    corpus[700, :40] = 1 + 2.0 ** -8
+    corpus[700, 40:] = -(1 + 3 * 2.0 ** -8)
+    corpus[300] = 253 / 1024
+    corpus[1200, :40] = -(1 + 2.0 ** -8)      # same construction, lowest scores
+    corpus[1200, 40:] = 1 + 3 * 2.0 ** -8
+    q = np.ones((1, d), np.float32)
+    for k in (1, 2, 5):
+        g_idx, g_sc = _both(eng, corpus, q, k, upload=(k == 1))
+        assert g_idx[0, 0] == 700 and g_sc[0, 0] == np.float32(15.875)
+        if k > 1:
+            assert g_idx[0, 1] == 300 and g_sc[0, 1] == np.float32(15.8125)
+    o_idx, o_sc = oracle.search(corpus, q, 5)
+    check_retrieval(g_idx[0], g_sc[0], o_idx[0], o_sc[0], corpus, q[0], oracle)
+
+
+def test_filtered_nonfinite_bf16_sum(eng):
+    """Row 7 is (v, -v, 0, ...) with 3 v finite in fp32 while 3 bf16(v)
+    overflows: its bf16 sum is inf + (-inf) = NaN, its fp32 score 0.  A NaN sum
+    bounds nothing; the row must still be re-scored and the rest ranked."""
+    d = 8
+    v = np.float32(10913 * 2.0 ** 113)           # rounds up to 171 2^119 in bf16
+    assert np.isfinite(np.float32(3) * v)
+    corpus = workloads.gaussian_rows(3_000, d, config_id=590)
+    corpus[7] = 0.0
+    corpus[7, 0], corpus[7, 1] = v, -v
+    q = np.zeros((1, d), np.float32)
+    q[0, :2] = 3.0
+    q[0, 2:] = 0.5
+    for k in (1, 3, 40):
+        _with_oracle(eng, corpus, q, k)
+
+
+def test_filtered_zero_query_overflowing_row_norm(eng):
+    """A row whose L2 norm overflows fp32 (inf) with a zero query: the bound's
+    product 0 x inf is NaN; every score is 0 and ties go to the lowest indices."""
+    d = 16
+    corpus = workloads.gaussian_rows(2_000, d, config_id=595)
+    corpus[1, :3] = np.float32(3.0e38)
+    g_idx, g_sc = _both(eng, corpus, np.zeros((1, d), np.float32), 10)
+    assert list(g_idx[0]) == list(range(10)) and np.all(g_sc == 0)
+
+
 def test_filtered_shared_engines():
     corpus = workloads.gaussian_rows(50_000, 1024, config_id=560)
     qs = workloads.gaussian_rows(4, 1024, config_id=560, stream=1)

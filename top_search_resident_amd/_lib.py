@@ -17,7 +17,7 @@ EXPORTS = (
     "rt_engine_create", "rt_engine_create_shared", "rt_engine_destroy", "upload_corpus_rowmajor", "search_resident",
     "search_resident_metric", "rt_enable_filtered", "search_resident_filtered", "topk_select", "rt_status_string", "rt_last_hip_error", "rt_profile_enable",
     "rt_profile_read", "rt_engine_info", "rt_check_create", "rt_check_upload",
-    "rt_check_search", "rt_check_search_metric", "rt_check_select",
+    "rt_check_search", "rt_check_search_metric", "rt_check_select", "rt_filter_bounds",
 )
 
 _lib = None
@@ -67,6 +67,7 @@ def load():
         "rt_check_search": ([i32, i32, i64, vp, i32, i32, vp, vp], ctypes.c_int),
         "rt_check_search_metric": ([i32, i32, i64, vp, i32, i32, i32, vp, vp], ctypes.c_int),
         "rt_check_select": ([i32, vp, i32, i64, i32, vp, vp], ctypes.c_int),
+        "rt_filter_bounds": ([i32, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -81,3 +82,12 @@ def status_string(status):
         return load().rt_status_string(int(status)).decode()
     except ImportError:
         return str(status)
+
+
+def filter_bounds(d):
+    """(cb, delta) of search_resident_filtered's bound at depth d (host-only)."""
+    out = (ctypes.c_float * 2)()
+    st = load().rt_filter_bounds(int(d), out)
+    if st != RT_OK:
+        raise ResidentTopKError(st, "rt_filter_bounds")
+    return float(out[0]), float(out[1])

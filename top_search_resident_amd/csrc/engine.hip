@@ -167,6 +167,13 @@ rt_status rt_check_select(int32_t max_k, const void *values, int32_t dtype, int6
     return RT_OK;
 }
 
+rt_status rt_filter_bounds(int32_t d, float *out2) {
+    if (d < 1 || out2 == nullptr) return RT_EINVAL;
+    out2[0] = rt::filter_bound_factor(d);
+    out2[1] = rt::filter_underflow_slack(d);
+    return RT_OK;
+}
+
 void rt_engine_destroy(rt_engine *e) {
     if (!e) return;
     int prev = 0;
@@ -470,7 +477,7 @@ rt_status search_resident_filtered(rt_engine *e, const float *queries, int32_t q
         const rt::TreeLaunch t2 = tree_for(e, p2, kp, k, 1, out_idx, out_scores, nullptr, 0);
         rt::FilterLaunch f;
         f.cb = rt::filter_bound_factor(d);
-        f.delta = ldexpf((float)d, -126);
+        f.delta = rt::filter_underflow_slack(d);
         f.ubuf = e->ubuf;
         f.uld = (r->max_n + 63) / 64 * 64;
         f.thr = e->thr;

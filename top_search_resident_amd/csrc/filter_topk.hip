@@ -23,13 +23,23 @@ RT_EXTERN_F(16)
 bool filtered_search_ok(int d) { return d % 8 == 0 && gemv_fast_path_ok(d); }
 
 float filter_bound_factor(int d) {
-    // |a - s| <= |x| |q| (2^-9 + gamma_d (2 + 2^-9)), gamma_d = d u / (1 - d u),
-    // u = 2^-24; then rounded up for the fp32 evaluation of e = cb |q| |x| + delta
-    // and of a - e, a + e (a relative 2^-10 covers both with a wide margin).
+    // |a - s| <= |x| |q| (2^-8 + gamma_d (2 + 2^-8)), gamma_d = d u / (1 - d u),
+    // u = 2^-24 (2^-8: bf16 rounding; gamma_d: the fp32 sums a and s); then
+    // rounded up for the fp32 evaluation of e = cb |q| |x| + delta and of
+    // a - e, a + e (a relative 2^-10 covers both with a wide margin).
     const double u = ldexp(1.0, -24);
     const double gamma = d * u / (1.0 - d * u);
-    const double c = (ldexp(1.0, -9) + gamma * (2.0 + ldexp(1.0, -9))) * (1.0 + ldexp(1.0, -10));
+    const double c = (ldexp(1.0, -8) + gamma * (2.0 + ldexp(1.0, -8))) * (1.0 + ldexp(1.0, -10));
     return nextafterf((float)c, INFINITY);
+}
+
+float filter_underflow_slack(int d) {
+    // Values below 2^-126 round to bf16 with an absolute error of at most
+    // 2^-134 (|q|_1 <= sqrt(d) |q| of it), and each of the 2d fused
+    // multiply-adds of the two sums loses at most 2^-126 to underflow even when
+    // results below 2^-126 are flushed: 3 d 2^-126 max(|q|, 1) covers both;
+    // 4 d 2^-126 leaves room for rounding e.
+    return ldexpf((float)d, -124);
 }
 
 hipError_t launch_filtered_search(const float *corpus, const uint16_t *corpus16, const float *rnorm, int64_t n,

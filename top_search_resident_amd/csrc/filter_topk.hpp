@@ -6,19 +6,23 @@
 // bf16 copy of the corpus resident as well, a first pass reads half the bytes:
 // for row i it computes a_i = sum_j bf16(x_ij) q_j in fp32 and a bound e_i with
 // |a_i - s_i| <= e_i, where s_i is the fp32 score the plain path computes.
-// The bound follows from the rounding of x to bf16 (relative 2^-9) and from
-// the fp32 summation error of both sums (gamma_D = D u / (1 - D u) times the
-// sum of |terms|), with sum_j |x_ij q_j| <= |x_i| |q| (Cauchy-Schwarz):
-//     e_i = |x_i| |q| (2^-9 + gamma_D (2 + 2^-9)), rounded up (host: cb),
-// plus d 2^-126 max(|q|, 1), which covers the absolute rounding of subnormal
-// values and products.  The first pass finds T, the k-th largest lower bound
-// a_i - e_i (k rows have s_i >= T), and stores every upper bound a_i + e_i.  Any row with a_i + e_i < T has s_i < T <= the k-th
-// largest s, so the top-k by s lies among the rows with a_i + e_i >= T: the
-// second pass re-scores exactly those rows in fp32 with the plain path's
-// arithmetic (lane_chain + group_sum) and selects among them.  The answer is
-// the plain path's answer, bit for bit.  For Gaussian unit rows at 1M x 1024
-// the band [T - 2 e, T] holds about a hundred rows, so the second pass reads
-// ~4 MB of bounds and a few hundred fp32 rows.
+// The bound follows from the rounding of x to bf16 (8 significant bits, so
+// round-to-nearest-even is off by at most 2^-8 relative) and from the fp32
+// summation error of both sums (gamma_D = D u / (1 - D u), u = 2^-24, times
+// the sum of |terms|), with sum_j |x_ij q_j| <= |x_i| |q| (Cauchy-Schwarz):
+//     e_i = |x_i| |q| (2^-8 + gamma_D (2 + 2^-8)), rounded up (host: cb),
+// plus 4 D 2^-126 max(|q|, 1), which covers the absolute rounding of values
+// below 2^-126 and of products and sums that underflow (flushed or not) in
+// both sums.  A bf16 sum or bound that is not finite bounds nothing: that row
+// gets the bounds -inf and +inf (always re-scored, never sets T).  The first
+// pass finds T, the k-th largest lower bound a_i - e_i (k rows have s_i >= T),
+// and stores every upper bound a_i + e_i.  Any row with a_i + e_i < T has
+// s_i < T <= the k-th largest s, so the top-k by s lies among the rows with
+// a_i + e_i >= T: the second pass re-scores exactly those rows in fp32 with
+// the plain path's arithmetic (lane_chain + group_sum) and selects among them.
+// The answer is the plain path's answer, bit for bit.  For Gaussian unit rows
+// at 1M x 1024 and k = 100 the band [T - 2 e, T] holds a few hundred rows, so
+// the second pass reads ~4 MB of bounds and a few hundred fp32 rows.
 #pragma once
 #include "stream_topk.hpp"
 
@@ -27,7 +31,7 @@ namespace rt {
 // Extra arguments of the two passes.
 struct FilterArgs {
     float cb;        // bound factor: e_i = cb |q| |x_i| + delta
-    float delta;     // absolute slack for subnormal values, times max(|q|, 1)
+    float delta;     // absolute slack for underflow, times max(|q|, 1)
     float *ubuf;     // [segments][uld] upper bounds a_i + e_i (pass 1 writes, pass 2 reads)
     int64_t uld;
     float *thr;      // [segments] T, the k-th largest lower bound (written by pass 1's tree)
@@ -134,8 +138,10 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_bound_kernel(
                 a = group_sum(a, LG);
                 const float e = fmaf(eq, rn[s][u], dl);
                 const int64_t row = rs + u * RPS + h;
-                if (g == 0 && row < r_end) ub[row] = a + e;
-                lo[u] = a - e;
+                // false for an overflowed or NaN sum or bound: the row is kept
+                const bool known = fabsf(a) <= __FLT_MAX__ && e <= __FLT_MAX__;
+                if (g == 0 && row < r_end) ub[row] = known ? a + e : __builtin_huge_valf();
+                lo[u] = known ? a - e : -__builtin_huge_valf();
             }
             if constexpr (P > 0) {
                 load_step(s, rs + P * STEP);

@@ -53,8 +53,10 @@ struct FilterLaunch {
     float *thr;      // [segments] k-th largest lower bound, written by pass 1
 };
 
-// Bound factor cb for depth d (fp64 on the host, rounded up; see filter_topk.hpp).
+// Bound factor cb for depth d (fp64 on the host, rounded up; see filter_topk.hpp)
+// and the absolute slack delta (times max(|q|, 1)) for underflow.
 float filter_bound_factor(int d);
+float filter_underflow_slack(int d);
 // Depths the filtered search handles: d % 8 == 0 and the fp32 fast-path shapes.
 bool filtered_search_ok(int d);
 // Lane-group shape (G = 2^log2g lanes, L 16-byte loads per lane) for rows of
