@@ -153,18 +153,24 @@ rt_status search_resident_metric(rt_engine *e, const float *queries, int32_t q, 
 rt_status rt_enable_filtered(rt_engine *e);
 
 /*
- * Exact top-k by inner product, the same answer as search_resident (indices,
- * order and fp32 scores, bit for bit), reading the fp32 rows only where they
- * can matter.  "Reduced-precision storage with exact re-rank": a first pass
- * scores every row from the bf16 copy (half the bytes) and bounds the
- * difference to the fp32 score from the rounding to bf16 and the fp32
- * summation error of both sums (with the rows' and the query's L2 norms,
- * Cauchy-Schwarz); the k-th largest lower bound T is certified to be at most
- * the k-th largest fp32 score, so only rows whose upper bound reaches T are
- * scored in fp32 by the second pass -- with the plain path's arithmetic -- and
- * ranked.  Arguments, layouts and errors as search_resident; RT_ESTATE also
- * when rt_enable_filtered was not called on this engine.  If the depth is not
- * a multiple of 8 or above 2048, or a corpus value is not finite in bf16, the
+ * Exact top-k by inner product: for each query, the answer search_resident
+ * gives for that query alone (indices, order and fp32 scores, bit for bit),
+ * reading the fp32 rows only where they can matter.  "Reduced-precision
+ * storage with exact re-rank" ("CUDA Programming Model Series 9: Efficient
+ * TopK", section 4.3): a first pass scores every row from the bf16 copy (half
+ * the bytes) and bounds the difference to the fp32 score from the rounding to
+ * bf16 and the fp32 summation error of both sums (with the rows' and the
+ * query's L2 norms, Cauchy-Schwarz); a threshold T certified to be at most the
+ * k-th largest fp32 score follows from the lower bounds, so only rows whose
+ * upper bound reaches T are scored in fp32 by the second pass -- with the
+ * single-query scan's arithmetic -- and ranked.  A batch (q > 1) on an engine
+ * created with max_q > 1 and a depth of 256, 384, 512, 768 or 1024 runs the
+ * first pass once for all queries on bf16 matrix cores, with the query split
+ * into two bf16 parts (constants: rt_filter_bounds_batched) and T the k-th
+ * largest of the per-query maxima of the lower bounds over 32-row tiles.
+ * Arguments, layouts and errors as search_resident; RT_ESTATE also when
+ * rt_enable_filtered was not called on this engine.  If the depth is not a
+ * multiple of 8 or above 2048, or a corpus value is not finite in bf16, the
  * call runs the plain fp32 scan instead (same answer).  Inner product only.
  * Asynchronous on `stream`.
  */
@@ -241,6 +247,22 @@ rt_status rt_check_select(int32_t max_k, const void *values, int32_t dtype, int6
  * results below 2^-126.  RT_EINVAL for d < 1 or a NULL out2.
  */
 rt_status rt_filter_bounds(int32_t d, float *out2);
+
+/*
+ * The same two constants for the batched first pass of
+ * search_resident_filtered, host-only: out2 = [cb, delta] with
+ * |a - s| <= cb |q| |x| + delta max(|q|, 1) max(|x|, 1), where a is the bf16
+ * matrix-core sum of bf16(x) against the query split into two bf16 parts.
+ * cb = (2^-8 + 2^-16 + 2^-24 + gamma_d + 1.02 g) (1 + 2^-10), rounded up to
+ * fp32: 2^-8 + 2^-16 + 2^-24 bounds the rounding of x and of the query's two
+ * parts, gamma_d = d 2^-24 / (1 - d 2^-24) the single-query scan's fp32 sum,
+ * g = 8 d 2^-24 / (1 - 8 d 2^-24) the matrix core's fp32 accumulation of the
+ * 2 d exact bf16 products in any order and rounding direction, with room to
+ * spare, on sum |bf16(x)| |parts| <= 1.02 |x| |q|.  delta = 16 d 2^-126 covers
+ * values, products and partial sums below 2^-126.  RT_EINVAL for d < 1 or a
+ * NULL out2.
+ */
+rt_status rt_filter_bounds_batched(int32_t d, float *out2);
 
 #ifdef __cplusplus
 }

@@ -138,9 +138,11 @@ class ResidentTopK:
         _check(self._lib.rt_enable_filtered(self._h), "rt_enable_filtered", self._h)
 
     def search_resident_filtered(self, queries, k, out_idx=None, out_scores=None, stream=None):
-        """Exact inner-product top-k (the same answer as search_resident) that
-        reads a bf16 copy of the corpus first and the fp32 rows only where their
-        certified score bounds reach the k-th lower bound."""
+        """Exact inner-product top-k (for each query, the answer
+        search_resident gives for that query alone) that reads a bf16 copy of
+        the corpus first and the fp32 rows only where their certified score
+        bounds reach a certified threshold.  A batch runs one bf16 matrix-core
+        first pass for all of its queries."""
         torch = _torch()
         if queries.dim() == 1:
             queries = queries.view(1, -1)
@@ -193,8 +195,10 @@ class ResidentTopK:
         _check(self._lib.rt_profile_enable(self._h, 1 if on else 0), "rt_profile_enable")
 
     def profile_read(self):
-        """Stage durations (ms) of the last call: (partial stage, merge stage,
-        batched scoring kernel or 0).  The stream must have finished."""
+        """Device durations (ms) of the last call: (the whole call, its first
+        kernel when it ran more than one -- the batched scoring kernel, or the
+        first pass of a filtered search -- else 0, the rest).  The stream must
+        have finished."""
         out = (ctypes.c_float * 3)()
         _check(self._lib.rt_profile_read(self._h, out), "rt_profile_read", self._h)
         return float(out[0]), float(out[1]), float(out[2])

@@ -18,6 +18,7 @@ EXPORTS = (
     "search_resident_metric", "rt_enable_filtered", "search_resident_filtered", "topk_select", "rt_status_string", "rt_last_hip_error", "rt_profile_enable",
     "rt_profile_read", "rt_engine_info", "rt_check_create", "rt_check_upload",
     "rt_check_search", "rt_check_search_metric", "rt_check_select", "rt_filter_bounds",
+    "rt_filter_bounds_batched",
 )
 
 _lib = None
@@ -68,6 +69,7 @@ def load():
         "rt_check_search_metric": ([i32, i32, i64, vp, i32, i32, i32, vp, vp], ctypes.c_int),
         "rt_check_select": ([i32, vp, i32, i64, i32, vp, vp], ctypes.c_int),
         "rt_filter_bounds": ([i32, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
+        "rt_filter_bounds_batched": ([i32, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -84,10 +86,13 @@ def status_string(status):
         return str(status)
 
 
-def filter_bounds(d):
-    """(cb, delta) of search_resident_filtered's bound at depth d (host-only)."""
+def filter_bounds(d, batched=False):
+    """(cb, delta) of search_resident_filtered's bound at depth d (host-only):
+    the single-query first pass, or with batched=True the bf16 matrix-core
+    first pass of a batch."""
     out = (ctypes.c_float * 2)()
-    st = load().rt_filter_bounds(int(d), out)
+    name = "rt_filter_bounds_batched" if batched else "rt_filter_bounds"
+    st = getattr(load(), name)(int(d), out)
     if st != RT_OK:
-        raise ResidentTopKError(st, "rt_filter_bounds")
+        raise ResidentTopKError(st, name)
     return float(out[0]), float(out[1])

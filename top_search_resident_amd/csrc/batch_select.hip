@@ -172,30 +172,22 @@ __device__ __forceinline__ void scan_tiles(const uint32_t *tm, int64_t tiles, F 
     }
 }
 
-__global__ __launch_bounds__(kBatchSelectThreads) void tile_bound_select_kernel(const uint32_t *__restrict__ rows,
-                                                                              int64_t ld, int64_t n,
-                                                                              const uint32_t *__restrict__ tmax,
-                                                                              int64_t tld, SelectOut o) {
-    __shared__ uint64_t sm[kSortCap];
-    __shared__ uint32_t sh[kDigitBins];
-    __shared__ uint32_t scan_buf[kBatchSelectThreads];
-    __shared__ uint32_t tl[kTileListCap];
-    __shared__ uint32_t s_vals[4];
-    const int seg = blockIdx.y;
+// Step 1 of tile_bound_select_kernel below, for the rows' tile maxima tm[0 ..
+// tiles): the lower edge of a key bin that holds the k-th largest tile
+// maximum, so at least k tiles reach it (as a key; 0, below every key, when
+// there are fewer than k tiles).  Every thread of the workgroup calls it and
+// gets the same value.  Tile maxima crowd into a few top-11-bit bins, so the
+// first try histograms a window just below the largest tile maximum in 2048
+// bins of 2^12 key units (2^23 units: one octave for fp32), counting only keys
+// inside it: few keys, spread out, few LDS collisions.  If fewer than k keys
+// fall inside, two plain 11-bit passes over all keys pin the top 22 bits
+// instead.
+__device__ uint32_t tile_max_bound(const uint32_t *tm, int64_t tiles, int k, uint32_t *sh, uint32_t *scan_buf,
+                                   uint32_t *s_vals) {
     const int t = threadIdx.x;
     const int lane = lane_id();
-    const uint32_t *row = rows + (int64_t)seg * ld;
-    const uint32_t *tm = tmax + (int64_t)seg * tld;
-    const int64_t tiles = (n + 31) / 32;
-
-    // 1. the bound.  Tile maxima crowd into a few top-11-bit bins, so the
-    //    first try histograms a window just below the largest tile maximum in
-    //    2048 bins of 2^12 key units (2^23 units: one octave for fp32),
-    //    counting only keys inside it: few keys, spread out, few LDS
-    //    collisions.  If fewer than k keys fall inside, two plain 11-bit
-    //    passes over all keys pin the top 22 bits instead.
     uint32_t bound = 0;
-    if (tiles >= o.k) {
+    if (tiles >= k) {
         uint32_t top = 0;
         scan_tiles(tm, tiles, [&](int64_t, bool ok, uint32_t key) {
             if (ok) top = max(top, key);
@@ -218,14 +210,14 @@ __global__ __launch_bounds__(kBatchSelectThreads) void tile_bound_select_kernel(
         const uint32_t before = incl - c0 - c1;
         if (t == 0) s_vals[1] = 0xffffffffu;
         __syncthreads();
-        if (before < (uint32_t)o.k && incl >= (uint32_t)o.k)
-            s_vals[1] = (before + c0 >= (uint32_t)o.k) ? (uint32_t)(2 * t) : (uint32_t)(2 * t + 1);
+        if (before < (uint32_t)k && incl >= (uint32_t)k)
+            s_vals[1] = (before + c0 >= (uint32_t)k) ? (uint32_t)(2 * t) : (uint32_t)(2 * t + 1);
         __syncthreads();
         const uint32_t dist = s_vals[1];
         if (dist != 0xffffffffu) {
             bound = (top - dist) << 12;
         } else {
-            uint32_t prefix = 0, pmask = 0, need = (uint32_t)o.k;
+            uint32_t prefix = 0, pmask = 0, need = (uint32_t)k;
             for (int pass = 0; pass < 2; ++pass) {
                 const int shift = pass == 0 ? 21 : 10;
                 for (int b = t; b < kDigitBins; b += blockDim.x) sh[b] = 0u;
@@ -255,6 +247,27 @@ __global__ __launch_bounds__(kBatchSelectThreads) void tile_bound_select_kernel(
             bound = prefix;
         }
     }
+    return bound;
+}
+
+__global__ __launch_bounds__(kBatchSelectThreads) void tile_bound_select_kernel(const uint32_t *__restrict__ rows,
+                                                                              int64_t ld, int64_t n,
+                                                                              const uint32_t *__restrict__ tmax,
+                                                                              int64_t tld, SelectOut o) {
+    __shared__ uint64_t sm[kSortCap];
+    __shared__ uint32_t sh[kDigitBins];
+    __shared__ uint32_t scan_buf[kBatchSelectThreads];
+    __shared__ uint32_t tl[kTileListCap];
+    __shared__ uint32_t s_vals[4];
+    const int seg = blockIdx.y;
+    const int t = threadIdx.x;
+    const int lane = lane_id();
+    const uint32_t *row = rows + (int64_t)seg * ld;
+    const uint32_t *tm = tmax + (int64_t)seg * tld;
+    const int64_t tiles = (n + 31) / 32;
+
+    // 1. the bound (tile_max_bound)
+    const uint32_t bound = tile_max_bound(tm, tiles, o.k, sh, scan_buf, s_vals);
 
     // 2. tiles reaching the bound, then their elements >= bound
     if (t == 0) {
@@ -330,6 +343,33 @@ __global__ __launch_bounds__(kBatchSelectThreads) void tile_bound_select_kernel(
     __syncthreads();
     block_sort_desc(sm, msz);
     for (int r = t; r < o.k; r += blockDim.x) write_result(o, seg, r, sm[r]);
+}
+
+// Per query, the threshold of the batched filtered search (mfma_filter.hip):
+// thr[seg] = the value of tile_max_bound over that query's per-tile maxima of
+// the rows' lower bounds.  At least k tiles reach it and each holds a row whose
+// lower bound, hence whose fp32 score, reaches it, so the k-th largest score
+// is at or above it; -inf when there are fewer than k tiles (every row stays a
+// candidate).
+__global__ __launch_bounds__(kBatchSelectThreads) void tile_threshold_kernel(const uint32_t *__restrict__ tmax,
+                                                                           int64_t tld, int64_t tiles, int k,
+                                                                           float *__restrict__ thr) {
+    __shared__ uint32_t sh[kDigitBins];
+    __shared__ uint32_t scan_buf[kBatchSelectThreads];
+    __shared__ uint32_t s_vals[4];
+    const int seg = blockIdx.x;
+    const uint32_t bound = tile_max_bound(tmax + (int64_t)seg * tld, tiles, k, sh, scan_buf, s_vals);
+    // keys below -inf's stand for nothing real: every row is a candidate then
+    if (threadIdx.x == 0)
+        thr[seg] = (bound > order_key_f32(-INFINITY)) ? f32_of_order_key(bound) : -INFINITY;
+}
+
+hipError_t launch_tile_threshold(const float *tmax, int64_t tld, int64_t n, int segments, int k, float *thr,
+                                 hipStream_t stream) {
+    const int64_t tiles = (n + 31) / 32;
+    hipLaunchKernelGGL(tile_threshold_kernel, dim3((unsigned)segments), dim3(kBatchSelectThreads), 0, stream,
+                       reinterpret_cast<const uint32_t *>(tmax), tld, tiles, k, thr);
+    return hipGetLastError();
 }
 
 hipError_t launch_tile_bound_select(const float *rows, int64_t ld, int64_t n, const float *tmax, int64_t tld,

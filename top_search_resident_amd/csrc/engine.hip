@@ -174,6 +174,13 @@ rt_status rt_filter_bounds(int32_t d, float *out2) {
     return RT_OK;
 }
 
+rt_status rt_filter_bounds_batched(int32_t d, float *out2) {
+    if (d < 1 || out2 == nullptr) return RT_EINVAL;
+    out2[0] = rt::filter_bound_factor_batched(d);
+    out2[1] = rt::filter_underflow_slack_batched(d);
+    return RT_OK;
+}
+
 void rt_engine_destroy(rt_engine *e) {
     if (!e) return;
     int prev = 0;
@@ -224,6 +231,7 @@ static rt_status setup_scratch(rt_engine *e) {
     if (!ok) return RT_ENOMEM;
     err = hipMemset(e->counters, 0, sizeof(uint32_t) * (size_t)(kMaxQ * kMaxWgsPerSeg));
     if (err == hipSuccess) err = rt::prepare_mfma_scores();
+    if (err == hipSuccess) err = rt::prepare_mfma_filter();
     for (int i = 0; i < 4 && err == hipSuccess; ++i) err = hipEventCreate(&e->ev[i]);
     if (err == hipSuccess) err = hipDeviceSynchronize();
     if (err != hipSuccess) {
@@ -468,9 +476,30 @@ rt_status search_resident_filtered(rt_engine *e, const float *queries, int32_t q
     (void)hipGetDevice(&prev);
     hipError_t err = hipSetDevice(e->device);
     const int kp = kp_for(k);
+    const int64_t uld = (r->max_n + 63) / 64 * 64;
+    // A batch on an engine with batch buffers: bounds for all queries from one
+    // bf16 MFMA pass over the copy, per-query thresholds from tile maxima.
+    const bool batched = q > 1 && e->tmax != nullptr && rt::mfma_filter_ok(d);
     e->had_batch_kernel = false;
     if (err == hipSuccess) err = prologue(e, s);
-    if (err == hipSuccess) {
+    if (err == hipSuccess && batched) {
+        err = rt::launch_mfma_bound(r->corpus16, n, d, queries, q, r->rnorm, e->ubuf, uld, e->tmax, e->tile_ld,
+                                    e->num_cus, s);
+        if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[3], s);
+        if (err == hipSuccess) err = rt::launch_tile_threshold(e->tmax, e->tile_ld, n, q, k, e->thr, s);
+        if (err == hipSuccess) {
+            const Plan p2 = plan_stream(n, q, kp, 512, e->num_cus, kScoreWavesPerCu, rt::gemv_waves(kp));
+            const rt::TreeLaunch t2 = tree_for(e, p2, kp, k, 1, out_idx, out_scores, nullptr, 0);
+            rt::FilterLaunch f;
+            f.cb = rt::filter_bound_factor_batched(d);
+            f.delta = rt::filter_underflow_slack_batched(d);
+            f.ubuf = e->ubuf;
+            f.uld = uld;
+            f.thr = e->thr;
+            err = rt::launch_filtered_pass2(r->corpus, n, d, queries, q, p2.per_wave, p2.wgs, t2, f, s);
+        }
+        e->had_batch_kernel = e->profiling;
+    } else if (err == hipSuccess) {
         const Plan p1 = plan_stream(n, q, kp, 32, e->num_cus, kScoreWavesPerCu, rt::gemv_waves(kp));
         const Plan p2 = plan_stream(n, q, kp, 512, e->num_cus, kScoreWavesPerCu, rt::gemv_waves(kp));
         const rt::TreeLaunch t1 = tree_for(e, p1, kp, k, 3, nullptr, e->thr, nullptr, 0);
@@ -479,7 +508,7 @@ rt_status search_resident_filtered(rt_engine *e, const float *queries, int32_t q
         f.cb = rt::filter_bound_factor(d);
         f.delta = rt::filter_underflow_slack(d);
         f.ubuf = e->ubuf;
-        f.uld = (r->max_n + 63) / 64 * 64;
+        f.uld = uld;
         f.thr = e->thr;
         e->had_batch_kernel = e->profiling;
         err = rt::launch_filtered_search(r->corpus, r->corpus16, r->rnorm, n, d, queries, q, p1.per_wave, p1.wgs, t1,

@@ -74,6 +74,23 @@ hipError_t launch_filtered_search(const float *corpus, const uint16_t *corpus16,
     }
 }
 
+hipError_t launch_filtered_pass2(const float *corpus, int64_t n, int d, const float *queries, int segments,
+                                 int64_t rows_per_wave, int wgs, const TreeLaunch &t, const FilterLaunch &f,
+                                 hipStream_t stream) {
+    if (!filtered_search_ok(d)) return hipErrorInvalidValue;
+    int lg4 = 6, L4 = 8;
+    pick_gemv_shape(d / 4, &lg4, &L4);
+    const dim3 g(wgs, segments);
+    switch (t.kp / 64) {
+        case 1: return launch_filtered_r<1>(lg4, L4, g, stream, corpus, n, d, queries, rows_per_wave, t, f);
+        case 2: return launch_filtered_r<2>(lg4, L4, g, stream, corpus, n, d, queries, rows_per_wave, t, f);
+        case 4: return launch_filtered_r<4>(lg4, L4, g, stream, corpus, n, d, queries, rows_per_wave, t, f);
+        case 8: return launch_filtered_r<8>(lg4, L4, g, stream, corpus, n, d, queries, rows_per_wave, t, f);
+        case 16: return launch_filtered_r<16>(lg4, L4, g, stream, corpus, n, d, queries, rows_per_wave, t, f);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 // Round to nearest even; a value that is not finite or rounds to infinity is
 // reported through *bad (its copy is then unusable for bounds).
 __global__ __launch_bounds__(256) void to_bf16_kernel(const float *__restrict__ x, uint16_t *__restrict__ y,

@@ -72,6 +72,31 @@ hipError_t launch_filtered_search(const float *corpus, const uint16_t *corpus16,
                                   const TreeLaunch &t1, int64_t rows_per_wave2, int wgs2, const TreeLaunch &t2,
                                   const FilterLaunch &f, hipEvent_t between, hipStream_t stream);
 
+// Pass 2 of the filtered search alone: for each of `segments` queries, re-score
+// in fp32 the rows whose upper bound f.ubuf[seg][row] reaches f.thr[seg] and
+// select among them (grid (wgs, segments)).
+hipError_t launch_filtered_pass2(const float *corpus, int64_t n, int d, const float *queries, int segments,
+                                 int64_t rows_per_wave, int wgs, const TreeLaunch &t, const FilterLaunch &f,
+                                 hipStream_t stream);
+
+// Batched filtered search (mfma_filter.hip).  Depths with a compile-time
+// bf16 MFMA bound kernel (d in {256, 384, 512, 768, 1024}); its bound factor and
+// underflow slack (e = cb |q| |x| + delta max(|q|, 1) max(|x|, 1)).
+bool mfma_filter_ok(int d);
+float filter_bound_factor_batched(int d);
+float filter_underflow_slack_batched(int d);
+hipError_t prepare_mfma_filter();
+// Pass 1 for q <= 32 queries: upper bounds ubuf[query * uld + row] and, per
+// query, the largest lower bound of every 32-row tile, tlb[query * tld + tile].
+hipError_t launch_mfma_bound(const uint16_t *corpus16, int64_t n, int d, const float *queries, int q,
+                             const float *rnorm, float *ubuf, int64_t uld, float *tlb, int64_t tld, int num_cus,
+                             hipStream_t stream);
+// Per query, thr[seg] <= the k-th largest of that query's tile maxima of lower
+// bounds tmax[seg * tld + tile] (a bin edge below it; -inf when n has fewer
+// than k tiles), so at least k rows have a lower bound at or above it.
+hipError_t launch_tile_threshold(const float *tmax, int64_t tld, int64_t n, int segments, int k, float *thr,
+                                 hipStream_t stream);
+
 // corpus16[i] = bf16 of corpus[i] (round to nearest even), i < count; *bad is set
 // to 1 if any value is not finite or rounds to infinity (the caller clears it).
 hipError_t launch_to_bf16(const float *corpus, uint16_t *corpus16, int64_t count, uint32_t *bad, int num_cus,
