@@ -249,20 +249,24 @@ rt_status rt_check_select(int32_t max_k, const void *values, int32_t dtype, int6
 rt_status rt_filter_bounds(int32_t d, float *out2);
 
 /*
- * The same two constants for the batched first pass of
- * search_resident_filtered, host-only: out2 = [cb, delta] with
- * |a - s| <= cb |q| |x| + delta max(|q|, 1) max(|x|, 1), where a is the bf16
- * matrix-core sum of bf16(x) against the query split into two bf16 parts.
- * cb = (2^-8 + 2^-16 + 2^-24 + gamma_d + 1.02 g) (1 + 2^-10), rounded up to
- * fp32: 2^-8 + 2^-16 + 2^-24 bounds the rounding of x and of the query's two
- * parts, gamma_d = d 2^-24 / (1 - d 2^-24) the single-query scan's fp32 sum,
- * g = 8 d 2^-24 / (1 - 8 d 2^-24) the matrix core's fp32 accumulation of the
- * 2 d exact bf16 products in any order and rounding direction, with room to
- * spare, on sum |bf16(x)| |parts| <= 1.02 |x| |q|.  delta = 16 d 2^-126 covers
+ * The constants of the batched first pass of search_resident_filtered,
+ * host-only: out3 = [cr, cx, delta] with
+ *   |a - s| <= |q| (cr |x - bf16(x)| + cx |x|) + delta max(|q|, 1) max(|x|, 1),
+ * where a is the bf16 matrix-core sum of bf16(x) against the query split into
+ * two bf16 parts (hi = bf16(q), lo = bf16(q - hi)) and s the single-query
+ * scan's fp32 score.  |x - bf16(x)| is computed per row with the bf16 copy and
+ * rounded up.  cr = (1 + 2^-16) (1 + 2^-10) and cx = (2^-16 + gamma_d + 1.02 g)
+ * (1 + 2^-10), each rounded up to fp32: Cauchy-Schwarz on the row's rounding
+ * error against the split query (|hi + lo| <= (1 + 2^-16) |q|), 2^-16 for the
+ * split's own error, gamma_d = d 2^-24 / (1 - d 2^-24) for the scan's fp32 sum,
+ * and g = 8 d 2^-24 / (1 - 8 d 2^-24) for the matrix core's fp32 accumulation
+ * of the 2 d exact products in any order and rounding direction, with room to
+ * spare, on sum |bf16(x)| (|hi| + |lo|) <= 1.02 |x| |q|; the factor (1 + 2^-10)
+ * absorbs the fp32 evaluation of the bound.  delta = 16 d 2^-126 covers
  * values, products and partial sums below 2^-126.  RT_EINVAL for d < 1 or a
- * NULL out2.
+ * NULL out3.
  */
-rt_status rt_filter_bounds_batched(int32_t d, float *out2);
+rt_status rt_filter_bounds_batched(int32_t d, float *out3);
 
 #ifdef __cplusplus
 }

@@ -4,15 +4,16 @@ host (no GPU).
 For a row x and query q the batched pass computes a = sum_j bf16(x_j) hi_j +
 bf16(x_j) lo_j on bf16 matrix cores, with the query split into two bf16 parts
 hi = bf16(q), lo = bf16(q - hi); the single-query scan computes s = the fp32
-dot product of x with q.  The library's constants (cb, delta) =
+dot product of x with q.  The library's constants (cr, cx, delta) =
 rt_filter_bounds_batched(d) must give
-    |a - s| <= cb |q| |x| + delta max(|q|, 1) max(|x|, 1)
+    |a - s| <= |q| (cr |x - bf16(x)| + cx |x|) + delta max(|q|, 1) max(|x|, 1)
 for any fp32 accumulation order and rounding direction of the 2 d exact
 products.  bf16 rounding here is torch's float -> bfloat16 conversion (round to
 nearest, ties to even), a library routine independent of the HIP code.  The
 worst case is built by hand: every element of x sits halfway between two bf16
 values and rounds down, so a falls short by 2^-8 of sum |x q|, the most that
-rounding to 8 significant bits allows; half the factor fails it.  The query
+rounding to 8 significant bits allows, and equals |x - bf16(x)| |q|: half of cr
+fails it.  The query
 split is checked on its own: q - (hi + lo) is at most 2^-16 |q|."""
 from fractions import Fraction
 
@@ -71,10 +72,13 @@ def _plain_sums(x, q):
 
 
 def _bound(d, x, q):
-    cb, delta = _lib.filter_bounds(d, batched=True)
+    """The library's bound, with |x - bf16(x)| and the norms in fp64 (the
+    library rounds them up to fp32)."""
+    cr, cx, delta = _lib.filter_bounds_batched(d)
     nx = float(np.sqrt(np.sum(x.astype(np.float64) ** 2)))
     nq = float(np.sqrt(np.sum(q.astype(np.float64) ** 2)))
-    return cb * nq * nx + delta * max(nq, 1.0) * max(nx, 1.0), cb, nx, nq
+    ne = float(np.sqrt(np.sum((x.astype(np.float64) - _bf16(x).astype(np.float64)) ** 2)))
+    return nq * (cr * ne + cx * nx) + delta * max(nq, 1.0) * max(nx, 1.0), cr, ne, nq
 
 
 def _check(x, q):
@@ -123,12 +127,12 @@ def test_worst_case_is_covered_and_tight():
     exact_a = sum(Fraction(float(a)) * (Fraction(float(h)) + Fraction(float(l))) for a, h, l in zip(xb, hi, lo))
     exact_s = sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(x, q))
     err = float(exact_s - exact_a)
-    bound, cb, nx, nq = _bound(64, x, q)
+    bound, cr, ne, nq = _bound(64, x, q)
     assert err <= bound
-    # the full 2^-8 is needed: the shortfall is above 0.99 2^-8 of |x| |q|, so
-    # half the library's factor (or a single-rounding 2^-9) would not cover it
-    assert err / (nx * nq) > 0.99 * 2.0 ** -8
-    assert err > 0.5 * cb * nx * nq
+    # the whole rounding error counts: the shortfall equals |x - bf16(x)| |q|,
+    # so half of cr (or a bound that charged only part of it) fails
+    assert abs(err - ne * nq) <= 1e-12 * err
+    assert err > 0.5 * cr * ne * nq + (bound - cr * ne * nq)
     _check(x, q)
 
 
@@ -163,18 +167,27 @@ def test_gaussian_unit_rows_within_bound():
 
 def test_constants_follow_the_derivation():
     for d in (1, 256, 768, 1024, 100_000):
-        cb, delta = _lib.filter_bounds(d, batched=True)
+        cr, cx, delta = _lib.filter_bounds_batched(d)
         u = Fraction(1, 2 ** 24)
         gamma = d * u / (1 - d * u)
         g8 = 8 * d * u / (1 - 8 * d * u)
-        base = Fraction(1, 2 ** 8) + Fraction(1, 2 ** 16) + u + gamma + Fraction(102, 100) * g8
-        assert Fraction(cb) >= base * (1 + Fraction(1, 1024))
-        assert Fraction(cb) <= base * (1 + Fraction(1, 512))
+        base_r = 1 + Fraction(1, 2 ** 16)
+        base_x = Fraction(1, 2 ** 16) + gamma + Fraction(102, 100) * g8
+        for c, base in ((cr, base_r), (cx, base_x)):
+            assert Fraction(c) >= base * (1 + Fraction(1, 1024))
+            assert Fraction(c) <= base * (1 + Fraction(1, 512))
         assert Fraction(delta) == Fraction(16 * d, 2 ** 126)
-        # wider than the single-query pass, which rounds only the row
-        assert cb > _lib.filter_bounds(d)[0]
+
+
+def test_rounding_error_norm_is_smaller_than_the_elementwise_bound():
+    """For Gaussian rows |x - bf16(x)| is well below 2^-8 |x| (what an
+    elementwise bound would charge): the reason the bound uses it."""
+    x = workloads.gaussian_rows(64, 768, config_id=902).astype(np.float64)
+    ne = np.linalg.norm(x - _bf16(x.astype(np.float32)), axis=1)
+    ratio = ne / np.linalg.norm(x, axis=1) / 2.0 ** -8
+    assert np.all(ratio < 0.6) and np.all(ratio > 0.2)
 
 
 def test_rejects_bad_depth():
     with pytest.raises(_lib.ResidentTopKError):
-        _lib.filter_bounds(0, batched=True)
+        _lib.filter_bounds_batched(0)

@@ -86,13 +86,20 @@ def status_string(status):
         return str(status)
 
 
-def filter_bounds(d, batched=False):
-    """(cb, delta) of search_resident_filtered's bound at depth d (host-only):
-    the single-query first pass, or with batched=True the bf16 matrix-core
-    first pass of a batch."""
+def filter_bounds(d):
+    """(cb, delta) of search_resident_filtered's single-query bound at depth d
+    (host-only)."""
     out = (ctypes.c_float * 2)()
-    name = "rt_filter_bounds_batched" if batched else "rt_filter_bounds"
-    st = getattr(load(), name)(int(d), out)
+    st = load().rt_filter_bounds(int(d), out)
     if st != RT_OK:
-        raise ResidentTopKError(st, name)
+        raise ResidentTopKError(st, "rt_filter_bounds")
     return float(out[0]), float(out[1])
+
+
+def filter_bounds_batched(d):
+    """(cr, cx, delta) of the batched first pass's bound at depth d (host-only)."""
+    out = (ctypes.c_float * 3)()
+    st = load().rt_filter_bounds_batched(int(d), out)
+    if st != RT_OK:
+        raise ResidentTopKError(st, "rt_filter_bounds_batched")
+    return float(out[0]), float(out[1]), float(out[2])

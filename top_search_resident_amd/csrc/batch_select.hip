@@ -193,7 +193,10 @@ __device__ uint32_t tile_max_bound(const uint32_t *tm, int64_t tiles, int k, uin
             if (ok) top = max(top, key);
         });
         for (int off = 32; off >= 1; off >>= 1) top = max(top, (uint32_t)__shfl_xor((int)top, off));
-        if (t == 0) s_vals[0] = 0u;
+        if (t == 0) {
+            s_vals[0] = 0u;
+            s_vals[1] = 0xffffffffu;
+        }
         for (int b = t; b < kDigitBins; b += blockDim.x) sh[b] = 0u;
         __syncthreads();
         if (lane == 0) atomicMax(&s_vals[0], top);
@@ -204,14 +207,40 @@ __device__ uint32_t tile_max_bound(const uint32_t *tm, int64_t tiles, int k, uin
             if (ok && dist < (uint32_t)kDigitBins) atomicAdd(&sh[dist], 1u);
         });
         __syncthreads();
-        // lowest window bin (distance from the top) whose prefix count reaches k
-        const uint32_t c0 = sh[2 * t], c1 = sh[2 * t + 1];
-        const uint32_t incl = block_inclusive_scan(c0 + c1, scan_buf);
-        const uint32_t before = incl - c0 - c1;
-        if (t == 0) s_vals[1] = 0xffffffffu;
-        __syncthreads();
-        if (before < (uint32_t)k && incl >= (uint32_t)k)
-            s_vals[1] = (before + c0 >= (uint32_t)k) ? (uint32_t)(2 * t) : (uint32_t)(2 * t + 1);
+        // lowest window bin (distance from the top) whose prefix count reaches
+        // k, found by one wave: lane l sums bins 32 l .. 32 l + 31, a wave
+        // prefix sum finds the lane whose range holds it, that lane walks its
+        // bins (one workgroup barrier instead of a block-wide scan)
+        if (t < 64) {
+            constexpr int B = kDigitBins / 64;
+            uint32_t c[B];
+            uint32_t sum = 0;
+#pragma unroll
+            for (int i = 0; i < B; ++i) {
+                c[i] = sh[B * t + i];
+                sum += c[i];
+            }
+            uint32_t incl = sum;
+#pragma unroll
+            for (int off = 1; off < 64; off <<= 1) {
+                const uint32_t y = __shfl_up(incl, off, 64);
+                if (t >= off) incl += y;
+            }
+            uint32_t before = incl - sum;
+            if (before < (uint32_t)k && incl >= (uint32_t)k) {
+                uint32_t found = 0xffffffffu;
+#pragma unroll
+                for (int i = 0; i < B; ++i) {
+                    if (found == 0xffffffffu) {
+                        if (before + c[i] >= (uint32_t)k)
+                            found = (uint32_t)(B * t + i);
+                        else
+                            before += c[i];
+                    }
+                }
+                s_vals[1] = found;
+            }
+        }
         __syncthreads();
         const uint32_t dist = s_vals[1];
         if (dist != 0xffffffffu) {

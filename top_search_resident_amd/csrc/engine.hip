@@ -82,6 +82,7 @@ struct rt_resident {
     float *rnorm = nullptr;   // L2 norm of every resident row (cosine metric), roundup(max_n, 64) floats
     uint16_t *corpus16 = nullptr;  // bf16 copy, max_n x max_d (after rt_enable_filtered)
     uint32_t *bad16 = nullptr;     // set by the conversion when a value is not finite in bf16
+    float *err16 = nullptr;        // per row, an upper bound on |row - bf16 copy| (after rt_enable_filtered)
     bool copy16_ok = false;        // the bf16 copy matches the resident corpus and is usable
 };
 
@@ -174,10 +175,9 @@ rt_status rt_filter_bounds(int32_t d, float *out2) {
     return RT_OK;
 }
 
-rt_status rt_filter_bounds_batched(int32_t d, float *out2) {
-    if (d < 1 || out2 == nullptr) return RT_EINVAL;
-    out2[0] = rt::filter_bound_factor_batched(d);
-    out2[1] = rt::filter_underflow_slack_batched(d);
+rt_status rt_filter_bounds_batched(int32_t d, float *out3) {
+    if (d < 1 || out3 == nullptr) return RT_EINVAL;
+    rt::filter_bound_constants_batched(d, &out3[0], &out3[1], &out3[2]);
     return RT_OK;
 }
 
@@ -200,6 +200,7 @@ void rt_engine_destroy(rt_engine *e) {
         (void)hipFree(e->res->rnorm);
         (void)hipFree(e->res->corpus16);
         (void)hipFree(e->res->bad16);
+        (void)hipFree(e->res->err16);
         delete e->res;
     }
     (void)hipSetDevice(prev);
@@ -322,6 +323,7 @@ static hipError_t refresh_copy16(rt_resident *r, int64_t n, int32_t d, int num_c
     *ok = false;
     hipError_t err = hipMemset(r->bad16, 0, sizeof(uint32_t));
     if (err == hipSuccess) err = rt::launch_to_bf16(r->corpus, r->corpus16, n * (int64_t)d, r->bad16, num_cus, nullptr);
+    if (err == hipSuccess) err = rt::launch_bf16_row_errors(r->corpus, n, d, r->err16, num_cus, nullptr);
     uint32_t bad = 1;
     if (err == hipSuccess) err = hipMemcpy(&bad, r->bad16, sizeof(uint32_t), hipMemcpyDeviceToHost);
     if (err == hipSuccess) *ok = (bad == 0);
@@ -368,9 +370,14 @@ rt_status rt_enable_filtered(rt_engine *e) {
     if (err == hipSuccess && !r->corpus16) {
         if (!dev_alloc(reinterpret_cast<void **>(&r->corpus16),
                        sizeof(uint16_t) * (size_t)r->max_n * (size_t)r->max_d) ||
-            !dev_alloc(reinterpret_cast<void **>(&r->bad16), sizeof(uint32_t))) {
+            !dev_alloc(reinterpret_cast<void **>(&r->bad16), sizeof(uint32_t)) ||
+            !dev_alloc(reinterpret_cast<void **>(&r->err16), sizeof(float) * (size_t)ld)) {
             (void)hipFree(r->corpus16);
+            (void)hipFree(r->bad16);
+            (void)hipFree(r->err16);
             r->corpus16 = nullptr;
+            r->bad16 = nullptr;
+            r->err16 = nullptr;
             st = RT_ENOMEM;
         } else if (r->n > 0) {
             bool ok16 = false;
@@ -483,16 +490,16 @@ rt_status search_resident_filtered(rt_engine *e, const float *queries, int32_t q
     e->had_batch_kernel = false;
     if (err == hipSuccess) err = prologue(e, s);
     if (err == hipSuccess && batched) {
-        err = rt::launch_mfma_bound(r->corpus16, n, d, queries, q, r->rnorm, e->ubuf, uld, e->tmax, e->tile_ld,
-                                    e->num_cus, s);
+        err = rt::launch_mfma_bound(r->corpus16, n, d, queries, q, r->rnorm, r->err16, e->ubuf, uld, e->tmax,
+                                    e->tile_ld, e->num_cus, s);
         if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[3], s);
         if (err == hipSuccess) err = rt::launch_tile_threshold(e->tmax, e->tile_ld, n, q, k, e->thr, s);
         if (err == hipSuccess) {
             const Plan p2 = plan_stream(n, q, kp, 512, e->num_cus, kScoreWavesPerCu, rt::gemv_waves(kp));
             const rt::TreeLaunch t2 = tree_for(e, p2, kp, k, 1, out_idx, out_scores, nullptr, 0);
-            rt::FilterLaunch f;
-            f.cb = rt::filter_bound_factor_batched(d);
-            f.delta = rt::filter_underflow_slack_batched(d);
+            rt::FilterLaunch f;  // pass 2 reads only the bounds and thresholds
+            f.cb = 0.f;
+            f.delta = 0.f;
             f.ubuf = e->ubuf;
             f.uld = uld;
             f.thr = e->thr;

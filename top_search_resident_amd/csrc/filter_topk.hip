@@ -106,6 +106,47 @@ __global__ __launch_bounds__(256) void to_bf16_kernel(const float *__restrict__ 
     if (__ballot(flag != 0) != 0 && lane_id() == 0) atomicOr(bad, 1u);
 }
 
+// err[row] >= || x - bf16(x) || for every row x (bf16 as to_bf16_kernel rounds):
+// each difference is exact in fp32 (the bits that rounding drops) and its
+// square exact in fp64; the fp64 sum (error <= d 2^-53 relative) and square
+// root are rounded up by a relative 2^-40 and then to fp32 upward, so the value
+// is never below the true norm.  One wave per row; a value that overflows in
+// bf16 leaves the copy unusable anyway (to_bf16_kernel's flag).
+__global__ __launch_bounds__(256) void bf16_row_error_kernel(const float *__restrict__ corpus, int64_t n, int d,
+                                                             float *__restrict__ err) {
+    const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
+    const int lane = lane_id();
+    for (int64_t row = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave_in_group(); row < n; row += waves) {
+        const float *v = corpus + row * (int64_t)d;
+        double s = 0.0;
+        for (int c = lane; c < d; c += 64) {
+            const float x = v[c];
+            const uint32_t b = __float_as_uint(x);
+            const float xb = __uint_as_float(((b + 0x7fffu + ((b >> 16) & 1u)) >> 16) << 16);
+            const double e = (double)x - (double)xb;
+            s = fma(e, e, s);
+        }
+#pragma unroll
+        for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
+        if (lane == 0) {
+            const double up = sqrt(s) * (1.0 + 0x1p-40);
+            float f = (float)up;
+            if ((double)f < up) f = __uint_as_float(__float_as_uint(f) + 1u);  // next fp32 up (f >= 0)
+            err[row] = f;
+        }
+    }
+}
+
+hipError_t launch_bf16_row_errors(const float *corpus, int64_t n, int d, float *err, int num_cus,
+                                  hipStream_t stream) {
+    int64_t blocks = (n + 3) / 4;
+    const int64_t cap = (int64_t)num_cus * 16;
+    if (blocks > cap) blocks = cap;
+    if (blocks < 1) blocks = 1;
+    hipLaunchKernelGGL(bf16_row_error_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, corpus, n, d, err);
+    return hipGetLastError();
+}
+
 hipError_t launch_to_bf16(const float *corpus, uint16_t *corpus16, int64_t count, uint32_t *bad, int num_cus,
                           hipStream_t stream) {
     int64_t blocks = (count + 255) / 256;

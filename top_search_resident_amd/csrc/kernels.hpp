@@ -80,22 +80,27 @@ hipError_t launch_filtered_pass2(const float *corpus, int64_t n, int d, const fl
                                  hipStream_t stream);
 
 // Batched filtered search (mfma_filter.hip).  Depths with a compile-time
-// bf16 MFMA bound kernel (d in {256, 384, 512, 768, 1024}); its bound factor and
-// underflow slack (e = cb |q| |x| + delta max(|q|, 1) max(|x|, 1)).
+// bf16 MFMA bound kernel (d in {256, 384, 512, 768, 1024}); the bound's
+// constants: e = |q| (cr |x - bf16(x)| + cx |x|) + delta max(|q|, 1) max(|x|, 1).
 bool mfma_filter_ok(int d);
-float filter_bound_factor_batched(int d);
-float filter_underflow_slack_batched(int d);
+void filter_bound_constants_batched(int d, float *cr, float *cx, float *delta);
 hipError_t prepare_mfma_filter();
 // Pass 1 for q <= 32 queries: upper bounds ubuf[query * uld + row] and, per
 // query, the largest lower bound of every 32-row tile, tlb[query * tld + tile].
+// rnorm[i] = |x_i|, rerr[i] >= |x_i - bf16(x_i)| (both readable up to a
+// multiple of 32 rows past n).
 hipError_t launch_mfma_bound(const uint16_t *corpus16, int64_t n, int d, const float *queries, int q,
-                             const float *rnorm, float *ubuf, int64_t uld, float *tlb, int64_t tld, int num_cus,
-                             hipStream_t stream);
+                             const float *rnorm, const float *rerr, float *ubuf, int64_t uld, float *tlb, int64_t tld,
+                             int num_cus, hipStream_t stream);
 // Per query, thr[seg] <= the k-th largest of that query's tile maxima of lower
 // bounds tmax[seg * tld + tile] (a bin edge below it; -inf when n has fewer
 // than k tiles), so at least k rows have a lower bound at or above it.
 hipError_t launch_tile_threshold(const float *tmax, int64_t tld, int64_t n, int segments, int k, float *thr,
                                  hipStream_t stream);
+
+// err[row] >= the L2 norm of corpus row - its bf16 copy, for rows < n.
+hipError_t launch_bf16_row_errors(const float *corpus, int64_t n, int d, float *err, int num_cus,
+                                  hipStream_t stream);
 
 // corpus16[i] = bf16 of corpus[i] (round to nearest even), i < count; *bad is set
 // to 1 if any value is not finite or rounds to infinity (the caller clears it).

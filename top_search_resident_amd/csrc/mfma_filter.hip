@@ -28,17 +28,25 @@
 //     plain scan's arithmetic and selected.
 // So each query's answer is the plain single-query scan's answer, bit for bit.
 //
-// The bound (host: filter_bound_factor_batched / filter_underflow_slack_batched):
-//   |a - s| <= |x| |q| (2^-8 + 2^-16 + 2^-24 + gamma_D + 1.02 g) + slack,
-// where 2^-8 (+ 2^-16 + 2^-24) is the rounding of x to bf16 and of q to hi + lo,
-// gamma_D = D u / (1 - D u), u = 2^-24, the plain scan's fp32 sum, and
-// g = 8 D u / (1 - 8 D u) the matrix core's fp32 accumulation of the 2 D exact
-// products (any summation order with directed rounding at every step allows
-// 4 D u; the factor 2 leaves room for alignment inside the unit), applied to
-// sum |bf16(x)| (|hi| + |lo|) <= 1.02 sum |x q| <= 1.02 |x| |q| (Cauchy-Schwarz).
-// The slack, 16 D 2^-126 max(|q|, 1) max(|x|, 1), covers values, products and
-// partial sums below 2^-126 whether the unit flushes them or not.  A sum or
-// bound that is not finite gives the row the bounds -inf and +inf.
+// The bound (host: filter_bound_constants_batched).  With x~ = bf16(x),
+// q' = hi + lo, P = sum x q and A = sum x~ q' (exact), and u = 2^-24:
+//   |A - P| <= |x~ - x| |q'| + 2^-16 |x| |q|  (Cauchy-Schwarz on the rounding
+//              error vector; |q'| <= (1 + 2^-16) |q|),
+//   |a - A| <= 1.02 g |x| |q|, g = 8 d u / (1 - 8 d u): the matrix core's fp32
+//              accumulation of the 2 d exact products in any order and
+//              rounding direction allows 4 d u on sum |x~| (|hi| + |lo|) <=
+//              1.02 |x| |q|; the factor 2 leaves room for alignment inside
+//              the unit,
+//   |P - s| <= gamma_d |x| |q|, gamma_d = d u / (1 - d u) (the plain scan),
+// so e = |q| (cr |x~ - x| + cx |x|) + delta max(|q|, 1) max(|x|, 1) with
+// cr = (1 + 2^-16) and cx = 2^-16 + gamma_d + 1.02 g, both times (1 + 2^-10)
+// and rounded up (the 2^-10 absorbs the fp32 evaluation of e and a +- e), and
+// delta = 16 d 2^-126 for values, products and partial sums below 2^-126
+// whether the unit flushes them or not.  |x~ - x| per row is computed once with
+// the bf16 copy, rounded up (bf16_row_error_kernel); for rows of Gaussian
+// entries it is about 0.4 2^-8 |x|, against 2^-8 |x| for the elementwise
+// worst case.  A sum or bound that is not finite gives the row the bounds
+// -inf and +inf.
 #include <math.h>
 
 #include <utility>
@@ -94,8 +102,9 @@ __device__ __forceinline__ int bound_swizzle(int r) { return (r ^ (r >> 3)) & 7;
 template <int NCK, int NW, int KPF>
 __global__ __launch_bounds__(NW * 64) void mfma_bound_kernel(const uint16_t *__restrict__ corpus16, int64_t n,
                                                             const float *__restrict__ queries, int q,
-                                                            const float *__restrict__ rnorm, float cb, float delta,
-                                                            float *__restrict__ ubuf, int64_t uld,
+                                                            const float *__restrict__ rnorm,
+                                                            const float *__restrict__ rerr, float cr, float cx,
+                                                            float delta, float *__restrict__ ubuf, int64_t uld,
                                                             float *__restrict__ tlb, int64_t tld,
                                                             int64_t tiles_per_wave) {
     static_assert(KPF >= 1 && KPF < NCK && NCK % KPF == 0, "pipeline shape");
@@ -127,7 +136,8 @@ __global__ __launch_bounds__(NW * 64) void mfma_bound_kernel(const uint16_t *__r
     const int rsub = lane >> 3;  // row within a load instruction's 8 rows
     const int unit = lane & 7;   // 16-byte unit within the chunk
     const float qn = qn_s[m];
-    const float eq = cb * qn;
+    const float er = cr * qn;
+    const float ex = cx * qn;
     const float dl = delta * fmaxf(qn, 1.f);
     const bool has_q = m < q;
     const int64_t wave = (int64_t)blockIdx.x * NW + wv;
@@ -189,11 +199,11 @@ __global__ __launch_bounds__(NW * 64) void mfma_bound_kernel(const uint16_t *__r
         asm volatile("" : "+v"(qoff));
         const uint16_t *qhr = qh + m * dp + 8 * h + qoff;
         const uint16_t *qlr = ql + m * dp + 8 * h + qoff;
-        float4 rn[4];
-        {
-            const float *pr = rnorm + t * 32 + 4 * h;
+        float4 rn[4], re[4];
 #pragma unroll
-            for (int gg = 0; gg < 4; ++gg) rn[gg] = *reinterpret_cast<const float4 *>(pr + 8 * gg);
+        for (int gg = 0; gg < 4; ++gg) {
+            rn[gg] = *reinterpret_cast<const float4 *>(rnorm + t * 32 + 4 * h + 8 * gg);
+            re[gg] = *reinterpret_cast<const float4 *>(rerr + t * 32 + 4 * h + 8 * gg);
         }
         floatx16 acc;
 #pragma unroll
@@ -242,7 +252,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_bound_kernel(const uint16_t *__r
             for (int c = 0; c < 4; ++c) {
                 const float a = acc[4 * gg + c];
                 const float rv = comp4(rn[gg], c);
-                const float e = fmaf(eq, rv, dl * fmaxf(rv, 1.f));
+                const float e = fmaf(er, comp4(re[gg], c), fmaf(ex, rv, dl * fmaxf(rv, 1.f)));
                 // false for an overflowed or NaN sum or bound: the row is kept
                 const bool known = fabsf(a) <= __FLT_MAX__ && e <= __FLT_MAX__;
                 ubv[c] = known ? a + e : __builtin_huge_valf();
@@ -272,15 +282,15 @@ __global__ __launch_bounds__(NW * 64) void mfma_bound_kernel(const uint16_t *__r
 
 bool mfma_filter_ok(int d) { return d == 256 || d == 384 || d == 512 || d == 768 || d == 1024; }
 
-float filter_bound_factor_batched(int d) {
+void filter_bound_constants_batched(int d, float *cr, float *cx, float *delta) {
     const double u = ldexp(1.0, -24);
     const double gamma = d * u / (1.0 - d * u);
     const double g8 = 8.0 * d * u / (1.0 - 8.0 * d * u);
-    const double c = (ldexp(1.0, -8) + ldexp(1.0, -16) + ldexp(1.0, -24) + gamma + 1.02 * g8) * (1.0 + ldexp(1.0, -10));
-    return nextafterf((float)c, INFINITY);
+    const double slack = 1.0 + ldexp(1.0, -10);
+    *cr = nextafterf((float)((1.0 + ldexp(1.0, -16)) * slack), INFINITY);
+    *cx = nextafterf((float)((ldexp(1.0, -16) + gamma + 1.02 * g8) * slack), INFINITY);
+    *delta = ldexpf((float)d, -122);
 }
-
-float filter_underflow_slack_batched(int d) { return ldexpf((float)d, -122); }
 
 // Pass 1's shapes: (chunks NCK = d / 64, waves per workgroup NW, chunks in
 // flight per wave KPF).  One workgroup per CU; NW is what the LDS holds next to
@@ -303,18 +313,18 @@ hipError_t prepare_mfma_filter() {
 }
 
 hipError_t launch_mfma_bound(const uint16_t *corpus16, int64_t n, int d, const float *queries, int q,
-                             const float *rnorm, float *ubuf, int64_t uld, float *tlb, int64_t tld, int num_cus,
-                             hipStream_t stream) {
+                             const float *rnorm, const float *rerr, float *ubuf, int64_t uld, float *tlb, int64_t tld,
+                             int num_cus, hipStream_t stream) {
     const int64_t tiles = (n + 31) / 32;
-    const float cb = filter_bound_factor_batched(d);
-    const float delta = filter_underflow_slack_batched(d);
+    float cr, cx, delta;
+    filter_bound_constants_batched(d, &cr, &cx, &delta);
 #define RT_LAUNCH(NCK, NW, KPF)                                                                                 \
     if (d == NCK * 64) {                                                                                        \
         const int64_t tpw = (tiles + (int64_t)num_cus * NW - 1) / ((int64_t)num_cus * NW);                      \
         const int64_t blocks = (tiles + tpw * NW - 1) / (tpw * NW);                                             \
         hipLaunchKernelGGL((mfma_bound_kernel<NCK, NW, KPF>), dim3((unsigned)blocks), dim3(64 * NW),            \
-                           bound_lds_bytes(d, NW), stream, corpus16, n, queries, q, rnorm, cb, delta, ubuf, uld, \
-                           tlb, tld, tpw);                                                                      \
+                           bound_lds_bytes(d, NW), stream, corpus16, n, queries, q, rnorm, rerr, cr, cx, delta,  \
+                           ubuf, uld, tlb, tld, tpw);                                                           \
         return hipGetLastError();                                                                               \
     }
     RT_BOUND_DEPTHS(RT_LAUNCH)
