@@ -389,7 +389,7 @@ def batched_filtered_leg(args, torch, eng, qdev, ks, n, d):
     wall = time.perf_counter() - t0
     eng.profile(False)
     tiles = (n + 31) // 32
-    pass1_bytes = n * d * 2 + q * d * 4 + n * 4 + q * n * 4 + q * tiles * 4
+    pass1_bytes = n * d * 2 + q * d * 4 + n * 8 + q * n * 4 + q * tiles * 4  # bf16 rows, queries, two norms, bounds
     all_p1 = float(np.mean(np.concatenate([np.asarray(p1[k]) for k in ks])))
     return {"value": q * steps * len(ks) / wall, "unit": "queries/s", "steps": steps,
             "identical_to_single_query_scan": True,

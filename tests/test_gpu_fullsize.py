@@ -111,6 +111,22 @@ def test_batched_500k():
         for k in w["ks"]:
             for qi in range(qs.shape[0]):
                 check_retrieval(res[k][0][qi], res[k][1][qi], o_idx[qi, :k], o_sc[qi, :k], corpus, qs[qi], oracle)
+        # the same batch through the bf16 matrix-core filter (the benchmark's
+        # filtered leg): every query's answer is the single-query scan's, bit
+        # for bit, and passes the oracle rules
+        print(f"[fullsize] {name}: filtered batch", flush=True)
+        eng.enable_filtered()
+        for k in w["ks"]:
+            f_idx, f_sc = eng.search_resident_filtered(qdev, k)
+            plain = [eng.search_resident(qdev[qi:qi + 1], k) for qi in range(qs.shape[0])]
+            torch.cuda.synchronize()
+            p_idx = np.concatenate([p[0].cpu().numpy() for p in plain])
+            p_sc = np.concatenate([p[1].cpu().numpy() for p in plain])
+            f_idx, f_sc = f_idx.cpu().numpy(), f_sc.cpu().numpy()
+            assert np.array_equal(f_idx, p_idx), k
+            assert np.array_equal(f_sc.view(np.uint32), p_sc.view(np.uint32)), k
+            for qi in range(qs.shape[0]):
+                check_retrieval(f_idx[qi], f_sc[qi], o_idx[qi, :k], o_sc[qi, :k], corpus, qs[qi], oracle)
 
 
 def test_cosine_1m():
