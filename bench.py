@@ -19,9 +19,10 @@ cpu_baseline: the CPU oracle (fp64 dots + full sort) timed on this host's cores
 on a bounded sample of the same queries; the same sample's GPU answers are
 checked against it (R1-R4) before the line is printed.
 
-filtered_exact: the same queries through search_resident_filtered (a bf16 copy
-scanned first, fp32 rows re-scored only where certified bounds reach the k-th
-lower bound); its answers are checked to equal the plain scan's bit for bit
+filtered_exact: the same queries through search_resident_filtered (a reduced-
+precision copy scanned first -- fp8 codes for this corpus size, bf16 for small
+ones -- and fp32 rows re-scored only where certified bounds reach the
+threshold); its answers are checked to equal the plain scan's bit for bit
 before it is timed.  Reported beside `value`, which stays the plain fp32 scan.
 
 Other workloads (--workload): c1_10k_384, c2_50k_768, c2_100k_768,
@@ -198,15 +199,19 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
 
     if args.filtered:
         eng.enable_filtered()
+        eng.set_filter_storage(args.filter_storage)
     wall, lat, part, merge = time_search(eng, torch, qdev, ks, args.steps, args.warmup, metric=args.metric,
                                          filtered=args.filtered)
+    path = eng.filter_path_used() if args.filtered else None
     nq = args.steps * len(ks)
     qps = nq / wall
     # algorithmic bytes per launch of the dominant kernel: the corpus and the
     # query, plus the rows' norms for the cosine metric; for the filtered search
-    # the bf16 pass: the bf16 corpus, the rows' norms and the upper bounds it
-    # writes
-    if args.filtered:
+    # its first pass: the bf16 rows (or fp8 codes with per-row scales and error
+    # norms), the rows' norms and the upper bounds it writes
+    if args.filtered and path == "fp8":
+        corpus_bytes = n * d + d * 4 + n * 12 + n * 4
+    elif args.filtered:
         corpus_bytes = n * d * 2 + d * 4 + n * 4 + n * 4
     else:
         corpus_bytes = n * d * 4 + d * 4 + (n * 4 if args.metric == "cosine" else 0)
@@ -227,7 +232,7 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
     achieved = corpus_bytes / (avg_ms * 1e-3) / 1e9
     line = {
         "metric": (METRIC if (name, args.metric, args.filtered) == ("c3_1m_1024", "dot", False)
-                   else f"queries/s + p50 latency ({name}, {'bf16-filtered exact ' if args.filtered else ''}"
+                   else f"queries/s + p50 latency ({name}, {f'{path}-filtered exact ' if args.filtered else ''}"
                         f"{args.metric})"),
         "value": qps, "unit": "queries/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": wall / args.steps * 1e3, "higher_is_better": True, "scaling": "weak",
@@ -235,7 +240,7 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
         "config": {"workload": f"{name}: resident {n} x {d} fp32 corpus (Gaussian, L2-normalised rows), "
                                f"sequential single queries, K in {list(ks)}; one step = one query per K"
                                + ("; cosine metric" if args.metric == "cosine" else "")
-                               + ("; bf16-filtered exact search (answers identical to the fp32 scan)"
+                               + (f"; {path}-filtered exact search (answers identical to the fp32 scan)"
                                   if args.filtered else ""),
                    "n": n, "d": d, "ks": list(ks), "queries_per_step": len(ks), "metric": args.metric,
                    "filtered": bool(args.filtered)},
@@ -246,7 +251,8 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
                                  if (n, d, ks, args.metric, args.filtered) == (1_000_000, 1024, (8, 32, 100), "dot", False)
                                  else None),
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, profiles/)",
-                     "kernel": ("gemv_bound_kernel (bf16 pass of the filtered search)" if args.filtered else
+                     "kernel": ((("gemv_bound8_kernel" if path == "fp8" else "gemv_bound_kernel")
+                                 + f" ({path} first pass of the filtered search)") if args.filtered else
                                 "gemv_topk_kernel (fused scoring, per-wave top-K lists and merge tree)"),
                      "bytes_per_launch": corpus_bytes, "avg_launch_us": avg_ms * 1e3},
         "input_gen_s": gen_s,
@@ -277,11 +283,14 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
 
 
 def filtered_leg(args, torch, eng, qdev, ks, n, d):
-    """The same queries through search_resident_filtered (bf16 pass + exact fp32
-    re-rank of the rows whose bounds reach the k-th lower bound): its answers are
-    first checked to be identical, bit for bit, to the plain scan's on a sample,
-    then timed like the plain scan."""
+    """The same queries through search_resident_filtered (a reduced-precision
+    first pass -- bf16, or fp8 for a large corpus, as the engine chooses unless
+    --filter-storage says otherwise -- then the exact fp32 re-rank of the rows
+    whose bounds reach the threshold): its answers are first checked to be
+    identical, bit for bit, to the plain scan's on a sample, then timed like the
+    plain scan."""
     eng.enable_filtered()
+    eng.set_filter_storage(args.filter_storage)
     for qi in range(min(5, qdev.shape[0])):
         for k in ks:
             a = eng.search_resident(qdev[qi:qi + 1], k)
@@ -289,18 +298,22 @@ def filtered_leg(args, torch, eng, qdev, ks, n, d):
             torch.cuda.synchronize()
             if not (torch.equal(a[0], b[0]) and torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))):
                 raise SystemExit(f"filtered search differs from the plain scan (query {qi}, k {k})")
+    path = eng.filter_path_used()
     steps = min(args.steps, 300)
     wall, lat, part, merge = time_search(eng, torch, qdev, ks, steps, args.warmup, filtered=True)
-    pass1_bytes = n * d * 2 + d * 4 + n * 4 + n * 4  # bf16 rows, query, row norms, upper bounds written
+    if path == "fp8":  # codes, query, row norms + scales + error norms, upper bounds written
+        pass1_bytes, kernel = n * d + d * 4 + n * 12 + n * 4, "gemv_bound8_kernel"
+    else:  # bf16 rows, query, row norms, upper bounds written
+        pass1_bytes, kernel = n * d * 2 + d * 4 + n * 4 + n * 4, "gemv_bound_kernel"
     p1 = float(np.mean(np.concatenate([np.asarray(part[k]) for k in ks])))
     return {"value": steps * len(ks) / wall, "unit": "queries/s", "steps": steps,
-            "identical_to_fp32_scan": True,
+            "identical_to_fp32_scan": True, "first_pass_storage": path,
             "per_k": {str(k): {"p50_us": pct(lat[k], 50), "p99_us": pct(lat[k], 99),
                                "device_p50_us": pct(np.asarray(merge[k]) * 1e3, 50),
-                               "bf16_pass_avg_us": float(np.mean(part[k]) * 1e3)} for k in ks},
-            "bf16_pass": {"kernel": "gemv_bound_kernel", "bytes_per_launch": pass1_bytes,
-                          "avg_launch_us": p1 * 1e3, "achieved_gbs": pass1_bytes / (p1 * 1e-3) / 1e9,
-                          "frac_of_hbm_peak": pass1_bytes / (p1 * 1e-3) / 1e9 / HBM_PEAK_GBS}}
+                               "first_pass_avg_us": float(np.mean(part[k]) * 1e3)} for k in ks},
+            "first_pass": {"kernel": kernel, "bytes_per_launch": pass1_bytes,
+                           "avg_launch_us": p1 * 1e3, "achieved_gbs": pass1_bytes / (p1 * 1e-3) / 1e9,
+                           "frac_of_hbm_peak": pass1_bytes / (p1 * 1e-3) / 1e9 / HBM_PEAK_GBS}}
 
 
 def run_concurrent(args, torch, eng, corpus, qhost, qdev, ks, name, gen_s):
@@ -568,6 +581,8 @@ def main():
                     help="similarity for the retrieval workloads (the headline line is the inner product)")
     ap.add_argument("--filtered", action="store_true",
                     help="single-query workloads: search_resident_filtered (bf16 pass + exact fp32 re-rank)")
+    ap.add_argument("--filter-storage", choices=["auto", "bf16", "fp8"], default="auto",
+                    help="first pass of the single-query filtered search (auto: fp8 for a large corpus)")
     ap.add_argument("--no-filtered-leg", action="store_true",
                     help="skip the extra timing of search_resident_filtered on single-query workloads")
     ap.add_argument("--streams", type=int, default=1,

@@ -62,6 +62,18 @@ typedef enum { RT_DTYPE_INT32 = 0, RT_DTYPE_FLOAT32 = 1 } rt_dtype;
  * with cosine enabled, divides it by the query's and the row's L2 norms). */
 typedef enum { RT_METRIC_DOT = 0, RT_METRIC_COSINE = 1 } rt_metric;
 
+/* The first pass of a single-query filtered search (rt_set_filter_storage). */
+typedef enum { RT_FILTER_AUTO = 0, RT_FILTER_BF16 = 1, RT_FILTER_FP8 = 2 } rt_filter_storage;
+
+/* What the last search_resident_filtered call ran (rt_filter_path_used). */
+typedef enum {
+    RT_FILTER_PATH_NONE = 0,        /* no filtered search yet */
+    RT_FILTER_PATH_PLAIN = 1,       /* the plain fp32 scan (copy unusable or depth not covered) */
+    RT_FILTER_PATH_BF16 = 2,        /* bf16 first pass, one query per segment */
+    RT_FILTER_PATH_FP8 = 3,         /* fp8 first pass, one query per segment */
+    RT_FILTER_PATH_BF16_MATRIX = 4  /* bf16 matrix-core first pass for the whole batch */
+} rt_filter_path;
+
 /*
  * Create an engine on HIP device `device` and allocate, once, everything later
  * calls need, sized for the worst case: a corpus of max_n x max_d fp32, results
@@ -144,9 +156,11 @@ rt_status search_resident_metric(rt_engine *e, const float *queries, int32_t q, 
 
 /*
  * Prepare an engine for search_resident_filtered: allocate, once, a bf16 copy
- * of the resident corpus (max_n x max_d x 2 bytes, shared by every engine that
- * shares the corpus, refreshed by each upload) and this engine's scratch for
- * the filtered search (4 x max_q x roundup(max_n, 64) bytes of row bounds).
+ * of the resident corpus (max_n x max_d x 2 bytes) and an fp8 copy (max_n x
+ * max_d bytes of e4m3 codes and 8 bytes per row of scales and error norms),
+ * shared by every engine that shares the corpus and refreshed by each upload,
+ * and this engine's scratch for the filtered search (4 x max_q x
+ * roundup(max_n, 64) bytes of row bounds).
  * Like rt_engine_create, it allocates: call it at set-up, not per query.
  * RT_EINVAL for NULL, RT_ENOMEM if the memory is not available.
  */
@@ -174,6 +188,23 @@ rt_status rt_enable_filtered(rt_engine *e);
  * call runs the plain fp32 scan instead (same answer).  Inner product only.
  * Asynchronous on `stream`.
  */
+/*
+ * Which first pass a single-query filtered search takes (host-only setting of
+ * the engine): RT_FILTER_BF16, RT_FILTER_FP8 (rows stored as e4m3 codes of
+ * row / s with a power-of-two scale s per row: a quarter of the fp32 bytes,
+ * bound e = |q| (cr |x - x~| + cx |x|) + delta max(|q|, 1) max(s, 1), constants
+ * from rt_filter_bounds_fp8; wider than bf16's, so more rows reach the
+ * re-rank), or RT_FILTER_AUTO (the default: fp8 from 2^26 corpus elements
+ * on).  The fp8 pass covers d in {256, 384, 512, 768, 1024, 1536, 2048} and a
+ * corpus whose values are finite; otherwise the bf16 pass runs.  Batches on an
+ * engine with batch buffers always take the bf16 matrix-core pass.  The answer
+ * is the same in every case.  RT_EINVAL for NULL or an unknown value.
+ */
+rt_status rt_set_filter_storage(rt_engine *e, int32_t storage);
+
+/* The rt_filter_path of the last search_resident_filtered call (host-only). */
+int32_t rt_filter_path_used(const rt_engine *e);
+
 rt_status search_resident_filtered(rt_engine *e, const float *queries, int32_t q, int32_t k,
                                    int32_t *out_idx, float *out_scores, void *stream);
 
@@ -267,6 +298,20 @@ rt_status rt_filter_bounds(int32_t d, float *out2);
  * NULL out3.
  */
 rt_status rt_filter_bounds_batched(int32_t d, float *out3);
+
+/*
+ * The constants of the fp8 first pass, host-only: out3 = [cr, cx, delta] with
+ *   |a - s| <= |q| (cr |x - x~| + cx |x|) + delta max(|q|, 1) max(sc, 1),
+ * where x~ = sc dec(codes) is the stored row (sc its power-of-two scale,
+ * |x - x~| computed per row from the codes and rounded up), a = sc times the
+ * fp32 sum of dec(codes) q and s the single-query scan's fp32 score.
+ * cr = (1 + gamma_d) (1 + 2^-10), cx = 2 gamma_d (1 + 2^-10), each rounded up
+ * to fp32, gamma_d = d 2^-24 / (1 - d 2^-24): Cauchy-Schwarz on the rounding
+ * error vector, gamma_d for a's fp32 sum over sum |x~ q| <= (|x| + |x - x~|) |q|
+ * and gamma_d for the scan's.  delta = 4 d 2^-126 covers underflow.  RT_EINVAL
+ * for d < 1 or a NULL out3.
+ */
+rt_status rt_filter_bounds_fp8(int32_t d, float *out3);
 
 #ifdef __cplusplus
 }

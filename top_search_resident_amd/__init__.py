@@ -137,6 +137,21 @@ class ResidentTopK:
         search_resident_filtered (once, at set-up)."""
         _check(self._lib.rt_enable_filtered(self._h), "rt_enable_filtered", self._h)
 
+    _STORAGE = {"auto": 0, "bf16": 1, "fp8": 2}
+    _PATHS = {0: None, 1: "plain", 2: "bf16", 3: "fp8", 4: "bf16_matrix"}
+
+    def set_filter_storage(self, storage):
+        """First pass of a single-query filtered search: "auto" (fp8 for large
+        corpora), "bf16" or "fp8".  The answers are the same."""
+        if storage not in self._STORAGE:
+            raise ValueError(f"storage must be one of {sorted(self._STORAGE)}")
+        _check(self._lib.rt_set_filter_storage(self._h, self._STORAGE[storage]), "rt_set_filter_storage", self._h)
+
+    def filter_path_used(self):
+        """What the last search_resident_filtered call ran: "plain", "bf16",
+        "fp8", "bf16_matrix" (a batch), or None."""
+        return self._PATHS.get(int(self._lib.rt_filter_path_used(self._h)))
+
     def search_resident_filtered(self, queries, k, out_idx=None, out_scores=None, stream=None):
         """Exact inner-product top-k (for each query, the answer
         search_resident gives for that query alone) that reads a bf16 copy of

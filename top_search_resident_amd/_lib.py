@@ -18,7 +18,7 @@ EXPORTS = (
     "search_resident_metric", "rt_enable_filtered", "search_resident_filtered", "topk_select", "rt_status_string", "rt_last_hip_error", "rt_profile_enable",
     "rt_profile_read", "rt_engine_info", "rt_check_create", "rt_check_upload",
     "rt_check_search", "rt_check_search_metric", "rt_check_select", "rt_filter_bounds",
-    "rt_filter_bounds_batched",
+    "rt_filter_bounds_batched", "rt_filter_bounds_fp8", "rt_set_filter_storage", "rt_filter_path_used",
 )
 
 _lib = None
@@ -70,6 +70,9 @@ def load():
         "rt_check_select": ([i32, vp, i32, i64, i32, vp, vp], ctypes.c_int),
         "rt_filter_bounds": ([i32, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
         "rt_filter_bounds_batched": ([i32, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
+        "rt_filter_bounds_fp8": ([i32, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
+        "rt_set_filter_storage": ([vp, i32], ctypes.c_int),
+        "rt_filter_path_used": ([vp], ctypes.c_int32),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)
@@ -94,6 +97,15 @@ def filter_bounds(d):
     if st != RT_OK:
         raise ResidentTopKError(st, "rt_filter_bounds")
     return float(out[0]), float(out[1])
+
+
+def filter_bounds_fp8(d):
+    """(cr, cx, delta) of the fp8 first pass's bound at depth d (host-only)."""
+    out = (ctypes.c_float * 3)()
+    st = load().rt_filter_bounds_fp8(int(d), out)
+    if st != RT_OK:
+        raise ResidentTopKError(st, "rt_filter_bounds_fp8")
+    return float(out[0]), float(out[1]), float(out[2])
 
 
 def filter_bounds_batched(d):

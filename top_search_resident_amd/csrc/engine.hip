@@ -15,6 +15,7 @@
 #include <new>
 
 #include "../../include/resident_topk.h"
+#include "filter8_host.hpp"
 #include "kernels.hpp"
 
 namespace {
@@ -67,6 +68,10 @@ Plan plan_stream(int64_t units, int segments, int kp, int64_t min_per_wave, int 
     return p;
 }
 
+// Corpus size (n x d elements) from which a single-query filtered search takes
+// the fp8 first pass when the engine leaves the choice to the library.
+constexpr int64_t kFp8MinElements = int64_t(1) << 26;
+
 // Fewest rows a scoring wave streams: about 24 KB of rows (4 to 32 rows).  A
 // small corpus then spreads over more CUs with shorter chains of dependent
 // steps per wave (measured on MI355X, p50 per query: 10k x 384 15.8 -> 14.2 us,
@@ -93,6 +98,11 @@ struct rt_resident {
     uint16_t *corpus16 = nullptr;  // bf16 copy, max_n x max_d (after rt_enable_filtered)
     uint32_t *bad16 = nullptr;     // set by the conversion when a value is not finite in bf16
     float *err16 = nullptr;        // per row, an upper bound on |row - bf16 copy| (after rt_enable_filtered)
+    uint8_t *corpus8 = nullptr;    // e4m3 codes of each row / its scale, max_n x max_d (after rt_enable_filtered)
+    float *scale8 = nullptr;       // per row, the power-of-two scale of its codes
+    float *err8 = nullptr;         // per row, an upper bound on |row - scale x decoded codes|
+    uint32_t *bad8 = nullptr;      // set by the conversion when a value is not finite
+    bool copy8_ok = false;         // the fp8 copy matches the resident corpus and is usable
     bool copy16_ok = false;        // the bf16 copy matches the resident corpus and is usable
 };
 
@@ -108,6 +118,8 @@ struct rt_engine {
     uint32_t *counters = nullptr;   // kMaxQ x kMaxWgsPerSeg arrival counters
     float *ubuf = nullptr;          // filtered search: max_q x roundup(max_n, 64) upper bounds
     float *thr = nullptr;           // filtered search: max_q thresholds
+    int32_t filter_storage = RT_FILTER_AUTO;  // first pass of a single-query filtered search
+    int32_t filter_path = RT_FILTER_PATH_NONE;  // what the last filtered call ran
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
     bool profiling = false;
     bool had_batch_kernel = false;
@@ -185,6 +197,20 @@ rt_status rt_filter_bounds(int32_t d, float *out2) {
     return RT_OK;
 }
 
+rt_status rt_filter_bounds_fp8(int32_t d, float *out3) {
+    if (d < 1 || out3 == nullptr) return RT_EINVAL;
+    rt::filter_bound_constants_fp8(d, &out3[0], &out3[1], &out3[2]);
+    return RT_OK;
+}
+
+rt_status rt_set_filter_storage(rt_engine *e, int32_t storage) {
+    if (!e || (storage != RT_FILTER_AUTO && storage != RT_FILTER_BF16 && storage != RT_FILTER_FP8)) return RT_EINVAL;
+    e->filter_storage = storage;
+    return RT_OK;
+}
+
+int32_t rt_filter_path_used(const rt_engine *e) { return e ? e->filter_path : RT_FILTER_PATH_NONE; }
+
 rt_status rt_filter_bounds_batched(int32_t d, float *out3) {
     if (d < 1 || out3 == nullptr) return RT_EINVAL;
     rt::filter_bound_constants_batched(d, &out3[0], &out3[1], &out3[2]);
@@ -211,6 +237,10 @@ void rt_engine_destroy(rt_engine *e) {
         (void)hipFree(e->res->corpus16);
         (void)hipFree(e->res->bad16);
         (void)hipFree(e->res->err16);
+        (void)hipFree(e->res->corpus8);
+        (void)hipFree(e->res->scale8);
+        (void)hipFree(e->res->err8);
+        (void)hipFree(e->res->bad8);
         delete e->res;
     }
     (void)hipSetDevice(prev);
@@ -340,6 +370,20 @@ static hipError_t refresh_copy16(rt_resident *r, int64_t n, int32_t d, int num_c
     return err;
 }
 
+// Rebuild the fp8 copy (synchronous); *ok tells whether it is usable (a depth
+// with an fp8 first pass and every value finite).
+static hipError_t refresh_copy8(rt_resident *r, int64_t n, int32_t d, int num_cus, bool *ok) {
+    *ok = false;
+    if (!rt::fp8_search_ok(d)) return hipSuccess;
+    hipError_t err = hipMemset(r->bad8, 0, sizeof(uint32_t));
+    if (err == hipSuccess)
+        err = rt::launch_to_fp8(r->corpus, n, d, r->corpus8, r->scale8, r->err8, r->bad8, num_cus, nullptr);
+    uint32_t bad = 1;
+    if (err == hipSuccess) err = hipMemcpy(&bad, r->bad8, sizeof(uint32_t), hipMemcpyDeviceToHost);
+    if (err == hipSuccess) *ok = (bad == 0);
+    return err;
+}
+
 rt_status upload_corpus_rowmajor(rt_engine *e, const float *corpus, int64_t n, int32_t d) {
     if (!e) return RT_EINVAL;
     rt_resident *r = e->res;
@@ -354,8 +398,10 @@ rt_status upload_corpus_rowmajor(rt_engine *e, const float *corpus, int64_t n, i
     // computed once per upload.
     if (err == hipSuccess) err = rt::launch_row_norms(r->corpus, n, d, r->rnorm, e->num_cus, nullptr);
     r->copy16_ok = false;
-    bool ok16 = false;
+    r->copy8_ok = false;
+    bool ok16 = false, ok8 = false;
     if (err == hipSuccess && r->corpus16) err = refresh_copy16(r, n, d, e->num_cus, &ok16);
+    if (err == hipSuccess && r->corpus8) err = refresh_copy8(r, n, d, e->num_cus, &ok8);
     if (err == hipSuccess) err = hipDeviceSynchronize();
     (void)hipSetDevice(prev);
     if (err != hipSuccess) {
@@ -366,6 +412,7 @@ rt_status upload_corpus_rowmajor(rt_engine *e, const float *corpus, int64_t n, i
     r->n = n;
     r->d = d;
     r->copy16_ok = ok16;
+    r->copy8_ok = ok8;
     return RT_OK;
 }
 
@@ -393,6 +440,26 @@ rt_status rt_enable_filtered(rt_engine *e) {
             bool ok16 = false;
             err = refresh_copy16(r, r->n, r->d, e->num_cus, &ok16);
             if (err == hipSuccess) r->copy16_ok = ok16;
+        }
+    }
+    if (err == hipSuccess && st == RT_OK && !r->corpus8) {
+        if (!dev_alloc(reinterpret_cast<void **>(&r->corpus8), (size_t)r->max_n * (size_t)r->max_d) ||
+            !dev_alloc(reinterpret_cast<void **>(&r->scale8), sizeof(float) * (size_t)ld) ||
+            !dev_alloc(reinterpret_cast<void **>(&r->err8), sizeof(float) * (size_t)ld) ||
+            !dev_alloc(reinterpret_cast<void **>(&r->bad8), sizeof(uint32_t))) {
+            (void)hipFree(r->corpus8);
+            (void)hipFree(r->scale8);
+            (void)hipFree(r->err8);
+            (void)hipFree(r->bad8);
+            r->corpus8 = nullptr;
+            r->scale8 = nullptr;
+            r->err8 = nullptr;
+            r->bad8 = nullptr;
+            st = RT_ENOMEM;
+        } else if (r->n > 0) {
+            bool ok8 = false;
+            err = refresh_copy8(r, r->n, r->d, e->num_cus, &ok8);
+            if (err == hipSuccess) r->copy8_ok = ok8;
         }
     }
     if (err == hipSuccess && st == RT_OK && !e->ubuf) {
@@ -486,8 +553,10 @@ rt_status search_resident_filtered(rt_engine *e, const float *queries, int32_t q
     rt_resident *r = e->res;
     const int64_t n = r->n;
     const int d = r->d;
-    if (!r->copy16_ok || !rt::filtered_search_ok(d))  // same answer through the plain scan
+    if (!r->copy16_ok || !rt::filtered_search_ok(d)) {  // same answer through the plain scan
+        e->filter_path = RT_FILTER_PATH_PLAIN;
         return search_resident_metric(e, queries, q, k, RT_METRIC_DOT, out_idx, out_scores, stream);
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     int prev = 0;
     (void)hipGetDevice(&prev);
@@ -500,6 +569,7 @@ rt_status search_resident_filtered(rt_engine *e, const float *queries, int32_t q
     e->had_batch_kernel = false;
     if (err == hipSuccess) err = prologue(e, s);
     if (err == hipSuccess && batched) {
+        e->filter_path = RT_FILTER_PATH_BF16_MATRIX;
         err = rt::launch_mfma_bound(r->corpus16, n, d, queries, q, r->rnorm, r->err16, e->ubuf, uld, e->tmax,
                                     e->tile_ld, e->num_cus, s);
         if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[3], s);
@@ -517,6 +587,12 @@ rt_status search_resident_filtered(rt_engine *e, const float *queries, int32_t q
         }
         e->had_batch_kernel = e->profiling;
     } else if (err == hipSuccess) {
+        // The fp8 first pass reads a quarter of the fp32 bytes but lets far more
+        // rows through to the re-rank (a wider bound): chosen for large corpora,
+        // or when the engine asks for it.
+        const bool fp8 = r->copy8_ok && rt::fp8_search_ok(d) &&
+                         (e->filter_storage == RT_FILTER_FP8 ||
+                          (e->filter_storage == RT_FILTER_AUTO && n * (int64_t)d >= kFp8MinElements));
         const Plan p1 = plan_stream(n, q, kp, 32, e->num_cus, kScoreWavesPerCu, rt::gemv_waves(kp));
         const Plan p2 = plan_stream(n, q, kp, 512, e->num_cus, kScoreWavesPerCu, rt::gemv_waves(kp));
         const rt::TreeLaunch t1 = tree_for(e, p1, kp, k, 3, nullptr, e->thr, nullptr, 0);
@@ -528,8 +604,16 @@ rt_status search_resident_filtered(rt_engine *e, const float *queries, int32_t q
         f.uld = uld;
         f.thr = e->thr;
         e->had_batch_kernel = e->profiling;
-        err = rt::launch_filtered_search(r->corpus, r->corpus16, r->rnorm, n, d, queries, q, p1.per_wave, p1.wgs, t1,
-                                         p2.per_wave, p2.wgs, t2, f, e->profiling ? e->ev[3] : nullptr, s);
+        if (fp8) {
+            e->filter_path = RT_FILTER_PATH_FP8;
+            err = rt::launch_filtered_search8(r->corpus, r->corpus8, r->scale8, r->err8, r->rnorm, n, d, queries, q,
+                                              p1.per_wave, p1.wgs, t1, p2.per_wave, p2.wgs, t2, f,
+                                              e->profiling ? e->ev[3] : nullptr, s);
+        } else {
+            e->filter_path = RT_FILTER_PATH_BF16;
+            err = rt::launch_filtered_search(r->corpus, r->corpus16, r->rnorm, n, d, queries, q, p1.per_wave, p1.wgs,
+                                             t1, p2.per_wave, p2.wgs, t2, f, e->profiling ? e->ev[3] : nullptr, s);
+        }
     }
     if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[1], s);
     (void)hipSetDevice(prev);
