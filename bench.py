@@ -207,10 +207,10 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
     qps = nq / wall
     # algorithmic bytes per launch of the dominant kernel: the corpus and the
     # query, plus the rows' norms for the cosine metric; for the filtered search
-    # its first pass: the bf16 rows (or fp8 codes with per-row scales and error
-    # norms), the rows' norms and the upper bounds it writes
+    # its first pass: the bf16 rows and the rows' norms (or the fp8 codes and a
+    # {scale, bound part} pair per row) and the upper bounds it writes
     if args.filtered and path == "fp8":
-        corpus_bytes = n * d + d * 4 + n * 12 + n * 4
+        corpus_bytes = n * d + d * 4 + n * 8 + n * 4
     elif args.filtered:
         corpus_bytes = n * d * 2 + d * 4 + n * 4 + n * 4
     else:
@@ -301,8 +301,8 @@ def filtered_leg(args, torch, eng, qdev, ks, n, d):
     path = eng.filter_path_used()
     steps = min(args.steps, 300)
     wall, lat, part, merge = time_search(eng, torch, qdev, ks, steps, args.warmup, filtered=True)
-    if path == "fp8":  # codes, query, row norms + scales + error norms, upper bounds written
-        pass1_bytes, kernel = n * d + d * 4 + n * 12 + n * 4, "gemv_bound8_kernel"
+    if path == "fp8":  # codes, query, per-row {scale, bound part}, upper bounds written
+        pass1_bytes, kernel = n * d + d * 4 + n * 8 + n * 4, "gemv_bound8_kernel"
     else:  # bf16 rows, query, row norms, upper bounds written
         pass1_bytes, kernel = n * d * 2 + d * 4 + n * 4 + n * 4, "gemv_bound_kernel"
     p1 = float(np.mean(np.concatenate([np.asarray(part[k]) for k in ks])))

@@ -99,8 +99,7 @@ struct rt_resident {
     uint32_t *bad16 = nullptr;     // set by the conversion when a value is not finite in bf16
     float *err16 = nullptr;        // per row, an upper bound on |row - bf16 copy| (after rt_enable_filtered)
     uint8_t *corpus8 = nullptr;    // e4m3 codes of each row / its scale, max_n x max_d (after rt_enable_filtered)
-    float *scale8 = nullptr;       // per row, the power-of-two scale of its codes
-    float *err8 = nullptr;         // per row, an upper bound on |row - scale x decoded codes|
+    float2 *meta8 = nullptr;       // per row {power-of-two scale s, the row's part of the fp8 bound}
     uint32_t *bad8 = nullptr;      // set by the conversion when a value is not finite
     bool copy8_ok = false;         // the fp8 copy matches the resident corpus and is usable
     bool copy16_ok = false;        // the bf16 copy matches the resident corpus and is usable
@@ -238,8 +237,7 @@ void rt_engine_destroy(rt_engine *e) {
         (void)hipFree(e->res->bad16);
         (void)hipFree(e->res->err16);
         (void)hipFree(e->res->corpus8);
-        (void)hipFree(e->res->scale8);
-        (void)hipFree(e->res->err8);
+        (void)hipFree(e->res->meta8);
         (void)hipFree(e->res->bad8);
         delete e->res;
     }
@@ -377,7 +375,7 @@ static hipError_t refresh_copy8(rt_resident *r, int64_t n, int32_t d, int num_cu
     if (!rt::fp8_search_ok(d)) return hipSuccess;
     hipError_t err = hipMemset(r->bad8, 0, sizeof(uint32_t));
     if (err == hipSuccess)
-        err = rt::launch_to_fp8(r->corpus, n, d, r->corpus8, r->scale8, r->err8, r->bad8, num_cus, nullptr);
+        err = rt::launch_to_fp8(r->corpus, n, d, r->rnorm, r->corpus8, r->meta8, r->bad8, num_cus, nullptr);
     uint32_t bad = 1;
     if (err == hipSuccess) err = hipMemcpy(&bad, r->bad8, sizeof(uint32_t), hipMemcpyDeviceToHost);
     if (err == hipSuccess) *ok = (bad == 0);
@@ -444,16 +442,13 @@ rt_status rt_enable_filtered(rt_engine *e) {
     }
     if (err == hipSuccess && st == RT_OK && !r->corpus8) {
         if (!dev_alloc(reinterpret_cast<void **>(&r->corpus8), (size_t)r->max_n * (size_t)r->max_d) ||
-            !dev_alloc(reinterpret_cast<void **>(&r->scale8), sizeof(float) * (size_t)ld) ||
-            !dev_alloc(reinterpret_cast<void **>(&r->err8), sizeof(float) * (size_t)ld) ||
+            !dev_alloc(reinterpret_cast<void **>(&r->meta8), sizeof(float2) * (size_t)ld) ||
             !dev_alloc(reinterpret_cast<void **>(&r->bad8), sizeof(uint32_t))) {
             (void)hipFree(r->corpus8);
-            (void)hipFree(r->scale8);
-            (void)hipFree(r->err8);
+            (void)hipFree(r->meta8);
             (void)hipFree(r->bad8);
             r->corpus8 = nullptr;
-            r->scale8 = nullptr;
-            r->err8 = nullptr;
+            r->meta8 = nullptr;
             r->bad8 = nullptr;
             st = RT_ENOMEM;
         } else if (r->n > 0) {
@@ -606,7 +601,7 @@ rt_status search_resident_filtered(rt_engine *e, const float *queries, int32_t q
         e->had_batch_kernel = e->profiling;
         if (fp8) {
             e->filter_path = RT_FILTER_PATH_FP8;
-            err = rt::launch_filtered_search8(r->corpus, r->corpus8, r->scale8, r->err8, r->rnorm, n, d, queries, q,
+            err = rt::launch_filtered_search8(r->corpus, r->corpus8, r->meta8, n, d, queries, q,
                                               p1.per_wave, p1.wgs, t1, p2.per_wave, p2.wgs, t2, f,
                                               e->profiling ? e->ev[3] : nullptr, s);
         } else {

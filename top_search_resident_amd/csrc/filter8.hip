@@ -7,9 +7,17 @@
 
 namespace rt {
 
-// Depths with an fp8 first pass, and their lane-group shapes over 16-byte
-// blocks (d16 = d / 16): the fewest wasted lanes, as pick_gemv_shape chooses.
-#define RT_FP8_SHAPES(X) X(4, 1) X(3, 3) X(5, 1) X(4, 3) X(6, 1) X(5, 3) X(6, 2)
+// Depths with an fp8 first pass and their lane-group shapes X(d16, LG, L, P)
+// over 16-byte blocks (d16 = d / 16 = G L exactly), P steps of loads in flight:
+// about 4 KB of codes per wave step, four blocks per lane where four divide the
+// row, else three, two steps ahead (measured on MI355X at 2^30 elements, pass 1
+// at K = 8 against whole-row groups of one or two blocks four steps ahead:
+// d = 1024 172.7 against 193.1 us, 512 191.5 against 205.3, 768 184.4 against
+// 186.3, 2048 184.9 against 182.8); rows of 256 keep 16-lane groups of one
+// block, two rows per step four steps ahead (212.6 us against 230.4 for 4-lane
+// groups of four blocks).
+#define RT_FP8_SHAPES(X) \
+    X(16, 4, 1, 4) X(24, 3, 3, 2) X(32, 3, 4, 2) X(48, 4, 3, 2) X(64, 4, 4, 2) X(96, 5, 3, 2) X(128, 5, 4, 2)
 
 bool fp8_search_ok(int d) {
     return d == 256 || d == 384 || d == 512 || d == 768 || d == 1024 || d == 1536 || d == 2048;
@@ -26,13 +34,15 @@ void filter_bound_constants_fp8(int d, float *cr, float *cx, float *delta) {
 
 // One wave per row: s = the power of two with max |x| <= 224 s (s >= 2^-126;
 // 1 for a zero row), codes = e4m3 of x / s (the hardware conversion), and
-// err >= |x - s dec(codes)| from the stored codes themselves (fp64 sum of
-// squares of exact differences, square root rounded up by 2^-40, then to fp32
-// upward).  A value that is not finite sets *bad.  Lane l converts elements
-// 16 l .. 16 l + 15 of each 1024-element chunk (d % 16 == 0).
+// meta = {s, c}, c >= cr err + cx rnorm[row] (rounded up), err >= |x - s
+// dec(codes)| from the stored codes themselves (fp64 sum of squares of exact
+// differences, square root rounded up by 2^-40).  A value that is not finite
+// sets *bad.  Lane l converts elements 16 l .. 16 l + 15 of each 1024-element
+// chunk (d % 16 == 0).
 __global__ __launch_bounds__(256) void to_fp8_kernel(const float *__restrict__ corpus, int64_t n, int d,
-                                                     uint8_t *__restrict__ codes, float *__restrict__ scale,
-                                                     float *__restrict__ err, uint32_t *bad) {
+                                                     const float *__restrict__ rnorm, float cr, float cx,
+                                                     uint8_t *__restrict__ codes, float2 *__restrict__ meta,
+                                                     uint32_t *bad) {
     const int64_t waves = (int64_t)gridDim.x * (blockDim.x >> 6);
     const int lane = lane_id();
     uint32_t flag = 0;
@@ -81,37 +91,40 @@ __global__ __launch_bounds__(256) void to_fp8_kernel(const float *__restrict__ c
 #pragma unroll
         for (int m = 32; m >= 1; m >>= 1) ss += __shfl_xor(ss, m);
         if (lane == 0) {
-            const double up = sqrt(ss) * (1.0 + 0x1p-40);
-            float r = (float)up;
-            if ((double)r < up) r = __uint_as_float(__float_as_uint(r) + 1u);  // next fp32 up (r >= 0)
-            scale[row] = s;
-            err[row] = r;
+            // each fp64 step below rounds by at most 2^-53 relative: 2^-40 covers them
+            const double up = ((double)cr * (sqrt(ss) * (1.0 + 0x1p-40)) + (double)cx * (double)rnorm[row]) *
+                              (1.0 + 0x1p-40);
+            float c = (float)up;
+            if ((double)c < up) c = __uint_as_float(__float_as_uint(c) + 1u);  // next fp32 up (c >= 0)
+            meta[row] = make_float2(s, c);
         }
     }
     if (__ballot(flag != 0) != 0 && lane == 0) atomicOr(bad, 1u);
 }
 
-hipError_t launch_to_fp8(const float *corpus, int64_t n, int d, uint8_t *codes, float *scale, float *err,
+hipError_t launch_to_fp8(const float *corpus, int64_t n, int d, const float *rnorm, uint8_t *codes, float2 *meta,
                          uint32_t *bad, int num_cus, hipStream_t stream) {
+    float cr = 0.f, cx = 0.f, delta = 0.f;
+    filter_bound_constants_fp8(d, &cr, &cx, &delta);
     int64_t blocks = (n + 3) / 4;
     const int64_t cap = (int64_t)num_cus * 16;
     if (blocks > cap) blocks = cap;
     if (blocks < 1) blocks = 1;
-    hipLaunchKernelGGL(to_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, corpus, n, d, codes, scale, err,
-                       bad);
+    hipLaunchKernelGGL(to_fp8_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, corpus, n, d, rnorm, cr, cx,
+                       codes, meta, bad);
     return hipGetLastError();
 }
 
 template <int R>
-static hipError_t launch_bound8_r(int lg, int L, dim3 grid, hipStream_t s, const Fp8Rows &fr, int64_t n, int d,
-                                  const float *queries, const float *rnorm, int64_t per_wave, const TreeLaunch &t,
-                                  const FilterLaunch &f) {
+static hipError_t launch_bound8_r(dim3 grid, hipStream_t s, const Fp8Rows &fr, int64_t n, int d,
+                                  const float *queries, int64_t per_wave, const TreeLaunch &t, const FilterLaunch &f) {
     const TreeArgs ta = make_tree(t);
     const FilterArgs fa = make_filter(f);
     const dim3 block(64 * gemv_waves(64 * R));
-#define RT_SHAPE8(LGV, LV)                                                                                       \
-    if (lg == LGV && L == LV) {                                                                                  \
-        hipLaunchKernelGGL((gemv_bound8_kernel<LGV, LV, R, 4>), grid, block, 0, s, fr, n, d, queries, rnorm,     \
+#define RT_SHAPE8(D16, LGV, LV, PV)                                                                              \
+    static_assert((1 << LGV) * LV == D16, "an fp8 shape covers its row exactly");                                \
+    if (d == 16 * D16) {                                                                                         \
+        hipLaunchKernelGGL((gemv_bound8_kernel<LGV, LV, R, PV>), grid, block, 0, s, fr, n, d, queries,           \
                            per_wave, ta, fa);                                                                    \
         return hipGetLastError();                                                                                \
     }
@@ -120,27 +133,24 @@ static hipError_t launch_bound8_r(int lg, int L, dim3 grid, hipStream_t s, const
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_filtered_search8(const float *corpus, const uint8_t *codes, const float *scale, const float *err8,
-                                   const float *rnorm, int64_t n, int d, const float *queries, int segments,
-                                   int64_t rows_per_wave1, int wgs1, const TreeLaunch &t1, int64_t rows_per_wave2,
-                                   int wgs2, const TreeLaunch &t2, const FilterLaunch &f, hipEvent_t between,
-                                   hipStream_t stream) {
+hipError_t launch_filtered_search8(const float *corpus, const uint8_t *codes, const float2 *meta, int64_t n, int d,
+                                   const float *queries, int segments, int64_t rows_per_wave1, int wgs1,
+                                   const TreeLaunch &t1, int64_t rows_per_wave2, int wgs2, const TreeLaunch &t2,
+                                   const FilterLaunch &f, hipEvent_t between, hipStream_t stream) {
     if (!fp8_search_ok(d)) return hipErrorInvalidValue;
-    int lg = 6, L = 8;
-    pick_gemv_shape(d / 16, &lg, &L);
     Fp8Rows fr;
     fr.codes = codes;
-    fr.scale = scale;
-    fr.err = err8;
-    filter_bound_constants_fp8(d, &fr.cr, &fr.cx, &fr.delta);
+    fr.meta = meta;
+    float cr = 0.f, cx = 0.f;
+    filter_bound_constants_fp8(d, &cr, &cx, &fr.delta);
     const dim3 g1(wgs1, segments);
     hipError_t err;
     switch (t1.kp / 64) {
-        case 1: err = launch_bound8_r<1>(lg, L, g1, stream, fr, n, d, queries, rnorm, rows_per_wave1, t1, f); break;
-        case 2: err = launch_bound8_r<2>(lg, L, g1, stream, fr, n, d, queries, rnorm, rows_per_wave1, t1, f); break;
-        case 4: err = launch_bound8_r<4>(lg, L, g1, stream, fr, n, d, queries, rnorm, rows_per_wave1, t1, f); break;
-        case 8: err = launch_bound8_r<8>(lg, L, g1, stream, fr, n, d, queries, rnorm, rows_per_wave1, t1, f); break;
-        case 16: err = launch_bound8_r<16>(lg, L, g1, stream, fr, n, d, queries, rnorm, rows_per_wave1, t1, f); break;
+        case 1: err = launch_bound8_r<1>(g1, stream, fr, n, d, queries, rows_per_wave1, t1, f); break;
+        case 2: err = launch_bound8_r<2>(g1, stream, fr, n, d, queries, rows_per_wave1, t1, f); break;
+        case 4: err = launch_bound8_r<4>(g1, stream, fr, n, d, queries, rows_per_wave1, t1, f); break;
+        case 8: err = launch_bound8_r<8>(g1, stream, fr, n, d, queries, rows_per_wave1, t1, f); break;
+        case 16: err = launch_bound8_r<16>(g1, stream, fr, n, d, queries, rows_per_wave1, t1, f); break;
         default: return hipErrorInvalidValue;
     }
     if (err != hipSuccess) return err;

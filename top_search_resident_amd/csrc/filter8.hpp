@@ -16,12 +16,16 @@
 // (|x - x~| computed per row from the stored codes, rounded up), gamma_D for
 // the fp32 sum of a over sum |x~_j q_j| <= (|x| + |x - x~|) |q| and gamma_D for
 // the plain scan's sum; delta = 4 D 2^-126 covers underflow of products and
-// partial sums (scaled by s in a).  The upper bound a + e is stored and the
-// lower bound a - e ranked; the tree's root writes the k-th lower bound, and
-// the bf16 path's second pass (gemv_filtered_kernel) re-scores the rows whose
-// upper bound reaches it.  The error norm of an e4m3 row is ~0.027 |x| for
-// Gaussian rows (bf16: ~0.0017 |x|), so many more rows reach the threshold;
-// the pass pays only where the corpus is large.
+// partial sums (scaled by s in a).  The row's part of the bound, c = cr |x - x~|
+// + cx |x|, is computed with the copy and stored beside s (one float2 per row),
+// so a row costs D + 8 bytes to read and e = |q| c + delta max(|q|, 1) max(s, 1)
+// (the fp32 roundings of c and e are far inside the 2^-10 slack of cr and cx).
+// The upper bound a + e is stored and the lower bound a - e ranked; the tree's
+// root writes the k-th lower bound, and the bf16 path's second pass
+// (gemv_filtered_kernel) re-scores the rows whose upper bound reaches it.  The
+// error norm of an e4m3 row is ~0.027 |x| for Gaussian rows (bf16: ~0.0017
+// |x|), so many more rows reach the threshold; the pass pays only where the
+// corpus is large.
 #pragma once
 #include "filter_topk.hpp"
 
@@ -29,10 +33,9 @@ namespace rt {
 
 // Extra per-row data of the fp8 first pass.
 struct Fp8Rows {
-    const uint8_t *codes;   // n x d e4m3 codes, row-major
-    const float *scale;     // per row s (a power of two)
-    const float *err;       // per row, >= |x - s dec(codes)|
-    float cr, cx, delta;    // bound constants
+    const uint8_t *codes;  // n x d e4m3 codes, row-major
+    const float2 *meta;    // per row {s (a power of two), c = cr |x - x~| + cx |x|}
+    float delta;           // bound constant
 };
 
 __device__ __forceinline__ float fp8_block_dot(const uint4 &v, const float4 (&q)[4], float a) {
@@ -51,12 +54,13 @@ __device__ __forceinline__ float fp8_block_dot(const uint4 &v, const float4 (&q)
 }
 
 // Lane-group layout as gemv_bound_kernel, over 16-byte blocks of 16 codes (d16 =
-// d / 16 blocks per row): lane g of a group of G = 2^LG lanes owns blocks g,
-// g + G, ... (L loads); loads run P steps ahead.
+// d / 16 blocks per row, exactly G L: the launcher checks it, so no block is
+// padded): lane g of a group of G = 2^LG lanes owns blocks g, g + G, ... (L
+// loads); loads run P steps ahead.
 template <int LG, int L, int R, int P>
 __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_bound8_kernel(
-    Fp8Rows fr, int64_t n, int d, const float *__restrict__ queries, const float *__restrict__ rnorm,
-    int64_t rows_per_wave, TreeArgs ta, FilterArgs fa) {
+    Fp8Rows fr, int64_t n, int d, const float *__restrict__ queries, int64_t rows_per_wave, TreeArgs ta,
+    FilterArgs fa) {
     constexpr int G = 1 << LG;
     constexpr int RPS = 64 >> LG;
     constexpr int U = RowUnroll<L>::value;
@@ -81,24 +85,17 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_bound8_kernel(
     WaveSelector<R> sel;
     sel.init(ta.k);
     const float qnorm = wave_l2_norm(qrow, d);
-    const float er = fr.cr * qnorm;
-    const float ex = fr.cx * qnorm;
     const float dl = fr.delta * fmaxf(qnorm, 1.f);
 
-    // The sixteen query values of each of this lane's blocks; blocks past the
-    // row end load the last block and are and-ed with a zero mask.
+    // The sixteen query values of each of this lane's blocks.
     float4 qv[L][4];
     int colc[L];
-    uint32_t cmask[L];
 #pragma unroll
     for (int j = 0; j < L; ++j) {
-        const int col = j * G + g;
-        const bool in = col < d16;
-        colc[j] = in ? col : d16 - 1;
-        cmask[j] = in ? 0xffffffffu : 0u;
+        colc[j] = j * G + g;
         const float4 *q4 = reinterpret_cast<const float4 *>(qrow) + 4 * colc[j];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) qv[j][i] = in ? q4[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int i = 0; i < 4; ++i) qv[j][i] = q4[i];
     }
 
     const int64_t r_begin = wave * rows_per_wave;
@@ -107,7 +104,7 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_bound8_kernel(
         const uint4 *__restrict__ c8 = reinterpret_cast<const uint4 *>(fr.codes);
         const int64_t last = r_end - 1;
         uint4 x[P][U][L];
-        float rn[P][U], rs[P][U], re[P][U];
+        float2 mt[P][U];
         auto load_step = [&](int s, int64_t r0) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -116,9 +113,7 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_bound8_kernel(
                 const uint4 *p = c8 + row * d16;
 #pragma unroll
                 for (int j = 0; j < L; ++j) x[s][u][j] = load_nt(p + colc[j]);
-                rn[s][u] = rnorm[row];
-                rs[s][u] = fr.scale[row];
-                re[s][u] = fr.err[row];
+                mt[s][u] = fr.meta[row];
             }
         };
         auto consume = [&](int s, int64_t rs0) {
@@ -127,16 +122,10 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_bound8_kernel(
             for (int u = 0; u < U; ++u) {
                 float a = 0.f;
 #pragma unroll
-                for (int j = 0; j < L; ++j) {
-                    uint4 v = x[s][u][j];
-                    v.x &= cmask[j];
-                    v.y &= cmask[j];
-                    v.z &= cmask[j];
-                    v.w &= cmask[j];
-                    a = fp8_block_dot(v, qv[j], a);
-                }
-                a = group_sum(a, LG) * rs[s][u];
-                const float e = fmaf(er, re[s][u], fmaf(ex, rn[s][u], dl * fmaxf(rs[s][u], 1.f)));
+                for (int j = 0; j < L; ++j) a = fp8_block_dot(x[s][u][j], qv[j], a);
+                const float sc = mt[s][u].x;
+                a = group_sum(a, LG) * sc;
+                const float e = fmaf(qnorm, mt[s][u].y, dl * fmaxf(sc, 1.f));
                 const int64_t row = rs0 + u * RPS + h;
                 // false for an overflowed or NaN sum or bound: the row is kept
                 const bool known = fabsf(a) <= __FLT_MAX__ && e <= __FLT_MAX__;

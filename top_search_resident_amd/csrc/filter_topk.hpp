@@ -176,11 +176,15 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_bound_kernel(
     finish_workgroup<R, W * 64>(sel, sm, &ms, ta, seg);
 }
 
-// Pass 2.  A wave takes rows_per_wave rows in blocks of 64: every lane reads one
-// upper bound (eight blocks' bounds are loaded at once), a ballot lists the rows
-// reaching T, and the wave's lane groups score those rows -- RPS of them at a
-// time -- exactly as gemv_topk_kernel does (lane_chain + group_sum with the same
-// shape), then offer them to the selectors.  Rows below T are never read.
+// Pass 2.  A wave takes rows_per_wave rows in chunks of 512: every lane reads
+// eight upper bounds (one per block of 64 rows, all loaded at once), and the
+// rows reaching T are listed in row order in the wave's LDS list (ballot +
+// mbcnt).  The wave then scores the list C * RPS rows at a time: the loads of C
+// rows per lane group are issued together (a wave's few candidates are spread
+// over its chunk, so taking them together saves a round trip to memory per
+// candidate), then each row is reduced exactly as gemv_topk_kernel does
+// (lane_chain + group_sum with the same shape) and offered to the selectors.
+// Rows below T are never read.
 template <int LG, int L, int R>
 __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_filtered_kernel(
     const float *__restrict__ corpus, int64_t n, int d, const float *__restrict__ queries,
@@ -188,10 +192,12 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_filtered_kernel(
     constexpr int G = 1 << LG;
     constexpr int RPS = 64 >> LG;
     constexpr int NB = 8;  // blocks of 64 bounds loaded at once
+    constexpr int C = (16 / L) < 1 ? 1 : ((16 / L) > 4 ? 4 : 16 / L);  // rows per lane group in flight
     constexpr int W = gemv_waves(64 * R);
     __shared__ uint64_t stage[W][128];
     __shared__ uint64_t sm[kTreeEntries];
     __shared__ MergeScratch ms;
+    __shared__ uint16_t list[W][NB * 64];  // per wave: the chunk's rows reaching T
 
     const int seg = blockIdx.y;
     const int lane = lane_id();
@@ -200,6 +206,7 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_filtered_kernel(
     const int g = lane & (G - 1);
     const int h = lane >> LG;
     const int d4 = d >> 2;
+    uint16_t *const my_list = list[wv];
     const float4 *__restrict__ q4 = reinterpret_cast<const float4 *>(queries + (int64_t)seg * d);
     const float4 *__restrict__ c4 = reinterpret_cast<const float4 *>(corpus);
     const float *__restrict__ ub = fa.ubuf + (int64_t)seg * fa.uld;
@@ -229,31 +236,44 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_filtered_kernel(
             const int64_t row = b0 + b * 64 + lane;
             uu[b] = ub[row < r_end ? row : r_end - 1];
         }
+        int count = 0;  // wave-uniform
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
-            const int64_t row0 = b0 + b * 64;
-            uint64_t m = __ballot(row0 + lane < r_end && uu[b] >= T);
-            while (m != 0) {  // wave-uniform
-                // group h takes the h-th remaining candidate
-                int mine = -1;
+            const bool hit = b0 + b * 64 + lane < r_end && uu[b] >= T;
+            const uint64_t mb = __ballot(hit);
+            if (hit) my_list[count + lanes_below(mb)] = (uint16_t)(b * 64 + lane);
+            count += __popcll(mb);
+        }
+        wave_lds_sync();
+        for (int t0 = 0; t0 < count; t0 += C * RPS) {
+            // entry t0 + c RPS + h goes to group h in batch c; slots past the
+            // end re-read entry t0 (in cache) and offer nothing, so loads and
+            // uses stay unconditional
+            const int first = my_list[t0];
+            int mine[C];
 #pragma unroll
-                for (int i = 0; i < RPS; ++i) {
-                    if (m != 0) {
-                        const int bit = __builtin_ctzll(m);
-                        m &= m - 1;
-                        if (i == h) mine = bit;
-                    }
-                }
-                const int64_t row = row0 + (mine >= 0 ? mine : 0);
-                float4 x[L];
+            for (int c = 0; c < C; ++c) {
+                const int t = t0 + c * RPS + h;
+                mine[c] = t < count ? (int)my_list[t] : -1;
+            }
+            float4 x[C][L];
 #pragma unroll
-                for (int j = 0; j < L; ++j) x[j] = c4[row * d4 + colc[j]];
-                const float s = group_sum(lane_chain<G, L>(x, qv, cmask), LG);
-                const bool valid = (g == 0) && (mine >= 0);
+            for (int c = 0; c < C; ++c) {
+                const int64_t row = b0 + (mine[c] >= 0 ? mine[c] : first);
+#pragma unroll
+                for (int j = 0; j < L; ++j) x[c][j] = c4[row * d4 + colc[j]];
+            }
+            __builtin_amdgcn_sched_barrier(0);  // all C rows' loads before any use
+#pragma unroll
+            for (int c = 0; c < C; ++c) {
+                const int64_t row = b0 + (mine[c] >= 0 ? mine[c] : first);
+                const float s = group_sum(lane_chain<G, L>(x[c], qv, cmask), LG);
+                const bool valid = (g == 0) && (mine[c] >= 0);
                 const uint64_t rank = make_rank(order_key_f32(s), (uint32_t)row);
                 sel.offer(my_stage, rank, valid && rank > sel.thr);
             }
         }
+        wave_lds_sync();  // the list is rewritten by the next chunk
     }
     sel.finish(my_stage);
     finish_workgroup<R, W * 64>(sel, sm, &ms, ta, seg);
