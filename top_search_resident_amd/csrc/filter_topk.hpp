@@ -24,6 +24,8 @@
 // at 1M x 1024 and k = 100 the band [T - 2 e, T] holds a few hundred rows, so
 // the second pass reads ~4 MB of bounds and a few hundred fp32 rows.
 #pragma once
+#include <type_traits>
+
 #include "stream_topk.hpp"
 
 namespace rt {
@@ -245,33 +247,41 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_filtered_kernel(
             count += __popcll(mb);
         }
         wave_lds_sync();
-        for (int t0 = 0; t0 < count; t0 += C * RPS) {
-            // entry t0 + c RPS + h goes to group h in batch c; slots past the
-            // end re-read entry t0 (in cache) and offer nothing, so loads and
-            // uses stay unconditional
+        // NC batches from list entry t0: entry t0 + c RPS + h goes to group h in
+        // batch c; slots past the end re-read entry t0 (in cache) and offer
+        // nothing, so loads and uses stay unconditional
+        auto score = [&](auto nc, int t0) {
+            constexpr int NC = decltype(nc)::value;
             const int first = my_list[t0];
-            int mine[C];
+            int mine[NC];
 #pragma unroll
-            for (int c = 0; c < C; ++c) {
+            for (int c = 0; c < NC; ++c) {
                 const int t = t0 + c * RPS + h;
                 mine[c] = t < count ? (int)my_list[t] : -1;
             }
-            float4 x[C][L];
+            float4 x[NC][L];
 #pragma unroll
-            for (int c = 0; c < C; ++c) {
+            for (int c = 0; c < NC; ++c) {
                 const int64_t row = b0 + (mine[c] >= 0 ? mine[c] : first);
 #pragma unroll
                 for (int j = 0; j < L; ++j) x[c][j] = c4[row * d4 + colc[j]];
             }
-            __builtin_amdgcn_sched_barrier(0);  // all C rows' loads before any use
+            __builtin_amdgcn_sched_barrier(0);  // all NC rows' loads before any use
 #pragma unroll
-            for (int c = 0; c < C; ++c) {
+            for (int c = 0; c < NC; ++c) {
                 const int64_t row = b0 + (mine[c] >= 0 ? mine[c] : first);
                 const float s = group_sum(lane_chain<G, L>(x[c], qv, cmask), LG);
                 const bool valid = (g == 0) && (mine[c] >= 0);
                 const uint64_t rank = make_rank(order_key_f32(s), (uint32_t)row);
                 sel.offer(my_stage, rank, valid && rank > sel.thr);
             }
+        };
+        for (int t0 = 0; t0 < count; t0 += C * RPS) {
+            // most waves of a tight bound hold one batch or none
+            if (count - t0 <= RPS)
+                score(std::integral_constant<int, 1>{}, t0);
+            else
+                score(std::integral_constant<int, C>{}, t0);
         }
         wave_lds_sync();  // the list is rewritten by the next chunk
     }
