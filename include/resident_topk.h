@@ -236,8 +236,8 @@ int32_t rt_last_hip_error(const rt_engine *e);
  * select records HIP events on its stream around its kernels; after the stream
  * has finished, rt_profile_read returns the last call's device times in
  * milliseconds: [0] = the whole call, [1] = its first kernel when it ran two
- * (the batched scoring kernel of a batch, the bf16 pass of a filtered search;
- * 0 otherwise), [2] = the rest (the streaming top-K kernel: scoring or
+ * (the batched scoring kernel of a batch, the first (bf16 or fp8) pass of a
+ * filtered search, the bound pass of a filtered batch; 0 otherwise), [2] = the rest (the streaming top-K kernel: scoring or
  * raw-array selection, per-block lists and the merge tree), i.e. [0] - [1].  The events
  * are created by rt_engine_create.  RT_EINVAL on NULL arguments.
  */
