@@ -32,6 +32,7 @@ measurement; the default line is c3_1m_1024.
 import argparse
 import json
 import os
+import subprocess
 import sys
 import time
 
@@ -260,6 +261,9 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
     if args.e2e_reps:
         line["end_to_end_pcie"] = time_end_to_end(eng, torch, qhost, ks, args.e2e_reps, metric=args.metric,
                                                   filtered=args.filtered)
+    if not args.filtered:
+        line["hbm_read_ceiling"] = read_ceiling(eng, n * d * 4, avg_ms)
+    line["gpu_clocks"] = gpu_clocks()
     if not args.filtered and args.metric == "dot" and not args.no_filtered_leg and d % 8 == 0:
         line["filtered_exact"] = filtered_leg(args, torch, eng, qdev, ks, n, d)
     if not args.no_cpu_baseline:
@@ -280,6 +284,32 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
                                                       metric=args.metric)
     eng.close()
     return line
+
+
+def read_ceiling(eng, corpus_bytes, scan_ms, reps=20):
+    """The same run's plain streaming read of the resident corpus
+    (rt_read_probe): the achievable read bandwidth that the scan's is compared
+    with."""
+    eng.read_probe(reps=3)  # warm-up
+    ms = eng.read_probe(reps=reps)
+    gbs = corpus_bytes / (ms * 1e-3) / 1e9
+    return {"kernel": "read_probe_kernel (a contiguous chunk per wave, non-temporal 16-byte loads, no other work)",
+            "bytes": corpus_bytes,
+            "avg_launch_us": ms * 1e3, "gbs": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
+            "scan_frac_of_ceiling": ms / scan_ms}
+
+
+def gpu_clocks():
+    """Current GPU clocks as rocm-smi reports them (clocks are not locked);
+    None when the tool is missing or says nothing usable."""
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        data = json.loads(out.stdout)
+    except (OSError, ValueError, subprocess.SubprocessError):
+        return None
+    cards = {c: {k: v for k, v in vals.items() if "clock" in k.lower() or "clk" in k.lower()}
+             for c, vals in data.items() if isinstance(vals, dict)}
+    return {c: v for c, v in cards.items() if v} or None
 
 
 def filtered_leg(args, torch, eng, qdev, ks, n, d):

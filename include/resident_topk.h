@@ -245,6 +245,20 @@ rt_status rt_profile_enable(rt_engine *e, int32_t on);
 rt_status rt_profile_read(rt_engine *e, float *ms3);
 
 /*
+ * Read-bandwidth reference for measurements (the achievable ceiling that the
+ * scan is compared with): `reps` launches on `stream` of a plain streaming
+ * kernel that reads the resident fp32 corpus once each (its first
+ * 16 * floor(n * d / 4) bytes, a contiguous chunk per wave, non-temporal
+ * 16-byte loads, eight in flight per lane, 4 waves per CU) and does no other
+ * work; the launches are timed with
+ * the engine's events (so the last call's rt_profile_read times are replaced)
+ * and synchronised, and *out_ms receives the average device time per launch.
+ * The engine's merge-tree scratch may receive one word per wave.  RT_EINVAL on a
+ * NULL engine or out_ms or reps < 1; RT_ESTATE before an upload.
+ */
+rt_status rt_read_probe(rt_engine *e, int32_t reps, void *stream, float *out_ms);
+
+/*
  * Engine limits and state, for callers and tests: out7 receives
  * [max_n, max_d, max_k, max_q, resident_n, resident_d, device].
  */

@@ -322,3 +322,25 @@ def test_error_paths():
         e.close()
     with pytest.raises(ResidentTopKError):
         ResidentTopK(1 << 40, 64, 8, 1)  # beyond the int32 index range
+
+
+def test_read_probe(eng):
+    """rt_read_probe times a plain read of the resident corpus; it rejects bad
+    arguments, and the searches after it (it writes into the merge-tree
+    scratch) still match the oracle."""
+    corpus = workloads.gaussian_rows(150_000, 1024, config_id=13)
+    qs = workloads.gaussian_rows(2, 1024, config_id=13, stream=1)
+    eng.upload_corpus_rowmajor(corpus)
+    ms = eng.read_probe(reps=5)
+    nbytes = corpus.nbytes
+    print(f"[read probe] {nbytes} B in {ms * 1e3:.1f} us", flush=True)
+    assert 0.0 < ms < 50.0
+    assert nbytes / (ms * 1e-3) < 8.5e12  # no faster than the HBM peak
+    with pytest.raises(ResidentTopKError) as ei:
+        eng.read_probe(reps=0)
+    assert ei.value.status == 1
+    _check_against_oracle(eng, corpus, qs, 64)
+    with ResidentTopK(100, 8, 4, 1) as e:
+        with pytest.raises(ResidentTopKError) as ei:
+            e.read_probe()  # nothing resident
+        assert ei.value.status == 2

@@ -217,3 +217,12 @@ class ResidentTopK:
         out = (ctypes.c_float * 3)()
         _check(self._lib.rt_profile_read(self._h, out), "rt_profile_read", self._h)
         return float(out[0]), float(out[1]), float(out[2])
+
+    def read_probe(self, reps=20, stream=None):
+        """Average device time (ms) of one plain streaming read of the resident
+        fp32 corpus (rt_read_probe): the read ceiling that the scan is measured
+        against.  Synchronises the stream; replaces the last profile."""
+        out = ctypes.c_float(0.0)
+        _check(self._lib.rt_read_probe(self._h, int(reps), _stream_handle(stream), ctypes.byref(out)),
+               "rt_read_probe", self._h)
+        return float(out.value)

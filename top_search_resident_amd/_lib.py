@@ -19,6 +19,7 @@ EXPORTS = (
     "rt_profile_read", "rt_engine_info", "rt_check_create", "rt_check_upload",
     "rt_check_search", "rt_check_search_metric", "rt_check_select", "rt_filter_bounds",
     "rt_filter_bounds_batched", "rt_filter_bounds_fp8", "rt_set_filter_storage", "rt_filter_path_used",
+    "rt_read_probe",
 )
 
 _lib = None
@@ -62,6 +63,7 @@ def load():
         "rt_last_hip_error": ([vp], i32),
         "rt_profile_enable": ([vp, i32], ctypes.c_int),
         "rt_profile_read": ([vp, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
+        "rt_read_probe": ([vp, i32, vp, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
         "rt_engine_info": ([vp, ctypes.POINTER(i64)], ctypes.c_int),
         "rt_check_create": ([i64, i32, i32, i32], ctypes.c_int),
         "rt_check_upload": ([i64, i32, vp, i64, i32], ctypes.c_int),

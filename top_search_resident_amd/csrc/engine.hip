@@ -17,6 +17,7 @@
 #include "../../include/resident_topk.h"
 #include "filter8_host.hpp"
 #include "kernels.hpp"
+#include "read_probe.hpp"
 
 namespace {
 
@@ -657,6 +658,31 @@ rt_status rt_profile_read(rt_engine *e, float *ms3) {
         return RT_EHIP;
     }
     ms3[2] = ms3[0] - ms3[1];
+    return RT_OK;
+}
+
+rt_status rt_read_probe(rt_engine *e, int32_t reps, void *stream, float *out_ms) {
+    if (!e || !out_ms || reps < 1) return RT_EINVAL;
+    rt_resident *r = e->res;
+    if (r->n < 1) return RT_ESTATE;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    int prev = 0;
+    (void)hipGetDevice(&prev);
+    hipError_t err = hipSetDevice(e->device);
+    const int64_t n16 = r->n * (int64_t)r->d / 4;
+    // the merge-tree array (kTreeRanks words, rewritten by every search) takes any per-wave word
+    uint32_t *sink = reinterpret_cast<uint32_t *>(e->tree);
+    if (err == hipSuccess) err = hipEventRecord(e->ev[0], s);
+    for (int32_t i = 0; i < reps && err == hipSuccess; ++i)
+        err = rt::launch_read_probe(r->corpus, n16, sink, e->num_cus, s);
+    if (err == hipSuccess) err = hipEventRecord(e->ev[1], s);
+    if (err == hipSuccess) err = hipEventSynchronize(e->ev[1]);
+    float ms = 0.f;
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms, e->ev[0], e->ev[1]);
+    e->had_batch_kernel = false;
+    (void)hipSetDevice(prev);
+    if (err != hipSuccess) return hip_fail(e, err);
+    *out_ms = ms / (float)reps;
     return RT_OK;
 }
 
