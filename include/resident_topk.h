@@ -156,8 +156,9 @@ rt_status search_resident_metric(rt_engine *e, const float *queries, int32_t q, 
 
 /*
  * Prepare an engine for search_resident_filtered: allocate, once, a bf16 copy
- * of the resident corpus (max_n x max_d x 2 bytes) and an fp8 copy (max_n x
- * max_d bytes of e4m3 codes and 8 bytes per row of scales and error norms),
+ * of the resident corpus (max_n x max_d x 2 bytes) with 4 bytes per row of
+ * bf16 error norms, and an fp8 copy (max_n x max_d bytes of e4m3 codes and 8
+ * bytes per row: the scale and the row's part of the fp8 bound),
  * shared by every engine that shares the corpus and refreshed by each upload,
  * and this engine's scratch for the filtered search (4 x max_q x
  * roundup(max_n, 64) bytes of row bounds).
@@ -318,7 +319,8 @@ rt_status rt_filter_bounds_batched(int32_t d, float *out3);
  *   |a - s| <= |q| (cr |x - x~| + cx |x|) + delta max(|q|, 1) max(sc, 1),
  * where x~ = sc dec(codes) is the stored row (sc its power-of-two scale,
  * |x - x~| computed per row from the codes and rounded up), a = sc times the
- * fp32 sum of dec(codes) q and s the single-query scan's fp32 score.
+ * fp32 sum of dec(codes) q and s the single-query scan's fp32 score.  The row's
+ * part cr |x - x~| + cx |x| is computed once per upload (rounded up to fp32).
  * cr = (1 + gamma_d) (1 + 2^-10), cx = 2 gamma_d (1 + 2^-10), each rounded up
  * to fp32, gamma_d = d 2^-24 / (1 - d 2^-24): Cauchy-Schwarz on the rounding
  * error vector, gamma_d for a's fp32 sum over sum |x~ q| <= (|x| + |x - x~|) |q|
