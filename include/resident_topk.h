@@ -186,8 +186,9 @@ rt_status rt_enable_filtered(rt_engine *e);
  * Arguments, layouts and errors as search_resident; RT_ESTATE also when
  * rt_enable_filtered was not called on this engine.  If the depth is not a
  * multiple of 8 or above 2048, or a corpus value is not finite in bf16, the
- * call runs the plain fp32 scan instead (same answer).  Inner product only.
- * Asynchronous on `stream`.
+ * call runs the plain fp32 scan instead, one query at a time (same answers).
+ * Asynchronous on `stream`.  search_resident_filtered_metric(RT_METRIC_DOT)
+ * is the same call.
  */
 /*
  * Which first pass a single-query filtered search takes (host-only setting of
@@ -208,6 +209,22 @@ int32_t rt_filter_path_used(const rt_engine *e);
 
 rt_status search_resident_filtered(rt_engine *e, const float *queries, int32_t q, int32_t k,
                                    int32_t *out_idx, float *out_scores, void *stream);
+
+/*
+ * search_resident_filtered with a metric: RT_METRIC_DOT as above, or
+ * RT_METRIC_COSINE, whose answer is search_resident_metric's cosine answer for
+ * that query alone (indices, order and fp32 scores, bit for bit: the cosine
+ * sum / (|q| |x|), -inf where that product is not positive).  The first pass
+ * turns each row's inner-product bounds into cosine bounds through the same
+ * fp32 product |q| |x| that the scan divides by (widened by 2^-20 relative and
+ * FLT_MIN absolute for the roundings of the divisions); the second pass
+ * re-scores with the scan's arithmetic.  A cosine batch runs the single-query
+ * passes with one segment per query.  Arguments, layouts and errors as
+ * search_resident_metric; RT_ESTATE also when rt_enable_filtered was not
+ * called on this engine.  Asynchronous on `stream`.
+ */
+rt_status search_resident_filtered_metric(rt_engine *e, const float *queries, int32_t q, int32_t k, int32_t metric,
+                                          int32_t *out_idx, float *out_scores, void *stream);
 
 /*
  * Plain top-k of a raw device array, no scoring ("CUDA Programming Model

@@ -152,12 +152,16 @@ class ResidentTopK:
         "fp8", "bf16_matrix" (a batch), or None."""
         return self._PATHS.get(int(self._lib.rt_filter_path_used(self._h)))
 
-    def search_resident_filtered(self, queries, k, out_idx=None, out_scores=None, stream=None):
-        """Exact inner-product top-k (for each query, the answer
-        search_resident gives for that query alone) that reads a bf16 copy of
-        the corpus first and the fp32 rows only where their certified score
-        bounds reach a certified threshold.  A batch runs one bf16 matrix-core
-        first pass for all of its queries."""
+    def search_resident_filtered(self, queries, k, out_idx=None, out_scores=None, stream=None, metric="dot"):
+        """Exact top-k by inner product (metric="dot") or cosine similarity
+        (metric="cosine") -- for each query, the answer search_resident gives
+        for that query alone -- that reads a reduced-precision copy of the
+        corpus first and the fp32 rows only where their certified score bounds
+        reach a certified threshold.  An inner-product batch runs one bf16
+        matrix-core first pass for all of its queries."""
+        metrics = {"dot": RT_METRIC_DOT, "cosine": RT_METRIC_COSINE}
+        if metric not in metrics:
+            raise ValueError(f"metric must be one of {sorted(metrics)}")
         torch = _torch()
         if queries.dim() == 1:
             queries = queries.view(1, -1)
@@ -172,9 +176,9 @@ class ResidentTopK:
             raise TypeError("out_idx must be int32 and out_scores float32")
         if out_idx.numel() < q * k or out_scores.numel() < q * k:
             raise ValueError("output buffers are too small")
-        st = self._lib.search_resident_filtered(self._h, ctypes.c_void_p(queries.data_ptr()), int(q), int(k),
-                                                ctypes.c_void_p(out_idx.data_ptr()),
-                                                ctypes.c_void_p(out_scores.data_ptr()), _stream_handle(stream))
+        st = self._lib.search_resident_filtered_metric(self._h, ctypes.c_void_p(queries.data_ptr()), int(q), int(k),
+                                                       metrics[metric], ctypes.c_void_p(out_idx.data_ptr()),
+                                                       ctypes.c_void_p(out_scores.data_ptr()), _stream_handle(stream))
         _check(st, "search_resident_filtered", self._h)
         return out_idx, out_scores
 

@@ -540,18 +540,25 @@ rt_status search_resident(rt_engine *e, const float *queries, int32_t q, int32_t
     return search_resident_metric(e, queries, q, k, RT_METRIC_DOT, out_idx, out_scores, stream);
 }
 
-rt_status search_resident_filtered(rt_engine *e, const float *queries, int32_t q, int32_t k, int32_t *out_idx,
-                                   float *out_scores, void *stream) {
+rt_status search_resident_filtered_metric(rt_engine *e, const float *queries, int32_t q, int32_t k, int32_t metric,
+                                          int32_t *out_idx, float *out_scores, void *stream) {
     if (!e) return RT_EINVAL;
-    rt_status st = rt_check_search(e->max_k, e->max_q, e->res->n, queries, q, k, out_idx, out_scores);
+    rt_status st =
+        rt_check_search_metric(e->max_k, e->max_q, e->res->n, queries, q, k, metric, out_idx, out_scores);
     if (st != RT_OK) return st;
     if (!e->ubuf) return RT_ESTATE;  // rt_enable_filtered was not called on this engine
     rt_resident *r = e->res;
     const int64_t n = r->n;
     const int d = r->d;
-    if (!r->copy16_ok || !rt::filtered_search_ok(d)) {  // same answer through the plain scan
+    const bool cosine = metric == RT_METRIC_COSINE;
+    if (!r->copy16_ok || !rt::filtered_search_ok(d)) {
+        // the same answers through the plain scan, one query at a time (a plain
+        // batch sums in another order)
         e->filter_path = RT_FILTER_PATH_PLAIN;
-        return search_resident_metric(e, queries, q, k, RT_METRIC_DOT, out_idx, out_scores, stream);
+        for (int32_t i = 0; i < q && st == RT_OK; ++i)
+            st = search_resident_metric(e, queries + (int64_t)i * d, 1, k, metric, out_idx + (int64_t)i * k,
+                                        out_scores + (int64_t)i * k, stream);
+        return st;
     }
     hipStream_t s = static_cast<hipStream_t>(stream);
     int prev = 0;
@@ -560,8 +567,10 @@ rt_status search_resident_filtered(rt_engine *e, const float *queries, int32_t q
     const int kp = kp_for(k);
     const int64_t uld = (r->max_n + 63) / 64 * 64;
     // A batch on an engine with batch buffers: bounds for all queries from one
-    // bf16 MFMA pass over the copy, per-query thresholds from tile maxima.
-    const bool batched = q > 1 && e->tmax != nullptr && rt::mfma_filter_ok(d);
+    // bf16 MFMA pass over the copy, per-query thresholds from tile maxima
+    // (inner product; a cosine batch takes the single-query passes, one
+    // segment per query).
+    const bool batched = !cosine && q > 1 && e->tmax != nullptr && rt::mfma_filter_ok(d);
     e->had_batch_kernel = false;
     if (err == hipSuccess) err = prologue(e, s);
     if (err == hipSuccess && batched) {
@@ -599,6 +608,7 @@ rt_status search_resident_filtered(rt_engine *e, const float *queries, int32_t q
         f.ubuf = e->ubuf;
         f.uld = uld;
         f.thr = e->thr;
+        f.crn = cosine ? r->rnorm : nullptr;
         e->had_batch_kernel = e->profiling;
         if (fp8) {
             e->filter_path = RT_FILTER_PATH_FP8;
@@ -615,6 +625,11 @@ rt_status search_resident_filtered(rt_engine *e, const float *queries, int32_t q
     (void)hipSetDevice(prev);
     if (err != hipSuccess) return hip_fail(e, err);
     return RT_OK;
+}
+
+rt_status search_resident_filtered(rt_engine *e, const float *queries, int32_t q, int32_t k, int32_t *out_idx,
+                                   float *out_scores, void *stream) {
+    return search_resident_filtered_metric(e, queries, q, k, RT_METRIC_DOT, out_idx, out_scores, stream);
 }
 
 rt_status topk_select(rt_engine *e, const void *values, int32_t dtype, int64_t n, int32_t k, int32_t *out_idx,

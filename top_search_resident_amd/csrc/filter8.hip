@@ -124,8 +124,12 @@ static hipError_t launch_bound8_r(dim3 grid, hipStream_t s, const Fp8Rows &fr, i
 #define RT_SHAPE8(D16, LGV, LV, PV)                                                                              \
     static_assert((1 << LGV) * LV == D16, "an fp8 shape covers its row exactly");                                \
     if (d == 16 * D16) {                                                                                         \
-        hipLaunchKernelGGL((gemv_bound8_kernel<LGV, LV, R, PV>), grid, block, 0, s, fr, n, d, queries,           \
-                           per_wave, ta, fa);                                                                    \
+        if (fa.crn)                                                                                              \
+            hipLaunchKernelGGL((gemv_bound8_kernel<LGV, LV, R, PV, true>), grid, block, 0, s, fr, n, d, queries, \
+                               per_wave, ta, fa);                                                                \
+        else                                                                                                     \
+            hipLaunchKernelGGL((gemv_bound8_kernel<LGV, LV, R, PV, false>), grid, block, 0, s, fr, n, d,         \
+                               queries, per_wave, ta, fa);                                                       \
         return hipGetLastError();                                                                                \
     }
     RT_FP8_SHAPES(RT_SHAPE8)

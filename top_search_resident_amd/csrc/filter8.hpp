@@ -57,7 +57,8 @@ __device__ __forceinline__ float fp8_block_dot(const uint4 &v, const float4 (&q)
 // d / 16 blocks per row, exactly G L: the launcher checks it, so no block is
 // padded): lane g of a group of G = 2^LG lanes owns blocks g, g + G, ... (L
 // loads); loads run P steps ahead.
-template <int LG, int L, int R, int P>
+// COS: cosine bounds from fa.crn (the rows' L2 norms, 4 more bytes per row).
+template <int LG, int L, int R, int P, bool COS>
 __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_bound8_kernel(
     Fp8Rows fr, int64_t n, int d, const float *__restrict__ queries, int64_t rows_per_wave, TreeArgs ta,
     FilterArgs fa) {
@@ -105,6 +106,7 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_bound8_kernel(
         const int64_t last = r_end - 1;
         uint4 x[P][U][L];
         float2 mt[P][U];
+        float cn[P][U];
         auto load_step = [&](int s, int64_t r0) {
 #pragma unroll
             for (int u = 0; u < U; ++u) {
@@ -114,6 +116,7 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_bound8_kernel(
 #pragma unroll
                 for (int j = 0; j < L; ++j) x[s][u][j] = load_nt(p + colc[j]);
                 mt[s][u] = fr.meta[row];
+                if constexpr (COS) cn[s][u] = fa.crn[row];
             }
         };
         auto consume = [&](int s, int64_t rs0) {
@@ -129,8 +132,11 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_bound8_kernel(
                 const int64_t row = rs0 + u * RPS + h;
                 // false for an overflowed or NaN sum or bound: the row is kept
                 const bool known = fabsf(a) <= __FLT_MAX__ && e <= __FLT_MAX__;
-                if (g == 0 && row < r_end) ub[row] = known ? a + e : __builtin_huge_valf();
-                lo[u] = known ? a - e : -__builtin_huge_valf();
+                float hi = known ? a + e : __builtin_huge_valf();
+                float lw = known ? a - e : -__builtin_huge_valf();
+                if constexpr (COS) cosine_bounds(known, a, e, qnorm, cn[s][u], hi, lw);
+                if (g == 0 && row < r_end) ub[row] = hi;
+                lo[u] = lw;
             }
             load_step(s, rs0 + P * STEP);
             __builtin_amdgcn_sched_barrier(0);

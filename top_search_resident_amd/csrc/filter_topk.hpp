@@ -37,7 +37,31 @@ struct FilterArgs {
     float *ubuf;     // [segments][uld] upper bounds a_i + e_i (pass 1 writes, pass 2 reads)
     int64_t uld;
     float *thr;      // [segments] T, the k-th largest lower bound (written by pass 1's tree)
+    const float *crn;  // cosine metric: the rows' L2 norms (null for the inner product)
 };
+
+// Cosine bounds from the inner-product bounds a - e <= acc <= a + e of the
+// plain scan's fp32 sum acc.  The plain cosine is acc / den with den = |q| |x|
+// rounded to fp32 as cosine_of computes it (the same two fp32 values here, so
+// the same den), or -inf when den is not positive.  Its division rounds by at
+// most 2^-24 relative (2^-149 absolute below the normal range), as do a + e,
+// a - e and the divisions below: widening by 2^-20 relative and FLT_MIN
+// absolute covers them.  `known` false (an overflowed sum or bound) leaves the
+// row's bounds at (+inf, -inf) unless den says -inf exactly.
+__device__ __forceinline__ void cosine_bounds(bool known, float a, float e, float qnorm, float rn, float &hi,
+                                              float &lo) {
+    const float den = qnorm * rn;
+    if (!(den > 0.f)) {
+        hi = -__builtin_huge_valf();
+        lo = -__builtin_huge_valf();
+        return;
+    }
+    if (!known) return;
+    const float h = (a + e) / den;
+    const float l = (a - e) / den;
+    hi = h + fmaf(fabsf(h), 0x1p-20f, __FLT_MIN__);
+    lo = l - fmaf(fabsf(l), 0x1p-20f, __FLT_MIN__);
+}
 
 // bf16 -> fp32 of the two halves of a 32-bit word.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -51,7 +75,7 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // P = 4, measured on MI355X).  Per row: a (fp32 FMA chain per lane, group_sum), the
 // bound e, the upper bound written to ubuf, the lower bound ranked by the wave
 // selectors; the merge tree's root writes the k-th lower bound to thr[seg].
-template <int LG, int L, int R, int P>
+template <int LG, int L, int R, int P, bool COS>
 __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_bound_kernel(
     const uint16_t *__restrict__ corpus16, int64_t n, int d, const float *__restrict__ queries,
     const float *__restrict__ rnorm, int64_t rows_per_wave, TreeArgs ta, FilterArgs fa) {
@@ -142,8 +166,11 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_bound_kernel(
                 const int64_t row = rs + u * RPS + h;
                 // false for an overflowed or NaN sum or bound: the row is kept
                 const bool known = fabsf(a) <= __FLT_MAX__ && e <= __FLT_MAX__;
-                if (g == 0 && row < r_end) ub[row] = known ? a + e : __builtin_huge_valf();
-                lo[u] = known ? a - e : -__builtin_huge_valf();
+                float hi = known ? a + e : __builtin_huge_valf();
+                float lw = known ? a - e : -__builtin_huge_valf();
+                if constexpr (COS) cosine_bounds(known, a, e, qnorm, rn[s][u], hi, lw);
+                if (g == 0 && row < r_end) ub[row] = hi;
+                lo[u] = lw;
             }
             if constexpr (P > 0) {
                 load_step(s, rs + P * STEP);
@@ -187,7 +214,7 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_bound_kernel(
 // candidate), then each row is reduced exactly as gemv_topk_kernel does
 // (lane_chain + group_sum with the same shape) and offered to the selectors.
 // Rows below T are never read.
-template <int LG, int L, int R>
+template <int LG, int L, int R, bool COS>
 __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_filtered_kernel(
     const float *__restrict__ corpus, int64_t n, int d, const float *__restrict__ queries,
     int64_t rows_per_wave, TreeArgs ta, FilterArgs fa) {
@@ -217,6 +244,8 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_filtered_kernel(
     WaveSelector<R> sel;
     sel.init(ta.k);
     const float T = fa.thr[seg];
+    float qnorm = 0.f;  // the cosine's query norm, computed as the plain scan does
+    if constexpr (COS) qnorm = wave_l2_norm(queries + (int64_t)seg * d, d);
 
     float4 qv[L];
     int colc[L];
@@ -270,7 +299,8 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_filtered_kernel(
 #pragma unroll
             for (int c = 0; c < NC; ++c) {
                 const int64_t row = b0 + (mine[c] >= 0 ? mine[c] : first);
-                const float s = group_sum(lane_chain<G, L>(x[c], qv, cmask), LG);
+                float s = group_sum(lane_chain<G, L>(x[c], qv, cmask), LG);
+                if constexpr (COS) s = cosine_of(s, qnorm, fa.crn[row]);
                 const bool valid = (g == 0) && (mine[c] >= 0);
                 const uint64_t rank = make_rank(order_key_f32(s), (uint32_t)row);
                 sel.offer(my_stage, rank, valid && rank > sel.thr);
@@ -296,6 +326,7 @@ inline FilterArgs make_filter(const FilterLaunch &f) {
     fa.ubuf = f.ubuf;
     fa.uld = f.uld;
     fa.thr = f.thr;
+    fa.crn = f.crn;
     return fa;
 }
 
@@ -311,12 +342,18 @@ hipError_t launch_bound_r(int lg, int L, bool ahead, dim3 grid, hipStream_t s, c
     const dim3 block(64 * gemv_waves(64 * R));
 #define RT_SHAPE(LGV, LV)                                                                                         \
     if (lg == LGV && L == LV) {                                                                                   \
-        if (ahead)                                                                                                \
-            hipLaunchKernelGGL((gemv_bound_kernel<LGV, LV, R, 2>), grid, block, 0, s, corpus16, n, d, queries,    \
-                               rnorm, per_wave, ta, fa);                                                          \
+        if (ahead && fa.crn)                                                                                      \
+            hipLaunchKernelGGL((gemv_bound_kernel<LGV, LV, R, 2, true>), grid, block, 0, s, corpus16, n, d,       \
+                               queries, rnorm, per_wave, ta, fa);                                                 \
+        else if (ahead)                                                                                           \
+            hipLaunchKernelGGL((gemv_bound_kernel<LGV, LV, R, 2, false>), grid, block, 0, s, corpus16, n, d,      \
+                               queries, rnorm, per_wave, ta, fa);                                                 \
+        else if (fa.crn)                                                                                          \
+            hipLaunchKernelGGL((gemv_bound_kernel<LGV, LV, R, 4, true>), grid, block, 0, s, corpus16, n, d,       \
+                               queries, rnorm, per_wave, ta, fa);                                                 \
         else                                                                                                      \
-            hipLaunchKernelGGL((gemv_bound_kernel<LGV, LV, R, 4>), grid, block, 0, s, corpus16, n, d, queries,    \
-                               rnorm, per_wave, ta, fa);                                                          \
+            hipLaunchKernelGGL((gemv_bound_kernel<LGV, LV, R, 4, false>), grid, block, 0, s, corpus16, n, d,      \
+                               queries, rnorm, per_wave, ta, fa);                                                 \
         return hipGetLastError();                                                                                 \
     }
     RT_GEMV_SHAPES(RT_SHAPE)
@@ -332,8 +369,12 @@ hipError_t launch_filtered_r(int lg, int L, dim3 grid, hipStream_t s, const floa
     const dim3 block(64 * gemv_waves(64 * R));
 #define RT_SHAPE(LGV, LV)                                                                                         \
     if (lg == LGV && L == LV) {                                                                                   \
-        hipLaunchKernelGGL((gemv_filtered_kernel<LGV, LV, R>), grid, block, 0, s, corpus, n, d, queries,          \
-                           per_wave, ta, fa);                                                                     \
+        if (fa.crn)                                                                                               \
+            hipLaunchKernelGGL((gemv_filtered_kernel<LGV, LV, R, true>), grid, block, 0, s, corpus, n, d,         \
+                               queries, per_wave, ta, fa);                                                        \
+        else                                                                                                      \
+            hipLaunchKernelGGL((gemv_filtered_kernel<LGV, LV, R, false>), grid, block, 0, s, corpus, n, d,        \
+                               queries, per_wave, ta, fa);                                                        \
         return hipGetLastError();                                                                                 \
     }
     RT_GEMV_SHAPES(RT_SHAPE)

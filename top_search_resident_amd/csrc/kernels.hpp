@@ -51,6 +51,7 @@ struct FilterLaunch {
     float *ubuf;     // [segments][uld] upper bounds, written by pass 1
     int64_t uld;
     float *thr;      // [segments] k-th largest lower bound, written by pass 1
+    const float *crn = nullptr;  // cosine metric: the rows' L2 norms (null: inner product)
 };
 
 // Bound factor cb for depth d (fp64 on the host, rounded up; see filter_topk.hpp)
