@@ -91,7 +91,7 @@ def time_search(eng, torch, qdev, ks, steps, warmup, profile=True, metric="dot",
     bf16 pass time in place of the streaming-kernel time)."""
     def search(q, k, oi, os_, stream):
         if filtered:
-            return eng.search_resident_filtered(q, k, oi, os_, stream=stream)
+            return eng.search_resident_filtered(q, k, oi, os_, stream=stream, metric=metric)
         return eng.search_resident(q, k, oi, os_, stream=stream, metric=metric)
 
     n_q = qdev.shape[0]
@@ -143,7 +143,7 @@ def time_end_to_end(eng, torch, qhost, ks, reps, metric="dot", filtered=False):
             s = time.perf_counter_ns()
             qdev.copy_(pin_q, non_blocking=True)
             if filtered:
-                eng.search_resident_filtered(qdev, k, oi, os_, stream=stream)
+                eng.search_resident_filtered(qdev, k, oi, os_, stream=stream, metric=metric)
             else:
                 eng.search_resident(qdev, k, oi, os_, stream=stream, metric=metric)
             hi.copy_(oi, non_blocking=True)
@@ -211,7 +211,7 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
     # its first pass: the bf16 rows and the rows' norms (or the fp8 codes and a
     # {scale, bound part} pair per row) and the upper bounds it writes
     if args.filtered and path == "fp8":
-        corpus_bytes = n * d + d * 4 + n * 8 + n * 4
+        corpus_bytes = n * d + d * 4 + n * 8 + n * 4 + (n * 4 if args.metric == "cosine" else 0)
     elif args.filtered:
         corpus_bytes = n * d * 2 + d * 4 + n * 4 + n * 4
     else:
@@ -264,7 +264,7 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
     if not args.filtered:
         line["hbm_read_ceiling"] = read_ceiling(eng, n * d * 4, avg_ms)
     line["gpu_clocks"] = gpu_clocks()
-    if not args.filtered and args.metric == "dot" and not args.no_filtered_leg and d % 8 == 0:
+    if not args.filtered and not args.no_filtered_leg and d % 8 == 0:
         line["filtered_exact"] = filtered_leg(args, torch, eng, qdev, ks, n, d)
     if not args.no_cpu_baseline:
         sample = min(args.cpu_queries, qhost.shape[0])
@@ -274,7 +274,7 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
             gs = np.empty((sample, k), np.float32)
             for qi in range(sample):
                 if args.filtered:
-                    a, b = eng.search_resident_filtered(qdev[qi:qi + 1], k)
+                    a, b = eng.search_resident_filtered(qdev[qi:qi + 1], k, metric=args.metric)
                 else:
                     a, b = eng.search_resident(qdev[qi:qi + 1], k, metric=args.metric)
                 torch.cuda.synchronize()
@@ -323,20 +323,22 @@ def filtered_leg(args, torch, eng, qdev, ks, n, d):
     eng.set_filter_storage(args.filter_storage)
     for qi in range(min(5, qdev.shape[0])):
         for k in ks:
-            a = eng.search_resident(qdev[qi:qi + 1], k)
-            b = eng.search_resident_filtered(qdev[qi:qi + 1], k)
+            a = eng.search_resident(qdev[qi:qi + 1], k, metric=args.metric)
+            b = eng.search_resident_filtered(qdev[qi:qi + 1], k, metric=args.metric)
             torch.cuda.synchronize()
             if not (torch.equal(a[0], b[0]) and torch.equal(a[1].view(torch.int32), b[1].view(torch.int32))):
                 raise SystemExit(f"filtered search differs from the plain scan (query {qi}, k {k})")
     path = eng.filter_path_used()
     steps = min(args.steps, 300)
-    wall, lat, part, merge = time_search(eng, torch, qdev, ks, steps, args.warmup, filtered=True)
-    if path == "fp8":  # codes, query, per-row {scale, bound part}, upper bounds written
-        pass1_bytes, kernel = n * d + d * 4 + n * 8 + n * 4, "gemv_bound8_kernel"
+    wall, lat, part, merge = time_search(eng, torch, qdev, ks, steps, args.warmup, metric=args.metric,
+                                         filtered=True)
+    if path == "fp8":  # codes, query, per-row {scale, bound part} (+ row norm for the cosine), bounds written
+        pass1_bytes = n * d + d * 4 + n * 8 + n * 4 + (n * 4 if args.metric == "cosine" else 0)
+        kernel = "gemv_bound8_kernel"
     else:  # bf16 rows, query, row norms, upper bounds written
         pass1_bytes, kernel = n * d * 2 + d * 4 + n * 4 + n * 4, "gemv_bound_kernel"
     p1 = float(np.mean(np.concatenate([np.asarray(part[k]) for k in ks])))
-    return {"value": steps * len(ks) / wall, "unit": "queries/s", "steps": steps,
+    return {"value": steps * len(ks) / wall, "unit": "queries/s", "steps": steps, "metric": args.metric,
             "identical_to_fp32_scan": True, "first_pass_storage": path,
             "per_k": {str(k): {"p50_us": pct(lat[k], 50), "p99_us": pct(lat[k], 99),
                                "device_p50_us": pct(np.asarray(merge[k]) * 1e3, 50),
