@@ -47,7 +47,8 @@ struct FilterArgs {
 // most 2^-24 relative (2^-149 absolute below the normal range), as do a + e,
 // a - e and the divisions below: widening by 2^-20 relative and FLT_MIN
 // absolute covers them.  `known` false (an overflowed sum or bound) leaves the
-// row's bounds at (+inf, -inf) unless den says -inf exactly.
+// row's bounds at (+inf, -inf) unless den says -inf exactly, and a quotient
+// that overflows gives the infinite bound on its side (never inf - inf).
 __device__ __forceinline__ void cosine_bounds(bool known, float a, float e, float qnorm, float rn, float &hi,
                                               float &lo) {
     const float den = qnorm * rn;
@@ -59,8 +60,8 @@ __device__ __forceinline__ void cosine_bounds(bool known, float a, float e, floa
     if (!known) return;
     const float h = (a + e) / den;
     const float l = (a - e) / den;
-    hi = h + fmaf(fabsf(h), 0x1p-20f, __FLT_MIN__);
-    lo = l - fmaf(fabsf(l), 0x1p-20f, __FLT_MIN__);
+    hi = fabsf(h) <= __FLT_MAX__ ? h + fmaf(fabsf(h), 0x1p-20f, __FLT_MIN__) : __builtin_huge_valf();
+    lo = fabsf(l) <= __FLT_MAX__ ? l - fmaf(fabsf(l), 0x1p-20f, __FLT_MIN__) : -__builtin_huge_valf();
 }
 
 // bf16 -> fp32 of the two halves of a 32-bit word.
