@@ -640,7 +640,8 @@ def main():
     if args.copy_calibration:
         copy_calibration(torch, args.copy_calibration, max(1, args.steps))
         return
-    from top_search_resident_amd import ResidentTopK, workloads
+    import workloads
+    from top_search_resident_amd import ResidentTopK
     if args.workload == "c4_1e8_int32":
         line = run_int32(args, torch, ResidentTopK, workloads)
     else:

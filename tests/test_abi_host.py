@@ -110,3 +110,23 @@ def test_entry_points_reject_null_engine(lib):
     assert lib.rt_engine_create(0, 8, 8, 1, 0, ctypes.byref(out)) == EINVAL and not out.value
     assert lib.rt_engine_create_shared(NULL, 8, 1, ctypes.byref(out)) == EINVAL and not out.value
     lib.rt_engine_destroy(NULL)  # ignored
+
+
+def test_binding_rejects_bad_tensors_on_the_host():
+    """The binding passes only addresses to the C ABI, so it must refuse, before
+    any call, a buffer a kernel cannot use: a host tensor, the wrong dtype, a
+    non-contiguous view or one too small, and queries whose width is not the
+    resident depth."""
+    torch = pytest.importorskip("torch")
+    import top_search_resident_amd as pkg
+    ok = torch.empty(8, dtype=torch.int32)
+    with pytest.raises(TypeError, match="CUDA"):
+        pkg._check_tensor(ok, "out_idx", torch.int32, 8, 0)          # host memory
+    with pytest.raises(TypeError, match="int32"):
+        pkg._check_tensor(torch.empty(8, dtype=torch.float32), "out_idx", torch.int32, 8, 0)
+    with pytest.raises(TypeError, match="torch tensor"):
+        pkg._check_tensor(ok.numpy(), "out_idx", torch.int32, 8, 0)
+    with pytest.raises(TypeError, match="CUDA"):
+        pkg._check_queries(torch.zeros((2, 16)), 16, 0)
+    with pytest.raises(ValueError, match=r"\[q, d\]"):
+        pkg._check_queries(torch.zeros((2, 4, 4)), 16, 0)

@@ -20,7 +20,8 @@ from fractions import Fraction
 import numpy as np
 import pytest
 
-from top_search_resident_amd import _lib, workloads
+import workloads
+from top_search_resident_amd import _lib
 
 torch = pytest.importorskip("torch")
 

@@ -15,7 +15,8 @@ import pytest
 
 import oracle
 from gpu_util import check_retrieval
-from top_search_resident_amd import ResidentTopK, workloads
+import workloads
+from top_search_resident_amd import ResidentTopK
 
 pytestmark = pytest.mark.gpu
 

@@ -9,7 +9,8 @@ import pytest
 
 import oracle
 from gpu_util import REL_TOL, SCALE_FLOOR, check_exact_topk_property, check_retrieval, cs_bound
-from top_search_resident_amd import ResidentTopK, workloads
+import workloads
+from top_search_resident_amd import ResidentTopK
 
 pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
@@ -82,6 +83,32 @@ def test_single_query_workloads(name, n_full, n_complete):
                     assert eng.filter_path_used() == "fp8"
                     assert np.array_equal(f_idx.cpu().numpy()[0], g_idx[qi]), (name, k, qi)
                     assert np.array_equal(f_sc.cpu().numpy()[0].view(np.uint32), g_sc[qi].view(np.uint32))
+
+
+def test_c3_repeat_is_bit_identical():
+    """One query at the large single-query size, repeated 50 times at each K:
+    the merge tree's workgroups arrive in a different order on every call, yet
+    the indices and score bits must not change (the order is the comparator's,
+    decided on the device, with no float sum across workgroups)."""
+    name = "c3_1m_1024"
+    print(f"[fullsize] {name} repeat: generating inputs", flush=True)
+    corpus, qs = workloads.retrieval_inputs(name, queries=2)
+    n, d = corpus.shape
+    ks = workloads.WORKLOADS[name]["ks"]
+    with ResidentTopK(n, d, max(ks), 1) as eng:
+        eng.upload_corpus_rowmajor(corpus)
+        qdev = torch.from_numpy(qs).cuda()
+        for k in ks:
+            outs = []
+            for rep in range(50):
+                outs.append(eng.search_resident(qdev[:1], k))
+            torch.cuda.synchronize()
+            i0, s0 = outs[0][0].cpu().numpy(), outs[0][1].cpu().numpy()
+            for rep, (i, s) in enumerate(outs[1:], 1):
+                assert np.array_equal(i.cpu().numpy(), i0), (k, rep)
+                assert np.array_equal(s.cpu().numpy().view(np.uint32), s0.view(np.uint32)), (k, rep)
+        o_idx, o_sc = oracle.search(corpus, qs[:1], max(ks))
+        check_retrieval(i0[0], s0[0], o_idx[0, :max(ks)], o_sc[0, :max(ks)], corpus, qs[0], oracle)
 
 
 def test_int32_1e8():

@@ -8,7 +8,8 @@ import pytest
 
 import oracle
 from gpu_util import check_exact_topk_property, check_retrieval
-from top_search_resident_amd import ResidentTopK, ResidentTopKError, workloads
+import workloads
+from top_search_resident_amd import ResidentTopK, ResidentTopKError
 
 pytestmark = pytest.mark.gpu
 
@@ -181,16 +182,30 @@ def test_batched_ragged_last_tile(eng):
         assert np.all(g_idx[:, 0] == np.array([n - 1, n - 2, n - 3, n - 4]))
 
 
+def _same(a, b):
+    return np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+
+
 def test_deterministic_repeat(eng):
+    """Repeated searches give the same indices and score bits: the batch (MFMA
+    scorer + tile-bounded selection) and each single query (streaming kernel,
+    per-wave lists and the cross-workgroup merge tree, whose arrival order
+    varies from call to call)."""
     corpus = workloads.gaussian_rows(60_000, 768, config_id=12)
     qs = workloads.gaussian_rows(4, 768, config_id=12, stream=1)
     a = _search(eng, corpus, qs, 100)
     b = _search(eng, corpus, qs, 100)
-    eng.upload_corpus_rowmajor(corpus)
-    q1 = torch.from_numpy(qs[:1]).cuda()
-    c_idx, c_sc = eng.search_resident(q1, 100)
-    torch.cuda.synchronize()
-    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1].view(np.uint32), b[1].view(np.uint32))
+    assert _same(a, b), "batched search not deterministic"
+    for qi in range(4):
+        q1 = torch.from_numpy(qs[qi:qi + 1]).cuda()
+        first = None
+        for rep in range(10):
+            idx, sc = eng.search_resident(q1, 100)
+            torch.cuda.synchronize()
+            cur = (idx.cpu().numpy(), sc.cpu().numpy())
+            if first is None:
+                first = cur
+            assert _same(first, cur), f"single query {qi} differs on repeat {rep}"
 
 
 def test_stream_argument(eng):
@@ -322,6 +337,51 @@ def test_error_paths():
         e.close()
     with pytest.raises(ResidentTopKError):
         ResidentTopK(1 << 40, 64, 8, 1)  # beyond the int32 index range
+
+
+def test_binding_rejects_bad_buffers():
+    """Checks the binding makes before anything is enqueued (the C ABI only sees
+    addresses): query width against the resident depth, and output buffers that
+    are host memory, non-contiguous, of the wrong dtype or too small."""
+    with ResidentTopK(1000, 64, 32, 4, device=0) as e:
+        e.upload_corpus_rowmajor(np.ones((100, 64), np.float32))
+        q = torch.zeros((1, 64), dtype=torch.float32, device="cuda")
+        with pytest.raises(ValueError, match="width"):
+            e.search_resident(torch.zeros((1, 32), dtype=torch.float32, device="cuda"), 8)
+        with pytest.raises(ValueError, match="width"):
+            e.search_resident(torch.zeros((1, 65), dtype=torch.float32, device="cuda"), 8)
+        with pytest.raises(TypeError, match="CUDA"):
+            e.search_resident(q, 8, out_idx=torch.empty((1, 8), dtype=torch.int32))
+        with pytest.raises(TypeError, match="CUDA"):
+            e.search_resident(q, 8, out_scores=torch.empty((1, 8), dtype=torch.float32))
+        with pytest.raises(TypeError, match="contiguous"):
+            e.search_resident(q, 8, out_idx=torch.empty((8, 2), dtype=torch.int32, device="cuda").t())
+        with pytest.raises(ValueError, match="needed"):
+            e.search_resident(q, 8, out_scores=torch.empty(7, dtype=torch.float32, device="cuda"))
+        with pytest.raises(TypeError, match="float32"):
+            e.search_resident(q, 8, out_scores=torch.empty(8, dtype=torch.float64, device="cuda"))
+        with pytest.raises(ResidentTopKError):
+            e.search_resident(q, 0)
+        v = torch.arange(100, dtype=torch.int32, device="cuda")
+        with pytest.raises(TypeError, match="CUDA"):
+            e.topk_select(v, 4, out_values=torch.empty(4, dtype=torch.int32))
+        with pytest.raises(TypeError, match="int32"):
+            e.topk_select(v, 4, out_values=torch.empty(4, dtype=torch.float32, device="cuda"))
+        with pytest.raises(TypeError, match="contiguous"):
+            e.topk_select(torch.arange(200, dtype=torch.int32, device="cuda")[::2], 4)
+        # the engine still works after every refusal
+        idx, _ = e.search_resident(q, 8)
+        i2, v2 = e.topk_select(v, 4)
+        torch.cuda.synchronize()
+        assert list(idx.cpu().numpy()[0]) == list(range(8))
+        assert list(i2.cpu().numpy()) == [99, 98, 97, 96]
+        # a shared engine follows the resident depth of the corpus it shares
+        with e.shared() as s2:
+            with pytest.raises(ValueError, match="width"):
+                s2.search_resident(torch.zeros((1, 32), dtype=torch.float32, device="cuda"), 8)
+            e.upload_corpus_rowmajor(np.ones((50, 32), np.float32))
+            s2.search_resident(torch.zeros((1, 32), dtype=torch.float32, device="cuda"), 8)
+            torch.cuda.synchronize()
 
 
 def test_read_probe(eng):

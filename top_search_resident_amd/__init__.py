@@ -30,6 +30,42 @@ def _check(status, what, eng=None):
         raise ResidentTopKError(status, what, hip)
 
 
+def _check_tensor(t, name, dtype, min_numel, device):
+    """Raise before anything is enqueued unless `t` is a contiguous CUDA tensor
+    of `dtype` on cuda:`device` with at least `min_numel` elements: the C ABI
+    receives only its address, and a kernel writing through a host address or
+    past the end of a buffer faults the GPU."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if t.device.index != device:
+        raise ValueError(f"{name} is on {t.device}, the engine on cuda:{device}")
+    if not t.is_contiguous():
+        raise TypeError(f"{name} must be contiguous")
+    if t.numel() < min_numel:
+        raise ValueError(f"{name} holds {t.numel()} elements, {min_numel} needed")
+
+
+def _check_queries(queries, d, device):
+    """A contiguous fp32 CUDA tensor [q, d] (or [d]) on the engine's device whose
+    width is the resident depth d (the C ABI reads q * d floats)."""
+    torch = _torch()
+    if not isinstance(queries, torch.Tensor):
+        raise TypeError("queries must be a torch tensor")
+    if queries.dim() == 1:
+        queries = queries.view(1, -1)
+    if queries.dim() != 2:
+        raise ValueError("queries must be [q, d] or [d]")
+    _check_tensor(queries, "queries", torch.float32, 0, device)
+    if d is not None and queries.shape[1] != d:
+        raise ValueError(f"queries have width {queries.shape[1]}, the resident corpus depth {d}")
+    return queries
+
+
 def _stream_handle(stream):
     torch = _torch()
     if stream is None:
@@ -53,6 +89,9 @@ class ResidentTopK:
             _check(st, "rt_engine_create_shared")
         self.device = int(device)
         self.max_n, self.max_d, self.max_k, self.max_q = int(max_n), int(max_d), int(max_k), int(max_q)
+        # Resident depth, shared by every engine that shares the corpus (an
+        # upload through any of them changes it for all); None before an upload.
+        self._res = _share._res if _share is not None else {"d": None}
 
     def shared(self, max_k=None, max_q=None):
         """A new engine that searches this engine's resident corpus (no copy) with
@@ -80,6 +119,24 @@ class ResidentTopK:
         except Exception:
             pass
 
+    def _lib_resident_d(self):
+        out = (ctypes.c_int64 * 7)()
+        _check(self._lib.rt_engine_info(self._h, out), "rt_engine_info")
+        return int(out[5]) or None
+
+    def _outputs(self, q, k, out_idx, out_val, val_dtype, name_val, like):
+        torch = _torch()
+        if k < 1:
+            raise ResidentTopKError(_lib.RT_EINVAL, f"k = {k}")
+        if out_idx is None:
+            out_idx = torch.empty((q, k) if q else (k,), dtype=torch.int32, device=like.device)
+        if out_val is None:
+            out_val = torch.empty((q, k) if q else (k,), dtype=val_dtype, device=like.device)
+        n = max(q, 1) * k
+        _check_tensor(out_idx, "out_idx", torch.int32, n, self.device)
+        _check_tensor(out_val, name_val, val_dtype, n, self.device)
+        return out_idx, out_val
+
     def info(self):
         out = (ctypes.c_int64 * 7)()
         _check(self._lib.rt_engine_info(self._h, out), "rt_engine_info")
@@ -101,6 +158,9 @@ class ResidentTopK:
                 raise TypeError("corpus must be a C-contiguous 2-D float32 array")
             ptr, (n, d) = corpus.ctypes.data, corpus.shape
         st = self._lib.upload_corpus_rowmajor(self._h, ctypes.c_void_p(ptr), int(n), int(d))
+        # the library's state decides: a rejected upload keeps the previous
+        # corpus, a failed copy leaves none
+        self._res["d"] = self._lib_resident_d()
         _check(st, "upload_corpus_rowmajor", self._h)
         self._keep = corpus  # not needed after the synchronous copy; kept only until the next upload
 
@@ -113,19 +173,9 @@ class ResidentTopK:
         metrics = {"dot": RT_METRIC_DOT, "cosine": RT_METRIC_COSINE}
         if metric not in metrics:
             raise ValueError(f"metric must be one of {sorted(metrics)}")
-        if queries.dim() == 1:
-            queries = queries.view(1, -1)
-        if queries.dtype != torch.float32 or not queries.is_cuda or not queries.is_contiguous():
-            raise TypeError("queries must be a contiguous float32 CUDA tensor")
+        queries = _check_queries(queries, self._res["d"], self.device)
         q = queries.shape[0]
-        if out_idx is None:
-            out_idx = torch.empty((q, k), dtype=torch.int32, device=queries.device)
-        if out_scores is None:
-            out_scores = torch.empty((q, k), dtype=torch.float32, device=queries.device)
-        if out_idx.dtype != torch.int32 or out_scores.dtype != torch.float32:
-            raise TypeError("out_idx must be int32 and out_scores float32")
-        if out_idx.numel() < q * k or out_scores.numel() < q * k:
-            raise ValueError("output buffers are too small")
+        out_idx, out_scores = self._outputs(q, int(k), out_idx, out_scores, torch.float32, "out_scores", queries)
         st = self._lib.search_resident_metric(self._h, ctypes.c_void_p(queries.data_ptr()), int(q), int(k),
                                               metrics[metric], ctypes.c_void_p(out_idx.data_ptr()),
                                               ctypes.c_void_p(out_scores.data_ptr()), _stream_handle(stream))
@@ -159,23 +209,13 @@ class ResidentTopK:
         corpus first and the fp32 rows only where their certified score bounds
         reach a certified threshold.  An inner-product batch runs one bf16
         matrix-core first pass for all of its queries."""
+        torch = _torch()
         metrics = {"dot": RT_METRIC_DOT, "cosine": RT_METRIC_COSINE}
         if metric not in metrics:
             raise ValueError(f"metric must be one of {sorted(metrics)}")
-        torch = _torch()
-        if queries.dim() == 1:
-            queries = queries.view(1, -1)
-        if queries.dtype != torch.float32 or not queries.is_cuda or not queries.is_contiguous():
-            raise TypeError("queries must be a contiguous float32 CUDA tensor")
+        queries = _check_queries(queries, self._res["d"], self.device)
         q = queries.shape[0]
-        if out_idx is None:
-            out_idx = torch.empty((q, k), dtype=torch.int32, device=queries.device)
-        if out_scores is None:
-            out_scores = torch.empty((q, k), dtype=torch.float32, device=queries.device)
-        if out_idx.dtype != torch.int32 or out_scores.dtype != torch.float32:
-            raise TypeError("out_idx must be int32 and out_scores float32")
-        if out_idx.numel() < q * k or out_scores.numel() < q * k:
-            raise ValueError("output buffers are too small")
+        out_idx, out_scores = self._outputs(q, int(k), out_idx, out_scores, torch.float32, "out_scores", queries)
         st = self._lib.search_resident_filtered_metric(self._h, ctypes.c_void_p(queries.data_ptr()), int(q), int(k),
                                                        metrics[metric], ctypes.c_void_p(out_idx.data_ptr()),
                                                        ctypes.c_void_p(out_scores.data_ptr()), _stream_handle(stream))
@@ -192,17 +232,9 @@ class ResidentTopK:
             dt = RT_DTYPE_FLOAT32
         else:
             raise TypeError("topk_select takes int32 or float32 tensors")
-        if not values.is_cuda or not values.is_contiguous():
-            raise TypeError("values must be a contiguous CUDA tensor")
+        _check_tensor(values, "values", values.dtype, 1, self.device)
         values = values.view(-1)
-        if out_idx is None:
-            out_idx = torch.empty(k, dtype=torch.int32, device=values.device)
-        if out_values is None:
-            out_values = torch.empty(k, dtype=values.dtype, device=values.device)
-        if out_idx.dtype != torch.int32 or out_values.dtype != values.dtype:
-            raise TypeError("out_idx must be int32 and out_values must match the input dtype")
-        if out_idx.numel() < k or out_values.numel() < k:
-            raise ValueError("output buffers are too small")
+        out_idx, out_values = self._outputs(0, int(k), out_idx, out_values, values.dtype, "out_values", values)
         st = self._lib.topk_select(self._h, ctypes.c_void_p(values.data_ptr()), dt, int(values.numel()),
                                    int(k), ctypes.c_void_p(out_idx.data_ptr()),
                                    ctypes.c_void_p(out_values.data_ptr()), _stream_handle(stream))
