@@ -243,6 +243,30 @@ rt_status search_resident_filtered_metric(rt_engine *e, const float *queries, in
 rt_status topk_select(rt_engine *e, const void *values, int32_t dtype, int64_t n, int32_t k,
                       int32_t *out_idx, void *out_values, void *stream);
 
+/*
+ * topk_select for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same selection, kernels and answers as topk_select, with no engine.  It
+ * allocates nothing -- no hipMalloc, hipFree or allocating library call -- and
+ * keeps the kernels' scratch (merge-tree lists and arrival counters) in a
+ * static device array of 4 MiB + 8 KiB that each GPU holds from the first call
+ * on it until the process ends.
+ *   values     device, n elements of `dtype`, 4-byte aligned, on the calling
+ *              thread's current HIP device (as are the outputs and `stream`)
+ *   out_idx    device, k int32: element positions, best-first
+ *   out_values device, k elements of `dtype`: bit-for-bit copies of the input
+ * Order and ties as topk_select.  RT_EINVAL: null pointer, unknown dtype,
+ * misaligned values, n < 1, n > 2^31-1, k < 1, k > 1024, k > n (checked
+ * before anything is enqueued; outputs untouched).  RT_EHIP: a HIP call or
+ * launch failed (the next call first clears the counters with a fill kernel).
+ * The array's size bounds the number of workgroups a call runs (fewer for
+ * k > 256), not n.  Every call on one GPU shares that GPU's array and leaves
+ * its counters zero: calls that overlap on one GPU (other streams, other
+ * threads) race and must not be issued.  Asynchronous on `stream`.
+ */
+rt_status topk_select_noalloc(const void *values, int32_t dtype, int64_t n, int32_t k, int32_t *out_idx,
+                              void *out_values, void *stream);
+
 /* Static, human-readable name of a status code. */
 const char *rt_status_string(rt_status s);
 

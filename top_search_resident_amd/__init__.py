@@ -16,7 +16,7 @@ import ctypes
 from . import _lib
 from ._lib import ResidentTopKError, RT_DTYPE_FLOAT32, RT_DTYPE_INT32, RT_METRIC_COSINE, RT_METRIC_DOT
 
-__all__ = ["ResidentTopK", "ResidentTopKError"]
+__all__ = ["ResidentTopK", "ResidentTopKError", "topk_select_noalloc"]
 
 
 def _torch():
@@ -71,6 +71,35 @@ def _stream_handle(stream):
     if stream is None:
         stream = torch.cuda.current_stream()
     return ctypes.c_void_p(stream.cuda_stream)
+
+
+def topk_select_noalloc(values, k, out_idx=None, out_values=None, stream=None):
+    """topk_select without an engine: the library allocates nothing (its kernels'
+    scratch is a static device array per GPU).  values: a contiguous int32 or
+    float32 CUDA tensor on the current device.  Returns (idx int32 [k], values
+    [k]) on the device, best-first.  Calls overlapping on one GPU race on the
+    shared array."""
+    torch = _torch()
+    lib = _lib.load()
+    if not isinstance(values, torch.Tensor) or values.dtype not in (torch.int32, torch.float32):
+        raise TypeError("topk_select_noalloc takes int32 or float32 tensors")
+    dev = torch.cuda.current_device()
+    _check_tensor(values, "values", values.dtype, 1, dev)
+    k = int(k)
+    if k < 1:
+        raise ResidentTopKError(_lib.RT_EINVAL, f"k = {k}")
+    if out_idx is None:
+        out_idx = torch.empty(k, dtype=torch.int32, device=values.device)
+    if out_values is None:
+        out_values = torch.empty(k, dtype=values.dtype, device=values.device)
+    _check_tensor(out_idx, "out_idx", torch.int32, k, dev)
+    _check_tensor(out_values, "out_values", values.dtype, k, dev)
+    dt = RT_DTYPE_INT32 if values.dtype == torch.int32 else RT_DTYPE_FLOAT32
+    st = lib.topk_select_noalloc(ctypes.c_void_p(values.data_ptr()), dt, int(values.numel()), k,
+                                 ctypes.c_void_p(out_idx.data_ptr()), ctypes.c_void_p(out_values.data_ptr()),
+                                 _stream_handle(stream))
+    _check(st, "topk_select_noalloc")
+    return out_idx, out_values
 
 
 class ResidentTopK:

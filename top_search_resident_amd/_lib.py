@@ -19,7 +19,7 @@ EXPORTS = (
     "rt_profile_read", "rt_engine_info", "rt_check_create", "rt_check_upload",
     "rt_check_search", "rt_check_search_metric", "rt_check_select", "rt_filter_bounds",
     "rt_filter_bounds_batched", "rt_filter_bounds_fp8", "rt_set_filter_storage", "rt_filter_path_used",
-    "rt_read_probe", "search_resident_filtered_metric",
+    "rt_read_probe", "search_resident_filtered_metric", "topk_select_noalloc",
 )
 
 _lib = None
@@ -60,6 +60,7 @@ def load():
         "search_resident_filtered": ([vp, vp, i32, i32, vp, vp, vp], ctypes.c_int),
         "search_resident_filtered_metric": ([vp, vp, i32, i32, i32, vp, vp, vp], ctypes.c_int),
         "topk_select": ([vp, vp, i32, i64, i32, vp, vp, vp], ctypes.c_int),
+        "topk_select_noalloc": ([vp, i32, i64, i32, vp, vp, vp], ctypes.c_int),
         "rt_status_string": ([ctypes.c_int], ctypes.c_char_p),
         "rt_last_hip_error": ([vp], i32),
         "rt_profile_enable": ([vp, i32], ctypes.c_int),

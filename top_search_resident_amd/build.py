@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(HERE, "libresident_topk.so")
-SOURCES = ["engine.hip", "stream_topk.hip", "mfma_scores.hip", "batch_select.hip", "filter_topk.hip", "mfma_filter.hip", "filter8.hip", "read_probe.hip"] + \
+SOURCES = ["engine.hip", "stream_topk.hip", "mfma_scores.hip", "batch_select.hip", "filter_topk.hip", "mfma_filter.hip", "filter8.hip", "read_probe.hip", "select_static.hip"] + \
     [f"stream_r{r}{m}.hip" for r in (16, 8, 4, 2, 1) for m in ("", "c")] + \
     [f"filter_r{r}.hip" for r in (16, 8, 4, 2, 1)]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -29,12 +29,25 @@ def _run(cmd):
     return res
 
 
-def build(verbose=False):
+def _newest_header():
+    heads = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")]
+    heads.append(os.path.join(ROOT, "include", "resident_topk.h"))
+    return max(os.path.getmtime(h) for h in heads)
+
+
+def build(verbose=False, force=True):
+    """Compile every source (force=True, what the build check runs) or only the
+    objects older than their source or any header (force=False), then link."""
     os.makedirs(BUILD_DIR, exist_ok=True)
+    newest_header = _newest_header()
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
-        _run([HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        path = os.path.join(CSRC, src)
+        if (not force and os.path.exists(obj) and
+                os.path.getmtime(obj) > max(os.path.getmtime(path), newest_header)):
+            return obj
+        _run([HIPCC, *FLAGS, "-c", path, "-o", obj])
         return obj
 
     with ThreadPoolExecutor(max(1, min(len(SOURCES), os.cpu_count() or 1))) as ex:
@@ -48,4 +61,5 @@ def build(verbose=False):
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    import sys
+    build(verbose=True, force="--changed" not in sys.argv)

@@ -17,6 +17,7 @@
 #include "../../include/resident_topk.h"
 #include "filter8_host.hpp"
 #include "kernels.hpp"
+#include "plan.hpp"
 #include "read_probe.hpp"
 
 namespace {
@@ -29,44 +30,15 @@ constexpr int32_t kMaxQ = 32;
 constexpr int64_t kTreeRanks = int64_t(1) << 23;
 // Most streaming workgroups per segment (bounds the counter array).
 constexpr int64_t kMaxWgsPerSeg = 2048;
-// Streaming waves per CU the planner aims for (measured on MI355X): 8 for the
-// scorer -- one 8-wave workgroup per CU beat 4-wave pairs and 16 waves per CU
-// from 10k x 384 to 1M x 1024 -- and 16 for raw-array selection (1e8 int32).
-constexpr int64_t kScoreWavesPerCu = 8;
-constexpr int64_t kSelectWavesPerCu = 16;
 
-int kp_for(int k) {
-    int kp = 64;
-    while (kp < k) kp <<= 1;
-    return kp;
-}
+using rt::kp_for;
+using rt::kScoreWavesPerCu;
+using rt::Plan;
 
-struct Plan {
-    int wgs;            // workgroups per segment
-    int64_t per_wave;   // rows (scoring) or 16-byte groups (raw arrays) per wave
-};
-
-// Split `units` (rows or 16-byte groups) of each of `segments` segments over
-// waves: at least `min_per_wave` units per wave, about waves_per_cu waves per CU
-// in total, and the merge tree (<= 2 lists per workgroup) must fit its storage.
 Plan plan_stream(int64_t units, int segments, int kp, int64_t min_per_wave, int num_cus, int64_t waves_per_cu,
                  int waves_per_wg) {
-    int64_t target = (int64_t)num_cus * waves_per_cu / segments;
-    if (target < waves_per_wg) target = waves_per_wg;
-    int64_t waves = (units + min_per_wave - 1) / min_per_wave;
-    if (waves > target) waves = target;
-    if (waves < 1) waves = 1;
-    int64_t wgs = (waves + waves_per_wg - 1) / waves_per_wg;
-    const int64_t cap = kTreeRanks / ((int64_t)segments * 2 * kp);
-    if (wgs > cap) wgs = cap;
-    if (wgs > kMaxWgsPerSeg) wgs = kMaxWgsPerSeg;
-    if (wgs < 1) wgs = 1;
-    waves = wgs * waves_per_wg;
-    Plan p;
-    p.wgs = (int)wgs;
-    p.per_wave = (units + waves - 1) / waves;
-    if (p.per_wave < 1) p.per_wave = 1;
-    return p;
+    return rt::plan_stream(units, segments, kp, min_per_wave, num_cus, waves_per_cu, waves_per_wg, kTreeRanks,
+                           kMaxWgsPerSeg);
 }
 
 // Corpus size (n x d elements) from which a single-query filtered search takes
@@ -473,19 +445,7 @@ rt_status rt_enable_filtered(rt_engine *e) {
 
 static rt::TreeLaunch tree_for(rt_engine *e, const Plan &p, int kp, int k, int mode, int32_t *out_idx,
                                void *out_val, const void *src, int64_t src_stride) {
-    rt::TreeLaunch t;
-    t.tree = e->tree;
-    t.counters = e->counters;
-    t.seg_tree_stride = 2 * (int64_t)p.wgs * kp;
-    t.seg_ctr_stride = p.wgs;
-    t.kp = kp;
-    t.k = k;
-    t.mode = mode;
-    t.out_idx = out_idx;
-    t.out_val = out_val;
-    t.src = src;
-    t.src_seg_stride = src_stride;
-    return t;
+    return rt::tree_launch(e->tree, e->counters, p.wgs, p, kp, k, mode, out_idx, out_val, src, src_stride);
 }
 
 static hipError_t prologue(rt_engine *e, hipStream_t s) {
@@ -644,8 +604,7 @@ rt_status topk_select(rt_engine *e, const void *values, int32_t dtype, int64_t n
     const int kp = kp_for(k);
     e->had_batch_kernel = false;
     if (err == hipSuccess) err = prologue(e, s);
-    const int64_t head = (int64_t)((reinterpret_cast<uintptr_t>(values) & 15u) >> 2);
-    const Plan p = plan_stream((n + head + 3) / 4, 1, kp, 256, e->num_cus, kSelectWavesPerCu, rt::select_waves(kp));
+    const Plan p = rt::plan_select(values, n, kp, e->num_cus, kTreeRanks, kMaxWgsPerSeg);
     const rt::TreeLaunch t = tree_for(e, p, kp, k, 2, out_idx, out_values, values, 0);
     if (err == hipSuccess) err = rt::launch_select_topk(values, 0, n, dtype, 1, p.per_wave, p.wgs, t, s);
     if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[1], s);
