@@ -96,12 +96,15 @@ def test_planted_near_ties(eng):
         _check_against_oracle(eng, corpus, qs, k)
 
 
-@pytest.mark.parametrize("q,d,k", [(2, 768, 100), (7, 1024, 8), (32, 768, 1024), (32, 384, 100),
-                                   (5, 100, 20), (3, 2048, 16), (32, 1024, 1)])
-def test_batched_queries(eng, q, d, k):
-    """Batches go through the MFMA scorer when d % 4 == 0 and d <= 1024, else
-    through the vector path once per query."""
-    n = 20_011
+@pytest.mark.parametrize("q,d,k,n", [(2, 768, 100, 20_011), (7, 1024, 8, 20_011), (32, 768, 1024, 20_011),
+                                     (32, 384, 100, 20_011), (5, 100, 20, 20_011), (3, 2048, 16, 20_011),
+                                     (32, 1024, 1, 20_011), (4, 512, 64, 20_011), (9, 256, 33, 65),
+                                     (3, 768, 20, 20), (32, 768, 31, 31), (6, 384, 7, 33)])
+def test_batched_queries(eng, q, d, k, n):
+    """Batches go through the MFMA scorers when d % 4 == 0 and d <= 1024 (the
+    direct-load kernel for d in {256, 384, 512, 768} and n >= 32, with a
+    ragged last tile loaded from row n - 32), else through the vector path
+    once per query."""
     corpus = workloads.gaussian_rows(n, d, config_id=55, stream=0)
     qs = workloads.gaussian_rows(q, d, config_id=55, stream=1)
     _check_against_oracle(eng, corpus, qs, k)

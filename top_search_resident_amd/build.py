@@ -29,23 +29,32 @@ def _run(cmd):
     return res
 
 
-def _newest_header():
-    heads = [os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hpp")]
-    heads.append(os.path.join(ROOT, "include", "resident_topk.h"))
-    return max(os.path.getmtime(h) for h in heads)
+def _newest_dependency(path, seen=None):
+    """Latest modification time of `path` and of the local headers it includes
+    (#include "..."), recursively."""
+    seen = set() if seen is None else seen
+    if path in seen or not os.path.exists(path):
+        return 0.0
+    seen.add(path)
+    newest = os.path.getmtime(path)
+    with open(path) as f:
+        for line in f:
+            line = line.strip()
+            if line.startswith("#include \""):
+                inc = os.path.normpath(os.path.join(os.path.dirname(path), line.split('"')[1]))
+                newest = max(newest, _newest_dependency(inc, seen))
+    return newest
 
 
 def build(verbose=False, force=True):
     """Compile every source (force=True, what the build check runs) or only the
     objects older than their source or any header (force=False), then link."""
     os.makedirs(BUILD_DIR, exist_ok=True)
-    newest_header = _newest_header()
 
     def compile_one(src):
         obj = os.path.join(BUILD_DIR, os.path.splitext(src)[0] + ".o")
         path = os.path.join(CSRC, src)
-        if (not force and os.path.exists(obj) and
-                os.path.getmtime(obj) > max(os.path.getmtime(path), newest_header)):
+        if not force and os.path.exists(obj) and os.path.getmtime(obj) > _newest_dependency(path):
             return obj
         _run([HIPCC, *FLAGS, "-c", path, "-o", obj])
         return obj

@@ -6,6 +6,11 @@
 // queries as missing (section 9); with a batch the corpus is read from HBM once
 // for all queries and the arithmetic runs on v_mfma_f32_32x32x2_f32.
 //
+// Two kernels.  For the inner product at d in {256, 384, 512, 768} (and n >= 32)
+// mfma_scores_dma_kernel below streams the corpus into LDS with direct loads
+// and keeps the query block in registers.  Every other batch (cosine, d = 1024,
+// other depths) runs the register-staged kernels described here.
+//
 // Tiling.  One workgroup per CU stages the whole 32 x d query block in LDS,
 // zero-padded to a whole number of pipeline rounds of 32 columns (row stride
 // padded by 4 floats to spread LDS banks).  Each wave owns tiles of 32 corpus
@@ -30,6 +35,7 @@
 // ld), and the tile's maximum per query is an in-register maximum plus one
 // exchange between the lane halves.
 #include "kernels.hpp"
+#include "lds_dma.hpp"
 #include "wave_topk.hpp"
 
 namespace rt {
@@ -312,6 +318,174 @@ __global__ __launch_bounds__(NT) void mfma_scores_fixed_kernel(const float *__re
     }
 }
 
+// Inner products for a depth of exactly d = 32 NCK (NCK in {8, 12, 16, 24}),
+// one wave per SIMD, with the whole query block held in registers and the
+// corpus streamed into LDS by direct loads.  Each wave owns consecutive 32-row
+// tiles; a tile is consumed in chunks of 32 columns (32 rows x 128 bytes = 4 KB)
+// through a ring of NR chunk slots in the wave's own LDS (no barrier: only the
+// wave itself writes and reads its slots).
+//
+//   - Loads: four direct-to-LDS instructions per chunk, each 8 rows x 128
+//     contiguous bytes with the non-temporal hint; unit u of row r lands at
+//     16-byte position u ^ f(r) of the row's 128-byte slot row (f below), which
+//     keeps the MFMA-layout reads free of bank conflicts; loads run NR - 2
+//     chunks ahead, across the wave's tiles.
+//   - Operands: for an MFMA step lane (m, kk) supplies corpus row m and query m
+//     at column 32 c + 4 (4 kk + i) + e of chunk c (i, e = 0..3): one 16-byte
+//     LDS read of the corpus unit and the matching query float4 from registers
+//     feed four v_mfma_f32_32x32x2_f32.  The next chunk's corpus operands are
+//     read before the current chunk's sixteen MFMAs issue.
+//   - Output: the tile's 32 x 32 sums are transposed through a 4 KB stage in
+//     LDS so that each store instruction writes 8 whole 128-byte score lines
+//     (non-temporal); per query the tile's maximum goes to tmax.
+// The query block costs d / 2 registers per lane (384 at d = 768), which is why
+// d = 1024 keeps the register-staged kernel above.  A ragged last tile is
+// loaded from row n - 32 (so every load is a whole row) and only its rows from
+// 32 t on are stored; n < 32 takes the other kernel.
+__device__ __forceinline__ int dma_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
+template <int NCK>
+struct DmaRing {
+    static constexpr int value = (NCK % 8 == 0) ? 8 : 6;  // slots, a divisor of NCK
+};
+
+template <int NCK>
+__global__ __launch_bounds__(256, 1) void mfma_scores_dma_kernel(const float *__restrict__ corpus, int64_t n,
+                                                                 const float *__restrict__ queries, int q,
+                                                                 float *__restrict__ scores, int64_t ld,
+                                                                 float *__restrict__ tmax, int64_t tld,
+                                                                 int64_t tiles_per_wave) {
+    constexpr int d = NCK * 32;
+    constexpr int NR = DmaRing<NCK>::value;
+    static_assert(NCK % NR == 0 && NR >= 4, "a chunk's ring slot must be a compile-time constant");
+    extern __shared__ __align__(16) char dma_lds[];  // per wave: NR chunk slots of 4 KB, then a 4 KB stage
+    const int lane = threadIdx.x & 63;
+    const int wv = wave_in_group();
+    const int m = lane & 31;
+    const int kk = lane >> 5;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
+    const int64_t tiles = (n + 31) / 32;
+    const int64_t t_begin = wave * tiles_per_wave;
+    const int64_t t_end = (t_begin + tiles_per_wave < tiles) ? t_begin + tiles_per_wave : tiles;
+    if (t_begin >= t_end) return;  // no barrier follows
+
+    // query operand of lane (m, kk): Q[m][32 c + 4 (4 kk + i) + e], zero for m >= q
+    float4 qreg[NCK][4];
+#pragma unroll
+    for (int c = 0; c < NCK; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            qreg[c][i] = (m < q) ? *reinterpret_cast<const float4 *>(queries + (int64_t)m * d + c * 32 + 4 * (4 * kk + i))
+                                 : make_float4(0.f, 0.f, 0.f, 0.f);
+    char *const ring = dma_lds + wv * ((NR + 1) * 4096);
+    char *const stage = ring + NR * 4096;
+    const uint32_t ring_lds = lds_addr(ring);
+    // direct-load lane mapping: instruction p of a chunk covers rows 8 p .. 8 p + 7
+    int voff[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int r = 8 * p + (lane >> 3);
+        const int u = (lane & 7) ^ dma_swizzle(r);
+        voff[p] = (r * d + u * 4) * 4;
+    }
+    int roff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) roff[i] = m * 128 + (((4 * kk + i) ^ dma_swizzle(m)) << 4);
+    auto load_row0 = [&](int64_t t) -> int64_t {
+        const int64_t r = t * 32;
+        return (r + 32 > n) ? n - 32 : r;
+    };
+    auto issue = [&](int64_t lr0, int c, int slot) {
+        const char *base = reinterpret_cast<const char *>(corpus + lr0 * d + c * 32);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) dma16_nt(base, voff[p], ring_lds + slot * 4096 + p * 1024);
+    };
+    const int64_t lr_first = load_row0(t_begin);
+#pragma unroll
+    for (int c = 0; c < NR - 1; ++c) issue(lr_first, c, c);
+    float4 a[2][4];
+    wait_vmcnt<4 * (NR - 2)>();  // chunk 0 has landed
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[0][i] = *reinterpret_cast<const float4 *>(ring + roff[i]);
+    for (int64_t t = t_begin; t < t_end; ++t) {
+        const int64_t lr = load_row0(t);
+        const int64_t lr_next = (t + 1 < t_end) ? load_row0(t + 1) : lr;  // past the last tile: reload, unused
+        floatx16 acc;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+        for (int c = 0; c < NCK; ++c) {
+            // chunk c + 1 (the next tile's chunk 0 after the last) must have
+            // landed: the loads issued after it are chunks c + 2 .. c + NR - 2
+            wait_vmcnt<4 * (NR - 3)>();
+            __builtin_amdgcn_sched_barrier(0);
+            {
+                const char *src = ring + ((c + 1) % NR) * 4096;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) a[(c + 1) & 1][i] = *reinterpret_cast<const float4 *>(src + roff[i]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            {
+                // refill the slot of chunk c - 1, whose operands were read an iteration ago
+                const int cn = c + NR - 1;  // a constant once the loop is unrolled
+                if (cn < NCK)
+                    issue(lr, cn, cn % NR);
+                else
+                    issue(lr_next, cn - NCK, cn % NR);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    acc = __builtin_amdgcn_mfma_f32_32x32x2f32(comp(a[c & 1][i], e), comp(qreg[c][i], e), acc, 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // lane (j, h) holds rows 8 g + 4 h + c' (register 4 g + c') of query j
+        const int j = lane & 31;
+        const int h = lane >> 5;
+        const int64_t row0 = t * 32;
+        float mx = -INFINITY;
+        if (lr == row0) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float4 v = make_float4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+                mx = fmaxf(mx, fmaxf(fmaxf(v.x, v.y), fmaxf(v.z, v.w)));
+                const int u = 2 * g + h;  // 16-byte unit of the query's 128-byte score line
+                *reinterpret_cast<float4 *>(stage + j * 128 + ((u ^ dma_swizzle(j)) << 4)) = v;
+            }
+            // 8 queries x 128 bytes per store instruction
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int jj = 8 * k + (lane >> 3);
+                const int su = lane & 7;
+                const float4 v = *reinterpret_cast<const float4 *>(stage + jj * 128 + ((su ^ dma_swizzle(jj)) << 4));
+                if (jj < q) {
+                    const f32x4_t w = {v.x, v.y, v.z, v.w};
+                    __builtin_nontemporal_store(w, reinterpret_cast<f32x4_t *>(scores + (int64_t)jj * ld + row0 + 4 * su));
+                }
+            }
+        } else if (j < q) {  // the ragged last tile, loaded from n - 32: rows from row0 on
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int64_t r = lr + 8 * g + 4 * h + c;
+                    if (r >= row0) {
+                        scores[(int64_t)j * ld + r] = acc[4 * g + c];
+                        mx = fmaxf(mx, acc[4 * g + c]);
+                    }
+                }
+        }
+        mx = fmaxf(mx, __uint_as_float(xor_u32<32>(__float_as_uint(mx))));
+        if (h == 0 && j < q) tmax[(int64_t)j * tld + t] = mx;
+    }
+    wait_vmcnt<0>();  // no direct load may still be writing LDS when the wave ends
+}
+
+static size_t dma_lds_bytes(int nck) { return (size_t)4 * ((nck % 8 == 0 ? 8 : 6) + 1) * 4096; }
+#define RT_MFMA_DMA(X) X(8) X(12) X(16) X(24)
+
 static size_t mfma_lds_bytes(int d, int kpf) { return (size_t)kMfmaMaxQ * (mfma_cols(d, kpf) + 4) * sizeof(float); }
 
 // Depths with a compile-time kernel (d = 32 * NCK); others take the runtime loop.
@@ -338,6 +512,12 @@ static hipError_t prepare_metric() {
 hipError_t prepare_mfma_scores() {
     hipError_t err = prepare_metric<false>();
     if (err == hipSuccess) err = prepare_metric<true>();
+#define RT_PREP_DMA(NCK)                                                                                 \
+    if (err == hipSuccess)                                                                               \
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_scores_dma_kernel<NCK>),          \
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)dma_lds_bytes(NCK));
+    RT_MFMA_DMA(RT_PREP_DMA)
+#undef RT_PREP_DMA
     return err;
 }
 
@@ -372,6 +552,19 @@ hipError_t launch_mfma_scores(const float *corpus, int64_t n, int d, const float
                               hipStream_t stream) {
     if (rnorm != nullptr)
         return launch_metric<true>(corpus, n, d, queries, q, rnorm, scores, ld, tmax, tld, num_cus, stream);
+    if (n >= 32) {
+        const int64_t tiles = (n + 31) / 32;
+        const int64_t tpw = (tiles + (int64_t)num_cus * 4 - 1) / ((int64_t)num_cus * 4);
+        const int64_t blocks = (tiles + tpw * 4 - 1) / (tpw * 4);
+#define RT_DMA(NCK)                                                                                        \
+        if (d == NCK * 32) {                                                                               \
+            hipLaunchKernelGGL((mfma_scores_dma_kernel<NCK>), dim3((unsigned)blocks), dim3(256),           \
+                               dma_lds_bytes(NCK), stream, corpus, n, queries, q, scores, ld, tmax, tld, tpw); \
+            return hipGetLastError();                                                                      \
+        }
+        RT_MFMA_DMA(RT_DMA)
+#undef RT_DMA
+    }
     return launch_metric<false>(corpus, n, d, queries, q, nullptr, scores, ld, tmax, tld, num_cus, stream);
 }
 
