@@ -535,8 +535,9 @@ rt_status search_resident_filtered_metric(rt_engine *e, const float *queries, in
     if (err == hipSuccess) err = prologue(e, s);
     if (err == hipSuccess && batched) {
         e->filter_path = RT_FILTER_PATH_BF16_MATRIX;
+        bool bounds16 = false;
         err = rt::launch_mfma_bound(r->corpus16, n, d, queries, q, r->rnorm, r->err16, e->ubuf, uld, e->tmax,
-                                    e->tile_ld, e->num_cus, s);
+                                    e->tile_ld, e->num_cus, s, &bounds16);
         if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[3], s);
         if (err == hipSuccess) err = rt::launch_tile_threshold(e->tmax, e->tile_ld, n, q, k, e->thr, s);
         if (err == hipSuccess) {
@@ -548,6 +549,7 @@ rt_status search_resident_filtered_metric(rt_engine *e, const float *queries, in
             f.ubuf = e->ubuf;
             f.uld = uld;
             f.thr = e->thr;
+            f.ub16 = bounds16 ? reinterpret_cast<const uint16_t *>(e->ubuf) : nullptr;
             err = rt::launch_filtered_pass2(r->corpus, n, d, queries, q, p2.per_wave, p2.wgs, t2, f, s);
         }
         e->had_batch_kernel = e->profiling;

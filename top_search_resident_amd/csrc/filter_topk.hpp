@@ -38,6 +38,7 @@ struct FilterArgs {
     int64_t uld;
     float *thr;      // [segments] T, the k-th largest lower bound (written by pass 1's tree)
     const float *crn;  // cosine metric: the rows' L2 norms (null for the inner product)
+    const uint16_t *ub16;  // pass 2: 16-bit upper bounds (top halves of fp32, rounded up) instead of ubuf
 };
 
 // Cosine bounds from the inner-product bounds a - e <= acc <= a + e of the
@@ -240,6 +241,7 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_filtered_kernel(
     const float4 *__restrict__ q4 = reinterpret_cast<const float4 *>(queries + (int64_t)seg * d);
     const float4 *__restrict__ c4 = reinterpret_cast<const float4 *>(corpus);
     const float *__restrict__ ub = fa.ubuf + (int64_t)seg * fa.uld;
+    const uint16_t *__restrict__ ub16 = fa.ub16 ? fa.ub16 + (int64_t)seg * fa.uld : nullptr;
     uint64_t *const my_stage = stage[wv];
 
     WaveSelector<R> sel;
@@ -263,10 +265,18 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_filtered_kernel(
     const int64_t r_end = (r_begin + rows_per_wave < n) ? r_begin + rows_per_wave : n;
     for (int64_t b0 = r_begin; b0 < r_end; b0 += (int64_t)NB * 64) {
         float uu[NB];
+        if (ub16) {  // wave-uniform
 #pragma unroll
-        for (int b = 0; b < NB; ++b) {
-            const int64_t row = b0 + b * 64 + lane;
-            uu[b] = ub[row < r_end ? row : r_end - 1];
+            for (int b = 0; b < NB; ++b) {
+                const int64_t row = b0 + b * 64 + lane;
+                uu[b] = __uint_as_float((uint32_t)ub16[row < r_end ? row : r_end - 1] << 16);
+            }
+        } else {
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                const int64_t row = b0 + b * 64 + lane;
+                uu[b] = ub[row < r_end ? row : r_end - 1];
+            }
         }
         int count = 0;  // wave-uniform
 #pragma unroll
@@ -328,6 +338,7 @@ inline FilterArgs make_filter(const FilterLaunch &f) {
     fa.uld = f.uld;
     fa.thr = f.thr;
     fa.crn = f.crn;
+    fa.ub16 = f.ub16;
     return fa;
 }
 

@@ -52,6 +52,7 @@ struct FilterLaunch {
     int64_t uld;
     float *thr;      // [segments] k-th largest lower bound, written by pass 1
     const float *crn = nullptr;  // cosine metric: the rows' L2 norms (null: inner product)
+    const uint16_t *ub16 = nullptr;  // pass 2: read 16-bit upper bounds (top halves of fp32) from here instead
 };
 
 // Bound factor cb for depth d (fp64 on the host, rounded up; see filter_topk.hpp)
@@ -89,10 +90,13 @@ hipError_t prepare_mfma_filter();
 // Pass 1 for q <= 32 queries: upper bounds ubuf[query * uld + row] and, per
 // query, the largest lower bound of every 32-row tile, tlb[query * tld + tile].
 // rnorm[i] = |x_i|, rerr[i] >= |x_i - bf16(x_i)| (both readable up to a
-// multiple of 32 rows past n).
+// multiple of 32 rows past n).  *bounds16 tells how the bounds were written:
+// false, fp32 at ubuf; true, 16-bit at (uint16_t *)ubuf (the top halves of
+// fp32 values rounded toward +inf), which pass 2 reads through
+// FilterLaunch::ub16.
 hipError_t launch_mfma_bound(const uint16_t *corpus16, int64_t n, int d, const float *queries, int q,
                              const float *rnorm, const float *rerr, float *ubuf, int64_t uld, float *tlb, int64_t tld,
-                             int num_cus, hipStream_t stream);
+                             int num_cus, hipStream_t stream, bool *bounds16);
 // Per query, thr[seg] <= the k-th largest of that query's tile maxima of lower
 // bounds tmax[seg * tld + tile] (a bin edge below it; -inf when n has fewer
 // than k tiles), so at least k rows have a lower bound at or above it.

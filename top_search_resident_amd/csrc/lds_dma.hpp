@@ -33,6 +33,10 @@ __device__ __forceinline__ void dma16_nt(const void *sbase, int voff, uint32_t l
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1 nt" ::"v"(voff), "s"(sbase), "s"(lds)
                  : "memory", "m0");
 }
+// 16 bytes per lane from the lane's own 64-bit address into LDS at lds + 16 * lane.
+__device__ __forceinline__ void dma16_nt_addr(const void *addr, uint32_t lds) {
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off nt" ::"v"(addr), "s"(lds) : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // s_waitcnt vmcnt(N), the other counters untouched (gfx9 encoding: vmcnt in
@@ -42,6 +46,13 @@ __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
 }
+
+// Position (in 16-byte units) of unit u of row r within a chunk slot of 32 rows
+// x 128 bytes is u ^ dma_swizzle(r): every 128-byte row stays whole (the 8
+// lanes loading it still read 128 contiguous bytes), and 16 lanes reading one
+// unit of 16 consecutive rows -- the MFMA-layout reads -- hit 16 distinct
+// 16-byte bank groups (also 8 distinct among any 8 consecutive rows).
+__device__ __forceinline__ int dma_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 
 // The 32-bit LDS address of a __shared__ / dynamic-LDS pointer, wave-uniform.
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {

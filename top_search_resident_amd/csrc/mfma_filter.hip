@@ -52,6 +52,7 @@
 #include <utility>
 
 #include "filter_topk.hpp"
+#include "lds_dma.hpp"
 
 namespace rt {
 
@@ -280,6 +281,295 @@ __global__ __launch_bounds__(NW * 64) void mfma_bound_kernel(const uint16_t *__r
     }
 }
 
+// Pass 1 through direct loads, for d = 64 NCK with NCK in {4, 6, 8, 12}: one
+// wave per SIMD, the query's bf16 hi and lo parts in registers (d / 2
+// registers per lane: 384 at d = 768), the corpus streamed into a ring of NR
+// 4 KB chunk slots in the wave's own LDS (32 rows x 128 bytes, loaded as 8 rows
+// x 128 contiguous bytes per instruction with the non-temporal hint, unit u of
+// row r at position u ^ f(r)), and each tile's row norms and error norms
+// loaded the same way into one of two small LDS slots (so no ordinary global
+// load is ever outstanding next to the ring: the compiler would drain the
+// ring to wait for it).  The MFMA layout is the one above (lane (m, h) takes
+// unit 2 s + h of row m for k-step s; hi and lo parts: two MFMAs per k-step).
+// The upper bounds are written as 16-bit values rounded toward +inf (the top
+// half of an fp32 word, incremented when a positive value loses bits), which
+// halves the bytes written -- in this streaming pass every byte written costs
+// more than a byte read (measured on MI355X: 64 MB of scattered writes next to
+// a full-rate read stream cost ~70 us, 16 MB ~30 us) -- at the price of a
+// slightly wider candidate band in pass 2 (2^-8 relative).  They are
+// transposed through LDS so each store writes whole 64-byte runs.  A ragged
+// last tile is loaded from row n - 32; only its rows from 32 t on are written.
+__device__ __forceinline__ uint16_t bf16_round_up_bits(float x) {
+    const uint32_t b = __float_as_uint(x);
+    const uint32_t hi = b >> 16;
+    // positive and inexact: the next bf16 up (also maps values above the
+    // largest bf16 to +inf); zero, negative or exact: dropping the low bits
+    // moves toward zero or changes nothing, which does not decrease the value
+    return (uint16_t)((!(b >> 31) && (b & 0xffffu)) ? hi + 1u : hi);
+}
+
+template <int NCK>
+struct BoundRing {
+    static constexpr int value = (NCK % 8 == 0) ? 8 : (NCK % 6 == 0 ? 6 : 4);
+};
+
+template <int NCK>
+struct BoundDma {
+    // At d = 768 the lo parts stay in LDS (with both parts in registers the
+    // kernel needs more than 512 of them), which leaves room for 6 chunk slots.
+    static constexpr bool kLoInLds = NCK > 8;
+    // chunk slots (<= NCK: the prologue fills them from the first tile); NR - 1
+    // chunks are loading while one is read
+    static constexpr int kRing = kLoInLds ? 6 : (NCK < 8 ? NCK : 8);
+    static constexpr int kLoStride = NCK * 128 + 16;  // bytes per query row of lo parts (padded)
+    static constexpr int kWaveLds = kRing * 4096 + 2048 + 512;  // ring, bound stage, two norm slots
+    static constexpr int kLoLds = kLoInLds ? 32 * kLoStride : 0;
+    static constexpr int kLds = kLoLds + 4 * kWaveLds;
+};
+
+template <int NCK>
+__global__ __launch_bounds__(256, 1) void mfma_bound_dma_kernel(const uint16_t *__restrict__ corpus16, int64_t n,
+                                                                const float *__restrict__ queries, int q,
+                                                                const float *__restrict__ rnorm,
+                                                                const float *__restrict__ rerr, float cr, float cx,
+                                                                float delta, uint16_t *__restrict__ ub16,
+                                                                int64_t uld, float *__restrict__ tlb, int64_t tld,
+                                                                int64_t tiles_per_wave) {
+    using L = BoundDma<NCK>;
+    constexpr int d = NCK * 64;
+    constexpr int NR = L::kRing;
+    static_assert(NR >= 4 && NR <= NCK, "ring");
+    static_assert(L::kLds + 32 * 4 <= 160 * 1024, "LDS");
+    // [lo parts of the query block, at d = 768] then per wave: NR chunk slots of
+    // 4 KB, a 2 KB stage for the bounds, two 256-byte norm slots
+    extern __shared__ __align__(16) char bound_lds[];
+    const int lane = threadIdx.x & 63;
+    const int wv = wave_in_group();
+    const int m = lane & 31;
+    const int h = lane >> 5;
+    const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
+    const int64_t tiles = (n + 31) / 32;
+    const int64_t t_begin = wave * tiles_per_wave;
+    const int64_t t_end = (t_begin + tiles_per_wave < tiles) ? t_begin + tiles_per_wave : tiles;
+    char *const lo_lds = bound_lds;
+    char *const wave_lds = bound_lds + L::kLoLds;
+    __shared__ float qn_s[32];
+
+    // The fp32 query block goes through LDS first (coalesced loads by the whole
+    // workgroup into the per-wave space, not yet in use); each wave computes
+    // the L2 norms of eight queries from it (as the other bound kernel does),
+    // and each lane builds query m's hi and lo parts for k-step s of chunk c
+    // (columns 64 c + 8 (2 s + h) .. + 7).
+    static_assert(32 * d * 4 <= 4 * L::kWaveLds, "query block fits the per-wave space");
+    {
+        float4 *qs4 = reinterpret_cast<float4 *>(wave_lds);
+        for (int i = threadIdx.x; i < 32 * d / 4; i += 256) {
+            const int r = i / (d / 4);
+            qs4[i] = (r < q) ? reinterpret_cast<const float4 *>(queries)[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+    }
+    __syncthreads();
+    for (int j = wv; j < 32; j += 4) {
+        const float v = wave_l2_norm(reinterpret_cast<const float *>(wave_lds) + j * d, d);
+        if (lane == 0) qn_s[j] = v;
+    }
+    uint4 qh[NCK][4];
+    uint4 ql[L::kLoInLds ? 1 : NCK][4];
+    {
+        const float *qrow = reinterpret_cast<const float *>(wave_lds) + m * d + 8 * h;
+#pragma unroll
+        for (int c = 0; c < NCK; ++c)
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const float4 v0 = *reinterpret_cast<const float4 *>(qrow + 64 * c + 16 * s);
+                const float4 v1 = *reinterpret_cast<const float4 *>(qrow + 64 * c + 16 * s + 4);
+                const float x[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                uint32_t hw[4], lw[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float x0 = x[2 * e], x1 = x[2 * e + 1];
+                    const uint32_t h0 = bf16_bits_rne(x0), h1 = bf16_bits_rne(x1);
+                    hw[e] = h0 | (h1 << 16);
+                    lw[e] = bf16_bits_rne(x0 - __uint_as_float(h0 << 16)) |
+                            (bf16_bits_rne(x1 - __uint_as_float(h1 << 16)) << 16);
+                }
+                qh[c][s] = make_uint4(hw[0], hw[1], hw[2], hw[3]);
+                if constexpr (L::kLoInLds)
+                    *reinterpret_cast<uint4 *>(lo_lds + m * L::kLoStride + (64 * c + 8 * (2 * s + h)) * 2) =
+                        make_uint4(lw[0], lw[1], lw[2], lw[3]);
+                else
+                    ql[c][s] = make_uint4(lw[0], lw[1], lw[2], lw[3]);
+                // one k-step at a time: hoisting every LDS read of the block
+                // ahead of the conversions would need ~d more registers
+                __builtin_amdgcn_sched_barrier(0);
+            }
+    }
+    __syncthreads();  // every wave has its query parts before any ring slot is loaded
+    if (t_begin >= t_end) return;  // no barrier follows
+    const float qn = qn_s[m];
+    const float er = cr * qn;
+    const float ex = cx * qn;
+    const float dl = delta * fmaxf(qn, 1.f);
+    const bool has_q = m < q;
+
+    char *const ring = wave_lds + wv * L::kWaveLds;
+    char *const stage = ring + NR * 4096;
+    char *const norms = stage + 2048;  // two 256-byte slots: [rnorm 32 floats][rerr 32 floats]
+    const uint32_t ring_lds = lds_addr(ring);
+    const uint32_t norms_lds = lds_addr(norms);
+    const char *const lo_row = lo_lds + m * L::kLoStride + 16 * h;
+    int voff[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+        const int r = 8 * p + (lane >> 3);
+        const int u = (lane & 7) ^ dma_swizzle(r);
+        voff[p] = (r * d + u * 8) * 2;
+    }
+    int roff[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) roff[s] = m * 128 + (((2 * s + h) ^ dma_swizzle(m)) << 4);
+    auto load_row0 = [&](int64_t t) -> int64_t {
+        const int64_t r = t * 32;
+        return (r + 32 > n) ? n - 32 : r;
+    };
+    auto issue = [&](int64_t lr0, int c, int slot) {
+        const char *base = reinterpret_cast<const char *>(corpus16 + lr0 * d + c * 64);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) dma16_nt(base, voff[p], ring_lds + slot * 4096 + p * 1024);
+    };
+    // rows lr0 .. lr0 + 31: lanes 0..7 their norms, lanes 8..15 their error
+    // norms, 256 bytes (the other lanes are masked off: one load instruction)
+    auto issue_norms = [&](int64_t lr0, int par) {
+        if (lane < 16) {
+            const float *src = (lane < 8) ? rnorm + lr0 + 4 * lane : rerr + lr0 + 4 * (lane - 8);
+            dma16_nt_addr(src, norms_lds + par * 256);
+        }
+    };
+    // Chunks are numbered across the wave's tiles; chunk g lives in slot g % NR
+    // (wave-uniform counters, not compile-time: NR need not divide NCK).  Once
+    // the operands of chunk g have been read, its slot is refilled with chunk
+    // g + NR, so NR - 1 chunks are loading while chunk g + 1 is waited for.
+    const int64_t lr_first = load_row0(t_begin);
+    issue_norms(lr_first, 0);
+#pragma unroll
+    for (int c = 0; c < NR; ++c) issue(lr_first, c, c);
+    int slot_cur = 0;  // slot of chunk g
+    uint4 a[2][4];
+    uint4 lo[2][4];  // lo parts of the chunk's query operands when they are kept in LDS
+    wait_vmcnt<4 * (NR - 1)>();  // the norms and chunk 0 have landed
+#pragma unroll
+    for (int s = 0; s < 4; ++s) a[0][s] = *reinterpret_cast<const uint4 *>(ring + roff[s]);
+    if constexpr (L::kLoInLds) {
+#pragma unroll
+        for (int s = 0; s < 4; ++s) lo[0][s] = *reinterpret_cast<const uint4 *>(lo_row + 32 * s);
+    }
+    for (int64_t t = t_begin; t < t_end; ++t) {
+        const int64_t lr = load_row0(t);
+        const int64_t lr_next = (t + 1 < t_end) ? load_row0(t + 1) : lr;  // past the last tile: reload, unused
+        const int par = (int)((t - t_begin) & 1);
+        floatx16 acc;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+        for (int c = 0; c < NCK; ++c) {
+            const int slot_next = (slot_cur + 1 == NR) ? 0 : slot_cur + 1;
+            // this chunk's corpus operands are in registers (the asm waits for
+            // their LDS reads); refill its slot with chunk c + NR (the next
+            // tile's chunk c + NR - NCK past the end, with that tile's norms)
+            asm volatile("" ::"v"(a[c & 1][0].x), "v"(a[c & 1][1].x), "v"(a[c & 1][2].x), "v"(a[c & 1][3].x));
+            __builtin_amdgcn_sched_barrier(0);
+            {
+                const int cn = c + NR;  // a constant once the loop is unrolled
+                if (cn < NCK) {
+                    issue(lr, cn, slot_cur);
+                } else {
+                    if (cn == NCK) issue_norms(lr_next, par ^ 1);
+                    issue(lr_next, cn - NCK, slot_cur);
+                }
+            }
+            // chunk c + 1 must have landed: the loads after it are chunks c + 2 .. c + NR
+            // (and perhaps the next tile's norms)
+            wait_vmcnt<4 * (NR - 1)>();
+            __builtin_amdgcn_sched_barrier(0);
+            {
+                const char *src = ring + slot_next * 4096;
+#pragma unroll
+                for (int s = 0; s < 4; ++s) a[(c + 1) & 1][s] = *reinterpret_cast<const uint4 *>(src + roff[s]);
+            }
+            if constexpr (L::kLoInLds) {
+                const int cq = (c + 1 < NCK) ? c + 1 : 0;  // the next tile starts again at chunk 0
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    lo[(c + 1) & 1][s] = *reinterpret_cast<const uint4 *>(lo_row + (64 * cq + 16 * s) * 2);
+            }
+            slot_cur = slot_next;
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const bf16x8 av = __builtin_bit_cast(bf16x8, a[c & 1][s]);
+                const uint4 qlo = L::kLoInLds ? lo[c & 1][s] : ql[L::kLoInLds ? 0 : c][s];
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, qh[c][s]), acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, __builtin_bit_cast(bf16x8, qlo), acc, 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // Bounds of rows lr + 8 g + 4 h + c' for query m (register 4 g + c').
+        const char *nslot = norms + par * 256;
+        const int64_t row0 = t * 32;
+        float mx = -__builtin_huge_valf();
+        uint32_t packed[4][2];
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float4 rn = *reinterpret_cast<const float4 *>(nslot + (8 * g + 4 * h) * 4);
+            const float4 re = *reinterpret_cast<const float4 *>(nslot + 128 + (8 * g + 4 * h) * 4);
+            uint16_t u16[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                const float av = acc[4 * g + c];
+                const float rv = comp4(rn, c);
+                const float e = fmaf(er, comp4(re, c), fmaf(ex, rv, dl * fmaxf(rv, 1.f)));
+                // false for an overflowed or NaN sum or bound: the row is kept
+                const bool known = fabsf(av) <= __FLT_MAX__ && e <= __FLT_MAX__;
+                const float ubv = known ? av + e : __builtin_huge_valf();
+                const float lbv = known ? av - e : -__builtin_huge_valf();
+                u16[c] = bf16_round_up_bits(ubv);
+                if (lr + 8 * g + 4 * h + c >= row0) mx = fmaxf(mx, lbv);
+            }
+            packed[g][0] = (uint32_t)u16[0] | ((uint32_t)u16[1] << 16);
+            packed[g][1] = (uint32_t)u16[2] | ((uint32_t)u16[3] << 16);
+        }
+        if (lr == row0) {
+            // stage [query][32 rows] x 2 bytes, then 4 lanes x 16 bytes per query run
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+                *reinterpret_cast<uint2 *>(stage + m * 64 + (8 * g + 4 * h) * 2) = make_uint2(packed[g][0], packed[g][1]);
+#pragma unroll
+            for (int k = 0; k < 2; ++k) {
+                const int jj = 16 * k + (lane >> 2);
+                const int su = lane & 3;
+                const uint4 v = *reinterpret_cast<const uint4 *>(stage + jj * 64 + su * 16);
+                if (jj < q) {
+                    const u32x4_t w = {v.x, v.y, v.z, v.w};
+                    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t *>(ub16 + (int64_t)jj * uld + row0 + 8 * su));
+                }
+            }
+        } else if (has_q) {  // the ragged last tile, loaded from n - 32: rows from row0 on
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const int64_t r = lr + 8 * g + 4 * h + c;
+                    if (r >= row0) ub16[(int64_t)m * uld + r] = (uint16_t)(packed[g][c >> 1] >> (16 * (c & 1)));
+                }
+        }
+        mx = fmaxf(mx, __uint_as_float(xor_u32<32>(__float_as_uint(mx))));
+        if (h == 0 && has_q) tlb[(int64_t)m * tld + t] = mx;
+    }
+    wait_vmcnt<0>();  // no direct load may still be writing LDS when the wave ends
+}
+
+#define RT_BOUND_DMA(X) X(4) X(6) X(8) X(12)
+
 bool mfma_filter_ok(int d) { return d == 256 || d == 384 || d == 512 || d == 768 || d == 1024; }
 
 void filter_bound_constants_batched(int d, float *cr, float *cx, float *delta) {
@@ -309,15 +599,36 @@ hipError_t prepare_mfma_filter() {
                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)bound_lds_bytes(NCK * 64, NW));
     RT_BOUND_DEPTHS(RT_PREP)
 #undef RT_PREP
+#define RT_PREP_DMA(NCK)                                                                                  \
+    if (err == hipSuccess)                                                                                \
+        err = hipFuncSetAttribute(reinterpret_cast<const void *>(&mfma_bound_dma_kernel<NCK>),            \
+                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)(size_t)BoundDma<NCK>::kLds);
+    RT_BOUND_DMA(RT_PREP_DMA)
+#undef RT_PREP_DMA
     return err;
 }
 
 hipError_t launch_mfma_bound(const uint16_t *corpus16, int64_t n, int d, const float *queries, int q,
                              const float *rnorm, const float *rerr, float *ubuf, int64_t uld, float *tlb, int64_t tld,
-                             int num_cus, hipStream_t stream) {
+                             int num_cus, hipStream_t stream, bool *bounds16) {
     const int64_t tiles = (n + 31) / 32;
     float cr, cx, delta;
     filter_bound_constants_batched(d, &cr, &cx, &delta);
+    *bounds16 = false;
+    if (n >= 32) {
+        const int64_t tpw = (tiles + (int64_t)num_cus * 4 - 1) / ((int64_t)num_cus * 4);
+        const int64_t blocks = (tiles + tpw * 4 - 1) / (tpw * 4);
+#define RT_LAUNCH_DMA(NCK)                                                                                      \
+        if (d == NCK * 64) {                                                                                    \
+            *bounds16 = true;                                                                                   \
+            hipLaunchKernelGGL((mfma_bound_dma_kernel<NCK>), dim3((unsigned)blocks), dim3(256),                 \
+                               (size_t)BoundDma<NCK>::kLds, stream, corpus16, n, queries, q, rnorm, rerr, cr, cx,  \
+                               delta, reinterpret_cast<uint16_t *>(ubuf), uld, tlb, tld, tpw);                  \
+            return hipGetLastError();                                                                           \
+        }
+        RT_BOUND_DMA(RT_LAUNCH_DMA)
+#undef RT_LAUNCH_DMA
+    }
 #define RT_LAUNCH(NCK, NW, KPF)                                                                                 \
     if (d == NCK * 64) {                                                                                        \
         const int64_t tpw = (tiles + (int64_t)num_cus * NW - 1) / ((int64_t)num_cus * NW);                      \

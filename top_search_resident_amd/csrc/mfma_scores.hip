@@ -342,8 +342,6 @@ __global__ __launch_bounds__(NT) void mfma_scores_fixed_kernel(const float *__re
 // d = 1024 keeps the register-staged kernel above.  A ragged last tile is
 // loaded from row n - 32 (so every load is a whole row) and only its rows from
 // 32 t on are stored; n < 32 takes the other kernel.
-__device__ __forceinline__ int dma_swizzle(int r) { return (r & 7) ^ ((r >> 3) & 1); }
-
 template <int NCK>
 struct DmaRing {
     static constexpr int value = (NCK % 8 == 0) ? 8 : 6;  // slots, a divisor of NCK
