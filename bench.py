@@ -25,9 +25,14 @@ ones -- and fp32 rows re-scored only where certified bounds reach the
 threshold); its answers are checked to equal the plain scan's bit for bit
 before it is timed.  Reported beside `value`, which stays the plain fp32 scan.
 
-Other workloads (--workload): c1_10k_384, c2_50k_768, c2_100k_768,
-c4_1e8_int32, c5_q32_500k_768 -- parity-test configurations, available for
-measurement; the default line is c3_1m_1024.
+The other four configurations run in the same default invocation and appear
+under `workloads` in the same line, each with its own protocol (1,000
+sequential queries per K at 10k x 384 and 50k/100k x 768, at least 100 calls per
+K for the 1e8 int32 top-K, 100 batches per K for the 32-query batch at 500k x
+768), its roofline fraction, the oracle timed on a bounded sample with the GPU
+answers checked against it, and for the batch the matrix-core utilisation.
+`--workload NAME` runs one configuration alone; `--n/--d/--k/--queries/--batch/
+--seed` run a free-form synthetic corpus of the same recipe.
 """
 import argparse
 import json
@@ -45,11 +50,11 @@ HBM_PEAK_GBS = 8000.0
 METRIC = "queries/s + p50 latency at N=1M,D=1024,K∈{8,32,100}; % of HBM peak"
 
 
-def measured_traffic():
-    """HBM bytes per launch of the scan kernel from the committed PMC summary,
-    if it was taken on the current kernel sources (else None)."""
+def profile_record(name):
+    """A committed PMC summary (profiles/<name>.json), if it was taken on the
+    current kernel sources (their sha256 matches), else None."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "gemv_topk_1m_x_1024_traffic.json")
+    path = os.path.join(ROOT, "profiles", name + ".json")
     try:
         with open(path) as f:
             data = json.load(f)
@@ -59,9 +64,71 @@ def measured_traffic():
                 h.update(f.read())
         if h.hexdigest() != data["kernel_sources_sha256"]:
             return None
-        return float(data["traffic_bytes_per_launch"]["mean over K=8,32,100"])
+        return data
     except (OSError, KeyError, ValueError):
         return None
+
+
+def measured_traffic(name="gemv_topk_1m_x_1024_traffic", key="mean over K=8,32,100"):
+    """HBM bytes per launch of a kernel from its committed PMC summary (FETCH_SIZE
+    x the copy calibration + WRITE_SIZE), if taken on the current sources."""
+    data = profile_record(name)
+    try:
+        return float(data["traffic_bytes_per_launch"][key]) if data else None
+    except (KeyError, TypeError, ValueError):
+        return None
+
+
+# Committed PMC summaries (profiles/<name>.json) of each workload's dominant
+# kernel: HBM bytes per launch and, for the batch, matrix-core busy cycles.
+TRAFFIC_PROFILES = {
+    "c1_10k_384": ("gemv_topk_10k_x_384_traffic", "mean"),
+    "c2_50k_768": ("gemv_topk_50k_x_768_traffic", "mean"),
+    "c2_100k_768": ("gemv_topk_100k_x_768_traffic", "mean"),
+    "c3_1m_1024": ("gemv_topk_1m_x_1024_traffic", "mean over K=8,32,100"),
+    "c4_1e8_int32": ("select_topk_1e8_int32_traffic", "mean"),
+    "c5_q32_500k_768": ("mfma_scores_32x500k_x_768_traffic", "mean"),
+}
+FP32_MFMA_PEAK_TFLOPS = 157.3
+
+# The other configurations of the default run, each with its own protocol.
+SUITE = (
+    ("c1_10k_384", dict(steps=1000, warmup=20, cpu_budget=3.0, cpu_queries=1, filtered_leg=False)),
+    ("c2_50k_768", dict(steps=1000, warmup=20, cpu_budget=4.0, cpu_queries=40, filtered_leg=True)),
+    ("c2_100k_768", dict(steps=1000, warmup=20, cpu_budget=4.0, cpu_queries=40, filtered_leg=True)),
+    ("c4_1e8_int32", dict(steps=100, warmup=5)),
+    ("c5_q32_500k_768", dict(steps=100, warmup=5, filtered_leg=True)),
+)
+
+
+def workload_traffic(name, metric="dot", filtered=False):
+    if metric != "dot" or filtered or name not in TRAFFIC_PROFILES:
+        return None
+    return measured_traffic(*TRAFFIC_PROFILES[name])
+
+
+def environment(torch, workloads):
+    """Versions, device and seeds of this run (inputs are synthetic and seeded)."""
+    def read(path):
+        try:
+            return open(path).read().strip()
+        except OSError:
+            return None
+    props = torch.cuda.get_device_properties(0)
+    return {
+        "rocm": read("/opt/rocm/.info/version"), "hip_runtime": torch.version.hip, "torch": torch.__version__,
+        "numpy": np.__version__, "python": sys.version.split()[0],
+        "gpu": props.name, "gcn_arch": getattr(props, "gcnArchName", None), "compute_units": props.multi_processor_count,
+        "gpu_memory_gib": round(props.total_memory / 2 ** 30, 1),
+        "clocks_locked": False,
+        "seeds": {"generator": "numpy PCG64, SeedSequence([base_seed, config_id, stream, chunk])",
+                  "base_seed": workloads.BASE_SEED,
+                  "config_ids": {k: v["config_id"] for k, v in workloads.WORKLOADS.items()},
+                  "streams": {"corpus": workloads.STREAM_CORPUS, "queries": workloads.STREAM_QUERIES,
+                              "plant_positions": workloads.STREAM_PLANT_POS, "plant_noise": workloads.STREAM_PLANT_NOISE,
+                              "duplicates": workloads.STREAM_DUP}},
+        "host_cores": host_cores(), "cpu_model": cpu_model(),
+    }
 
 
 def pct(a, p):
@@ -248,9 +315,7 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
         "per_k": per_k,
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": (measured_traffic()
-                                 if (n, d, ks, args.metric, args.filtered) == (1_000_000, 1024, (8, 32, 100), "dot", False)
-                                 else None),
+                     "traffic": workload_traffic(name, args.metric, args.filtered),
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, profiles/)",
                      "kernel": ((("gemv_bound8_kernel" if path == "fp8" else "gemv_bound_kernel")
                                  + f" ({path} first pass of the filtered search)") if args.filtered else
@@ -258,6 +323,16 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
                      "bytes_per_launch": corpus_bytes, "avg_launch_us": avg_ms * 1e3},
         "input_gen_s": gen_s,
     }
+    if getattr(args, "latency_queries", 0) and args.steps < args.latency_queries:
+        # the configuration's protocol: this many sequential queries per K, for
+        # the latency distribution (the timed steps above may be fewer)
+        _, llat, _, lmerge = time_search(eng, torch, qdev, ks, args.latency_queries, 0, metric=args.metric,
+                                         filtered=args.filtered)
+        line["latency_distribution"] = {
+            "queries_per_k": args.latency_queries,
+            "per_k": {str(k): {"p50_us": pct(llat[k], 50), "p99_us": pct(llat[k], 99),
+                               "device_p50_us": pct(np.asarray(lmerge[k]) * 1e3, 50),
+                               "device_p99_us": pct(np.asarray(lmerge[k]) * 1e3, 99)} for k in ks}}
     if args.e2e_reps:
         line["end_to_end_pcie"] = time_end_to_end(eng, torch, qhost, ks, args.e2e_reps, metric=args.metric,
                                                   filtered=args.filtered)
@@ -447,6 +522,26 @@ def batched_filtered_leg(args, torch, eng, qdev, ks, n, d):
                            "frac_of_hbm_peak": pass1_bytes / (all_p1 * 1e-3) / 1e9 / HBM_PEAK_GBS}}
 
 
+def mfma_kernel_name(n, d, metric):
+    if metric == "dot" and n >= 32 and d in (256, 384, 512, 768):
+        return "mfma_scores_dma_kernel (direct global-to-LDS loads, query block in registers)"
+    return "mfma_scores_fixed_kernel" if d in (256, 384, 512, 768, 1024) else "mfma_scores_kernel"
+
+
+def mfma_utilisation(name, flops, avg_ms, metric):
+    """The batch scorer's fp32 matrix-core rate against the dense fp32 MFMA
+    peak, and (from the committed PMC summary, when it matches the sources)
+    the fraction of SIMD cycles the matrix cores were busy."""
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    out = {"achieved_tflops": achieved, "peak_tflops": FP32_MFMA_PEAK_TFLOPS,
+           "frac_of_peak": achieved / FP32_MFMA_PEAK_TFLOPS, "flops_per_launch": flops, "busy_frac": None}
+    rec = profile_record(TRAFFIC_PROFILES[name][0]) if (metric == "dot" and name in TRAFFIC_PROFILES) else None
+    if rec and "mfma_busy_frac" in rec:
+        out["busy_frac"] = rec["mfma_busy_frac"]
+        out["busy_source"] = "profiles/" + TRAFFIC_PROFILES[name][0] + ".json (SQ_VALU_MFMA_BUSY_CYCLES)"
+    return out
+
+
 def run_batched(args, torch, eng, corpus, qhost, qdev, ks, name, gen_s):
     n, d = corpus.shape
     q = qdev.shape[0]
@@ -483,6 +578,8 @@ def run_batched(args, torch, eng, corpus, qhost, qdev, ks, name, gen_s):
         per_k[str(k)] = {"batches_per_s": len(lat[k]) / (np.sum(lat[k]) / 1e6),
                          "queries_per_s": q * len(lat[k]) / (np.sum(lat[k]) / 1e6),
                          "p50_us": pct(lat[k], 50), "p99_us": pct(lat[k], 99),
+                         "device_p50_us": pct(np.asarray(merge[k]) * 1e3, 50),
+                         "device_p99_us": pct(np.asarray(merge[k]) * 1e3, 99),
                          "mfma_kernel_avg_us": mfma_ms * 1e3,
                          "select_kernel_avg_us": float(np.mean(part[k])) * 1e3,
                          "device_avg_us": float(np.mean(merge[k])) * 1e3,
@@ -498,9 +595,11 @@ def run_batched(args, torch, eng, corpus, qhost, qdev, ks, name, gen_s):
                        "n": n, "d": d, "q": q, "ks": list(ks), "metric": args.metric},
             "per_k": per_k,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                         "kernel": "mfma_scores_fixed_kernel" if d in (256, 384, 512, 768, 1024) else "mfma_scores_kernel", "bytes_per_launch": corpus_bytes,
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": workload_traffic(name, args.metric),
+                         "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, profiles/)",
+                         "kernel": mfma_kernel_name(n, d, args.metric), "bytes_per_launch": corpus_bytes,
                          "avg_launch_us": float(np.mean(all_mf)) * 1e3},
+            "mfma": mfma_utilisation(name, flops, float(np.mean(all_mf)), args.metric),
             "input_gen_s": gen_s}
     if args.metric == "dot" and not args.no_filtered_leg:
         line["filtered_exact"] = batched_filtered_leg(args, torch, eng, qdev, ks, n, d)
@@ -524,9 +623,10 @@ def run_batched(args, torch, eng, corpus, qhost, qdev, ks, name, gen_s):
 
 
 def run_int32(args, torch, ResidentTopK, workloads):
-    w = workloads.WORKLOADS["c4_1e8_int32"]
+    name = args.workload
+    w = workloads.WORKLOADS[name]
     t = time.perf_counter()
-    v = workloads.int32_values()
+    v = workloads.int32_values(n=w["n"], dup_fraction=w["dup_fraction"], config_id=w["config_id"])
     gen_s = time.perf_counter() - t
     n = v.shape[0]
     ks = tuple(w["ks"])
@@ -557,19 +657,24 @@ def run_int32(args, torch, ResidentTopK, workloads):
     eng.profile(False)
     nbytes = n * 4
     per_k = {str(k): {"calls_per_s": len(lat[k]) / (np.sum(lat[k]) / 1e6), "p50_us": pct(lat[k], 50),
-                      "p99_us": pct(lat[k], 99), "scan_kernel_avg_us": float(np.mean(part[k])) * 1e3,
+                      "p99_us": pct(lat[k], 99), "device_p50_us": pct(np.asarray(merge[k]) * 1e3, 50),
+                      "device_p99_us": pct(np.asarray(merge[k]) * 1e3, 99),
+                      "scan_kernel_avg_us": float(np.mean(part[k])) * 1e3,
                       "scan_kernel_gbs": nbytes / (float(np.mean(part[k])) * 1e-3) / 1e9} for k in ks}
     all_part = np.concatenate([np.asarray(part[k]) for k in ks])
     achieved = nbytes / (float(np.mean(all_part)) * 1e-3) / 1e9
-    line = {"metric": "top-K calls/s (c4_1e8_int32)", "value": args.steps * len(ks) / wall, "unit": "calls/s",
+    line = {"metric": f"top-K calls/s ({name})", "value": args.steps * len(ks) / wall, "unit": "calls/s",
             "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": wall / args.steps * 1e3,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int32",
             "data": "synthetic",
-            "config": {"workload": f"c4_1e8_int32: raw top-K over {n} int32 (uniform, 1% duplicated), K in {list(ks)}",
+            "config": {"workload": f"{name}: raw top-K over {n} int32 (uniform, {w['dup_fraction']:.0%} duplicated), "
+                                   f"K in {list(ks)}",
                        "n": n, "ks": list(ks)},
             "per_k": per_k,
             "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": achieved / HBM_PEAK_GBS, "traffic": None, "kernel": "select_topk_kernel",
+                         "frac": achieved / HBM_PEAK_GBS, "traffic": workload_traffic(name),
+                         "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, profiles/)",
+                         "kernel": "select_topk_kernel",
                          "bytes_per_launch": nbytes, "avg_launch_us": float(np.mean(all_part)) * 1e3},
             "input_gen_s": gen_s}
     if not args.no_cpu_baseline:
@@ -603,12 +708,62 @@ def copy_calibration(torch, nbytes, reps):
     print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
 
 
+def run_one(args, torch, ResidentTopK, workloads):
+    if workloads.WORKLOADS[args.workload]["kind"] == "int32":
+        return run_int32(args, torch, ResidentTopK, workloads)
+    return run_retrieval(args, torch, ResidentTopK, workloads)
+
+
+def run_suite(args, torch, ResidentTopK, workloads):
+    """The other configurations, one after the other, each with its own
+    protocol; every one checks its GPU answers against the oracle."""
+    import copy
+    out = {}
+    for name, proto in SUITE:
+        sub = copy.copy(args)
+        sub.workload = name
+        sub.steps = proto["steps"]
+        sub.warmup = proto["warmup"]
+        sub.num_queries = 1000
+        sub.latency_queries = 0
+        sub.streams = 1
+        sub.filtered = False
+        sub.metric = "dot"
+        sub.no_filtered_leg = not proto.get("filtered_leg", False)
+        sub.cpu_budget = proto.get("cpu_budget", args.cpu_budget)
+        sub.cpu_queries = proto.get("cpu_queries", args.cpu_queries)
+        t0 = time.perf_counter()
+        print(f"[bench] {name}: start", file=sys.stderr, flush=True)
+        line = run_one(sub, torch, ResidentTopK, workloads)
+        line["wall_s"] = time.perf_counter() - t0
+        print(f"[bench] {name}: done in {line['wall_s']:.1f} s", file=sys.stderr, flush=True)
+        out[name] = line
+        torch.cuda.empty_cache()
+    return out
+
+
+def register_custom(args, workloads):
+    """A free-form synthetic workload of the same recipe (--n given)."""
+    ks = tuple(int(k) for k in str(args.k).split(","))
+    if args.dtype == "int32":
+        workloads.WORKLOADS["custom"] = dict(config_id=args.seed, n=args.n, ks=ks, kind="int32",
+                                             dup_fraction=args.dup_fraction)
+    else:
+        if args.d is None:
+            raise SystemExit("--d is required for a retrieval workload")
+        workloads.WORKLOADS["custom"] = dict(config_id=args.seed, n=args.n, d=args.d, ks=ks,
+                                             queries=args.queries, kind="retrieval", batch=args.batch)
+    return "custom"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", default="c3_1m_1024")
+    ap.add_argument("--workload", default=None,
+                    help="run one configuration alone (default: c3_1m_1024 as the headline, then the others)")
+    ap.add_argument("--headline-only", action="store_true", help="skip the other configurations")
     ap.add_argument("--metric", default="dot", choices=("dot", "cosine"),
                     help="similarity for the retrieval workloads (the headline line is the inner product)")
     ap.add_argument("--filtered", action="store_true",
@@ -620,11 +775,21 @@ def main():
     ap.add_argument("--streams", type=int, default=1,
                     help="single-query workloads: engines sharing the corpus, one stream each, searching concurrently")
     ap.add_argument("--num-queries", type=int, default=1000)
+    ap.add_argument("--latency-queries", type=int, default=1000,
+                    help="headline: sequential queries per K for the latency distribution")
     ap.add_argument("--cpu-queries", type=int, default=40)
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time in cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--e2e-reps", type=int, default=200)
     ap.add_argument("--copy-calibration", type=int, default=0, help="bytes; run only a plain copy kernel")
+    ap.add_argument("--n", type=int, default=None, help="free-form workload: rows (or int32 values)")
+    ap.add_argument("--d", type=int, default=None, help="free-form workload: depth")
+    ap.add_argument("--k", default="8,32,100", help="free-form workload: K values, comma-separated")
+    ap.add_argument("--queries", type=int, default=100, help="free-form workload: queries")
+    ap.add_argument("--batch", type=int, default=1, help="free-form workload: queries per batch (<= 32)")
+    ap.add_argument("--seed", type=int, default=1000, help="free-form workload: config id of the seed sequence")
+    ap.add_argument("--dtype", choices=("f32", "int32"), default="f32", help="free-form workload: data type")
+    ap.add_argument("--dup-fraction", type=float, default=0.01, help="free-form int32 workload: duplicated fraction")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -642,10 +807,18 @@ def main():
         return
     import workloads
     from top_search_resident_amd import ResidentTopK
-    if args.workload == "c4_1e8_int32":
-        line = run_int32(args, torch, ResidentTopK, workloads)
-    else:
-        line = run_retrieval(args, torch, ResidentTopK, workloads)
+    suite = args.workload is None and args.n is None and not args.headline_only
+    if args.n is not None:
+        args.workload = register_custom(args, workloads)
+    elif args.workload is None:
+        args.workload = "c3_1m_1024"
+    if args.workload != "c3_1m_1024" or args.filtered or args.metric != "dot":
+        args.latency_queries = 0
+    print(f"[bench] {args.workload}: start", file=sys.stderr, flush=True)
+    line = run_one(args, torch, ResidentTopK, workloads)
+    if suite and args.streams == 1:
+        line["workloads"] = run_suite(args, torch, ResidentTopK, workloads)
+    line["environment"] = environment(torch, workloads)
     print(json.dumps(line), flush=True)
 
 
