@@ -370,6 +370,26 @@ rt_status rt_filter_bounds_batched(int32_t d, float *out3);
  */
 rt_status rt_filter_bounds_fp8(int32_t d, float *out3);
 
+/*
+ * The cosine arithmetic of the scans and of the filtered search, evaluated on
+ * the host by the same source the kernels compile (host-only, no GPU needed;
+ * for tests and for callers reproducing a decision of the filter).
+ * rt_cosine_score: acc / (qnorm rnorm) in fp32, or -inf when that fp32
+ * product is not positive (search_resident_metric's cosine epilogue).
+ * rt_filter_cosine_bounds: out2 = [hi, lo], the bounds the first pass of the
+ * filtered cosine search derives from inner-product bounds a - e <= acc <= a + e
+ * ("GPU-Resident Top-K for Agentic RAG", section 4, Step 2, the cosine
+ * branch): fl(a +- e) / fl(qnorm rnorm) widened by 2^-20 relative and FLT_MIN
+ * absolute; (+inf, -inf) when known == 0 (an overflowed bound), (-inf, -inf)
+ * when the product of norms is not positive; a quotient that overflows gives
+ * the infinite bound on its side.  RT_EINVAL for a NULL out2.
+ * Range of the cosine (both paths): the fp32 inner product and the fp32
+ * product of the norms must be normal numbers; a pair whose |q| |x|
+ * underflows in fp32 (below ~1e-45) scores -inf like a zero row.
+ */
+float rt_cosine_score(float acc, float qnorm, float rnorm);
+rt_status rt_filter_cosine_bounds(int32_t known, float a, float e, float qnorm, float rnorm, float *out2);
+
 #ifdef __cplusplus
 }
 #endif

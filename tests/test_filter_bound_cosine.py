@@ -98,3 +98,60 @@ def test_overflow_and_zero():
     assert np.isposinf(hi) and np.isneginf(lo)
     hi, lo = _bounds(F32(0.0), F32(0.0), F32(2.0))
     assert hi > 0 > lo
+
+
+# ---- the library's own code (the function the kernels compile), on the host
+
+def _lib_bounds(lib, known, a, e, qnorm, rn):
+    import ctypes
+    out = (ctypes.c_float * 2)()
+    assert lib.rt_filter_cosine_bounds(int(known), float(a), float(e), float(qnorm), float(rn), out) == 0
+    return F32(out[0]), F32(out[1])
+
+
+def test_library_cosine_bounds_match_the_model():
+    """rt_filter_cosine_bounds runs the same cosine_bounds source as the first
+    passes of the filtered cosine search; bit for bit it must give the model's
+    bounds above on the same adversarial cases (den = qnorm x 1.0 exactly), the
+    (-inf, -inf) of a non-positive product of norms, and the untouched
+    (+inf, -inf) of an unknown bound."""
+    from top_search_resident_amd import _lib
+    lib = _lib.load()
+    rng = np.random.default_rng(2027)
+    n = 0
+    for a, e, den, acc in _cases(rng, 5000):
+        hi, lo = _lib_bounds(lib, True, a, e, den, 1.0)
+        mhi, mlo = _bounds(a, e, den)
+        assert hi.tobytes() == mhi.tobytes() and lo.tobytes() == mlo.tobytes(), (a, e, den, hi, mhi, lo, mlo)
+        with np.errstate(over="ignore", under="ignore"):
+            plain = F32(acc / den)
+        assert lo <= plain <= hi
+        n += 1
+    assert n > 10000
+    for qn, rn in ((0.0, 1.0), (1.0, 0.0), (-1.0, 1.0), (1e-30, 1e-30)):  # the last product underflows to 0
+        hi, lo = _lib_bounds(lib, True, 0.5, 0.1, qn, rn)
+        assert np.isneginf(hi) and np.isneginf(lo), (qn, rn)
+    hi, lo = _lib_bounds(lib, False, 0.5, 0.1, 2.0, 3.0)
+    assert np.isposinf(hi) and np.isneginf(lo)
+    hi, lo = _lib_bounds(lib, True, F32(3e38), F32(3e37), F32(1e-3), 1.0)
+    assert np.isposinf(hi) and np.isneginf(lo)
+
+
+def test_library_cosine_score():
+    """rt_cosine_score is the scans' cosine epilogue: fp32 acc / fl(qnorm rnorm),
+    -inf when that product is not positive (a zero row, a zero query, or norms
+    whose product underflows in fp32)."""
+    from top_search_resident_amd import _lib
+    lib = _lib.load()
+    rng = np.random.default_rng(5)
+    for _ in range(2000):
+        acc = F32(rng.standard_normal() * 10.0 ** rng.integers(-20, 20))
+        qn = F32(abs(rng.standard_normal()) * 10.0 ** rng.integers(-18, 18))
+        rn = F32(abs(rng.standard_normal()) * 10.0 ** rng.integers(-18, 18))
+        with np.errstate(over="ignore", under="ignore", invalid="ignore"):
+            den = F32(qn * rn)
+            want = F32(acc / den) if den > 0 else F32(-np.inf)
+        got = F32(lib.rt_cosine_score(float(acc), float(qn), float(rn)))
+        assert got.tobytes() == want.tobytes() or (np.isnan(got) and np.isnan(want)), (acc, qn, rn, got, want)
+    assert np.isneginf(lib.rt_cosine_score(1.0, 0.0, 5.0))
+    assert np.isneginf(lib.rt_cosine_score(1e-40, 1e-25, 1e-25))  # |q| |x| underflows: ranked as a zero row

@@ -119,3 +119,41 @@ def test_cosine_scaled_copies_tie_by_index(eng, q):
     assert list(g_idx[0, :len(copies)]) == copies
     assert np.unique(g_sc[0, :len(copies)].view(np.uint32)).size == 1
     assert list(o_idx[0, :len(copies)]) == copies
+
+
+def test_cosine_extreme_norms(eng):
+    """Rows whose lengths span 1e-17 .. 1e17 (and queries of length 1e-10 and
+    1e10): cosine is scale-invariant, so the ranking is that of the directions;
+    every product stays a normal fp32 number, and the GPU matches the oracle's
+    fp64 cosines for single queries and for a batch."""
+    n, d = 20_000, 256
+    rows = workloads.gaussian_rows(n, d, config_id=320)
+    rng = np.random.default_rng(320)
+    rows *= (10.0 ** rng.uniform(-17, 17, size=n)).astype(np.float32)[:, None]
+    for qscale in (1e-10, 1.0, 1e10):
+        q = workloads.gaussian_rows(3, d, config_id=320, stream=1) * np.float32(qscale)
+        for qi in range(3):
+            _check(eng, rows, q[qi:qi + 1], 50)
+        _check(eng, rows, q, 50)  # a batch (matrix-core kernel)
+
+
+def test_cosine_underflowing_norm_product_ranks_last(eng):
+    """The documented range limit: the cosine's denominator is the fp32 product
+    |q| |x|; for a row with |x| = 1e-30 and a query with |q| = 1e-20 it
+    underflows to 0 and the row scores -inf like a zero row (below every
+    finite cosine, ties by index), while rows of normal length rank by their
+    cosines."""
+    n, d, k = 1_000, 128, 1_000
+    rows = workloads.gaussian_rows(n, d, config_id=321)
+    tiny = np.arange(0, n, 7)
+    rows[tiny] *= np.float32(1e-30)
+    q = workloads.gaussian_rows(1, d, config_id=321, stream=1) * np.float32(1e-20)
+    g_idx, g_sc = _search(eng, rows, q, k)
+    ninf = np.isneginf(g_sc[0])
+    assert ninf.sum() == tiny.size
+    assert np.array_equal(np.sort(g_idx[0][ninf]), tiny) and np.all(np.diff(g_idx[0][ninf]) > 0)
+    assert not np.isinf(g_sc[0][:k - tiny.size]).any()
+    normal = np.setdiff1d(np.arange(n), tiny)
+    o_idx, o_sc = oracle.search(rows[normal], q, k - tiny.size, metric=1)
+    check_retrieval(g_idx[0][:k - tiny.size], g_sc[0][:k - tiny.size], normal[o_idx[0]], o_sc[0],
+                    rows, q[0], oracle, metric="cosine")

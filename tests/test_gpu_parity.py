@@ -342,6 +342,48 @@ def test_error_paths():
         ResidentTopK(1 << 40, 64, 8, 1)  # beyond the int32 index range
 
 
+def test_out_of_memory_paths():
+    """RT_ENOMEM: limits that pass every check but whose allocation exceeds
+    HBM.  rt_engine_create then returns no engine (and leaks nothing: a normal
+    engine works afterwards); rt_enable_filtered on an engine whose fp32
+    corpus fits but whose reduced-precision copies do not leaves that engine
+    working for the plain search."""
+    import ctypes
+    from top_search_resident_amd import _lib
+    lib = _lib.load()
+    torch.cuda.empty_cache()
+    h = ctypes.c_void_p(12345)
+    st = lib.rt_engine_create(2 ** 31 - 1, 65536, 8, 1, 0, ctypes.byref(h))  # a 512 TiB corpus
+    assert st == _lib.RT_ENOMEM, st
+    assert h.value is None
+    with pytest.raises(ResidentTopKError) as ei:
+        ResidentTopK(2 ** 31 - 1, 65536, 8, 1)
+    assert ei.value.status == _lib.RT_ENOMEM
+    free_b, total_b = torch.cuda.mem_get_info()
+    # a corpus of ~75% of the free memory: its bf16 copy (half of it) no longer fits
+    d = 64
+    max_n = min(2 ** 31 - 1, int(0.75 * free_b) // (4 * d))
+    with ResidentTopK(max_n, d, 16, 1) as e:
+        with pytest.raises(ResidentTopKError) as ei:
+            e.enable_filtered()
+        assert ei.value.status == _lib.RT_ENOMEM
+        corpus = workloads.gaussian_rows(5_000, d, config_id=31)
+        q = workloads.gaussian_rows(1, d, config_id=31, stream=1)
+        e.upload_corpus_rowmajor(corpus)
+        idx, sc = e.search_resident(torch.from_numpy(q).cuda(), 16)
+        torch.cuda.synchronize()
+        o_idx, o_sc = oracle.search(corpus, q, 16)
+        check_retrieval(idx.cpu().numpy()[0], sc.cpu().numpy()[0], o_idx[0], o_sc[0], corpus, q[0], oracle)
+        with pytest.raises(ResidentTopKError) as ei:
+            e.search_resident_filtered(torch.from_numpy(q).cuda(), 16)  # the filtered search was never enabled
+        assert ei.value.status == _lib.RT_ESTATE
+    with ResidentTopK(1000, 64, 8, 1) as e:  # everything was released
+        e.upload_corpus_rowmajor(np.ones((10, 64), np.float32))
+        idx, _ = e.search_resident(torch.ones((1, 64), dtype=torch.float32, device="cuda"), 3)
+        torch.cuda.synchronize()
+        assert list(idx.cpu().numpy()[0]) == [0, 1, 2]
+
+
 def test_binding_rejects_bad_buffers():
     """Checks the binding makes before anything is enqueued (the C ABI only sees
     addresses): query width against the resident depth, and output buffers that

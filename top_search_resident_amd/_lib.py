@@ -19,7 +19,8 @@ EXPORTS = (
     "rt_profile_read", "rt_engine_info", "rt_check_create", "rt_check_upload",
     "rt_check_search", "rt_check_search_metric", "rt_check_select", "rt_filter_bounds",
     "rt_filter_bounds_batched", "rt_filter_bounds_fp8", "rt_set_filter_storage", "rt_filter_path_used",
-    "rt_read_probe", "search_resident_filtered_metric", "topk_select_noalloc",
+    "rt_read_probe", "search_resident_filtered_metric", "topk_select_noalloc", "rt_cosine_score",
+    "rt_filter_cosine_bounds",
 )
 
 _lib = None
@@ -77,6 +78,9 @@ def load():
         "rt_filter_bounds_fp8": ([i32, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
         "rt_set_filter_storage": ([vp, i32], ctypes.c_int),
         "rt_filter_path_used": ([vp], ctypes.c_int32),
+        "rt_cosine_score": ([ctypes.c_float, ctypes.c_float, ctypes.c_float], ctypes.c_float),
+        "rt_filter_cosine_bounds": ([i32, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                     ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)

@@ -15,17 +15,16 @@
 #include <new>
 
 #include "../../include/resident_topk.h"
+#include "cosine_math.hpp"
 #include "filter8_host.hpp"
 #include "kernels.hpp"
+#include "limits.hpp"
 #include "plan.hpp"
 #include "read_probe.hpp"
 
 namespace {
 
-constexpr int64_t kMaxN = 2147483647LL;
-constexpr int32_t kMaxD = 65536;
-constexpr int32_t kMaxK = 1024;
-constexpr int32_t kMaxQ = 32;
+using rt::kMaxQ;
 // Merge-tree list storage (ranks) shared by all segments of a call: 64 MiB.
 constexpr int64_t kTreeRanks = int64_t(1) << 23;
 // Most streaming workgroups per segment (bounds the counter array).
@@ -110,64 +109,23 @@ static rt_status hip_fail(rt_engine *e, hipError_t err) {
 
 extern "C" {
 
-const char *rt_status_string(rt_status s) {
-    switch (s) {
-        case RT_OK: return "ok";
-        case RT_EINVAL: return "invalid argument";
-        case RT_ESTATE: return "invalid state (no corpus resident, or dimension mismatch)";
-        case RT_ENOMEM: return "device memory allocation failed";
-        case RT_EHIP: return "HIP runtime error";
-    }
-    return "unknown status";
-}
-
-rt_status rt_check_create(int64_t max_n, int32_t max_d, int32_t max_k, int32_t max_q) {
-    if (max_n < 1 || max_n > kMaxN) return RT_EINVAL;
-    if (max_d < 1 || max_d > kMaxD) return RT_EINVAL;
-    if (max_k < 1 || max_k > kMaxK) return RT_EINVAL;
-    if (max_q < 1 || max_q > kMaxQ) return RT_EINVAL;
-    return RT_OK;
-}
-
-rt_status rt_check_upload(int64_t max_n, int32_t max_d, const void *corpus, int64_t n, int32_t d) {
-    if (corpus == nullptr) return RT_EINVAL;
-    if (n < 1 || n > max_n) return RT_EINVAL;
-    if (d < 1 || d > max_d) return RT_EINVAL;
-    return RT_OK;
-}
-
-rt_status rt_check_search(int32_t max_k, int32_t max_q, int64_t resident_n, const void *queries, int32_t q,
-                          int32_t k, const void *out_idx, const void *out_scores) {
-    if (queries == nullptr || out_idx == nullptr || out_scores == nullptr) return RT_EINVAL;
-    if (q < 1 || q > max_q) return RT_EINVAL;
-    if (k < 1 || k > max_k) return RT_EINVAL;
-    if (resident_n < 1) return RT_ESTATE;
-    if (k > resident_n) return RT_EINVAL;
-    return RT_OK;
-}
-
-rt_status rt_check_search_metric(int32_t max_k, int32_t max_q, int64_t resident_n, const void *queries,
-                                 int32_t q, int32_t k, int32_t metric, const void *out_idx, const void *out_scores) {
-    if (metric != RT_METRIC_DOT && metric != RT_METRIC_COSINE) return RT_EINVAL;
-    return rt_check_search(max_k, max_q, resident_n, queries, q, k, out_idx, out_scores);
-}
-
-rt_status rt_check_select(int32_t max_k, const void *values, int32_t dtype, int64_t n, int32_t k,
-                          const void *out_idx, const void *out_values) {
-    if (values == nullptr || out_idx == nullptr || out_values == nullptr) return RT_EINVAL;
-    if (dtype != RT_DTYPE_INT32 && dtype != RT_DTYPE_FLOAT32) return RT_EINVAL;
-    if ((reinterpret_cast<uintptr_t>(values) & 3u) != 0) return RT_EINVAL;
-    if (n < 1 || n > kMaxN) return RT_EINVAL;
-    if (k < 1 || k > max_k || k > n) return RT_EINVAL;
-    return RT_OK;
-}
-
 rt_status rt_filter_bounds(int32_t d, float *out2) {
     if (d < 1 || out2 == nullptr) return RT_EINVAL;
     out2[0] = rt::filter_bound_factor(d);
     out2[1] = rt::filter_underflow_slack(d);
     return RT_OK;
 }
+
+rt_status rt_filter_cosine_bounds(int32_t known, float a, float e, float qnorm, float rnorm, float *out2) {
+    if (out2 == nullptr) return RT_EINVAL;
+    float hi = INFINITY, lo = -INFINITY;
+    rt::cosine_bounds(known != 0, a, e, qnorm, rnorm, hi, lo);
+    out2[0] = hi;
+    out2[1] = lo;
+    return RT_OK;
+}
+
+float rt_cosine_score(float acc, float qnorm, float rnorm) { return rt::cosine_of(acc, qnorm, rnorm); }
 
 rt_status rt_filter_bounds_fp8(int32_t d, float *out3) {
     if (d < 1 || out3 == nullptr) return RT_EINVAL;

@@ -41,30 +41,6 @@ struct FilterArgs {
     const uint16_t *ub16;  // pass 2: 16-bit upper bounds (top halves of fp32, rounded up) instead of ubuf
 };
 
-// Cosine bounds from the inner-product bounds a - e <= acc <= a + e of the
-// plain scan's fp32 sum acc.  The plain cosine is acc / den with den = |q| |x|
-// rounded to fp32 as cosine_of computes it (the same two fp32 values here, so
-// the same den), or -inf when den is not positive.  Its division rounds by at
-// most 2^-24 relative (2^-149 absolute below the normal range), as do a + e,
-// a - e and the divisions below: widening by 2^-20 relative and FLT_MIN
-// absolute covers them.  `known` false (an overflowed sum or bound) leaves the
-// row's bounds at (+inf, -inf) unless den says -inf exactly, and a quotient
-// that overflows gives the infinite bound on its side (never inf - inf).
-__device__ __forceinline__ void cosine_bounds(bool known, float a, float e, float qnorm, float rn, float &hi,
-                                              float &lo) {
-    const float den = qnorm * rn;
-    if (!(den > 0.f)) {
-        hi = -__builtin_huge_valf();
-        lo = -__builtin_huge_valf();
-        return;
-    }
-    if (!known) return;
-    const float h = (a + e) / den;
-    const float l = (a - e) / den;
-    hi = fabsf(h) <= __FLT_MAX__ ? h + fmaf(fabsf(h), 0x1p-20f, __FLT_MIN__) : __builtin_huge_valf();
-    lo = fabsf(l) <= __FLT_MAX__ ? l - fmaf(fabsf(l), 0x1p-20f, __FLT_MIN__) : -__builtin_huge_valf();
-}
-
 // bf16 -> fp32 of the two halves of a 32-bit word.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }

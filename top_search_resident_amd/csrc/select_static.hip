@@ -16,6 +16,7 @@
 
 #include "../../include/resident_topk.h"
 #include "kernels.hpp"
+#include "limits.hpp"
 #include "plan.hpp"
 
 namespace {
@@ -27,7 +28,7 @@ constexpr int64_t kStaticTreeRanks = int64_t(1) << 19;
 // Arrival counters: at most one per workgroup (all levels of the tree together
 // use fewer than the workgroup count).
 constexpr int64_t kStaticMaxWgs = 2048;
-constexpr int32_t kStaticMaxK = 1024;
+constexpr int32_t kStaticMaxK = rt::kMaxK;
 constexpr int kMaxDevices = 64;
 
 struct DeviceScratch {

@@ -20,6 +20,7 @@
 // (the pages' per-block selector is an O(K^2) single-lane bubble sort, section 3
 // "Problem A"; the 64-lane networks replace it).
 #pragma once
+#include "cosine_math.hpp"
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -209,15 +210,6 @@ __device__ __forceinline__ float wave_l2_norm(const float *__restrict__ v, int64
 #pragma unroll
     for (int m = 32; m >= 1; m >>= 1) s += __shfl_xor(s, m);
     return (float)sqrt(s);
-}
-
-// Cosine score from an inner product: acc / (|q| |x|), or -inf when that
-// product of norms is not positive (a zero row or a zero query) -- the pages'
-// cosine branch of the scoring kernel, in fp32 ("GPU-Resident Top-K for Agentic
-// RAG", section 4, Step 2).
-__device__ __forceinline__ float cosine_of(float acc, float qnorm, float rnorm) {
-    const float den = qnorm * rnorm;
-    return den > 0.f ? acc / den : -INFINITY;
 }
 
 // Number of set bits of `mask` below this lane.
