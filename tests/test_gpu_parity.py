@@ -287,6 +287,38 @@ def test_topk_int32_boundary_ties(eng):
         assert np.array_equal(g_val, o_val)
 
 
+def test_topk_arrival_tree(eng):
+    """Arrays long enough for more workgroups than one merge node takes (256
+    workgroups at 5M elements against 128 lists per node for k <= 32 and 64
+    for k <= 64), where raw-array selection groups the workgroups by arrival
+    order and merges nodes by binned selection.  The cases reach both of the
+    binned merge's ends: few candidates (random values), and more than one
+    wave can sort (heavy ties, a sorted array whose answer sits in the last
+    workgroup), which falls back to pairwise merging."""
+    n = 5_000_000
+    rng = np.random.default_rng(8)
+    cases = {
+        "random": workloads.int32_values(n=n, config_id=43),
+        "three_values": rng.integers(0, 3, size=n, dtype=np.int32),
+        "thousand_values": rng.integers(0, 1000, size=n, dtype=np.int32),
+        "ascending": np.arange(n, dtype=np.int32),
+        "descending": np.arange(n, 0, -1).astype(np.int32),
+    }
+    for name, v in cases.items():
+        for k in ((20, 32, 33, 50, 64) if name == "random" else (20, 50)):
+            o_idx, o_val = oracle.topk(v, k)
+            for rep in range(2):  # the second call checks the counters were left at zero
+                g_idx, g_val = _select(eng, v, k)
+                assert np.array_equal(g_idx, o_idx), (name, k, rep)
+                assert np.array_equal(g_val, o_val), (name, k, rep)
+    f = rng.standard_normal(n).astype(np.float32)
+    for k in (20, 64):
+        g_idx, g_val = _select(eng, f, k)
+        o_idx, o_val = oracle.topk(f, k)
+        assert np.array_equal(g_idx, o_idx), k
+        assert np.array_equal(g_val.view(np.uint32), o_val.view(np.uint32)), k
+
+
 def test_topk_float32_special_values(eng):
     rng = np.random.default_rng(6)
     v = rng.standard_normal(400_000).astype(np.float32)

@@ -13,7 +13,8 @@
 //      group of lanes, and feeds the scores into a register-resident best-K
 //      list (wave_topk.hpp) -- the N scores never reach HBM;
 //   2. the four waves of a workgroup merge their lists into one (LDS);
-//   3. merge tree: workgroups are grouped `fan` at a time; each workgroup stores
+//   3. merge tree (raw arrays: grouped by arrival order, see
+//      arrival_tree_finish): workgroups are grouped `fan` at a time; each workgroup stores
 //      its list, and the LAST workgroup of a group to finish (a global atomic
 //      counter per group) loads the group's lists, merges them and moves one
 //      level up; the last one at the root writes the K outputs.  Nothing waits
@@ -54,6 +55,7 @@ struct TreeArgs {
     uint32_t *out_val;       // [segments][k]
     const uint32_t *src;     // mode 2: the array the ranks index into
     int64_t src_seg_stride;
+    int arrival;             // nonzero: arrival-ordered groups and binned merges (see arrival_tree_finish)
 };
 
 __device__ __forceinline__ void write_output(const TreeArgs &ta, int seg, int r, uint64_t v) {
@@ -132,6 +134,7 @@ __device__ __forceinline__ void merge_short_lists_t(uint64_t *sm, int count) {
     for (int s = 1; s < count; s <<= 1) {
         const int pairs = (count - s + 2 * s - 1) / (2 * s);  // lists a = 0, 2s, ... with a + s < count
         for (int p0 = 0; p0 < pairs; p0 += slots) {
+            if (p0 + wave_in_group() * PER_WAVE >= pairs) break;  // no pair for this wave (uniform)
             const int p = p0 + slot;
             // Groups without a pair read list 0 (any in-range address) and
             // do not write.
@@ -159,9 +162,223 @@ __device__ __forceinline__ void merge_short_lists(uint64_t *sm, int count, int k
 }
 
 // LDS words the merges use besides the lists.
-struct MergeScratch {
+constexpr int kSelectBins = 256;
+struct alignas(16) MergeScratch {
+    int hist[kSelectBins];  // binned merge: entries per key bin, best bin first
+    uint32_t wave_hi[16];   // per wave: the largest key seen
+    uint32_t wave_lo[16];   // per wave: the largest key of a k-th list entry seen
+    int count;              // candidates gathered
+    int cut;                // last bin kept
+    int kept;               // entries in bins 0 .. cut
     int flag;
+    int ticket;             // arrival tree: this workgroup's ticket
 };
+
+// Largest 32-bit value over the wave, in every lane.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, xor_u32<1>(v));
+    v = max(v, xor_u32<2>(v));
+    v = max(v, xor_u32<4>(v));
+    v = max(v, xor_u32<8>(v));
+    v = max(v, xor_u32<16>(v));
+    v = max(v, xor_u32<32>(v));
+    return v;
+}
+
+// Inclusive prefix sum over the wave's lanes: DPP shifts within each row of
+// 16 lanes, then the row totals added in.
+__device__ __forceinline__ int wave_prefix_sum(int x) {
+    x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xF, 0xF, false);  // row_shr:1
+    x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xF, 0xF, false);  // row_shr:2
+    x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xF, 0xF, false);  // row_shr:4
+    x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xF, 0xF, false);  // row_shr:8
+    const int r0 = __builtin_amdgcn_readlane(x, 15);
+    const int r1 = __builtin_amdgcn_readlane(x, 31);
+    const int r2 = __builtin_amdgcn_readlane(x, 47);
+    const int row = lane_id() >> 4;
+    return x + (row >= 1 ? r0 : 0) + (row >= 2 ? r1 : 0) + (row >= 3 ? r2 : 0);
+}
+
+// Merge `count` best-first lists (list c at sm[c * stride ..], stride a power
+// of two <= 64, only the first k <= stride entries of a list matter; count *
+// stride <= kTreeEntries) into sm[0 .. k), best first.
+//
+// The best k-th entry of any list is a certified bound: that list alone holds
+// k entries at or above it, so every entry of the answer has a key at or
+// above its key `lo`.  The keys in [lo, largest key] are split into 256 equal
+// bins, the entries counted per bin, and the bins taken from the top until
+// they hold k entries: only entries of those bins can be in the answer.  When
+// at most 64 remain they are gathered at the front of sm and one wave sorts
+// them; otherwise (keys packed into few bins: heavy ties, very uneven
+// spreads) the lists are merged pairwise as they are.  Exact either way.  For
+// evenly spread scores the bins kept hold about k entries, so the cost is a
+// few LDS passes instead of log2(count) rounds of 64-bit merging networks.
+// Every thread of the workgroup must call it.
+template <int NT>
+__device__ __forceinline__ void merge_binned(uint64_t *sm, MergeScratch *ms, int count, int stride, int k) {
+    static_assert(NT / kWave <= 16 && NT >= kSelectBins, "per-wave bound slots and one bin per thread");
+    if (count <= 1) return;  // one list is its own best k
+    const int th = threadIdx.x;
+    const int lane = lane_id();
+    const int wv = wave_in_group();
+    constexpr int E = kTreeEntries / NT;
+    const int total = count * stride;
+    uint64_t v[E];
+    uint32_t hi = 0, lo = 0;
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+        const int i = u * NT + th;
+        const int pos = i & (stride - 1);
+        v[u] = (i < total && pos < k) ? sm[i] : 0ull;
+        hi = max(hi, rank_key(v[u]));
+        if (i < total && pos == k - 1) lo = max(lo, rank_key(v[u]));
+    }
+    if (th < kSelectBins) ms->hist[th] = 0;
+    if (th == 0) ms->count = 0;
+    hi = wave_max_u32(hi);
+    lo = wave_max_u32(lo);
+    if (lane == 0) {
+        ms->wave_hi[wv] = hi;
+        ms->wave_lo[wv] = lo;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NT / kWave; ++w) {
+        hi = max(hi, ms->wave_hi[w]);
+        lo = max(lo, ms->wave_lo[w]);
+    }
+    const uint32_t range = hi - lo;  // hi >= lo: lo is the key of an entry
+    const int shift = (range < kSelectBins) ? 0 : 32 - __clz((int)range) - 8;
+    int bin[E];  // best bin first; -1: below lo or not an entry
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+        const int i = u * NT + th;
+        const uint32_t key = rank_key(v[u]);
+        bin[u] = (i < total && (i & (stride - 1)) < k && key >= lo)
+                     ? kSelectBins - 1 - (int)((key - lo) >> shift)
+                     : -1;
+        if (bin[u] >= 0) atomicAdd(&ms->hist[bin[u]], 1);
+    }
+    __syncthreads();
+    if (th < kWave) {  // the first bin at which the running count reaches k
+        const int4 h = *reinterpret_cast<const int4 *>(&ms->hist[4 * lane]);
+        const int own = h.x + h.y + h.z + h.w;
+        const int incl = wave_prefix_sum(own);
+        const uint64_t reach = __ballot(incl >= k);  // nonzero: at least k entries have a key >= lo
+        if (lane == (int)__builtin_ctzll(reach)) {
+            int c = incl - own, b = 4 * lane;
+            const int hv[4] = {h.x, h.y, h.z, h.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (c < k) {
+                    c += hv[q];
+                    b = 4 * lane + q;
+                }
+            }
+            ms->cut = b;
+            ms->kept = c;
+        }
+    }
+    __syncthreads();
+    if (ms->kept > kWave) {  // uniform: too many candidates for one wave's sort
+        if (stride < kWave)
+            merge_short_lists(sm, count, stride);
+        else
+            merge_lds_lists<1>(sm, count);
+        return;
+    }
+    const int cut = ms->cut;
+    uint64_t keep[E];
+    int pass = 0;
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+        keep[u] = __ballot(bin[u] >= 0 && bin[u] <= cut);
+        pass += __popcll(keep[u]);
+    }
+    int base = 0;
+    if (lane == 0 && pass) base = atomicAdd(&ms->count, pass);
+    base = __shfl(base, 0);
+#pragma unroll
+    for (int u = 0; u < E; ++u) {  // sm is only read before the barriers above
+        if ((keep[u] >> lane) & 1) sm[base + lanes_below(keep[u])] = v[u];
+        base += __popcll(keep[u]);
+    }
+    __syncthreads();
+    const int c = ms->kept;  // k <= c <= 64
+    if (th < kWave) {
+        const uint64_t x = wave_sort64_desc((lane < c) ? sm[lane] : 0ull);
+        sm[lane] = x;
+    }
+    __syncthreads();
+}
+
+// Merge `count` best-first lists of `stride` entries (only the first k matter)
+// held at sm[c * stride ..] into sm[0 .. k): with `binned`, the binned
+// selection from 32 lists up (a node of 128 lists of 32 entries on one
+// 16-wave workgroup: 5.1 -> 2.7 us against seven pairwise rounds), pairwise
+// merges otherwise.
+template <int R, int NT>
+__device__ __forceinline__ void merge_lists(uint64_t *sm, MergeScratch *ms, int count, int stride, int k,
+                                            bool binned) {
+    if constexpr (R == 1) {
+        if (count >= 32 && binned)
+            merge_binned<NT>(sm, ms, count, stride, k);
+        else if (stride < kWave)
+            merge_short_lists(sm, count, stride);
+        else
+            merge_lds_lists<1>(sm, count);
+    } else {
+        merge_lds_lists<R>(sm, count);
+    }
+}
+
+// Load `count` lists of kc entries (the first k of each) from tree storage
+// at src into sm with device-coherent loads.  All of a thread's loads are
+// issued before any is stored to LDS (a loop of load-then-store pays one
+// device round trip per entry).  Ends with a barrier.
+template <int NT>
+__device__ __forceinline__ void load_lists(uint64_t *sm, const uint64_t *src, int count, int kc, int k) {
+    constexpr int E = kTreeEntries / NT;
+    uint64_t v[E];
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+        const int i = u * NT + threadIdx.x;
+        v[u] = (i < count * kc && (i & (kc - 1)) < k)
+                   ? __hip_atomic_load(&src[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                   : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < E; ++u) {
+        const int i = u * NT + threadIdx.x;
+        if (i < count * kc) sm[i] = v[u];
+    }
+    __syncthreads();
+}
+
+// Store the first k entries of sm as a list at dst (device-coherent), wait
+// for the stores to complete, and count this workgroup in at *ctr, whose
+// group completes with `expected` arrivals.  Returns (to every thread)
+// whether this workgroup completed it; the completing workgroup clears the
+// counter (and *also_clear, if given) for the next call.
+template <int NT>
+__device__ __forceinline__ bool store_and_arrive(const uint64_t *sm, uint64_t *dst, int k, uint32_t *ctr,
+                                                 int expected, uint32_t *also_clear, MergeScratch *ms) {
+    for (int i = threadIdx.x; i < k; i += NT)
+        __hip_atomic_store(&dst[i], sm[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);  // this thread's coherent list stores have completed
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const uint32_t arrived = atomicAdd(ctr, 1u);
+        const int last = (int)(arrived + 1 == (uint32_t)expected);
+        if (last) {  // all have arrived: clear for the next call
+            __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (also_clear) __hip_atomic_store(also_clear, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        ms->flag = last;
+    }
+    __syncthreads();
+    return ms->flag != 0;
+}
 
 // Step 3: a merge tree.  Each workgroup stores the first k entries of its list,
 // kc entries apart (kc = the smallest power of two >= k for k <= 32, else the
@@ -182,60 +399,99 @@ __device__ __forceinline__ void tree_finish(uint64_t *sm, MergeScratch *ms, cons
     int node = blockIdx.x;
     int64_t level_off = 0;
     int ctr_off = 0;
-    for (int i = threadIdx.x; i < k; i += NT)
-        __hip_atomic_store(&base[(int64_t)node * kc + i], sm[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     while (true) {
         const int parent = node / ta.fan;
         const int first = parent * ta.fan;
         const int children = (count - first < ta.fan) ? count - first : ta.fan;
-        __builtin_amdgcn_s_waitcnt(0);  // this thread's coherent list stores have completed
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            const uint32_t arrived = atomicAdd(&ctr[ctr_off + parent], 1u);
-            const int last = (int)(arrived + 1 == (uint32_t)children);
-            if (last)  // all children have arrived: clear for the next call
-                __hip_atomic_store(&ctr[ctr_off + parent], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            ms->flag = last;
-        }
-        __syncthreads();
-        if (!ms->flag) return;
-        // All of a thread's loads are issued before any is stored to LDS (a
-        // loop of load-then-store pays one device round trip per entry).
-        const uint64_t *src = base + level_off + (int64_t)first * kc;
-        constexpr int E = kTreeEntries / NT;
-        uint64_t v[E];
-#pragma unroll
-        for (int u = 0; u < E; ++u) {
-            const int i = u * NT + threadIdx.x;
-            v[u] = (i < children * kc && (i & (kc - 1)) < k)
-                       ? __hip_atomic_load(&src[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                       : 0ull;
-        }
-#pragma unroll
-        for (int u = 0; u < E; ++u) {
-            const int i = u * NT + threadIdx.x;
-            if (i < children * kc) sm[i] = v[u];
-        }
-        __syncthreads();
-        if (kc < kWave)
-            merge_short_lists(sm, children, kc);
-        else
-            merge_lds_lists<R>(sm, children);
+        if (!store_and_arrive<NT>(sm, base + level_off + (int64_t)node * kc, k, &ctr[ctr_off + parent], children,
+                                  nullptr, ms))
+            return;
+        load_lists<NT>(sm, base + level_off + (int64_t)first * kc, children, kc, k);
+        merge_lists<R, NT>(sm, ms, children, kc, k, ta.arrival != 0);
         const int up = (count + ta.fan - 1) / ta.fan;
         if (up == 1) {
             for (int r = threadIdx.x; r < k; r += NT) write_output(ta, seg, r, sm[r]);
             return;
         }
-        const int64_t next_off = level_off + (int64_t)count * kc;
-        for (int i = threadIdx.x; i < k; i += NT)
-            __hip_atomic_store(&base[next_off + (int64_t)parent * kc + i], sm[i], __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        level_off = next_off;
+        level_off += (int64_t)count * kc;
         ctr_off += up;
         node = parent;
         count = up;
-        __syncthreads();
     }
+}
+
+// The merge tree above makes the last workgroup to finish climb every level
+// of it, merging a full group at each.  When the grid needs more than one
+// level, the groups are formed by arrival order instead, so that the last
+// workgroups to finish merge little.  Each workgroup takes a ticket (0 for the
+// first to finish) as it finishes streaming.  Counting back from the last
+// ticket, r = count - 1 - ticket: r = 0 is a group of one, r in [2^j, 2^(j+1))
+// a group of 2^j while 2^j < fan, and the earlier tickets form groups of fan.
+// A group's last member to arrive merges the group's lists (a group of one
+// skips this); the group results are merged by the last group to complete,
+// which writes the outputs.  With ~count / fan + log2(fan) + 1 groups, the
+// last workgroup to finish typically stores its list and merges a dozen
+// lists, while the big groups were merged as their members arrived.
+struct ArrivalGroup {
+    int g;        // group number
+    int first_r;  // first member, counted back from the last ticket
+    int size;     // members
+};
+
+__device__ __forceinline__ ArrivalGroup arrival_group(int r, int count, int fan) {
+    ArrivalGroup a;
+    if (r == 0) {
+        a.g = 0;
+        a.first_r = 0;
+        a.size = 1;
+    } else if (r < fan) {
+        const int j = 31 - __clz(r);
+        a.g = j + 1;
+        a.first_r = 1 << j;
+        a.size = 1 << j;
+    } else {
+        const int q = (r - fan) / fan;
+        a.g = (31 - __clz(fan)) + 1 + q;
+        a.first_r = fan + q * fan;
+        a.size = fan;
+    }
+    if (a.first_r + a.size > count) a.size = count - a.first_r;
+    return a;
+}
+
+// Groups for `count` workgroups; the arrival tree is used when the position
+// tree would need two levels or more and the group results fit one merge:
+// counters [0, groups) per group, [groups] for the group results, [groups + 1]
+// for the tickets.
+__device__ __forceinline__ int arrival_groups(int count, int fan) { return arrival_group(count - 1, count, fan).g + 1; }
+__device__ __forceinline__ bool use_arrival_tree(const TreeArgs &ta, int count) {
+    if (!ta.arrival || count <= ta.fan) return false;
+    const int groups = arrival_groups(count, ta.fan);
+    return groups <= ta.fan && groups + 2 <= ta.seg_ctr_stride;
+}
+
+template <int R, int NT>
+__device__ __forceinline__ void arrival_tree_finish(uint64_t *sm, MergeScratch *ms, const TreeArgs &ta, int seg,
+                                                    int ticket) {
+    const int k = ta.k;
+    const int kc = ta.kc;
+    const int count = gridDim.x;
+    const int groups = arrival_groups(count, ta.fan);
+    uint64_t *base = ta.tree + (int64_t)seg * ta.seg_tree_stride;  // [count] ticket lists, then [groups] results
+    uint32_t *ctr = ta.counters + (int64_t)seg * ta.seg_ctr_stride;
+    uint64_t *const results = base + (int64_t)count * kc;
+    const ArrivalGroup a = arrival_group(count - 1 - ticket, count, ta.fan);
+    if (a.size > 1) {
+        if (!store_and_arrive<NT>(sm, base + (int64_t)ticket * kc, k, &ctr[a.g], a.size, nullptr, ms)) return;
+        const int first_ticket = count - a.first_r - a.size;
+        load_lists<NT>(sm, base + (int64_t)first_ticket * kc, a.size, kc, k);
+        merge_lists<R, NT>(sm, ms, a.size, kc, k, true);
+    }
+    if (!store_and_arrive<NT>(sm, results + (int64_t)a.g * kc, k, &ctr[groups], groups, &ctr[groups + 1], ms))
+        return;
+    load_lists<NT>(sm, results, groups, kc, k);
+    merge_lists<R, NT>(sm, ms, groups, kc, k, true);
+    for (int r = threadIdx.x; r < k; r += NT) write_output(ta, seg, r, sm[r]);
 }
 
 // Steps 2 and 3 above.  `sm` is kTreeEntries ranks of LDS; NT the workgroup size.
@@ -245,18 +501,32 @@ __device__ __forceinline__ void finish_workgroup(WaveSelector<R> &sel, uint64_t 
     constexpr int Kp = 64 * R;
     const int lane = lane_id();
     const int wv = wave_in_group();
+    const bool arrival = use_arrival_tree(ta, gridDim.x);
 
     // 2. the workgroup's wave lists -> one list in sm[0 .. Kp) (NT / 64 * Kp <= kTreeEntries).
 #pragma unroll
     for (int r = 0; r < R; ++r) sm[wv * Kp + r * 64 + lane] = sel.L[r];
     __syncthreads();
-    merge_lds_lists<R>(sm, NT / 64);
+    // Every wave has finished streaming: take the arrival ticket.  Its round
+    // trip overlaps the workgroup's merge (an increment: the compiler waits
+    // for an add's result at once, to spread it over the wave's lanes).
+    uint32_t ticket = 0;
+    if (arrival && threadIdx.x == 0)
+        ticket = atomicInc(&ta.counters[(int64_t)seg * ta.seg_ctr_stride + arrival_groups(gridDim.x, ta.fan) + 1],
+                           0xffffffffu);
+    merge_lists<R, NT>(sm, ms, NT / 64, Kp, ta.k, ta.arrival != 0);
     if (gridDim.x == 1) {
         for (int r = threadIdx.x; r < ta.k; r += NT) write_output(ta, seg, r, sm[r]);
         return;
     }
     // 3. across the workgroups of this segment.
-    tree_finish<R, NT>(sm, ms, ta, seg);
+    if (arrival) {
+        if (threadIdx.x == 0) ms->ticket = (int)ticket;
+        __syncthreads();
+        arrival_tree_finish<R, NT>(sm, ms, ta, seg, ms->ticket);
+    } else {
+        tree_finish<R, NT>(sm, ms, ta, seg);
+    }
 }
 
 // ---------------------------------------------------------------- scoring
@@ -622,7 +892,7 @@ __global__ __launch_bounds__(W * 64) void select_topk_kernel(
 
 // ---------------------------------------------------------------- per-list-size launchers
 
-inline TreeArgs make_tree(const TreeLaunch &t) {
+inline TreeArgs make_tree(const TreeLaunch &t, bool arrival = false) {
     TreeArgs ta;
     ta.tree = t.tree;
     ta.counters = t.counters;
@@ -636,6 +906,7 @@ inline TreeArgs make_tree(const TreeLaunch &t) {
     ta.out_val = static_cast<uint32_t *>(t.out_val);
     ta.src = static_cast<const uint32_t *>(t.src);
     ta.src_seg_stride = t.src_seg_stride;
+    ta.arrival = arrival;
     return ta;
 }
 
@@ -678,7 +949,12 @@ hipError_t launch_gemv_r(bool fast, int lg, int L, dim3 grid, hipStream_t s, con
 template <int R>
 hipError_t launch_select_r(int dtype, dim3 grid, hipStream_t s, const void *data, int64_t n, int64_t seg_stride,
                            int64_t per_wave, const TreeLaunch &t) {
-    const TreeArgs ta = make_tree(t);
+    // Raw arrays: one long stream per wave whose workgroups finish over a
+    // spread of several microseconds, which the arrival-ordered tree turns
+    // into merges done early (1e8 int32, K = 20 / 50: 77.2 / 80.2 -> 75.1 /
+    // 78.4 us).  The scorers' short streams finish together, and there it
+    // measured slower (50k x 768, K = 32: 36.8 -> 39.3 us).
+    const TreeArgs ta = make_tree(t, true);
     constexpr int W = select_waves(64 * R);
     const uint32_t *base = static_cast<const uint32_t *>(data);
     if (dtype == 0)
