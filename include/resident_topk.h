@@ -267,6 +267,53 @@ rt_status topk_select(rt_engine *e, const void *values, int32_t dtype, int64_t n
 rt_status topk_select_noalloc(const void *values, int32_t dtype, int64_t n, int32_t k, int32_t *out_idx,
                               void *out_values, void *stream);
 
+/*
+ * Dynamic batching of concurrent single-query searches ("GPU-Resident Top-K
+ * for Agentic RAG", section 1: many small agents retrieving against one
+ * corpus; section 9: no concurrency between queries inside one engine).
+ *
+ * A batcher owns engine `e` from creation to rt_batcher_destroy: nothing else
+ * may call `e` meanwhile (use rt_engine_create_shared for a second engine on
+ * the same corpus).  Any number of host threads submit single queries; one
+ * dispatcher thread gathers up to max_batch of them (1..min(32, e's max_q)),
+ * waiting at most max_wait_us (0..1e6) after the first arrives, and runs them
+ * as one batched search with k = the largest k in the batch; each request gets
+ * the first k entries of its row.
+ *   exact = 1: search_resident_filtered (requires rt_enable_filtered on e, else
+ *     RT_ESTATE); every request's answer is bit for bit the plain single-query
+ *     scan's.
+ *   exact = 0: search_resident; scores from the batched fp32 matrix-core
+ *     path, equal to the single-query scan's within fp32 rounding.
+ * The corpus must be resident (RT_ESTATE otherwise); a request whose batch
+ * finds the corpus changed (another depth, or fewer than k rows) fails with
+ * RT_ESTATE.  RT_ENOMEM / RT_EHIP: allocation (pinned staging, a stream,
+ * device buffers, the thread) failed.
+ */
+typedef struct rt_batcher rt_batcher; /* opaque */
+rt_status rt_batcher_create(rt_engine *e, int32_t max_batch, int32_t max_wait_us, int32_t exact,
+                            rt_batcher **out);
+/*
+ * Queue one query: `query` is host memory with the corpus depth's d floats,
+ * copied before the call returns; 1 <= k <= min(e's max_k, resident rows).
+ * out_idx / out_scores: host memory of k entries each, written before the
+ * request completes; keep them valid until rt_batcher_wait returns for the
+ * ticket.  *out_ticket identifies the request.  Thread-safe.  RT_EINVAL: bad
+ * argument; RT_ESTATE: the batcher is being destroyed.
+ */
+rt_status rt_batcher_submit(rt_batcher *b, const float *query, int32_t k, int32_t *out_idx, float *out_scores,
+                            uint64_t *out_ticket);
+/*
+ * Block until the request completes; returns its status (the search's, or
+ * RT_ESTATE as above).  Wait for every ticket exactly once (RT_EINVAL for an
+ * unknown or already-waited ticket).  Thread-safe.
+ */
+rt_status rt_batcher_wait(rt_batcher *b, uint64_t ticket);
+/* out4 = {batches run, queries served, largest batch, queries waiting}. */
+rt_status rt_batcher_stats(rt_batcher *b, int64_t *out4);
+/* Serve what is queued, stop the dispatcher and free the batcher (not the
+ * engine).  Call after every submitted ticket has been waited for. */
+void rt_batcher_destroy(rt_batcher *b);
+
 /* Static, human-readable name of a status code. */
 const char *rt_status_string(rt_status s);
 

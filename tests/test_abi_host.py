@@ -110,6 +110,16 @@ def test_entry_points_reject_null_engine(lib):
     assert lib.rt_engine_create(0, 8, 8, 1, 0, ctypes.byref(out)) == EINVAL and not out.value
     assert lib.rt_engine_create_shared(NULL, 8, 1, ctypes.byref(out)) == EINVAL and not out.value
     lib.rt_engine_destroy(NULL)  # ignored
+    b = ctypes.c_void_p()
+    assert lib.rt_batcher_create(NULL, 8, 100, 1, ctypes.byref(b)) == EINVAL and not b.value
+    assert lib.rt_batcher_create(P, 8, 100, 1, None) == EINVAL
+    assert lib.rt_batcher_create(P, 8, -1, 1, ctypes.byref(b)) == EINVAL and not b.value   # negative wait
+    assert lib.rt_batcher_create(P, 8, 100, 2, ctypes.byref(b)) == EINVAL and not b.value  # exact is 0 or 1
+    t = ctypes.c_uint64(0)
+    assert lib.rt_batcher_submit(NULL, P, 1, P, P, ctypes.byref(t)) == EINVAL
+    assert lib.rt_batcher_wait(NULL, 1) == EINVAL
+    assert lib.rt_batcher_stats(NULL, (ctypes.c_int64 * 4)()) == EINVAL
+    lib.rt_batcher_destroy(NULL)  # ignored
 
 
 def test_binding_rejects_bad_tensors_on_the_host():

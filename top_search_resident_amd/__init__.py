@@ -16,7 +16,7 @@ import ctypes
 from . import _lib
 from ._lib import ResidentTopKError, RT_DTYPE_FLOAT32, RT_DTYPE_INT32, RT_METRIC_COSINE, RT_METRIC_DOT
 
-__all__ = ["ResidentTopK", "ResidentTopKError", "topk_select_noalloc"]
+__all__ = ["ResidentTopK", "ResidentTopKError", "Batcher", "topk_select_noalloc"]
 
 
 def _torch():
@@ -291,3 +291,79 @@ class ResidentTopK:
         _check(self._lib.rt_read_probe(self._h, int(reps), _stream_handle(stream), ctypes.byref(out)),
                "rt_read_probe", self._h)
         return float(out.value)
+
+
+class Batcher:
+    """Dynamic batching of single-query searches from many threads
+    (rt_batcher_*): submissions that arrive within `max_wait_us` of each other
+    run as one batched search of up to `max_batch` queries on `engine`, which
+    the batcher uses alone until it is closed (take engine.shared() for other
+    work on the same corpus).  exact=True (the default) runs the batched
+    filtered search -- every answer equals the plain single-query scan's, bit
+    for bit -- and needs engine.enable_filtered() first; exact=False runs the
+    plain batched search (fp32 matrix cores)."""
+
+    def __init__(self, engine, max_batch=32, max_wait_us=200, exact=True):
+        self._lib = engine._lib
+        self._engine = engine  # keeps the engine open while the batcher uses it
+        self._h = ctypes.c_void_p()
+        st = self._lib.rt_batcher_create(engine._h, int(max_batch), int(max_wait_us), 1 if exact else 0,
+                                         ctypes.byref(self._h))
+        _check(st, "rt_batcher_create", engine._h)
+        self.d = engine._res["d"]
+
+    def submit(self, query, k):
+        """Queue one query (host fp32 [d], numpy or CPU tensor).  Returns a
+        handle for wait()."""
+        import numpy as np
+        if hasattr(query, "data_ptr"):
+            if query.device.type != "cpu":
+                raise TypeError("Batcher.submit takes host queries (numpy or CPU tensor)")
+            query = query.numpy()
+        q = np.ascontiguousarray(query, dtype=np.float32).reshape(-1)
+        if q.shape[0] != self.d:
+            raise ValueError(f"query has {q.shape[0]} values, the corpus depth is {self.d}")
+        k = int(k)
+        if k < 1:
+            raise ResidentTopKError(_lib.RT_EINVAL, f"k = {k}")
+        idx = np.empty(k, dtype=np.int32)
+        sc = np.empty(k, dtype=np.float32)
+        ticket = ctypes.c_uint64(0)
+        st = self._lib.rt_batcher_submit(self._h, q.ctypes.data, k, idx.ctypes.data, sc.ctypes.data,
+                                         ctypes.byref(ticket))
+        _check(st, "rt_batcher_submit")
+        return (int(ticket.value), idx, sc, q)  # the arrays stay referenced until wait()
+
+    def wait(self, handle):
+        """Block until the request completes; returns (idx int32 [k], scores
+        fp32 [k]) as numpy arrays, best-first."""
+        ticket, idx, sc, _ = handle
+        _check(self._lib.rt_batcher_wait(self._h, ctypes.c_uint64(ticket)), "rt_batcher_wait")
+        return idx, sc
+
+    def search(self, query, k):
+        """submit() + wait(): one blocking search, batched with whatever other
+        threads submit meanwhile."""
+        return self.wait(self.submit(query, k))
+
+    def stats(self):
+        out = (ctypes.c_int64 * 4)()
+        _check(self._lib.rt_batcher_stats(self._h, out), "rt_batcher_stats")
+        return dict(zip(("batches", "served", "largest_batch", "waiting"), [int(v) for v in out]))
+
+    def close(self):
+        if getattr(self, "_h", None) and self._h.value:
+            self._lib.rt_batcher_destroy(self._h)
+            self._h = ctypes.c_void_p()
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

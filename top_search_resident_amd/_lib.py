@@ -20,7 +20,8 @@ EXPORTS = (
     "rt_check_search", "rt_check_search_metric", "rt_check_select", "rt_filter_bounds",
     "rt_filter_bounds_batched", "rt_filter_bounds_fp8", "rt_set_filter_storage", "rt_filter_path_used",
     "rt_read_probe", "search_resident_filtered_metric", "topk_select_noalloc", "rt_cosine_score",
-    "rt_filter_cosine_bounds",
+    "rt_filter_cosine_bounds", "rt_batcher_create", "rt_batcher_submit", "rt_batcher_wait", "rt_batcher_stats",
+    "rt_batcher_destroy",
 )
 
 _lib = None
@@ -81,6 +82,11 @@ def load():
         "rt_cosine_score": ([ctypes.c_float, ctypes.c_float, ctypes.c_float], ctypes.c_float),
         "rt_filter_cosine_bounds": ([i32, ctypes.c_float, ctypes.c_float, ctypes.c_float, ctypes.c_float,
                                      ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
+        "rt_batcher_create": ([vp, i32, i32, i32, ctypes.POINTER(vp)], ctypes.c_int),
+        "rt_batcher_submit": ([vp, vp, i32, vp, vp, ctypes.POINTER(ctypes.c_uint64)], ctypes.c_int),
+        "rt_batcher_wait": ([vp, ctypes.c_uint64], ctypes.c_int),
+        "rt_batcher_stats": ([vp, ctypes.POINTER(i64)], ctypes.c_int),
+        "rt_batcher_destroy": ([vp], None),
     }
     for name, (args, res) in sig.items():
         f = getattr(lib, name)

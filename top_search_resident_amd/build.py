@@ -13,7 +13,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(HERE, "libresident_topk.so")
-SOURCES = ["engine.hip", "stream_topk.hip", "mfma_scores.hip", "batch_select.hip", "filter_topk.hip", "mfma_filter.hip", "filter8.hip", "read_probe.hip", "select_static.hip", "validate.cpp"] + \
+SOURCES = ["engine.hip", "stream_topk.hip", "mfma_scores.hip", "batch_select.hip", "filter_topk.hip", "mfma_filter.hip", "filter8.hip", "read_probe.hip", "select_static.hip", "batcher.hip", "validate.cpp"] + \
     [f"stream_r{r}{m}.hip" for r in (16, 8, 4, 2, 1) for m in ("", "c")] + \
     [f"filter_r{r}.hip" for r in (16, 8, 4, 2, 1)]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

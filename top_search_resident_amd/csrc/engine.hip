@@ -98,6 +98,10 @@ struct rt_engine {
     int32_t last_hip = 0;
 };
 
+namespace rt {
+bool engine_filtered_ready(const rt_engine *e) { return e != nullptr && e->ubuf != nullptr; }
+}  // namespace rt
+
 static rt_status hip_fail(rt_engine *e, hipError_t err) {
     if (e) {
         e->last_hip = (int32_t)err;
