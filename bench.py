@@ -246,6 +246,58 @@ def cpu_baseline_retrieval(corpus, qhost, kmax, gpu_results, budget_s, max_queri
             "host_cores": host_cores(), "cpu_model": cpu_model(), "parity": "ok"}
 
 
+def batcher_leg(args, torch, eng, qhost, ks):
+    """Many concurrent single-query clients (host threads, each issuing blocking
+    searches back to back, K cycling through the workload's K values) served
+    by one rt_batcher in exact mode: their queries run as batched filtered
+    searches.  Reports total queries/s, per-request latency (submit to answer,
+    host clock) and the batch sizes reached; a sample of answers is checked to
+    equal the single-query scan's bit for bit first."""
+    from concurrent.futures import ThreadPoolExecutor
+    from top_search_resident_amd import Batcher
+    clients, reps = args.batcher_clients, args.batcher_requests
+    be = eng.shared(max_k=max(ks), max_q=32)
+    be.enable_filtered()
+    nq = qhost.shape[0]
+    with Batcher(be, max_batch=32, max_wait_us=args.batcher_wait_us, exact=True) as b:
+        # parity first: a few answers against the plain single-query scan
+        for qi in range(min(8, nq)):
+            k = ks[qi % len(ks)]
+            bi, bs = b.search(qhost[qi], k)
+            si, ss = eng.search_resident(torch.from_numpy(qhost[qi:qi + 1]).cuda(), k)
+            torch.cuda.synchronize()
+            if not (np.array_equal(bi, si.cpu().numpy()[0]) and
+                    np.array_equal(bs.view(np.uint32), ss.cpu().numpy()[0].view(np.uint32))):
+                raise SystemExit("dynamic batching: answer differs from the single-query scan")
+
+        def client(c, count):
+            lat = []
+            for r in range(count):
+                i = (c * count + r) % nq
+                t0 = time.perf_counter()
+                b.search(qhost[i], ks[(c + r) % len(ks)])
+                lat.append((time.perf_counter() - t0) * 1e6)
+            return lat
+
+        with ThreadPoolExecutor(clients) as ex:  # warm-up
+            list(ex.map(lambda c: client(c, 2), range(clients)))
+        s0 = b.stats()
+        t0 = time.perf_counter()
+        with ThreadPoolExecutor(clients) as ex:
+            lats = list(ex.map(lambda c: client(c, reps), range(clients)))
+        wall = time.perf_counter() - t0
+        s1 = b.stats()
+    be.close()
+    lat = np.concatenate([np.asarray(x) for x in lats])
+    batches = s1["batches"] - s0["batches"]
+    return {"queries_per_s": lat.size / wall, "clients": clients, "requests": int(lat.size),
+            "ks": list(ks), "p50_us": pct(lat, 50), "p99_us": pct(lat, 99),
+            "batches": batches, "mean_batch": lat.size / max(batches, 1), "largest_batch": s1["largest_batch"],
+            "max_wait_us": args.batcher_wait_us, "mode": "exact (batched filtered search)",
+            "parity": "8 answers bit-identical to the single-query scan",
+            "note": "host threads in Python: each request also pays the binding's per-call cost"}
+
+
 def run_retrieval(args, torch, ResidentTopK, workloads):
     name = args.workload
     w = workloads.WORKLOADS[name]
@@ -341,6 +393,8 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
     line["gpu_clocks"] = gpu_clocks()
     if not args.filtered and not args.no_filtered_leg and d % 8 == 0:
         line["filtered_exact"] = filtered_leg(args, torch, eng, qdev, ks, n, d)
+    if not args.filtered and args.batcher_clients > 0 and d % 8 == 0 and args.metric == "dot":
+        line["dynamic_batching"] = batcher_leg(args, torch, eng, qhost, ks)
     if not args.no_cpu_baseline:
         sample = min(args.cpu_queries, qhost.shape[0])
         gpu_res = {}
@@ -777,6 +831,10 @@ def main():
     ap.add_argument("--num-queries", type=int, default=1000)
     ap.add_argument("--latency-queries", type=int, default=1000,
                     help="headline: sequential queries per K for the latency distribution")
+    ap.add_argument("--batcher-clients", type=int, default=64,
+                    help="concurrent single-query clients of the dynamic-batching leg (0: skip it)")
+    ap.add_argument("--batcher-requests", type=int, default=40, help="blocking searches per client")
+    ap.add_argument("--batcher-wait-us", type=int, default=300, help="batcher's longest wait for a batch to fill")
     ap.add_argument("--cpu-queries", type=int, default=40)
     ap.add_argument("--cpu-budget", type=float, default=20.0, help="seconds of oracle time in cpu_baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
