@@ -135,7 +135,12 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_bound8_kernel(
                 float hi = known ? a + e : __builtin_huge_valf();
                 float lw = known ? a - e : -__builtin_huge_valf();
                 if constexpr (COS) cosine_bounds(known, a, e, qnorm, cn[s][u], hi, lw);
-                if (g == 0 && row < r_end) ub[row] = hi;
+                if (g == 0 && row < r_end) {
+                    if (fa.ub16_out)  // uniform
+                        fa.ub16_out[(int64_t)seg * fa.uld + row] = bf16_round_up_bits(hi);
+                    else
+                        ub[row] = hi;
+                }
                 lo[u] = lw;
             }
             load_step(s, rs0 + P * STEP);

@@ -39,7 +39,19 @@ struct FilterArgs {
     float *thr;      // [segments] T, the k-th largest lower bound (written by pass 1's tree)
     const float *crn;  // cosine metric: the rows' L2 norms (null for the inner product)
     const uint16_t *ub16;  // pass 2: 16-bit upper bounds (top halves of fp32, rounded up) instead of ubuf
+    uint16_t *ub16_out;    // pass 1: write the upper bounds here as 16-bit values instead of to ubuf
 };
+
+// The top half of an fp32 value's bits, rounded toward +inf (bf16 rounded
+// up): positive and inexact, the next bf16 up (values above the largest bf16
+// go to +inf); zero, negative or exact, dropping the low bits moves toward
+// zero or changes nothing.  Either way the 16-bit value, widened, is >= x, so
+// an upper bound stays an upper bound.
+__device__ __forceinline__ uint16_t bf16_round_up_bits(float x) {
+    const uint32_t b = __float_as_uint(x);
+    const uint32_t hi = b >> 16;
+    return (uint16_t)((!(b >> 31) && (b & 0xffffu)) ? hi + 1u : hi);
+}
 
 // bf16 -> fp32 of the two halves of a 32-bit word.
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
@@ -51,8 +63,9 @@ __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w 
 // step carries half the bytes of an fp32 one, and with loads at use the pass
 // reached only 4.7 TB/s at 1M x 1024 (432 us; 326 us with P = 2, 320 us with
 // P = 4, measured on MI355X).  Per row: a (fp32 FMA chain per lane, group_sum), the
-// bound e, the upper bound written to ubuf, the lower bound ranked by the wave
-// selectors; the merge tree's root writes the k-th lower bound to thr[seg].
+// bound e, the upper bound written to ubuf (as a 16-bit value rounded up,
+// bf16_round_up_bits, when fa.ub16_out is set), the lower bound ranked by the
+// wave selectors; the merge tree's root writes the k-th lower bound to thr[seg].
 template <int LG, int L, int R, int P, bool COS>
 __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_bound_kernel(
     const uint16_t *__restrict__ corpus16, int64_t n, int d, const float *__restrict__ queries,
@@ -147,7 +160,12 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_bound_kernel(
                 float hi = known ? a + e : __builtin_huge_valf();
                 float lw = known ? a - e : -__builtin_huge_valf();
                 if constexpr (COS) cosine_bounds(known, a, e, qnorm, rn[s][u], hi, lw);
-                if (g == 0 && row < r_end) ub[row] = hi;
+                if (g == 0 && row < r_end) {
+                    if (fa.ub16_out)  // uniform
+                        fa.ub16_out[(int64_t)seg * fa.uld + row] = bf16_round_up_bits(hi);
+                    else
+                        ub[row] = hi;
+                }
                 lo[u] = lw;
             }
             if constexpr (P > 0) {
@@ -314,7 +332,8 @@ inline FilterArgs make_filter(const FilterLaunch &f) {
     fa.uld = f.uld;
     fa.thr = f.thr;
     fa.crn = f.crn;
-    fa.ub16 = f.ub16;
+    fa.ub16 = f.bounds16 ? reinterpret_cast<const uint16_t *>(f.ubuf) : f.ub16;
+    fa.ub16_out = f.bounds16 ? reinterpret_cast<uint16_t *>(f.ubuf) : nullptr;
     return fa;
 }
 

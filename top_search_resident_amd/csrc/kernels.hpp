@@ -53,6 +53,7 @@ struct FilterLaunch {
     float *thr;      // [segments] k-th largest lower bound, written by pass 1
     const float *crn = nullptr;  // cosine metric: the rows' L2 norms (null: inner product)
     const uint16_t *ub16 = nullptr;  // pass 2: read 16-bit upper bounds (top halves of fp32) from here instead
+    bool bounds16 = false;  // single-query passes: pass 1 writes 16-bit bounds at ubuf, pass 2 reads them there
 };
 
 // Bound factor cb for depth d (fp64 on the host, rounded up; see filter_topk.hpp)

@@ -299,14 +299,6 @@ __global__ __launch_bounds__(NW * 64) void mfma_bound_kernel(const uint16_t *__r
 // slightly wider candidate band in pass 2 (2^-8 relative).  They are
 // transposed through LDS so each store writes whole 64-byte runs.  A ragged
 // last tile is loaded from row n - 32; only its rows from 32 t on are written.
-__device__ __forceinline__ uint16_t bf16_round_up_bits(float x) {
-    const uint32_t b = __float_as_uint(x);
-    const uint32_t hi = b >> 16;
-    // positive and inexact: the next bf16 up (also maps values above the
-    // largest bf16 to +inf); zero, negative or exact: dropping the low bits
-    // moves toward zero or changes nothing, which does not decrease the value
-    return (uint16_t)((!(b >> 31) && (b & 0xffffu)) ? hi + 1u : hi);
-}
 
 template <int NCK>
 struct BoundRing {
