@@ -88,6 +88,7 @@ struct rt_batcher {
     uint64_t next_ticket = 1;
     bool stop = false;
     int64_t batches = 0, served = 0, largest = 0;
+    std::vector<std::shared_ptr<Request>> batch;  // the batch being served (dispatcher only)
     std::thread dispatcher;
 
     void run();
@@ -139,7 +140,7 @@ void rt_batcher::run() {
         // Collect until the batch is full or its oldest request has waited long enough.
         const Clock::time_point deadline = queue.front()->submitted + max_wait;
         while (!stop && (int32_t)queue.size() < max_batch && Clock::now() < deadline) work.wait_until(lk, deadline);
-        std::vector<std::shared_ptr<Request>> batch;
+        batch.clear();  // capacity max_batch, reserved at creation: no allocation here
         while (!queue.empty() && (int32_t)batch.size() < max_batch) {
             batch.push_back(queue.front());
             queue.pop_front();
@@ -196,6 +197,7 @@ rt_status rt_batcher_create(rt_engine *e, int32_t max_batch, int32_t max_wait_us
     }
     rt_batcher *raw = b.get();
     try {
+        raw->batch.reserve((size_t)max_batch);
         raw->dispatcher = std::thread([raw] { raw->run(); });
     } catch (...) {
         rt_batcher_destroy(b.release());
@@ -210,22 +212,32 @@ rt_status rt_batcher_submit(rt_batcher *b, const float *query, int32_t k, int32_
     if (b == nullptr || query == nullptr || out_idx == nullptr || out_scores == nullptr || out_ticket == nullptr)
         return RT_EINVAL;
     if (k < 1 || k > b->max_k) return RT_EINVAL;
-    auto r = std::make_shared<Request>();
-    r->query.assign(query, query + b->d);
-    r->k = k;
-    r->out_idx = out_idx;
-    r->out_scores = out_scores;
-    r->submitted = Clock::now();
-    {
-        std::lock_guard<std::mutex> lk(b->mu);
-        if (b->stop) return RT_ESTATE;
-        r->ticket = b->next_ticket++;
-        b->live.emplace(r->ticket, r);
-        b->queue.push_back(r);
-        *out_ticket = r->ticket;
+    try {  // allocation failures must not cross the C boundary
+        auto r = std::make_shared<Request>();
+        r->query.assign(query, query + b->d);
+        r->k = k;
+        r->out_idx = out_idx;
+        r->out_scores = out_scores;
+        r->submitted = Clock::now();
+        {
+            std::lock_guard<std::mutex> lk(b->mu);
+            if (b->stop) return RT_ESTATE;
+            r->ticket = b->next_ticket;
+            b->live.emplace(r->ticket, r);
+            try {
+                b->queue.push_back(r);
+            } catch (...) {
+                b->live.erase(r->ticket);
+                throw;
+            }
+            b->next_ticket += 1;
+            *out_ticket = r->ticket;
+        }
+        b->work.notify_one();
+        return RT_OK;
+    } catch (...) {
+        return RT_ENOMEM;
     }
-    b->work.notify_one();
-    return RT_OK;
 }
 
 rt_status rt_batcher_wait(rt_batcher *b, uint64_t ticket) {
