@@ -328,11 +328,11 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
     # algorithmic bytes per launch of the dominant kernel: the corpus and the
     # query, plus the rows' norms for the cosine metric; for the filtered search
     # its first pass: the bf16 rows and the rows' norms (or the fp8 codes and a
-    # {scale, bound part} pair per row) and the upper bounds it writes
+    # {scale, bound part} pair per row) and the 16-bit upper bounds it writes
     if args.filtered and path == "fp8":
-        corpus_bytes = n * d + d * 4 + n * 8 + n * 4 + (n * 4 if args.metric == "cosine" else 0)
+        corpus_bytes = n * d + d * 4 + n * 8 + n * 2 + (n * 4 if args.metric == "cosine" else 0)
     elif args.filtered:
-        corpus_bytes = n * d * 2 + d * 4 + n * 4 + n * 4
+        corpus_bytes = n * d * 2 + d * 4 + n * 4 + n * 2
     else:
         corpus_bytes = n * d * 4 + d * 4 + (n * 4 if args.metric == "cosine" else 0)
     per_k = {}
@@ -461,11 +461,11 @@ def filtered_leg(args, torch, eng, qdev, ks, n, d):
     steps = min(args.steps, 300)
     wall, lat, part, merge = time_search(eng, torch, qdev, ks, steps, args.warmup, metric=args.metric,
                                          filtered=True)
-    if path == "fp8":  # codes, query, per-row {scale, bound part} (+ row norm for the cosine), bounds written
-        pass1_bytes = n * d + d * 4 + n * 8 + n * 4 + (n * 4 if args.metric == "cosine" else 0)
+    if path == "fp8":  # codes, query, per-row {scale, bound part} (+ row norm for the cosine), 16-bit bounds written
+        pass1_bytes = n * d + d * 4 + n * 8 + n * 2 + (n * 4 if args.metric == "cosine" else 0)
         kernel = "gemv_bound8_kernel"
-    else:  # bf16 rows, query, row norms, upper bounds written
-        pass1_bytes, kernel = n * d * 2 + d * 4 + n * 4 + n * 4, "gemv_bound_kernel"
+    else:  # bf16 rows, query, row norms, 16-bit upper bounds written
+        pass1_bytes, kernel = n * d * 2 + d * 4 + n * 4 + n * 2, "gemv_bound_kernel"
     p1 = float(np.mean(np.concatenate([np.asarray(part[k]) for k in ks])))
     return {"value": steps * len(ks) / wall, "unit": "queries/s", "steps": steps, "metric": args.metric,
             "identical_to_fp32_scan": True, "first_pass_storage": path,
