@@ -19,9 +19,15 @@ from ._lib import ResidentTopKError, RT_DTYPE_FLOAT32, RT_DTYPE_INT32, RT_METRIC
 __all__ = ["ResidentTopK", "ResidentTopKError", "Batcher", "topk_select_noalloc"]
 
 
+_torch_module = None
+
+
 def _torch():
-    import torch
-    return torch
+    global _torch_module
+    if _torch_module is None:
+        import torch
+        _torch_module = torch
+    return _torch_module
 
 
 def _check(status, what, eng=None):
@@ -40,9 +46,10 @@ def _check_tensor(t, name, dtype, min_numel, device):
         raise TypeError(f"{name} must be a torch tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if not t.is_cuda:
-        raise TypeError(f"{name} must be a CUDA tensor")
-    if t.device.index != device:
+    dev = t.get_device()  # -1 for a host tensor; one call instead of is_cuda and device.index
+    if dev != device:
+        if dev < 0:
+            raise TypeError(f"{name} must be a CUDA tensor")
         raise ValueError(f"{name} is on {t.device}, the engine on cuda:{device}")
     if not t.is_contiguous():
         raise TypeError(f"{name} must be contiguous")
