@@ -319,6 +319,38 @@ def test_topk_arrival_tree(eng):
         assert np.array_equal(g_val.view(np.uint32), o_val.view(np.uint32)), k
 
 
+@pytest.mark.parametrize("case", range(16))
+def test_topk_tree_boundaries(eng, case):
+    """Sizes around the merge tree's shape changes for raw arrays: a workgroup
+    streams about 16k elements, a node merges 64 lists for 32 < k <= 64 and
+    128 for 16 < k <= 32, and past one node the workgroups are grouped by
+    arrival order -- so 1.05M and 2.1M elements are the boundaries, and 4.2M
+    reaches the 256-workgroup cap.  Each case draws its size around a
+    boundary, a k on either side of 32, a dtype, a value distribution (with
+    ties that overflow the binned merge's 64-entry sort) and a misaligned
+    start, and must match the oracle bit for bit."""
+    rng = np.random.default_rng(1000 + case)
+    base = [1_048_576, 2_097_152, 4_194_304, 1_200_000][case % 4]
+    n = int(base + rng.integers(-70_000, 70_000))
+    k = int(rng.choice([17, 20, 32, 33, 50, 64]))
+    offset = int(rng.integers(0, 4))
+    dist = case // 4  # 0 uniform, 1 few values, 2 sorted, 3 fp32 Gaussian with duplicates
+    if dist == 0:
+        v = rng.integers(-(2 ** 31), 2 ** 31, size=n + offset, dtype=np.int64).astype(np.int32)
+    elif dist == 1:
+        v = rng.integers(0, 5, size=n + offset, dtype=np.int32)
+    elif dist == 2:
+        v = np.sort(rng.integers(-(2 ** 31), 2 ** 31, size=n + offset, dtype=np.int64)).astype(np.int32)
+    else:
+        v = rng.standard_normal(n + offset).astype(np.float32)
+        v[rng.choice(v.size, 5000, replace=False)] = v[rng.choice(v.size, 5000, replace=False)]
+    print(f"[tree boundary] case {case}: n={n} k={k} offset={offset} dist={dist} dtype={v.dtype}", flush=True)
+    g_idx, g_val = _select(eng, v, k, offset=offset)
+    o_idx, o_val = oracle.topk(v[offset:], k)
+    assert np.array_equal(g_idx, o_idx), (case, n, k, offset, dist)
+    assert np.array_equal(g_val.view(np.uint32), o_val.view(np.uint32)), (case, n, k, offset, dist)
+
+
 def test_topk_float32_special_values(eng):
     rng = np.random.default_rng(6)
     v = rng.standard_normal(400_000).astype(np.float32)
