@@ -867,8 +867,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the row-sharded multi-GPU design is "
-                                   "documented but not built", "n_gpus": args.gpus}))
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the row-sharded multi-GPU design is "
+                                   "documented but not implemented", "n_gpus": args.gpus}))
         sys.exit(2)
 
     import torch
