@@ -8,7 +8,8 @@ Each query's answer must be the plain single-query scan's answer bit for bit
 every compile-time depth, batches of 2 to 32 queries, k from 1 to n, fewer
 tiles than k (no threshold: every row re-ranked), a ragged last tile, planted
 near-ties, exact integer ties, zero and huge queries, a smaller batch after a
-larger one on the same buffers, and a depth that falls back to the
+larger one on the same buffers, k above 256 (per-query candidate lists),
+lists longer than the in-LDS sort, and a depth that falls back to the
 per-query first pass."""
 import numpy as np
 import pytest
@@ -115,6 +116,32 @@ def test_batched_filtered_zero_and_huge_queries(eng):
     g_idx, g_sc = _both(eng, corpus, qs, 20)
     assert np.array_equal(g_idx[1], np.arange(20))
     _with_oracle(eng, corpus, qs[[0, 2, 4, 5]], 20)
+
+
+@pytest.mark.parametrize("k", [257, 512, 1024])
+def test_batched_filtered_large_k(eng, k):
+    """k above 256: the re-rank appends every row at or above T to a per-query
+    list and sorts the list."""
+    corpus = workloads.gaussian_rows(MAX_N, 768, config_id=717)
+    qs = workloads.gaussian_rows(32, 768, config_id=717, stream=1)
+    _with_oracle(eng, corpus, qs, k, check=(0, 31))
+
+
+def test_batched_filtered_long_candidate_lists(eng):
+    """More candidates than the in-LDS sort holds (8192): equal rows put all
+    20000 rows at T, integer scores tie over 8192 rows at the top; the
+    k-th largest candidate is found by a radix select over the list first."""
+    corpus = np.tile(workloads.gaussian_rows(1, 512, config_id=718), (20_000, 1))
+    qs = workloads.gaussian_rows(3, 512, config_id=718, stream=1)
+    g_idx, _ = _both(eng, corpus, qs, 600)
+    assert np.all(g_idx == np.arange(600)[None, :])
+    corpus = workloads.small_int_matrix(MAX_N, 256, lo=-1, hi=1, config_id=719)
+    qs = workloads.small_int_matrix(8, 256, lo=-1, hi=1, config_id=719, stream=1)
+    qs[:, 2:] = 0  # scores in [-2, 2]: over 8192 rows tie at the top score
+    g_idx, g_sc = _both(eng, corpus, qs, 1000)
+    o_idx, o_sc = oracle.search(corpus, qs, 1000)
+    assert np.array_equal(g_idx, o_idx)
+    assert np.array_equal(g_sc.astype(np.float64), o_sc)
 
 
 def test_batched_filtered_smaller_batch_after_larger(eng):

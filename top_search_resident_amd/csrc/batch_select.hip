@@ -401,6 +401,106 @@ hipError_t launch_tile_threshold(const float *tmax, int64_t tld, int64_t n, int 
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- candidate lists
+
+// Per segment (one workgroup each), the best k of the candidate lists that
+// launch_filtered_collect left in the slices of its waves: at least k ranks in
+// all (the threshold that admitted them certifies k rows).  Up to kSortCap
+// ranks are sorted in LDS.  More (many equal scores at the threshold) first
+// pin the k-th largest rank with eight histogram passes of 8 bits over the
+// slices in memory -- ranks are distinct, so exactly k are at or above it --
+// and sort those.  The slices are read in place, each by one wave.
+template <class F>
+__device__ __forceinline__ void for_each_candidate(const uint64_t *__restrict__ c, const uint32_t *__restrict__ cn,
+                                                   int waves, int64_t rows_per_wave, F f) {
+    constexpr int kWaves = kBatchSelectThreads / 64;
+    const int lane = threadIdx.x & 63;
+    for (int w = threadIdx.x >> 6; w < waves; w += kWaves) {
+        const int64_t cw = (int64_t)cn[w] < rows_per_wave ? (int64_t)cn[w] : rows_per_wave;
+        const uint64_t *__restrict__ cs = c + (int64_t)w * rows_per_wave;
+        for (int64_t i = lane; i < cw; i += 64) f(cs[i]);
+    }
+}
+
+__global__ __launch_bounds__(kBatchSelectThreads) void candidate_select_kernel(
+    const uint64_t *__restrict__ cand, int64_t ld, const uint32_t *__restrict__ cnt, int64_t cnt_ld, int waves,
+    int64_t rows_per_wave, SelectOut o) {
+    __shared__ uint64_t sm[kSortCap];
+    __shared__ uint32_t hist[256];
+    __shared__ uint64_t s_prefix;
+    __shared__ int s_need;
+    __shared__ uint32_t s_kept;
+    __shared__ uint32_t s_m;
+    const int seg = blockIdx.x;
+    const int t = threadIdx.x;
+    const int k = o.k;
+    const uint64_t *__restrict__ c = cand + (int64_t)seg * ld;
+    const uint32_t *__restrict__ cn = cnt + (int64_t)seg * cnt_ld;
+    if (t == 0) {
+        s_m = 0u;
+        s_kept = 0u;
+    }
+    __syncthreads();
+    uint32_t part = 0u;
+    for (int w = t; w < waves; w += kBatchSelectThreads) part += cn[w];
+    if (part) atomicAdd(&s_m, part);
+    __syncthreads();
+    const uint32_t m = s_m;
+    uint64_t kth = 0ull;  // keep ranks >= kth
+    if (m > (uint32_t)kSortCap) {
+        uint64_t prefix = 0ull, mask = 0ull;
+        int need = k;
+        for (int shift = 56; shift >= 0; shift -= 8) {
+            for (int b = t; b < 256; b += kBatchSelectThreads) hist[b] = 0u;
+            __syncthreads();
+            for_each_candidate(c, cn, waves, rows_per_wave, [&](uint64_t r) {
+                if ((r & mask) == prefix) atomicAdd(&hist[(r >> shift) & 255u], 1u);
+            });
+            __syncthreads();
+            if (t == 0) {  // the bin, from the top, in which the need-th largest lies
+                int above = 0, b = 255;
+                for (; b > 0 && above + (int)hist[b] < need; --b) above += (int)hist[b];
+                s_need = need - above;
+                s_prefix = prefix | ((uint64_t)b << shift);
+            }
+            __syncthreads();
+            need = s_need;
+            prefix = s_prefix;
+            mask |= 255ull << shift;
+            __syncthreads();
+        }
+        kth = prefix;  // the k-th largest rank itself
+    }
+    for_each_candidate(c, cn, waves, rows_per_wave, [&](uint64_t r) {
+        if (r >= kth) {
+            const uint32_t pos = atomicAdd(&s_kept, 1u);
+            if (pos < (uint32_t)kSortCap) sm[pos] = r;
+        }
+    });
+    __syncthreads();
+    const int kept = (int)min(s_kept, (uint32_t)kSortCap);  // m <= kSortCap, or exactly k
+    int M = 64;
+    while (M < kept) M <<= 1;
+    for (int i = kept + t; i < M; i += kBatchSelectThreads) sm[i] = 0ull;
+    __syncthreads();
+    block_sort_desc(sm, M);
+    for (int r = t; r < k; r += kBatchSelectThreads) write_result(o, seg, r, sm[r]);
+}
+
+hipError_t launch_candidate_select(const uint64_t *cand, int64_t ld, const uint32_t *cnt, int64_t cnt_ld,
+                                   int waves, int64_t rows_per_wave, int segments, int k, int32_t *out_idx,
+                                   float *out_scores, hipStream_t stream) {
+    if (k < 1 || k > kSortCap || waves < 1 || waves > cnt_ld || rows_per_wave < 1 || rows_per_wave > ld)
+        return hipErrorInvalidValue;
+    SelectOut o;
+    o.k = k;
+    o.out_idx = out_idx;
+    o.out_val = reinterpret_cast<uint32_t *>(out_scores);
+    hipLaunchKernelGGL(candidate_select_kernel, dim3(segments), dim3(kBatchSelectThreads), 0, stream, cand, ld, cnt,
+                       cnt_ld, waves, rows_per_wave, o);
+    return hipGetLastError();
+}
+
 hipError_t launch_tile_bound_select(const float *rows, int64_t ld, int64_t n, const float *tmax, int64_t tld,
                                     int segments, int k, int32_t *out_idx, float *out_scores, hipStream_t stream) {
     SelectOut o;

@@ -29,6 +29,7 @@ using rt::kMaxQ;
 constexpr int64_t kTreeRanks = int64_t(1) << 23;
 // Most streaming workgroups per segment (bounds the counter array).
 constexpr int64_t kMaxWgsPerSeg = 2048;
+constexpr int64_t kMaxCollectWaves = kMaxWgsPerSeg * rt::collect_waves();
 
 using rt::kp_for;
 using rt::kScoreWavesPerCu;
@@ -89,6 +90,8 @@ struct rt_engine {
     uint32_t *counters = nullptr;   // kMaxQ x kMaxWgsPerSeg arrival counters
     float *ubuf = nullptr;          // filtered search: max_q x roundup(max_n, 64) upper bounds
     float *thr = nullptr;           // filtered search: max_q thresholds
+    uint64_t *cand = nullptr;       // batched filtered search, large k: max_q x roundup(max_n, 64) candidate ranks
+    uint32_t *cand_cnt = nullptr;   // max_q x kMaxCollectWaves: ranks per wave's slice of cand
     int32_t filter_storage = RT_FILTER_AUTO;  // first pass of a single-query filtered search
     int32_t filter_path = RT_FILTER_PATH_NONE;  // what the last filtered call ran
     hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
@@ -163,6 +166,8 @@ void rt_engine_destroy(rt_engine *e) {
     (void)hipFree(e->counters);
     (void)hipFree(e->ubuf);
     (void)hipFree(e->thr);
+    (void)hipFree(e->cand);
+    (void)hipFree(e->cand_cnt);
     for (auto &ev : e->ev)
         if (ev) (void)hipEventDestroy(ev);
     if (e->res && e->res->refs.fetch_sub(1) == 1) {
@@ -396,7 +401,22 @@ rt_status rt_enable_filtered(rt_engine *e) {
         if (!dev_alloc(reinterpret_cast<void **>(&e->ubuf), sizeof(float) * (size_t)e->max_q * (size_t)ld) ||
             !dev_alloc(reinterpret_cast<void **>(&e->thr), sizeof(float) * (size_t)e->max_q)) {
             (void)hipFree(e->ubuf);
+            (void)hipFree(e->thr);
             e->ubuf = nullptr;
+            e->thr = nullptr;
+            st = RT_ENOMEM;
+        }
+    }
+    // Batches with large k re-rank into per-query candidate lists long enough
+    // for every row (set-up: the counts start at zero).
+    if (err == hipSuccess && st == RT_OK && e->max_q > 1 && !e->cand) {
+        if (!dev_alloc(reinterpret_cast<void **>(&e->cand), sizeof(uint64_t) * (size_t)e->max_q * (size_t)ld) ||
+            !dev_alloc(reinterpret_cast<void **>(&e->cand_cnt),
+                       sizeof(uint32_t) * (size_t)e->max_q * (size_t)kMaxCollectWaves)) {
+            (void)hipFree(e->cand);
+            (void)hipFree(e->cand_cnt);
+            e->cand = nullptr;
+            e->cand_cnt = nullptr;
             st = RT_ENOMEM;
         }
     }
@@ -502,7 +522,32 @@ rt_status search_resident_filtered_metric(rt_engine *e, const float *queries, in
                                     e->tile_ld, e->num_cus, s, &bounds16);
         if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[3], s);
         if (err == hipSuccess) err = rt::launch_tile_threshold(e->tmax, e->tile_ld, n, q, k, e->thr, s);
-        if (err == hipSuccess) {
+        // k > 256: per-wave candidate slices and one sort per query beat lists
+        // of 512 or 1024 entries per wave and their merge tree (500k x 768, 32
+        // queries, threshold + re-rank: 55 against 65 us at k = 257, 74 against
+        // 97 us at k = 1024); at k <= 256 the selectors are faster (52 against
+        // 54 us at k = 256).
+        const bool collect = e->cand != nullptr && kp >= 512;
+        if (err == hipSuccess && collect) {
+            const Plan pc = plan_stream(n, q, 64, 512, e->num_cus, kScoreWavesPerCu, rt::gemv_waves(64));
+            const rt::TreeLaunch tc = tree_for(e, pc, 64, 1, 1, nullptr, nullptr, nullptr, 0);  // selectors idle
+            rt::FilterLaunch f;
+            f.cb = 0.f;
+            f.delta = 0.f;
+            f.ubuf = e->ubuf;
+            f.uld = uld;
+            f.thr = e->thr;
+            f.ub16 = bounds16 ? reinterpret_cast<const uint16_t *>(e->ubuf) : nullptr;
+            f.cand = e->cand;
+            f.cand_ld = uld;
+            f.cand_cnt = e->cand_cnt;
+            f.cnt_ld = kMaxCollectWaves;
+            err = rt::launch_filtered_collect(r->corpus, n, d, queries, q, pc.per_wave, pc.wgs, tc, f, s);
+            if (err == hipSuccess)
+                err = rt::launch_candidate_select(e->cand, uld, e->cand_cnt, kMaxCollectWaves,
+                                                  pc.wgs * rt::collect_waves(), pc.per_wave, q, k, out_idx,
+                                                  out_scores, s);
+        } else if (err == hipSuccess) {
             const Plan p2 = plan_stream(n, q, kp, 512, e->num_cus, kScoreWavesPerCu, rt::gemv_waves(kp));
             const rt::TreeLaunch t2 = tree_for(e, p2, kp, k, 1, out_idx, out_scores, nullptr, 0);
             rt::FilterLaunch f;  // pass 2 reads only the bounds and thresholds

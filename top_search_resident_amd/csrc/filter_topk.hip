@@ -91,6 +91,18 @@ hipError_t launch_filtered_pass2(const float *corpus, int64_t n, int d, const fl
     }
 }
 
+hipError_t launch_filtered_collect(const float *corpus, int64_t n, int d, const float *queries, int segments,
+                                   int64_t rows_per_wave, int wgs, const TreeLaunch &t, const FilterLaunch &f,
+                                   hipStream_t stream) {
+    if (!filtered_search_ok(d) || f.cand == nullptr || f.cand_cnt == nullptr || f.cand_ld < n ||
+        f.cnt_ld < (int64_t)wgs * collect_waves() || t.k > 64)
+        return hipErrorInvalidValue;
+    int lg4 = 6, L4 = 8;
+    pick_gemv_shape(d / 4, &lg4, &L4);
+    // 64-entry list instantiations: in collect mode the selectors are idle
+    return launch_filtered_r<1>(lg4, L4, dim3(wgs, segments), stream, corpus, n, d, queries, rows_per_wave, t, f);
+}
+
 // Round to nearest even; a value that is not finite or rounds to infinity is
 // reported through *bad (its copy is then unusable for bounds).
 __global__ __launch_bounds__(256) void to_bf16_kernel(const float *__restrict__ x, uint16_t *__restrict__ y,

@@ -40,6 +40,11 @@ struct FilterArgs {
     const float *crn;  // cosine metric: the rows' L2 norms (null for the inner product)
     const uint16_t *ub16;  // pass 2: 16-bit upper bounds (top halves of fp32, rounded up) instead of ubuf
     uint16_t *ub16_out;    // pass 1: write the upper bounds here as 16-bit values instead of to ubuf
+    uint64_t *cand;        // pass 2, collect mode: the wave over rows [r0, r1) writes its
+                           // candidates' ranks to cand[seg * cand_ld + r0 ..] (cand_ld >= n)
+    int64_t cand_ld;
+    uint32_t *cand_cnt;    // and their number to cand_cnt[seg * cnt_ld + wave], every wave
+    int64_t cnt_ld;
 };
 
 // The top half of an fp32 value's bits, rounded toward +inf (bf16 rounded
@@ -257,6 +262,7 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_filtered_kernel(
 
     const int64_t r_begin = wave * rows_per_wave;
     const int64_t r_end = (r_begin + rows_per_wave < n) ? r_begin + rows_per_wave : n;
+    uint32_t ncand = 0;  // wave-uniform: collect mode's kept rows
     for (int64_t b0 = r_begin; b0 < r_end; b0 += (int64_t)NB * 64) {
         float uu[NB];
         if (ub16) {  // wave-uniform
@@ -308,7 +314,18 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_filtered_kernel(
                 if constexpr (COS) s = cosine_of(s, qnorm, fa.crn[row]);
                 const bool valid = (g == 0) && (mine[c] >= 0);
                 const uint64_t rank = make_rank(order_key_f32(s), (uint32_t)row);
-                sel.offer(my_stage, rank, valid && rank > sel.thr);
+                if (fa.cand) {  // uniform: collect mode, the rank goes to the wave's slice of the list
+                    // Scores below T are beaten by the k rows that certify T
+                    // (NaN stays: it fails every comparison).
+                    const bool keep = valid && !(s < T);
+                    const uint64_t mk = __ballot(keep);
+                    // a row is kept at most once, so the slice ends by r_end <= n <= cand_ld
+                    const int64_t pos = r_begin + ncand + lanes_below(mk);
+                    if (keep && pos < fa.cand_ld) fa.cand[(int64_t)seg * fa.cand_ld + pos] = rank;
+                    ncand += (uint32_t)__popcll(mk);
+                } else {
+                    sel.offer(my_stage, rank, valid && rank > sel.thr);
+                }
             }
         };
         for (int t0 = 0; t0 < count; t0 += C * RPS) {
@@ -319,6 +336,10 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_filtered_kernel(
                 score(std::integral_constant<int, C>{}, t0);
         }
         wave_lds_sync();  // the list is rewritten by the next chunk
+    }
+    if (fa.cand) {  // collect mode (uniform over the grid): candidate_select_kernel selects
+        if (lane == 0) fa.cand_cnt[(int64_t)seg * fa.cnt_ld + wave] = ncand;
+        return;
     }
     sel.finish(my_stage);
     finish_workgroup<R, W * 64>(sel, sm, &ms, ta, seg);
@@ -334,6 +355,10 @@ inline FilterArgs make_filter(const FilterLaunch &f) {
     fa.crn = f.crn;
     fa.ub16 = f.bounds16 ? reinterpret_cast<const uint16_t *>(f.ubuf) : f.ub16;
     fa.ub16_out = f.bounds16 ? reinterpret_cast<uint16_t *>(f.ubuf) : nullptr;
+    fa.cand = f.cand;
+    fa.cand_ld = f.cand_ld;
+    fa.cand_cnt = f.cand_cnt;
+    fa.cnt_ld = f.cnt_ld;
     return fa;
 }
 

@@ -54,6 +54,10 @@ struct FilterLaunch {
     const float *crn = nullptr;  // cosine metric: the rows' L2 norms (null: inner product)
     const uint16_t *ub16 = nullptr;  // pass 2: read 16-bit upper bounds (top halves of fp32) from here instead
     bool bounds16 = false;  // single-query passes: pass 1 writes 16-bit bounds at ubuf, pass 2 reads them there
+    uint64_t *cand = nullptr;     // pass 2 collect mode: candidate ranks (see launch_filtered_collect)
+    int64_t cand_ld = 0;
+    uint32_t *cand_cnt = nullptr;
+    int64_t cnt_ld = 0;
 };
 
 // Bound factor cb for depth d (fp64 on the host, rounded up; see filter_topk.hpp)
@@ -103,6 +107,24 @@ hipError_t launch_mfma_bound(const uint16_t *corpus16, int64_t n, int d, const f
 // than k tiles), so at least k rows have a lower bound at or above it.
 hipError_t launch_tile_threshold(const float *tmax, int64_t tld, int64_t n, int segments, int k, float *thr,
                                  hipStream_t stream);
+
+// Pass 2 of the batched filtered search for large k, in two launches.  Every
+// row whose upper bound reaches f.thr[seg] is re-scored in fp32 exactly as in
+// launch_filtered_pass2; if its score reaches the threshold too, its rank goes
+// to the slice of the list of the wave that took the row: the wave over rows
+// [w * rows_per_wave, ..) writes them from f.cand[seg * f.cand_ld + w *
+// rows_per_wave] on (f.cand_ld >= n: slices cannot overlap) and their number
+// to f.cand_cnt[seg * f.cnt_ld + w], for every w < wgs * collect_waves (so
+// f.cnt_ld >= that, and nothing needs clearing between calls).  Then
+// candidate_select gathers each segment's slices, sorts them and writes the
+// best k (index + score).
+constexpr int collect_waves() { return gemv_waves(64); }
+hipError_t launch_filtered_collect(const float *corpus, int64_t n, int d, const float *queries, int segments,
+                                   int64_t rows_per_wave, int wgs, const TreeLaunch &t, const FilterLaunch &f,
+                                   hipStream_t stream);
+hipError_t launch_candidate_select(const uint64_t *cand, int64_t ld, const uint32_t *cnt, int64_t cnt_ld,
+                                   int waves, int64_t rows_per_wave, int segments, int k, int32_t *out_idx,
+                                   float *out_scores, hipStream_t stream);
 
 // err[row] >= the L2 norm of corpus row - its bf16 copy, for rows < n.
 hipError_t launch_bf16_row_errors(const float *corpus, int64_t n, int d, float *err, int num_cus,
