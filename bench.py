@@ -35,9 +35,9 @@ answers checked against it, and for the batch the matrix-core utilisation.
 --seed` run a free-form synthetic corpus of the same recipe.
 """
 import argparse
+import glob
 import json
 import os
-import subprocess
 import sys
 import time
 
@@ -438,16 +438,23 @@ def read_ceiling(eng, corpus_bytes, scan_ms, reps=20):
 
 
 def gpu_clocks():
-    """Current GPU clocks as rocm-smi reports them (clocks are not locked);
-    None when the tool is missing or says nothing usable."""
-    try:
-        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
-        data = json.loads(out.stdout)
-    except (OSError, ValueError, subprocess.SubprocessError):
-        return None
-    cards = {c: {k: v for k, v in vals.items() if "clock" in k.lower() or "clk" in k.lower()}
-             for c, vals in data.items() if isinstance(vals, dict)}
-    return {c: v for c, v in cards.items() if v} or None
+    """Current GPU clock levels as the amdgpu driver lists them in sysfs (the
+    level in use is marked '*'; clocks are not locked); None when the files are
+    not readable.  A plain file read: no other program is started."""
+    out = {}
+    for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
+        vals = {}
+        for name in ("pp_dpm_sclk", "pp_dpm_mclk", "pp_dpm_fclk"):
+            try:
+                with open(os.path.join(dev, name)) as f:
+                    levels = [ln.strip() for ln in f if ln.strip()]
+            except OSError:
+                continue
+            current = [ln for ln in levels if ln.endswith("*")]
+            vals[name[7:]] = current[0] if current else levels
+        if vals:
+            out[os.path.basename(os.path.dirname(dev))] = vals
+    return out or None
 
 
 def filtered_leg(args, torch, eng, qdev, ks, n, d):
