@@ -438,9 +438,10 @@ def read_ceiling(eng, corpus_bytes, scan_ms, reps=20):
 
 
 def gpu_clocks():
-    """Current GPU clock levels as the amdgpu driver lists them in sysfs (the
-    level in use is marked '*'; clocks are not locked); None when the files are
-    not readable.  A plain file read: no other program is started."""
+    """GPU clock levels as the amdgpu driver lists them in sysfs, read after the
+    timed work (the level in use then is marked '*'; clocks are not locked);
+    None when the files are not readable.  A plain file read: no other program
+    is started."""
     out = {}
     for dev in sorted(glob.glob("/sys/class/drm/card*/device")):
         vals = {}
@@ -450,8 +451,7 @@ def gpu_clocks():
                     levels = [ln.strip() for ln in f if ln.strip()]
             except OSError:
                 continue
-            current = [ln for ln in levels if ln.endswith("*")]
-            vals[name[7:]] = current[0] if current else levels
+            vals[name[7:]] = levels
         if vals:
             out[os.path.basename(os.path.dirname(dev))] = vals
     return out or None
