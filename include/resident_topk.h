@@ -297,8 +297,9 @@ rt_status rt_batcher_create(rt_engine *e, int32_t max_batch, int32_t max_wait_us
  * copied before the call returns; 1 <= k <= min(e's max_k, resident rows).
  * out_idx / out_scores: host memory of k entries each, written before the
  * request completes; keep them valid until rt_batcher_wait returns for the
- * ticket.  *out_ticket identifies the request.  Thread-safe.  RT_EINVAL: bad
- * argument; RT_ESTATE: the batcher is being destroyed.
+ * ticket, or until rt_batcher_destroy returns.  *out_ticket identifies the
+ * request.  Thread-safe.  RT_EINVAL: bad argument; RT_ESTATE: the batcher is
+ * being destroyed.
  */
 rt_status rt_batcher_submit(rt_batcher *b, const float *query, int32_t k, int32_t *out_idx, float *out_scores,
                             uint64_t *out_ticket);
@@ -310,8 +311,9 @@ rt_status rt_batcher_submit(rt_batcher *b, const float *query, int32_t k, int32_
 rt_status rt_batcher_wait(rt_batcher *b, uint64_t ticket);
 /* out4 = {batches run, queries served, largest batch, queries waiting}. */
 rt_status rt_batcher_stats(rt_batcher *b, int64_t *out4);
-/* Serve what is queued, stop the dispatcher and free the batcher (not the
- * engine).  Call after every submitted ticket has been waited for. */
+/* Serve every queued request (its outputs are written, as if waited for),
+ * stop the dispatcher and free the batcher (not the engine).  No other thread
+ * may be inside, or enter, any rt_batcher_* call on `b` once this is called. */
 void rt_batcher_destroy(rt_batcher *b);
 
 /* Static, human-readable name of a status code. */

@@ -12,6 +12,8 @@ library is not built.
     idx, vals = eng.topk_select(values, k)          # device int32/fp32 [n] -> [k] each
 """
 import ctypes
+import threading
+import weakref
 
 from . import _lib
 from ._lib import ResidentTopKError, RT_DTYPE_FLOAT32, RT_DTYPE_INT32, RT_METRIC_COSINE, RT_METRIC_DOT
@@ -128,6 +130,7 @@ class ResidentTopK:
         # Resident depth, shared by every engine that shares the corpus (an
         # upload through any of them changes it for all); None before an upload.
         self._res = _share._res if _share is not None else {"d": None}
+        self._batchers = weakref.WeakSet()  # closed before this engine is
 
     def shared(self, max_k=None, max_q=None):
         """A new engine that searches this engine's resident corpus (no copy) with
@@ -139,6 +142,8 @@ class ResidentTopK:
 
     # -- lifecycle ---------------------------------------------------------
     def close(self):
+        for b in list(getattr(self, "_batchers", ())):
+            b.close()  # a batcher's dispatcher thread uses this engine
         if getattr(self, "_h", None) and self._h.value:
             self._lib.rt_engine_destroy(self._h)
             self._h = ctypes.c_void_p()
@@ -318,6 +323,12 @@ class Batcher:
                                          ctypes.byref(self._h))
         _check(st, "rt_batcher_create", engine._h)
         self.d = engine._res["d"]
+        # Output (and query) arrays of every request not yet waited for: the
+        # dispatcher thread writes the answers into them, so they must outlive
+        # the request even if the caller drops its handle.
+        self._pending = {}
+        self._lock = threading.Lock()
+        engine._batchers.add(self)
 
     def submit(self, query, k):
         """Queue one query (host fp32 [d], numpy or CPU tensor).  Returns a
@@ -339,13 +350,19 @@ class Batcher:
         st = self._lib.rt_batcher_submit(self._h, q.ctypes.data, k, idx.ctypes.data, sc.ctypes.data,
                                          ctypes.byref(ticket))
         _check(st, "rt_batcher_submit")
-        return (int(ticket.value), idx, sc, q)  # the arrays stay referenced until wait()
+        handle = (int(ticket.value), idx, sc, q)
+        with self._lock:
+            self._pending[handle[0]] = handle
+        return handle
 
     def wait(self, handle):
         """Block until the request completes; returns (idx int32 [k], scores
         fp32 [k]) as numpy arrays, best-first."""
         ticket, idx, sc, _ = handle
-        _check(self._lib.rt_batcher_wait(self._h, ctypes.c_uint64(ticket)), "rt_batcher_wait")
+        st = self._lib.rt_batcher_wait(self._h, ctypes.c_uint64(ticket))
+        with self._lock:  # once wait returns, nothing writes to this request's arrays
+            self._pending.pop(ticket, None)
+        _check(st, "rt_batcher_wait")
         return idx, sc
 
     def search(self, query, k):
@@ -359,9 +376,15 @@ class Batcher:
         return dict(zip(("batches", "served", "largest_batch", "waiting"), [int(v) for v in out]))
 
     def close(self):
+        """Serves every request still queued (their handles' arrays receive the
+        answers), then frees the batcher; wait() is not available afterwards.
+        No other thread may be inside submit() or wait() meanwhile."""
         if getattr(self, "_h", None) and self._h.value:
             self._lib.rt_batcher_destroy(self._h)
             self._h = ctypes.c_void_p()
+        if getattr(self, "_pending", None):
+            with self._lock:
+                self._pending.clear()
 
     def __enter__(self):
         return self
