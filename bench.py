@@ -192,7 +192,7 @@ def time_search(eng, torch, qdev, ks, steps, warmup, profile=True, metric="dot",
             lat[k].append((time.perf_counter_ns() - s) / 1e3)
             if sampled:
                 total, first, kern = eng.profile_read()
-                part[k].append(first if filtered else kern)
+                part[k].append(first if filtered and first > 0 else kern)  # no first pass: plain route
                 merge[k].append(total)
         if sampled:
             eng.profile(False)
@@ -340,7 +340,7 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
     # {scale, bound part} pair per row) and the 16-bit upper bounds it writes
     if args.filtered and path == "fp8":
         corpus_bytes = n * d + d * 4 + n * 8 + n * 2 + (n * 4 if args.metric == "cosine" else 0)
-    elif args.filtered:
+    elif args.filtered and path != "plain":
         corpus_bytes = n * d * 2 + d * 4 + n * 4 + n * 2
     else:
         corpus_bytes = n * d * 4 + d * 4 + (n * 4 if args.metric == "cosine" else 0)
@@ -379,8 +379,10 @@ def run_retrieval(args, torch, ResidentTopK, workloads):
                      "traffic": workload_traffic(name, args.metric, args.filtered),
                      "traffic_unit": "bytes per launch (rocprofv3 FETCH_SIZE x2 + WRITE_SIZE, profiles/)",
                      "kernel": ((("gemv_bound8_kernel" if path == "fp8" else "gemv_bound_kernel")
-                                 + f" ({path} first pass of the filtered search)") if args.filtered else
-                                "gemv_topk_kernel (fused scoring, per-wave top-K lists and merge tree)"),
+                                 + f" ({path} first pass of the filtered search)")
+                                if args.filtered and path != "plain" else
+                                "gemv_topk_kernel (fused scoring, per-wave top-K lists and merge tree)"
+                                + ("; the filtered search ran the plain scan" if args.filtered else "")),
                      "bytes_per_launch": corpus_bytes, "avg_launch_us": avg_ms * 1e3},
         "input_gen_s": gen_s,
     }
@@ -477,6 +479,12 @@ def filtered_leg(args, torch, eng, qdev, ks, n, d):
     steps = min(args.steps, 300)
     wall, lat, part, merge = time_search(eng, torch, qdev, ks, steps, args.warmup, metric=args.metric,
                                          filtered=True)
+    if path == "plain":  # a small corpus under --filter-storage auto: the engine runs the plain scan
+        return {"value": steps * len(ks) / wall, "unit": "queries/s", "steps": steps, "metric": args.metric,
+                "identical_to_fp32_scan": True, "first_pass_storage": path,
+                "note": "below the corpus size where the two passes pay off the engine runs the plain scan",
+                "per_k": {str(k): {"p50_us": pct(lat[k], 50), "p99_us": pct(lat[k], 99),
+                                   "device_p50_us": pct(np.asarray(merge[k]) * 1e3, 50)} for k in ks}}
     if path == "fp8":  # codes, query, per-row {scale, bound part} (+ row norm for the cosine), 16-bit bounds written
         pass1_bytes = n * d + d * 4 + n * 8 + n * 2 + (n * 4 if args.metric == "cosine" else 0)
         kernel = "gemv_bound8_kernel"

@@ -68,7 +68,8 @@ typedef enum { RT_FILTER_AUTO = 0, RT_FILTER_BF16 = 1, RT_FILTER_FP8 = 2 } rt_fi
 /* What the last search_resident_filtered call ran (rt_filter_path_used). */
 typedef enum {
     RT_FILTER_PATH_NONE = 0,        /* no filtered search yet */
-    RT_FILTER_PATH_PLAIN = 1,       /* the plain fp32 scan (copy unusable or depth not covered) */
+    RT_FILTER_PATH_PLAIN = 1,       /* the plain fp32 scan: copy unusable, depth not covered, or one
+                                       query over a small corpus under RT_FILTER_AUTO */
     RT_FILTER_PATH_BF16 = 2,        /* bf16 first pass, one query per segment */
     RT_FILTER_PATH_FP8 = 3,         /* fp8 first pass, one query per segment */
     RT_FILTER_PATH_BF16_MATRIX = 4  /* bf16 matrix-core first pass for the whole batch */
@@ -196,9 +197,11 @@ rt_status rt_enable_filtered(rt_engine *e);
  * row / s with a power-of-two scale s per row: a quarter of the fp32 bytes,
  * bound e = |q| (cr |x - x~| + cx |x|) + delta max(|q|, 1) max(s, 1), constants
  * from rt_filter_bounds_fp8; wider than bf16's, so more rows reach the
- * re-rank), or RT_FILTER_AUTO (the default: fp8 from 2^26 corpus elements
- * on).  The fp8 pass covers d in {256, 384, 512, 768, 1024, 1536, 2048} and a
- * corpus whose values are finite; otherwise the bf16 pass runs.  Batches on an
+ * re-rank), or RT_FILTER_AUTO (the default: for a single query, the plain
+ * fp32 scan below 44 x 2^20 corpus elements, where the two passes cost more
+ * than they save, and the fp8 pass from there on).  The fp8 pass covers d in
+ * {256, 384, 512, 768, 1024, 1536, 2048} and a corpus whose values are finite;
+ * otherwise the bf16 pass runs.  Batches on an
  * engine with batch buffers always take the bf16 matrix-core pass.  The answer
  * is the same in every case.  RT_EINVAL for NULL or an unknown value.
  */

@@ -4,7 +4,8 @@ the oracle acceptance rules, on shapes that exercise every lane-group layout of
 both passes, on inputs where many rows crowd the k-th score (planted near-ties,
 exact integer ties, all-equal rows, where the second pass has to re-score many
 or all rows), on zero rows and queries, on batches, on engines sharing a
-corpus, and on a corpus with values that overflow bf16 (plain-scan fallback)."""
+corpus, and on a corpus with values that overflow bf16 (plain-scan fallback), and the default
+storage choice, which runs the plain scan for one query over a small corpus."""
 import numpy as np
 import pytest
 
@@ -25,6 +26,7 @@ def eng():
     assert torch.cuda.is_available(), "a GPU is required for the parity tests"
     e = ResidentTopK(MAX_N, MAX_D, MAX_K, MAX_Q, device=0)
     e.enable_filtered()
+    e.set_filter_storage("bf16")  # the default would run the plain scan for a single query on these sizes
     yield e
     e.close()
 
@@ -192,3 +194,33 @@ def test_filtered_needs_enable():
         with pytest.raises(ResidentTopKError) as ei:
             e.search_resident_filtered(q, 4)
         assert ei.value.status == 2
+
+
+def test_filtered_auto_small_corpus_runs_the_plain_scan():
+    """Under the default storage choice a single query over a small corpus runs
+    the plain scan (the two passes cost more there); a batch still takes a
+    filtered path; a corpus above the threshold takes the fp8 pass.  Every
+    answer is the single-query scan's, bit for bit."""
+    with ResidentTopK(60_000, 1024, 64, 4) as e:
+        e.enable_filtered()
+        for n, want in ((20_000, "plain"), (60_000, "fp8")):  # 20.5M and 61.4M elements; threshold 46.1M
+            corpus = workloads.gaussian_rows(n, 1024, config_id=580)
+            qs = workloads.gaussian_rows(4, 1024, config_id=580, stream=1)
+            e.upload_corpus_rowmajor(corpus)
+            qd = torch.from_numpy(qs).cuda()
+            for i in range(2):
+                fi, fs = e.search_resident_filtered(qd[i:i + 1], 32)
+                torch.cuda.synchronize()
+                assert e.filter_path_used() == want, (n, e.filter_path_used())
+                pi, ps = e.search_resident(qd[i:i + 1], 32)
+                torch.cuda.synchronize()
+                assert np.array_equal(fi.cpu().numpy(), pi.cpu().numpy())
+                assert np.array_equal(fs.cpu().numpy().view(np.uint32), ps.cpu().numpy().view(np.uint32))
+            bi, bs = e.search_resident_filtered(qd, 32)
+            torch.cuda.synchronize()
+            assert e.filter_path_used() == "bf16_matrix"
+            for i in range(4):
+                pi, ps = e.search_resident(qd[i:i + 1], 32)
+                torch.cuda.synchronize()
+                assert np.array_equal(bi.cpu().numpy()[i], pi.cpu().numpy()[0])
+                assert np.array_equal(bs.cpu().numpy()[i].view(np.uint32), ps.cpu().numpy()[0].view(np.uint32))

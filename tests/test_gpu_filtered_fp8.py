@@ -127,8 +127,9 @@ def test_fp8_nonfinite_corpus_runs_the_plain_scan(eng):
 
 
 def test_storage_choice():
-    """"auto" keeps bf16 for a small corpus, "bf16" forces it; a depth without an
-    fp8 pass falls back to bf16; unknown names are rejected."""
+    """"auto" runs the plain scan for one query over a small corpus, "bf16" and
+    "fp8" force their passes; a depth without an fp8 pass falls back to bf16;
+    unknown names are rejected."""
     with ResidentTopK(4_000, 640, 64, 1) as e:
         e.enable_filtered()
         corpus = workloads.gaussian_rows(4_000, 512, config_id=816)
@@ -138,7 +139,7 @@ def test_storage_choice():
         assert e.filter_path_used() is None
         e.search_resident_filtered(qd, 5)
         torch.cuda.synchronize()
-        assert e.filter_path_used() == "bf16"
+        assert e.filter_path_used() == "plain"
         e.set_filter_storage("fp8")
         e.search_resident_filtered(qd, 5)
         torch.cuda.synchronize()

@@ -29,7 +29,9 @@ def test_random_search_shapes(case):
     k = int(min(n, rng.choice(KS)))
     metric = "cosine" if rng.random() < 0.3 else "dot"
     filtered = d % 8 == 0 and rng.random() < 0.5
-    print(f"[random search] case {case}: n={n} d={d} q={q} k={k} {metric} filtered={filtered}", flush=True)
+    storage = ("auto", "bf16", "fp8")[case % 3]  # first pass of a single-query filtered search
+    print(f"[random search] case {case}: n={n} d={d} q={q} k={k} {metric} filtered={filtered} {storage}",
+          flush=True)
     x = rng.standard_normal((n, d)).astype(np.float32)
     x /= np.linalg.norm(x, axis=1, keepdims=True).astype(np.float32) + np.float32(1e-30)
     if rng.random() < 0.3:  # duplicate rows: exact score ties
@@ -40,6 +42,7 @@ def test_random_search_shapes(case):
         qd = torch.from_numpy(qs).cuda()
         if filtered:
             eng.enable_filtered()
+            eng.set_filter_storage(storage)
             gi, gs = eng.search_resident_filtered(qd, k, metric=metric)
             ref = [eng.search_resident(qd[i:i + 1], k, metric=metric) for i in range(q)]
         else:

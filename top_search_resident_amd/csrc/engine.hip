@@ -41,9 +41,16 @@ Plan plan_stream(int64_t units, int segments, int kp, int64_t min_per_wave, int 
                            kMaxWgsPerSeg);
 }
 
-// Corpus size (n x d elements) from which a single-query filtered search takes
-// the fp8 first pass when the engine leaves the choice to the library.
-constexpr int64_t kFp8MinElements = int64_t(1) << 26;
+// Corpus size (n x d elements) from which a single-query filtered search pays
+// off when the engine leaves the choice to the library (RT_FILTER_AUTO), and
+// from which it then takes the fp8 first pass.  Below it the plain scan runs:
+// the two passes' fixed cost (two launches, two merge trees) outweighs the
+// bytes the first pass saves.  Host p50 per query at K = 8, d = 768, MI355X,
+// plain / bf16 first pass / fp8 first pass: 20k rows 31.7 / 44.0 / 48.3 us,
+// 50k rows 44.4 / 47.9 / 48.9 us, 65k rows 53.1 / 50.6 / 50.2 us, 80k rows
+// 56.5 / 54.4 / 51.0 us.  The answer is the same on every path.
+constexpr int64_t kFilteredMinElements = int64_t(44) << 20;
+constexpr int64_t kFp8MinElements = kFilteredMinElements;
 
 // Fewest rows a scoring wave streams: about 24 KB of rows (4 to 32 rows).  A
 // small corpus then spreads over more CUs with shorter chains of dependent
@@ -493,7 +500,8 @@ rt_status search_resident_filtered_metric(rt_engine *e, const float *queries, in
     const int64_t n = r->n;
     const int d = r->d;
     const bool cosine = metric == RT_METRIC_COSINE;
-    if (!r->copy16_ok || !rt::filtered_search_ok(d)) {
+    const bool small_auto = q == 1 && e->filter_storage == RT_FILTER_AUTO && n * (int64_t)d < kFilteredMinElements;
+    if (!r->copy16_ok || !rt::filtered_search_ok(d) || small_auto) {
         // the same answers through the plain scan, one query at a time (a plain
         // batch sums in another order)
         e->filter_path = RT_FILTER_PATH_PLAIN;
