@@ -232,8 +232,9 @@ class ResidentTopK:
     _PATHS = {0: None, 1: "plain", 2: "bf16", 3: "fp8", 4: "bf16_matrix"}
 
     def set_filter_storage(self, storage):
-        """First pass of a single-query filtered search: "auto" (fp8 for large
-        corpora), "bf16" or "fp8".  The answers are the same."""
+        """First pass of a single-query filtered search: "auto" (the plain scan
+        below ~46M corpus elements, where two passes cost more than they save,
+        fp8 from there on), "bf16" or "fp8".  The answers are the same."""
         if storage not in self._STORAGE:
             raise ValueError(f"storage must be one of {sorted(self._STORAGE)}")
         _check(self._lib.rt_set_filter_storage(self._h, self._STORAGE[storage]), "rt_set_filter_storage", self._h)
