@@ -6,14 +6,15 @@ on the same input bit for bit (indices, order and score bits), and the eager
 calls must still be right afterwards (the merge tree's counters, which each
 call leaves at zero, are shared by both).  Covers the single-query scan, the
 fp32 matrix-core batch, the filtered search (single query and batched, k below
-and above 256) and the raw-array selection."""
+and above 256) and the raw-array selection, with an engine and without one
+(topk_select_noalloc, meant for callers under capture)."""
 import numpy as np
 import pytest
 
 import oracle
 from gpu_util import check_retrieval
 import workloads
-from top_search_resident_amd import ResidentTopK
+from top_search_resident_amd import ResidentTopK, topk_select_noalloc
 
 pytestmark = pytest.mark.gpu
 
@@ -78,9 +79,10 @@ def test_search_graph_replays(eng, mode, q, k):
             check_retrieval(got_i[0], got_s[0], o_idx[0], o_sc[0], eng._corpus, qs[0], oracle)
 
 
-@pytest.mark.parametrize("dtype", ["int32", "float32"])
-def test_topk_select_graph_replays(eng, dtype):
-    print(f"[graph] topk_select {dtype}", flush=True)
+@pytest.mark.parametrize("dtype,noalloc", [("int32", False), ("float32", False), ("int32", True),
+                                           ("float32", True)])
+def test_topk_select_graph_replays(eng, dtype, noalloc):
+    print(f"[graph] topk_select {dtype} noalloc={noalloc}", flush=True)
     n, k = 3_000_001, 50
     rng = np.random.default_rng(992)
     if dtype == "int32":
@@ -90,7 +92,10 @@ def test_topk_select_graph_replays(eng, dtype):
     v_static = torch.from_numpy(host[0]).cuda()
     oi = torch.empty(k, dtype=torch.int32, device="cuda")
     ov = torch.empty(k, dtype=v_static.dtype, device="cuda")
-    g = _capture(lambda: eng.topk_select(v_static, k, oi, ov))
+    if noalloc:
+        g = _capture(lambda: topk_select_noalloc(v_static, k, oi, ov))
+    else:
+        g = _capture(lambda: eng.topk_select(v_static, k, oi, ov))
     for r in range(REPLAYS):
         v_static.copy_(torch.from_numpy(host[r]).cuda())
         g.replay()
