@@ -172,6 +172,45 @@ __device__ __forceinline__ void scan_tiles(const uint32_t *tm, int64_t tiles, F 
     }
 }
 
+// One segment's tile maxima as keys for the scans below: read once into
+// registers when they fit (tiles <= 16 per thread: every batched workload up
+// to 16,384 tiles, 524,288 rows), so the two or three scans of a call read
+// global memory once; otherwise each scan re-reads them (scan_tiles).
+struct TileKeys {
+    static constexpr int U = 16;
+    uint32_t kv[U];
+    const uint32_t *tm;
+    int64_t tiles;
+    bool cached;
+    __device__ __forceinline__ void load(const uint32_t *tm_, int64_t tiles_) {
+        tm = tm_;
+        tiles = tiles_;
+        cached = tiles <= (int64_t)U * blockDim.x;  // uniform over the workgroup
+        if (cached) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = (int64_t)u * blockDim.x + threadIdx.x;
+                kv[u] = tm[i < tiles ? i : tiles - 1];
+            }
+#pragma unroll
+            for (int u = 0; u < U; ++u) kv[u] = row_key(kv[u]);
+        }
+    }
+    // f(i, i < tiles, key of tile i), the same number of calls on every lane
+    template <typename F>
+    __device__ __forceinline__ void for_each(F &&f) const {
+        if (cached) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int64_t i = (int64_t)u * blockDim.x + threadIdx.x;
+                f(i, i < tiles, kv[u]);
+            }
+        } else {
+            scan_tiles(tm, tiles, f);
+        }
+    }
+};
+
 // Step 1 of tile_bound_select_kernel below, for the rows' tile maxima tm[0 ..
 // tiles): the lower edge of a key bin that holds the k-th largest tile
 // maximum, so at least k tiles reach it (as a key; 0, below every key, when
@@ -182,14 +221,15 @@ __device__ __forceinline__ void scan_tiles(const uint32_t *tm, int64_t tiles, F 
 // inside it: few keys, spread out, few LDS collisions.  If fewer than k keys
 // fall inside, two plain 11-bit passes over all keys pin the top 22 bits
 // instead.
-__device__ uint32_t tile_max_bound(const uint32_t *tm, int64_t tiles, int k, uint32_t *sh, uint32_t *scan_buf,
+__device__ uint32_t tile_max_bound(const TileKeys &keys, int k, uint32_t *sh, uint32_t *scan_buf,
                                    uint32_t *s_vals) {
+    const int64_t tiles = keys.tiles;
     const int t = threadIdx.x;
     const int lane = lane_id();
     uint32_t bound = 0;
     if (tiles >= k) {
         uint32_t top = 0;
-        scan_tiles(tm, tiles, [&](int64_t, bool ok, uint32_t key) {
+        keys.for_each([&](int64_t, bool ok, uint32_t key) {
             if (ok) top = max(top, key);
         });
         for (int off = 32; off >= 1; off >>= 1) top = max(top, (uint32_t)__shfl_xor((int)top, off));
@@ -202,7 +242,7 @@ __device__ uint32_t tile_max_bound(const uint32_t *tm, int64_t tiles, int k, uin
         if (lane == 0) atomicMax(&s_vals[0], top);
         __syncthreads();
         top = s_vals[0] >> 12;  // window: key >> 12 in (top - 2048, top]
-        scan_tiles(tm, tiles, [&](int64_t, bool ok, uint32_t key) {
+        keys.for_each([&](int64_t, bool ok, uint32_t key) {
             const uint32_t dist = top - (key >> 12);
             if (ok && dist < (uint32_t)kDigitBins) atomicAdd(&sh[dist], 1u);
         });
@@ -251,7 +291,7 @@ __device__ uint32_t tile_max_bound(const uint32_t *tm, int64_t tiles, int k, uin
                 const int shift = pass == 0 ? 21 : 10;
                 for (int b = t; b < kDigitBins; b += blockDim.x) sh[b] = 0u;
                 __syncthreads();
-                scan_tiles(tm, tiles, [&](int64_t, bool ok, uint32_t key) {
+                keys.for_each([&](int64_t, bool ok, uint32_t key) {
                     if (ok && (key & pmask) == prefix) atomicAdd(&sh[(key >> shift) & (kDigitBins - 1)], 1u);
                 });
                 __syncthreads();
@@ -294,9 +334,11 @@ __global__ __launch_bounds__(kBatchSelectThreads) void tile_bound_select_kernel(
     const uint32_t *row = rows + (int64_t)seg * ld;
     const uint32_t *tm = tmax + (int64_t)seg * tld;
     const int64_t tiles = (n + 31) / 32;
+    TileKeys keys;
+    keys.load(tm, tiles);
 
     // 1. the bound (tile_max_bound)
-    const uint32_t bound = tile_max_bound(tm, tiles, o.k, sh, scan_buf, s_vals);
+    const uint32_t bound = tile_max_bound(keys, o.k, sh, scan_buf, s_vals);
 
     // 2. tiles reaching the bound, then their elements >= bound
     if (t == 0) {
@@ -304,7 +346,7 @@ __global__ __launch_bounds__(kBatchSelectThreads) void tile_bound_select_kernel(
         s_vals[3] = 0u;  // kept ranks
     }
     __syncthreads();
-    scan_tiles(tm, tiles, [&](int64_t i, bool ok, uint32_t key) {
+    keys.for_each([&](int64_t i, bool ok, uint32_t key) {
         const bool take = ok && key >= bound;
         const uint64_t m = __ballot(take);
         if (m == 0) return;
@@ -387,7 +429,9 @@ __global__ __launch_bounds__(kBatchSelectThreads) void tile_threshold_kernel(con
     __shared__ uint32_t scan_buf[kBatchSelectThreads];
     __shared__ uint32_t s_vals[4];
     const int seg = blockIdx.x;
-    const uint32_t bound = tile_max_bound(tmax + (int64_t)seg * tld, tiles, k, sh, scan_buf, s_vals);
+    TileKeys keys;
+    keys.load(tmax + (int64_t)seg * tld, tiles);
+    const uint32_t bound = tile_max_bound(keys, k, sh, scan_buf, s_vals);
     // keys below -inf's stand for nothing real: every row is a candidate then
     if (threadIdx.x == 0)
         thr[seg] = (bound > order_key_f32(-INFINITY)) ? f32_of_order_key(bound) : -INFINITY;
