@@ -52,6 +52,15 @@ Plan plan_stream(int64_t units, int segments, int kp, int64_t min_per_wave, int 
 constexpr int64_t kFilteredMinElements = int64_t(44) << 20;
 constexpr int64_t kFp8MinElements = kFilteredMinElements;
 
+// Waves per CU of the batched filtered search's re-rank (pass 2).  With up to
+// 32 queries each gets 1/32 of them, and a wave walks its rows' bounds in
+// 512-row chunks, one memory round trip each; twice the scoring kernels' 8
+// shortens those chains, while more waves cost more in the merge trees.
+// MI355X, 32 x 500k x 768, threshold + re-rank at K = 100 / 1024: 8 waves
+// 39.9 / 68.4 us, 12: 37.3 / 65.3, 16: 34.4 / 63.9, 20: 43.5 / 73.2, 32:
+// 47.3 / 74.8 us.
+constexpr int64_t kBatchRerankWavesPerCu = 16;
+
 // Fewest rows a scoring wave streams: about 24 KB of rows (4 to 32 rows).  A
 // small corpus then spreads over more CUs with shorter chains of dependent
 // steps per wave (measured on MI355X, p50 per query: 10k x 384 15.8 -> 14.2 us,
@@ -537,7 +546,7 @@ rt_status search_resident_filtered_metric(rt_engine *e, const float *queries, in
         // 54 us at k = 256).
         const bool collect = e->cand != nullptr && kp >= 512;
         if (err == hipSuccess && collect) {
-            const Plan pc = plan_stream(n, q, 64, 512, e->num_cus, kScoreWavesPerCu, rt::gemv_waves(64));
+            const Plan pc = plan_stream(n, q, 64, 512, e->num_cus, kBatchRerankWavesPerCu, rt::gemv_waves(64));
             const rt::TreeLaunch tc = tree_for(e, pc, 64, 1, 1, nullptr, nullptr, nullptr, 0);  // selectors idle
             rt::FilterLaunch f;
             f.cb = 0.f;
@@ -556,7 +565,7 @@ rt_status search_resident_filtered_metric(rt_engine *e, const float *queries, in
                                                   pc.wgs * rt::collect_waves(), pc.per_wave, q, k, out_idx,
                                                   out_scores, s);
         } else if (err == hipSuccess) {
-            const Plan p2 = plan_stream(n, q, kp, 512, e->num_cus, kScoreWavesPerCu, rt::gemv_waves(kp));
+            const Plan p2 = plan_stream(n, q, kp, 512, e->num_cus, kBatchRerankWavesPerCu, rt::gemv_waves(kp));
             const rt::TreeLaunch t2 = tree_for(e, p2, kp, k, 1, out_idx, out_scores, nullptr, 0);
             rt::FilterLaunch f;  // pass 2 reads only the bounds and thresholds
             f.cb = 0.f;
