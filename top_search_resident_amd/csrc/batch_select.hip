@@ -453,7 +453,42 @@ hipError_t launch_tile_threshold(const float *tmax, int64_t tld, int64_t n, int 
 // ranks are sorted in LDS.  More (many equal scores at the threshold) first
 // pin the k-th largest rank with eight histogram passes of 8 bits over the
 // slices in memory -- ranks are distinct, so exactly k are at or above it --
-// and sort those.  The slices are read in place, each by one wave.
+// and sort those.  The slices are read in place: with up to kFlatSlices of
+// them their offsets go through LDS and each thread loads its candidates
+// independently; otherwise each wave walks whole slices.
+// Up to this many slices (waves of the collect pass per segment) the slices'
+// offsets go through LDS and every candidate is read by one independent load
+// (for_each_candidate_flat); more slices are walked one at a time by each wave.
+constexpr int kFlatSlices = kBatchSelectThreads;
+
+// Candidate i of a segment lies in the last slice w with off[w] <= i (off: the
+// exclusive prefix sums of the slices' counts, off[waves] = m), at position
+// i - off[w] of it.  Eight candidates per thread are located and loaded
+// before any is used.
+template <class F>
+__device__ __forceinline__ void for_each_candidate_flat(const uint64_t *__restrict__ c, const uint32_t *off,
+                                                        int waves, int64_t rows_per_wave, uint32_t m, F f) {
+    constexpr int U = 8;
+    for (uint32_t i0 = 0; i0 < m; i0 += (uint32_t)(U * kBatchSelectThreads)) {
+        uint64_t r[U];
+        bool ok[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t i = i0 + (uint32_t)(u * kBatchSelectThreads) + threadIdx.x;
+            ok[u] = i < m;
+            int lo = 0, hi = waves;  // off[lo] <= i < off[hi] while i < m
+            while (hi - lo > 1) {
+                const int mid = (lo + hi) >> 1;
+                if (off[mid] <= i) lo = mid; else hi = mid;
+            }
+            r[u] = c[ok[u] ? (int64_t)lo * rows_per_wave + (i - off[lo]) : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (ok[u]) f(r[u]);
+    }
+}
+
 template <class F>
 __device__ __forceinline__ void for_each_candidate(const uint64_t *__restrict__ c, const uint32_t *__restrict__ cn,
                                                    int waves, int64_t rows_per_wave, F f) {
@@ -475,21 +510,40 @@ __global__ __launch_bounds__(kBatchSelectThreads) void candidate_select_kernel(
     __shared__ int s_need;
     __shared__ uint32_t s_kept;
     __shared__ uint32_t s_m;
+    __shared__ uint32_t off[kFlatSlices + 1];
+    __shared__ uint32_t scan_buf[kBatchSelectThreads];
     const int seg = blockIdx.x;
     const int t = threadIdx.x;
     const int k = o.k;
     const uint64_t *__restrict__ c = cand + (int64_t)seg * ld;
     const uint32_t *__restrict__ cn = cnt + (int64_t)seg * cnt_ld;
+    const bool flat = waves <= kFlatSlices;  // uniform
     if (t == 0) {
         s_m = 0u;
         s_kept = 0u;
     }
     __syncthreads();
-    uint32_t part = 0u;
-    for (int w = t; w < waves; w += kBatchSelectThreads) part += cn[w];
-    if (part) atomicAdd(&s_m, part);
+    if (flat) {
+        const uint32_t v = t < waves ? (uint32_t)min((int64_t)cn[t], rows_per_wave) : 0u;
+        const uint32_t incl = block_inclusive_scan(v, scan_buf);
+        if (t < waves) off[t] = incl - v;
+        if (t == waves - 1) {
+            off[waves] = incl;
+            s_m = incl;
+        }
+    } else {
+        uint32_t part = 0u;
+        for (int w = t; w < waves; w += kBatchSelectThreads) part += min((int64_t)cn[w], rows_per_wave);
+        if (part) atomicAdd(&s_m, part);
+    }
     __syncthreads();
     const uint32_t m = s_m;
+    auto walk = [&](auto f) {
+        if (flat)
+            for_each_candidate_flat(c, off, waves, rows_per_wave, m, f);
+        else
+            for_each_candidate(c, cn, waves, rows_per_wave, f);
+    };
     uint64_t kth = 0ull;  // keep ranks >= kth
     if (m > (uint32_t)kSortCap) {
         uint64_t prefix = 0ull, mask = 0ull;
@@ -497,7 +551,7 @@ __global__ __launch_bounds__(kBatchSelectThreads) void candidate_select_kernel(
         for (int shift = 56; shift >= 0; shift -= 8) {
             for (int b = t; b < 256; b += kBatchSelectThreads) hist[b] = 0u;
             __syncthreads();
-            for_each_candidate(c, cn, waves, rows_per_wave, [&](uint64_t r) {
+            walk([&](uint64_t r) {
                 if ((r & mask) == prefix) atomicAdd(&hist[(r >> shift) & 255u], 1u);
             });
             __syncthreads();
@@ -515,7 +569,7 @@ __global__ __launch_bounds__(kBatchSelectThreads) void candidate_select_kernel(
         }
         kth = prefix;  // the k-th largest rank itself
     }
-    for_each_candidate(c, cn, waves, rows_per_wave, [&](uint64_t r) {
+    walk([&](uint64_t r) {
         if (r >= kth) {
             const uint32_t pos = atomicAdd(&s_kept, 1u);
             if (pos < (uint32_t)kSortCap) sm[pos] = r;
