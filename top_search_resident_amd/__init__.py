@@ -221,7 +221,7 @@ class ResidentTopK:
         """Exact top-k by inner product (metric="dot") or cosine similarity
         (metric="cosine").  queries: device fp32 [q, d] or [d].
         Returns (idx int32 [q, k], scores fp32 [q, k]) on the device, best-first;
-        enqueued on `stream` (default: torch's current stream)."""
+        enqueued on `stream` (default: torch's current stream on the engine's device)."""
         torch = _torch()
         metrics = {"dot": RT_METRIC_DOT, "cosine": RT_METRIC_COSINE}
         if metric not in metrics:
