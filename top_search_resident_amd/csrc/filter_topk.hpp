@@ -40,6 +40,7 @@ struct FilterArgs {
     const float *crn;  // cosine metric: the rows' L2 norms (null for the inner product)
     const uint16_t *ub16;  // pass 2: 16-bit upper bounds (top halves of fp32, rounded up) instead of ubuf
     uint16_t *ub16_out;    // pass 1: write the upper bounds here as 16-bit values instead of to ubuf
+    int ub_tq;             // nonzero: ub16 is tile-major, 32-row tiles of ub_tq queries x 32 rows each
     uint64_t *cand;        // pass 2, collect mode: the wave over rows [r0, r1) writes its
                            // candidates' ranks to cand[seg * cand_ld + r0 ..] (cand_ld >= n)
     int64_t cand_ld;
@@ -240,7 +241,9 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_filtered_kernel(
     const float4 *__restrict__ q4 = reinterpret_cast<const float4 *>(queries + (int64_t)seg * d);
     const float4 *__restrict__ c4 = reinterpret_cast<const float4 *>(corpus);
     const float *__restrict__ ub = fa.ubuf + (int64_t)seg * fa.uld;
-    const uint16_t *__restrict__ ub16 = fa.ub16 ? fa.ub16 + (int64_t)seg * fa.uld : nullptr;
+    const uint16_t *__restrict__ ub16 =
+        fa.ub16 ? fa.ub16 + (fa.ub_tq ? (int64_t)seg * 32 : (int64_t)seg * fa.uld) : nullptr;
+    const int64_t ub_tile = (int64_t)fa.ub_tq * 32;  // entries per tile when tile-major
     uint64_t *const my_stage = stage[wv];
 
     WaveSelector<R> sel;
@@ -268,8 +271,10 @@ __global__ __launch_bounds__(64 * gemv_waves(64 * R)) void gemv_filtered_kernel(
         if (ub16) {  // wave-uniform
 #pragma unroll
             for (int b = 0; b < NB; ++b) {
-                const int64_t row = b0 + b * 64 + lane;
-                uu[b] = __uint_as_float((uint32_t)ub16[row < r_end ? row : r_end - 1] << 16);
+                const int64_t row0 = b0 + b * 64 + lane;
+                const int64_t row = row0 < r_end ? row0 : r_end - 1;
+                const int64_t at = ub_tile ? (row >> 5) * ub_tile + (row & 31) : row;
+                uu[b] = __uint_as_float((uint32_t)ub16[at] << 16);
             }
         } else {
 #pragma unroll
@@ -355,6 +360,7 @@ inline FilterArgs make_filter(const FilterLaunch &f) {
     fa.crn = f.crn;
     fa.ub16 = f.bounds16 ? reinterpret_cast<const uint16_t *>(f.ubuf) : f.ub16;
     fa.ub16_out = f.bounds16 ? reinterpret_cast<uint16_t *>(f.ubuf) : nullptr;
+    fa.ub_tq = f.bounds16 ? 0 : f.ub_tq;
     fa.cand = f.cand;
     fa.cand_ld = f.cand_ld;
     fa.cand_cnt = f.cand_cnt;

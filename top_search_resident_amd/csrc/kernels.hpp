@@ -54,6 +54,7 @@ struct FilterLaunch {
     const float *crn = nullptr;  // cosine metric: the rows' L2 norms (null: inner product)
     const uint16_t *ub16 = nullptr;  // pass 2: read 16-bit upper bounds (top halves of fp32) from here instead
     bool bounds16 = false;  // single-query passes: pass 1 writes 16-bit bounds at ubuf, pass 2 reads them there
+    int ub_tq = 0;          // with ub16: nonzero if tile-major (as launch_mfma_bound's *tile_q)
     uint64_t *cand = nullptr;     // pass 2 collect mode: candidate ranks (see launch_filtered_collect)
     int64_t cand_ld = 0;
     uint32_t *cand_cnt = nullptr;
@@ -98,10 +99,12 @@ hipError_t prepare_mfma_filter();
 // multiple of 32 rows past n).  *bounds16 tells how the bounds were written:
 // false, fp32 at ubuf; true, 16-bit at (uint16_t *)ubuf (the top halves of
 // fp32 values rounded toward +inf), which pass 2 reads through
-// FilterLaunch::ub16.
+// FilterLaunch::ub16.  *tile_q tells their layout: 0, query-major as above;
+// otherwise tile-major, the bound of (query j, row r) at
+// (r / 32) * 32 * tile_q + 32 j + r % 32 (FilterLaunch::ub_tq).
 hipError_t launch_mfma_bound(const uint16_t *corpus16, int64_t n, int d, const float *queries, int q,
                              const float *rnorm, const float *rerr, float *ubuf, int64_t uld, float *tlb, int64_t tld,
-                             int num_cus, hipStream_t stream, bool *bounds16);
+                             int num_cus, hipStream_t stream, bool *bounds16, int *tile_q);
 // Per query, thr[seg] <= the k-th largest of that query's tile maxima of lower
 // bounds tmax[seg * tld + tile] (a bin edge below it; -inf when n has fewer
 // than k tiles), so at least k rows have a lower bound at or above it.

@@ -296,8 +296,12 @@ __global__ __launch_bounds__(NW * 64) void mfma_bound_kernel(const uint16_t *__r
 // halves the bytes written -- in this streaming pass every byte written costs
 // more than a byte read (measured on MI355X: 64 MB of scattered writes next to
 // a full-rate read stream cost ~70 us, 16 MB ~30 us) -- at the price of a
-// slightly wider candidate band in pass 2 (2^-8 relative).  They are
-// transposed through LDS so each store writes whole 64-byte runs.  A ragged
+// slightly wider candidate band in pass 2 (2^-8 relative).  They are laid out
+// tile-major: tile t's bounds are one block of 32 q entries at ub16 + 32 t q,
+// query j's 32 rows at offset 32 j, transposed through LDS so that each store
+// instruction writes 1 KB of contiguous lines (query-major rows, i.e. 64-byte
+// runs 1 MB apart, took 185.5 against 175.5 us at 32 x 500k x 768, measured
+// on MI355X; pass 2's half-line reads cost it ~2 us of that back).  A ragged
 // last tile is loaded from row n - 32; only its rows from 32 t on are written.
 
 template <int NCK>
@@ -325,7 +329,7 @@ __global__ __launch_bounds__(256, 1) void mfma_bound_dma_kernel(const uint16_t *
                                                                 const float *__restrict__ rnorm,
                                                                 const float *__restrict__ rerr, float cr, float cx,
                                                                 float delta, uint16_t *__restrict__ ub16,
-                                                                int64_t uld, float *__restrict__ tlb, int64_t tld,
+                                                                float *__restrict__ tlb, int64_t tld,
                                                                 int64_t tiles_per_wave) {
     using L = BoundDma<NCK>;
     constexpr int d = NCK * 64;
@@ -542,7 +546,7 @@ __global__ __launch_bounds__(256, 1) void mfma_bound_dma_kernel(const uint16_t *
                 const uint4 v = *reinterpret_cast<const uint4 *>(stage + jj * 64 + su * 16);
                 if (jj < q) {
                     const u32x4_t w = {v.x, v.y, v.z, v.w};
-                    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t *>(ub16 + (int64_t)jj * uld + row0 + 8 * su));
+                    __builtin_nontemporal_store(w, reinterpret_cast<u32x4_t *>(ub16 + row0 * q + jj * 32 + 8 * su));
                 }
             }
         } else if (has_q) {  // the ragged last tile, loaded from n - 32: rows from row0 on
@@ -551,7 +555,7 @@ __global__ __launch_bounds__(256, 1) void mfma_bound_dma_kernel(const uint16_t *
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     const int64_t r = lr + 8 * g + 4 * h + c;
-                    if (r >= row0) ub16[(int64_t)m * uld + r] = (uint16_t)(packed[g][c >> 1] >> (16 * (c & 1)));
+                    if (r >= row0) ub16[row0 * q + m * 32 + (r - row0)] = (uint16_t)(packed[g][c >> 1] >> (16 * (c & 1)));
                 }
         }
         mx = fmaxf(mx, __uint_as_float(xor_u32<32>(__float_as_uint(mx))));
@@ -602,8 +606,9 @@ hipError_t prepare_mfma_filter() {
 
 hipError_t launch_mfma_bound(const uint16_t *corpus16, int64_t n, int d, const float *queries, int q,
                              const float *rnorm, const float *rerr, float *ubuf, int64_t uld, float *tlb, int64_t tld,
-                             int num_cus, hipStream_t stream, bool *bounds16) {
+                             int num_cus, hipStream_t stream, bool *bounds16, int *tile_q) {
     const int64_t tiles = (n + 31) / 32;
+    *tile_q = 0;
     float cr, cx, delta;
     filter_bound_constants_batched(d, &cr, &cx, &delta);
     *bounds16 = false;
@@ -613,9 +618,10 @@ hipError_t launch_mfma_bound(const uint16_t *corpus16, int64_t n, int d, const f
 #define RT_LAUNCH_DMA(NCK)                                                                                      \
         if (d == NCK * 64) {                                                                                    \
             *bounds16 = true;                                                                                   \
+            *tile_q = q;                                                                                        \
             hipLaunchKernelGGL((mfma_bound_dma_kernel<NCK>), dim3((unsigned)blocks), dim3(256),                 \
                                (size_t)BoundDma<NCK>::kLds, stream, corpus16, n, queries, q, rnorm, rerr, cr, cx,  \
-                               delta, reinterpret_cast<uint16_t *>(ubuf), uld, tlb, tld, tpw);                  \
+                               delta, reinterpret_cast<uint16_t *>(ubuf), tlb, tld, tpw);                       \
             return hipGetLastError();                                                                           \
         }
         RT_BOUND_DMA(RT_LAUNCH_DMA)
