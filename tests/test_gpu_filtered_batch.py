@@ -63,6 +63,7 @@ def _with_oracle(eng, corpus, queries, k, check=None):
 @pytest.mark.parametrize("n,d,q,k", [
     (20_011, 768, 32, 100), (20_011, 1024, 32, 8), (40_000, 384, 17, 64), (30_000, 512, 8, 200),
     (9_000, 256, 32, 1024), (100_000, 768, 32, 32), (65, 768, 2, 65), (33, 512, 5, 5), (3_201, 1024, 32, 1),
+    (20, 512, 3, 5), (31, 256, 32, 31), (1, 768, 4, 1), (1_000, 1024, 7, 40),
 ])
 def test_batched_filtered_equals_plain(eng, n, d, q, k):
     corpus = workloads.gaussian_rows(n, d, config_id=700 + d % 97)

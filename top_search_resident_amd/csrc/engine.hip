@@ -534,10 +534,8 @@ rt_status search_resident_filtered_metric(rt_engine *e, const float *queries, in
     if (err == hipSuccess) err = prologue(e, s);
     if (err == hipSuccess && batched) {
         e->filter_path = RT_FILTER_PATH_BF16_MATRIX;
-        bool bounds16 = false;
-        int tile_q = 0;
-        err = rt::launch_mfma_bound(r->corpus16, n, d, queries, q, r->rnorm, r->err16, e->ubuf, uld, e->tmax,
-                                    e->tile_ld, e->num_cus, s, &bounds16, &tile_q);
+        err = rt::launch_mfma_bound(r->corpus16, n, d, queries, q, r->rnorm, r->err16, e->ubuf, e->tmax,
+                                    e->tile_ld, e->num_cus, s);
         if (err == hipSuccess && e->profiling) err = hipEventRecord(e->ev[3], s);
         if (err == hipSuccess) err = rt::launch_tile_threshold(e->tmax, e->tile_ld, n, q, k, e->thr, s);
         // k > 256: per-wave candidate slices and one sort per query beat lists
@@ -555,8 +553,8 @@ rt_status search_resident_filtered_metric(rt_engine *e, const float *queries, in
             f.ubuf = e->ubuf;
             f.uld = uld;
             f.thr = e->thr;
-            f.ub16 = bounds16 ? reinterpret_cast<const uint16_t *>(e->ubuf) : nullptr;
-            f.ub_tq = tile_q;
+            f.ub16 = reinterpret_cast<const uint16_t *>(e->ubuf);  // tile-major, q queries per tile
+            f.ub_tq = q;
             f.cand = e->cand;
             f.cand_ld = uld;
             f.cand_cnt = e->cand_cnt;
@@ -575,8 +573,8 @@ rt_status search_resident_filtered_metric(rt_engine *e, const float *queries, in
             f.ubuf = e->ubuf;
             f.uld = uld;
             f.thr = e->thr;
-            f.ub16 = bounds16 ? reinterpret_cast<const uint16_t *>(e->ubuf) : nullptr;
-            f.ub_tq = tile_q;
+            f.ub16 = reinterpret_cast<const uint16_t *>(e->ubuf);  // tile-major, q queries per tile
+            f.ub_tq = q;
             err = rt::launch_filtered_pass2(r->corpus, n, d, queries, q, p2.per_wave, p2.wgs, t2, f, s);
         }
         e->had_batch_kernel = e->profiling;

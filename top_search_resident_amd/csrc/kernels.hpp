@@ -54,7 +54,7 @@ struct FilterLaunch {
     const float *crn = nullptr;  // cosine metric: the rows' L2 norms (null: inner product)
     const uint16_t *ub16 = nullptr;  // pass 2: read 16-bit upper bounds (top halves of fp32) from here instead
     bool bounds16 = false;  // single-query passes: pass 1 writes 16-bit bounds at ubuf, pass 2 reads them there
-    int ub_tq = 0;          // with ub16: nonzero if tile-major (as launch_mfma_bound's *tile_q)
+    int ub_tq = 0;          // with ub16: nonzero if tile-major with this many queries per tile (launch_mfma_bound)
     uint64_t *cand = nullptr;     // pass 2 collect mode: candidate ranks (see launch_filtered_collect)
     int64_t cand_ld = 0;
     uint32_t *cand_cnt = nullptr;
@@ -93,18 +93,16 @@ hipError_t launch_filtered_pass2(const float *corpus, int64_t n, int d, const fl
 bool mfma_filter_ok(int d);
 void filter_bound_constants_batched(int d, float *cr, float *cx, float *delta);
 hipError_t prepare_mfma_filter();
-// Pass 1 for q <= 32 queries: upper bounds ubuf[query * uld + row] and, per
-// query, the largest lower bound of every 32-row tile, tlb[query * tld + tile].
-// rnorm[i] = |x_i|, rerr[i] >= |x_i - bf16(x_i)| (both readable up to a
-// multiple of 32 rows past n).  *bounds16 tells how the bounds were written:
-// false, fp32 at ubuf; true, 16-bit at (uint16_t *)ubuf (the top halves of
-// fp32 values rounded toward +inf), which pass 2 reads through
-// FilterLaunch::ub16.  *tile_q tells their layout: 0, query-major as above;
-// otherwise tile-major, the bound of (query j, row r) at
-// (r / 32) * 32 * tile_q + 32 j + r % 32 (FilterLaunch::ub_tq).
+// Pass 1 for q <= 32 queries: 16-bit upper bounds (the top halves of fp32
+// values rounded toward +inf) at (uint16_t *)ubuf, tile-major: the bound of
+// (query j, row r) at (r / 32) * 32 * q + 32 j + r % 32, i.e. q * roundup(n, 32)
+// entries, which pass 2 reads through FilterLaunch::ub16 with ub_tq = q; and,
+// per query, the largest lower bound of every 32-row tile, tlb[query * tld +
+// tile].  rnorm[i] = |x_i|, rerr[i] >= |x_i - bf16(x_i)| (both readable up to
+// a multiple of 32 rows past n).
 hipError_t launch_mfma_bound(const uint16_t *corpus16, int64_t n, int d, const float *queries, int q,
-                             const float *rnorm, const float *rerr, float *ubuf, int64_t uld, float *tlb, int64_t tld,
-                             int num_cus, hipStream_t stream, bool *bounds16, int *tile_q);
+                             const float *rnorm, const float *rerr, float *ubuf, float *tlb, int64_t tld,
+                             int num_cus, hipStream_t stream);
 // Per query, thr[seg] <= the k-th largest of that query's tile maxima of lower
 // bounds tmax[seg * tld + tile] (a bin edge below it; -inf when n has fewer
 // than k tiles), so at least k rows have a lower bound at or above it.

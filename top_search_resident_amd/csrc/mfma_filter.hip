@@ -16,8 +16,8 @@
 //     bf16(x_i) against the query split into two bf16 parts (q = hi + lo + r,
 //     |r| <= 2^-16 |q|), a bound e with |a - s| <= e, where s is the score the
 //     plain single-query scan computes in fp32, the upper bound a + e stored
-//     per (query, row), and per query the largest lower bound a - e of every
-//     32-row tile;
+//     per (query, row) as a 16-bit value rounded up (still an upper bound),
+//     and per query the largest lower bound a - e of every 32-row tile;
 //   pass 1b (tile_threshold_kernel, batch_select.hip): per query T = the lower
 //     edge of a key bin holding the k-th largest of those tile maxima.  k tiles
 //     reach T, each holds a row whose lower bound reaches T, so k rows have
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(NW * 64) void mfma_bound_kernel(const uint16_t *__r
                                                             const float *__restrict__ queries, int q,
                                                             const float *__restrict__ rnorm,
                                                             const float *__restrict__ rerr, float cr, float cx,
-                                                            float delta, float *__restrict__ ubuf, int64_t uld,
+                                                            float delta, uint16_t *__restrict__ ub16,
                                                             float *__restrict__ tlb, int64_t tld,
                                                             int64_t tiles_per_wave) {
     static_assert(KPF >= 1 && KPF < NCK && NCK % KPF == 0, "pipeline shape");
@@ -241,10 +241,13 @@ __global__ __launch_bounds__(NW * 64) void mfma_bound_kernel(const uint16_t *__r
                 blc[s] = bln[s];
             }
         });
-        // Bounds of the tile's rows for query m; upper bounds stored, the
+        // Bounds of the tile's rows for query m: upper bounds stored as 16-bit
+        // values rounded up, tile-major (tile t's block of 32 q entries at
+        // 32 t q, query m's rows at 32 m in it: the four stores of a tile fill
+        // its 64 q bytes, 16 contiguous bytes per query and instruction), the
         // tile's largest lower bound kept.
         float mx = -__builtin_huge_valf();
-        float *urow = ubuf + (int64_t)m * uld + t * 32 + 4 * h;
+        uint16_t *const ublk = ub16 + t * 32 * q + m * 32 + 4 * h;
 #pragma unroll
         for (int gg = 0; gg < 4; ++gg) {
             const int64_t r = t * 32 + 8 * gg + 4 * h;
@@ -260,13 +263,16 @@ __global__ __launch_bounds__(NW * 64) void mfma_bound_kernel(const uint16_t *__r
                 lbv[c] = known ? a - e : -__builtin_huge_valf();
             }
             if (r + 3 < n) {
-                if (has_q) *reinterpret_cast<float4 *>(urow + 8 * gg) = make_float4(ubv[0], ubv[1], ubv[2], ubv[3]);
+                if (has_q)
+                    *reinterpret_cast<uint2 *>(ublk + 8 * gg) =
+                        make_uint2((uint32_t)bf16_round_up_bits(ubv[0]) | ((uint32_t)bf16_round_up_bits(ubv[1]) << 16),
+                                   (uint32_t)bf16_round_up_bits(ubv[2]) | ((uint32_t)bf16_round_up_bits(ubv[3]) << 16));
                 mx = fmaxf(mx, fmaxf(fmaxf(lbv[0], lbv[1]), fmaxf(lbv[2], lbv[3])));
             } else {
 #pragma unroll
                 for (int c = 0; c < 4; ++c) {
                     if (r + c < n) {
-                        if (has_q) urow[8 * gg + c] = ubv[c];
+                        if (has_q) ublk[8 * gg + c] = bf16_round_up_bits(ubv[c]);
                         mx = fmaxf(mx, lbv[c]);
                     }
                 }
@@ -641,20 +647,16 @@ hipError_t prepare_mfma_filter() {
 }
 
 hipError_t launch_mfma_bound(const uint16_t *corpus16, int64_t n, int d, const float *queries, int q,
-                             const float *rnorm, const float *rerr, float *ubuf, int64_t uld, float *tlb, int64_t tld,
-                             int num_cus, hipStream_t stream, bool *bounds16, int *tile_q) {
+                             const float *rnorm, const float *rerr, float *ubuf, float *tlb, int64_t tld,
+                             int num_cus, hipStream_t stream) {
     const int64_t tiles = (n + 31) / 32;
-    *tile_q = 0;
     float cr, cx, delta;
     filter_bound_constants_batched(d, &cr, &cx, &delta);
-    *bounds16 = false;
     if (n >= 32) {
         const int64_t tpw = (tiles + (int64_t)num_cus * 4 - 1) / ((int64_t)num_cus * 4);
         const int64_t blocks = (tiles + tpw * 4 - 1) / (tpw * 4);
 #define RT_LAUNCH_DMA(NCK)                                                                                      \
         if (d == NCK * 64) {                                                                                    \
-            *bounds16 = true;                                                                                   \
-            *tile_q = q;                                                                                        \
             hipLaunchKernelGGL((mfma_bound_dma_kernel<NCK>), dim3((unsigned)blocks), dim3(256),                 \
                                (size_t)BoundDma<NCK>::kLds, stream, corpus16, n, queries, q, rnorm, rerr, cr, cx,  \
                                delta, reinterpret_cast<uint16_t *>(ubuf), tlb, tld, tpw);                       \
@@ -669,7 +671,7 @@ hipError_t launch_mfma_bound(const uint16_t *corpus16, int64_t n, int d, const f
         const int64_t blocks = (tiles + tpw * NW - 1) / (tpw * NW);                                             \
         hipLaunchKernelGGL((mfma_bound_kernel<NCK, NW, KPF>), dim3((unsigned)blocks), dim3(64 * NW),            \
                            bound_lds_bytes(d, NW), stream, corpus16, n, queries, q, rnorm, rerr, cr, cx, delta,  \
-                           ubuf, uld, tlb, tld, tpw);                                                           \
+                           reinterpret_cast<uint16_t *>(ubuf), tlb, tld, tpw);                                  \
         return hipGetLastError();                                                                               \
     }
     RT_BOUND_DEPTHS(RT_LAUNCH)
