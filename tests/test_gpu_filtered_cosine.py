@@ -139,3 +139,22 @@ def test_bad_metric(eng):
     q = torch.zeros((1, 256), dtype=torch.float32, device="cuda")
     with pytest.raises(ValueError):
         eng.search_resident_filtered(q, 4, metric="l2")
+
+
+def test_filtered_cosine_batch_long_wave_ranges():
+    """A cosine batch of 32 queries over 200,000 rows of depth 256 takes the
+    single-query passes with one segment per query.  On a 256-CU part that is
+    64 waves per query of 3,125 rows each, so the fp8 pass writes each wave's
+    bounds in two bursts (its LDS gather holds 2,048 rows)."""
+    n, d, k, q = 200_000, 256, 10, 32
+    e = ResidentTopK(n, d, 64, q, device=0)
+    try:
+        e.enable_filtered()
+        corpus = workloads.gaussian_rows(n, d, config_id=931)
+        qs = workloads.gaussian_rows(q, d, config_id=931, stream=1)
+        g_idx, g_sc = _both(e, corpus, qs, k, "fp8")
+        o_idx, o_sc = oracle.search(corpus, qs[:3], k, metric=1)
+        for qi in range(3):
+            check_retrieval(g_idx[qi], g_sc[qi], o_idx[qi], o_sc[qi], corpus, qs[qi], oracle, metric="cosine")
+    finally:
+        e.close()
