@@ -335,8 +335,7 @@ __global__ __launch_bounds__(256, 1) void mfma_bound_dma_kernel(const uint16_t *
                                                                 const float *__restrict__ rnorm,
                                                                 const float *__restrict__ rerr, float cr, float cx,
                                                                 float delta, uint16_t *__restrict__ ub16,
-                                                                float *__restrict__ tlb, int64_t tld,
-                                                                int64_t tiles_per_wave) {
+                                                                float *__restrict__ tlb, int64_t tld) {
     using L = BoundDma<NCK>;
     constexpr int d = NCK * 64;
     constexpr int NR = L::kRing;
@@ -351,8 +350,13 @@ __global__ __launch_bounds__(256, 1) void mfma_bound_dma_kernel(const uint16_t *
     const int h = lane >> 5;
     const int64_t wave = (int64_t)blockIdx.x * 4 + wv;
     const int64_t tiles = (n + 31) / 32;
-    const int64_t t_begin = wave * tiles_per_wave;
-    const int64_t t_end = (t_begin + tiles_per_wave < tiles) ? t_begin + tiles_per_wave : tiles;
+    // The tiles are split evenly over all waves (runs of floor or ceil of
+    // tiles / waves): with a fixed run length, at 500k rows 1024 waves of 16
+    // tiles left 11 of the 256 CUs idle (whole batch 208.5 against 202.9 us at
+    // K = 100, measured on MI355X).
+    const int64_t nwaves = (int64_t)gridDim.x * 4;
+    const int64_t t_begin = wave * tiles / nwaves;
+    const int64_t t_end = (wave + 1) * tiles / nwaves;
     char *const lo_lds = bound_lds;
     char *const wave_lds = bound_lds + L::kLoLds;
     __shared__ float qn_s[32];
@@ -653,13 +657,12 @@ hipError_t launch_mfma_bound(const uint16_t *corpus16, int64_t n, int d, const f
     float cr, cx, delta;
     filter_bound_constants_batched(d, &cr, &cx, &delta);
     if (n >= 32) {
-        const int64_t tpw = (tiles + (int64_t)num_cus * 4 - 1) / ((int64_t)num_cus * 4);
-        const int64_t blocks = (tiles + tpw * 4 - 1) / (tpw * 4);
+        const int64_t blocks = ((tiles + 3) / 4 < num_cus) ? (tiles + 3) / 4 : num_cus;
 #define RT_LAUNCH_DMA(NCK)                                                                                      \
         if (d == NCK * 64) {                                                                                    \
             hipLaunchKernelGGL((mfma_bound_dma_kernel<NCK>), dim3((unsigned)blocks), dim3(256),                 \
                                (size_t)BoundDma<NCK>::kLds, stream, corpus16, n, queries, q, rnorm, rerr, cr, cx,  \
-                               delta, reinterpret_cast<uint16_t *>(ubuf), tlb, tld, tpw);                       \
+                               delta, reinterpret_cast<uint16_t *>(ubuf), tlb, tld);                            \
             return hipGetLastError();                                                                           \
         }
         RT_BOUND_DMA(RT_LAUNCH_DMA)
